@@ -1,0 +1,384 @@
+"""Seeded synthetic inputs for paged-KV attention.
+
+This module only draws numbers and lays out block tables; it holds none of the
+attention arithmetic and none of the write indexing.  Both the fp64 oracle
+(via the tests) and the HIP library (via the tests, the smoke check and the
+benchmark) consume what it returns, so neither side can feed the other.
+
+What is generated follows the problem statement of the pages:
+
+* a pool of fixed-size blocks and a per-sequence block table of physical block
+  ids, with logical block ``b`` of a sequence covering token positions
+  ``[b*B, (b+1)*B)`` ("Build a Paged KV Cache in Pure Python", Step 2 and
+  Step 3: ``BlockAllocator`` / ``PagedKVCache.append``);
+* keys and values per sequence, shape ``(tokens, num_kv_heads, head_dim)``
+  (the per-block layout of ``KVCacheBlock`` in the same page, Step 1);
+* a query per sequence for decode, or a chunk of queries for prefill
+  ("Building a Streaming Sliding-Window Attention Engine in Pure Python",
+  Step 3 and Step 4: decode attends with the just-appended token, prefill with
+  every prompt token).
+
+Random streams.  Every array comes from its own counter-derived stream
+``numpy.random.Generator(PCG64(SeedSequence([seed, tag, index])))`` so that one
+sequence's keys/values can be regenerated alone (for sampled parity at full
+size) without drawing the rest.  Values are drawn as float32 N(0, 1), scaled,
+then rounded to nearest-even into the storage dtype; the rounded values are the
+data for both sides.
+
+Storage dtypes: ``"f32"`` -> numpy float32, ``"f16"`` -> numpy float16,
+``"bf16"`` -> numpy uint16 holding bfloat16 bit patterns (numpy has no
+bfloat16 type).
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Dict, List, Optional, Tuple
+
+import numpy as np
+
+TAG_LENGTHS = 0
+TAG_SEQ_KV = 1
+TAG_QUERY = 2
+TAG_PERM = 3
+TAG_PREFIX_KV = 4
+
+STORAGE = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16}
+ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2}
+
+
+def stream(seed: int, tag: int, index: int = 0) -> np.random.Generator:
+    """Independent PCG64 stream for (seed, tag, index)."""
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, tag, index])))
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 to bfloat16 (nearest, ties to even); return the uint16 bits."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    bias = ((u >> 16) & 1) + 0x7FFF
+    out = ((u + bias) >> 16).astype(np.uint16)
+    nan = np.isnan(x)
+    if nan.any():
+        out[nan] = 0x7FC0
+    return out
+
+
+def to_storage(x32: np.ndarray, dtype: str) -> np.ndarray:
+    """Round a float32 array into the storage dtype (see module docstring)."""
+    if dtype == "f32":
+        return np.ascontiguousarray(x32, dtype=np.float32)
+    if dtype == "f16":
+        return x32.astype(np.float16)
+    if dtype == "bf16":
+        return f32_to_bf16_bits(x32)
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def nan_fill(shape, dtype: str) -> np.ndarray:
+    """An array of quiet NaNs in the storage dtype (used to poison unused slots)."""
+    if dtype == "bf16":
+        return np.full(shape, 0x7FC0, dtype=np.uint16)
+    return np.full(shape, np.nan, dtype=STORAGE[dtype])
+
+
+def draw(rng: np.random.Generator, shape, dtype: str, scale: float = 1.0) -> np.ndarray:
+    x = rng.standard_normal(size=shape, dtype=np.float32)
+    if scale != 1.0:
+        x *= np.float32(scale)
+    return to_storage(x, dtype)
+
+
+@dataclasses.dataclass
+class SeqKV:
+    """Keys/values of one sequence for positions [start, start + len(k))."""
+    start: int
+    k: np.ndarray  # (n, Hkv, D) storage dtype
+    v: np.ndarray
+
+
+@dataclasses.dataclass
+class Workload:
+    name: str
+    kind: str  # "decode" | "prefill"
+    seed: int
+    num_seqs: int
+    num_heads: int
+    num_kv_heads: int
+    head_dim: int
+    block_size: int
+    dtype: str
+    num_blocks: int
+    max_blocks_per_seq: int
+    window: int
+    scale: float
+    context_lens: np.ndarray  # int32 [S], includes the query token(s)
+    block_tables: np.ndarray  # int32 [S, MB], -1 = unmapped
+    q: np.ndarray  # decode: [S, H, D]; prefill: [sum C, H, D]
+    seq_kv: List[SeqKV]  # per sequence; for prefill: the chunk tokens only
+    q_start: Optional[np.ndarray] = None  # prefill: int32 [S+1]
+    prefix: Optional[SeqKV] = None  # prefill: shared prefix tokens [0, P)
+    prefix_len: int = 0
+    shared_prefix_blocks: int = 0
+
+    @property
+    def max_context_len(self) -> int:
+        return int(self.context_lens.max()) if self.num_seqs else 0
+
+    @property
+    def max_q_len(self) -> int:
+        if self.q_start is None:
+            return 1
+        return int(np.diff(self.q_start).max()) if self.num_seqs else 0
+
+    def logical_kv(self, s: int) -> Tuple[int, np.ndarray, np.ndarray]:
+        """(first position, K, V) of every token of sequence s that has data."""
+        if self.kind == "prefill" and self.prefix is not None and self.prefix_len > 0:
+            k = np.concatenate([self.prefix.k, self.seq_kv[s].k], axis=0)
+            v = np.concatenate([self.prefix.v, self.seq_kv[s].v], axis=0)
+            return 0, k, v
+        e = self.seq_kv[s]
+        return e.start, e.k, e.v
+
+    def history_tokens(self):
+        """Tokens that are already in the cache before the timed step.
+
+        Yields (seq, first position, K, V) runs.  For decode this is every
+        token but the last (the step appends the query token, then attends);
+        for prefill it is the common prefix: written once through sequence 0's
+        table when its blocks are shared (the other sequences map the same
+        physical blocks), else through every sequence's own table.
+        """
+        if self.kind == "decode":
+            for s in range(self.num_seqs):
+                e = self.seq_kv[s]
+                n = e.k.shape[0] - 1
+                if n > 0:
+                    yield s, e.start, e.k[:n], e.v[:n]
+        elif self.prefix is not None and self.prefix_len > 0:
+            owners = [0] if self.shared_prefix_blocks > 0 else range(self.num_seqs)
+            for s in owners:
+                yield s, 0, self.prefix.k, self.prefix.v
+
+    def step_tokens(self):
+        """Tokens the timed step writes before attending: (seq_idx, pos, K, V)."""
+        seq_idx, pos, ks, vs = [], [], [], []
+        for s in range(self.num_seqs):
+            e = self.seq_kv[s]
+            L = int(self.context_lens[s])
+            if self.kind == "decode":
+                if L == 0:
+                    continue
+                seq_idx.append(np.array([s], np.int32))
+                pos.append(np.array([L - 1], np.int32))
+                ks.append(e.k[-1:])
+                vs.append(e.v[-1:])
+            else:
+                c = e.k.shape[0]
+                if c == 0:
+                    continue
+                seq_idx.append(np.full(c, s, np.int32))
+                pos.append(np.arange(L - c, L, dtype=np.int32))
+                ks.append(e.k)
+                vs.append(e.v)
+        shape = (0, self.num_kv_heads, self.head_dim)
+        if not seq_idx:
+            z = np.zeros(shape, STORAGE[self.dtype])
+            return np.zeros(0, np.int32), np.zeros(0, np.int32), z, z.copy()
+        return (np.concatenate(seq_idx), np.concatenate(pos),
+                np.ascontiguousarray(np.concatenate(ks)), np.ascontiguousarray(np.concatenate(vs)))
+
+    def kv_bytes_attended(self) -> int:
+        """Algorithmic K+V bytes one decode call must read: each attended
+        (token, kv-head) row once, for K and for V."""
+        eb = ELEM_BYTES[self.dtype]
+        L = self.context_lens.astype(np.int64)
+        if self.window > 0:
+            n = np.minimum(L, self.window)
+        else:
+            n = L
+        return int(n.sum()) * self.num_kv_heads * self.head_dim * 2 * eb
+
+
+def _deal_tables(rng_perm, blocks_per_seq: List[int], first_block: List[int], mb: int,
+                 num_blocks: int) -> np.ndarray:
+    """Hand out shuffled physical ids in sequence order; -1 elsewhere."""
+    perm = rng_perm.permutation(num_blocks).astype(np.int32)
+    tables = np.full((len(blocks_per_seq), mb), -1, dtype=np.int32)
+    at = 0
+    for s, (n, b0) in enumerate(zip(blocks_per_seq, first_block)):
+        tables[s, b0:b0 + n] = perm[at:at + n]
+        at += n
+    return tables
+
+
+def make_decode(*, lens, num_heads, num_kv_heads, head_dim, block_size, dtype, seed,
+                window=0, scale=None, k_scale=1.0, max_blocks_per_seq=None,
+                spare_blocks=0, name="decode") -> Workload:
+    """A batched single-query decode workload.
+
+    ``lens[s]`` is the context length of sequence s including the query token.
+    With ``window > 0`` only blocks that hold a position in ``[L-window, L)``
+    are mapped; table entries of blocks that end at or before ``L-window``
+    are -1 (freed).
+    """
+    lens = np.asarray(lens, dtype=np.int64)
+    S = len(lens)
+    B = block_size
+    first_block, nblocks, starts = [], [], []
+    for L in lens:
+        L = int(L)
+        if L == 0:
+            first_block.append(0)
+            nblocks.append(0)
+            starts.append(0)
+            continue
+        lo = max(0, L - window) if window > 0 else 0
+        b0 = lo // B
+        b1 = (L + B - 1) // B
+        first_block.append(b0)
+        nblocks.append(b1 - b0)
+        starts.append(b0 * B)
+    need_mb = max([b + n for b, n in zip(first_block, nblocks)] + [1])
+    mb = max_blocks_per_seq if max_blocks_per_seq is not None else need_mb
+    if mb < need_mb:
+        raise ValueError("max_blocks_per_seq too small")
+    nb = int(sum(nblocks)) + int(spare_blocks)
+    nb = max(nb, 1)
+    tables = _deal_tables(stream(seed, TAG_PERM), nblocks, first_block, mb, nb)
+    seq_kv = []
+    for s in range(S):
+        L = int(lens[s])
+        n = L - starts[s]
+        rng = stream(seed, TAG_SEQ_KV, s)
+        k = draw(rng, (n, num_kv_heads, head_dim), dtype, k_scale)
+        v = draw(rng, (n, num_kv_heads, head_dim), dtype)
+        seq_kv.append(SeqKV(starts[s], k, v))
+    q = draw(stream(seed, TAG_QUERY), (S, num_heads, head_dim), dtype)
+    if scale is None:
+        scale = 1.0 / math.sqrt(head_dim)
+    return Workload(name=name, kind="decode", seed=seed, num_seqs=S, num_heads=num_heads,
+                    num_kv_heads=num_kv_heads, head_dim=head_dim, block_size=B, dtype=dtype,
+                    num_blocks=nb, max_blocks_per_seq=mb, window=window, scale=float(scale),
+                    context_lens=lens.astype(np.int32), block_tables=tables, q=q, seq_kv=seq_kv)
+
+
+def make_prefill(*, prefix_len, chunk_lens, num_heads, num_kv_heads, head_dim, block_size,
+                 dtype, seed, window=0, scale=None, share_prefix=True, max_blocks_per_seq=None,
+                 name="prefill") -> Workload:
+    """Chunked prefill: every sequence has a common prefix of ``prefix_len``
+    tokens (already cached) followed by its own chunk of ``chunk_lens[s]``
+    query tokens.  With ``share_prefix`` the prefix blocks are one set of
+    physical blocks mapped by every table (``prefix_len`` must then be a
+    multiple of the block size); otherwise each sequence gets private copies.
+    """
+    chunk_lens = [int(c) for c in chunk_lens]
+    S = len(chunk_lens)
+    B = block_size
+    if share_prefix and prefix_len % B:
+        raise ValueError("a shared prefix must end on a block boundary")
+    pb = prefix_len // B if share_prefix else 0
+    lens = np.array([prefix_len + c for c in chunk_lens], dtype=np.int64)
+    priv = [((int(L) + B - 1) // B) - pb for L in lens]
+    need_mb = max([pb + p for p in priv] + [1])
+    mb = max_blocks_per_seq if max_blocks_per_seq is not None else need_mb
+    nb = max(pb + sum(priv), 1)
+    perm = stream(seed, TAG_PERM).permutation(nb).astype(np.int32)
+    tables = np.full((S, mb), -1, dtype=np.int32)
+    at = pb
+    for s in range(S):
+        tables[s, :pb] = perm[:pb]
+        tables[s, pb:pb + priv[s]] = perm[at:at + priv[s]]
+        at += priv[s]
+    rng = stream(seed, TAG_PREFIX_KV)
+    prefix = SeqKV(0, draw(rng, (prefix_len, num_kv_heads, head_dim), dtype),
+                   draw(rng, (prefix_len, num_kv_heads, head_dim), dtype))
+    seq_kv = []
+    for s in range(S):
+        rng = stream(seed, TAG_SEQ_KV, s)
+        k = draw(rng, (chunk_lens[s], num_kv_heads, head_dim), dtype)
+        v = draw(rng, (chunk_lens[s], num_kv_heads, head_dim), dtype)
+        seq_kv.append(SeqKV(prefix_len, k, v))
+    q_start = np.zeros(S + 1, dtype=np.int32)
+    q_start[1:] = np.cumsum(chunk_lens)
+    q = draw(stream(seed, TAG_QUERY), (int(q_start[-1]), num_heads, head_dim), dtype)
+    if scale is None:
+        scale = 1.0 / math.sqrt(head_dim)
+    return Workload(name=name, kind="prefill", seed=seed, num_seqs=S, num_heads=num_heads,
+                    num_kv_heads=num_kv_heads, head_dim=head_dim, block_size=B, dtype=dtype,
+                    num_blocks=nb, max_blocks_per_seq=mb, window=window, scale=float(scale),
+                    context_lens=lens.astype(np.int32), block_tables=tables, q=q, seq_kv=seq_kv,
+                    q_start=q_start, prefix=prefix, prefix_len=prefix_len,
+                    shared_prefix_blocks=pb)
+
+
+def private_prefix_copy(w: Workload, seed_perm: int = 7) -> Workload:
+    """The same prefill workload with the shared prefix blocks replaced by a
+    private copy per sequence (physical ids reshuffled)."""
+    assert w.kind == "prefill"
+    B = w.block_size
+    S = w.num_seqs
+    nblk = [int((int(L) + B - 1) // B) for L in w.context_lens]
+    nb = sum(nblk)
+    mb = max(nblk + [w.max_blocks_per_seq])
+    perm = stream(seed_perm, TAG_PERM).permutation(nb).astype(np.int32)
+    tables = np.full((S, mb), -1, dtype=np.int32)
+    at = 0
+    for s in range(S):
+        tables[s, :nblk[s]] = perm[at:at + nblk[s]]
+        at += nblk[s]
+    return dataclasses.replace(w, num_blocks=nb, max_blocks_per_seq=mb, block_tables=tables,
+                               shared_prefix_blocks=0)
+
+
+def repermute(w: Workload, seed_perm: int) -> Workload:
+    """The same decode workload with a different physical block assignment."""
+    assert w.kind == "decode"
+    mapped = w.block_tables >= 0
+    ids = w.block_tables[mapped]
+    rng = stream(seed_perm, TAG_PERM)
+    relabel = rng.permutation(w.num_blocks).astype(np.int32)
+    tables = w.block_tables.copy()
+    tables[mapped] = relabel[ids]
+    return dataclasses.replace(w, block_tables=tables)
+
+
+# The five workloads: a tiny fp32 decode, batched MHA decode, long-context GQA
+# decode, sliding-window decode and chunked prefill over a shared prefix.
+CONFIG_NAMES = {
+    1: "tiny_decode_mha4_d64_b16_L100_f32",
+    2: "batched_mha_decode_s32_h32_d128_b16_f16",
+    3: "gqa_long_decode_s64_h32kv8_d128_b32_bf16",
+    4: "sliding_window_decode_s16_h32kv8_d128_b16_w4096_bf16",
+    5: "chunked_prefill_shared_prefix_s8_h32kv8_d128_b16_bf16",
+}
+
+
+def config(idx: int, seed: Optional[int] = None) -> Workload:
+    """Build one of the five workloads.  ``seed`` defaults to the index."""
+    seed = idx if seed is None else seed
+    name = CONFIG_NAMES[idx]
+    if idx == 1:
+        return make_decode(lens=[100], num_heads=4, num_kv_heads=4, head_dim=64, block_size=16,
+                           dtype="f32", seed=seed, scale=1.0 / 8.0, spare_blocks=9, name=name)
+    if idx == 2:
+        lens = stream(seed, TAG_LENGTHS).integers(512, 4097, size=32)
+        return make_decode(lens=lens, num_heads=32, num_kv_heads=32, head_dim=128, block_size=16,
+                           dtype="f16", seed=seed, max_blocks_per_seq=256, name=name)
+    if idx == 3:
+        u = stream(seed, TAG_LENGTHS).uniform(math.log(1024), math.log(32768), size=64)
+        lens = np.clip(np.floor(np.exp(u)), 1024, 32768).astype(np.int64)
+        return make_decode(lens=lens, num_heads=32, num_kv_heads=8, head_dim=128, block_size=32,
+                           dtype="bf16", seed=seed, k_scale=3.0, max_blocks_per_seq=1024,
+                           name=name)
+    if idx == 4:
+        lens = stream(seed, TAG_LENGTHS).integers(16384, 32769, size=16)
+        live = sum(((int(L) + 15) // 16) - max(0, int(L) - 4096) // 16 for L in lens)
+        return make_decode(lens=lens, num_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
+                           dtype="bf16", seed=seed, window=4096, max_blocks_per_seq=2048,
+                           spare_blocks=(live + 9) // 10, name=name)
+    if idx == 5:
+        return make_prefill(prefix_len=2048, chunk_lens=[512] * 8, num_heads=32, num_kv_heads=8,
+                            head_dim=128, block_size=16, dtype="bf16", seed=seed,
+                            max_blocks_per_seq=160, name=name)
+    raise KeyError(idx)
