@@ -1,0 +1,242 @@
+#!/usr/bin/env python3
+"""Throughput of the paged-KV attention hot path on one MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic,
+seeded input already resident in HBM: write the step's new tokens' K/V into
+their pool slots through the block table (``paged_kv_write``), then attend
+(``paged_attn_decode`` for the decode workloads, ``paged_attn_prefill`` for
+the chunked-prefill one).  W untimed warm-up steps, then exactly K timed
+steps between two device synchronisations; HIP events on the launch stream
+also time the write and the attention call of every step.
+
+Prints one JSON line.  ``value`` is the algorithmic bytes one step must move
+(decode: every attended K/V row once per kv head, queries, outputs, table
+entries; plus the write's read and store) per second, or the algorithmic
+FLOP of the prefill (4 * head_dim per unmasked query/key pair and head) per
+second.  ``roofline`` relates the attention call alone to MI355X's peak (HBM
+8 TB/s; dense bf16/fp16 MFMA 2.5 PFLOP/s).  ``cpu_baseline`` times the fp64
+oracle on the host on a bounded sample of the same workload.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--config 2]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "paged decode attention KV-read GB/s (% of HBM peak); prefill TFLOP/s (% MFMA)"
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0}
+
+
+def decode_bytes(w) -> dict:
+    """Algorithmic bytes of one decode call and of the step's write."""
+    import numpy as np
+    eb = {"f32": 4, "f16": 2, "bf16": 2}[w.dtype]
+    S, H, D, B = w.num_seqs, w.num_heads, w.head_dim, w.block_size
+    L = w.context_lens.astype(np.int64)
+    lo = np.maximum(0, L - w.window) if w.window > 0 else np.zeros_like(L)
+    blocks = np.where(L > 0, (L + B - 1) // B - lo // B, 0)
+    attend = (w.kv_bytes_attended() + S * H * D * eb + S * H * D * 4 + S * H * 4
+              + int(blocks.sum()) * 4 + S * 4)
+    T = int((L > 0).sum())
+    write = T * w.num_kv_heads * D * eb * 2 * 2 + T * 8 + T * 4
+    return {"attend": attend, "write": write, "kv": w.kv_bytes_attended()}
+
+
+def prefill_flop(w) -> int:
+    """4 * D per unmasked (query, key) pair, per query head."""
+    total = 0
+    for s in range(w.num_seqs):
+        C = int(w.q_start[s + 1] - w.q_start[s])
+        L = int(w.context_lens[s])
+        for i in range(C):
+            p = L - C + i
+            n = p + 1 if w.window <= 0 else min(p + 1, w.window)
+            total += n
+    return 4 * w.head_dim * w.num_heads * total
+
+
+def source_hash(*names) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "paged_kv_cache_30_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel_key: str, src: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if
+    it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        rec = json.load(open(path)).get(kernel_key)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_hash") != src:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(w, target_s: float):
+    """fp64 oracle on the host, one thread, on the first sequences of the
+    workload until about target_s seconds of work (whole workload if less)."""
+    import numpy as np
+    import oracle.ref as ref
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    kp, vp = ref.build_pools(w)
+    import contextlib
+    ctx = threadpool_limits(limits=1) if threadpool_limits else contextlib.nullcontext()
+    eb = {"f32": 4, "f16": 2, "bf16": 2}[w.dtype]
+    done, elapsed, units = 0, 0.0, 0.0
+    with ctx:
+        while done < w.num_seqs and elapsed < target_s:
+            t = time.perf_counter()
+            if w.kind == "decode":
+                ref.decode(w.q, kp, vp, w.block_tables, w.context_lens, block_size=w.block_size,
+                           num_kv_heads=w.num_kv_heads, window=w.window, scale=w.scale, dtype=w.dtype,
+                           seqs=[done])
+                L = int(w.context_lens[done])
+                n = min(L, w.window) if w.window > 0 else L
+                units += n * w.num_kv_heads * w.head_dim * 2 * eb
+            else:
+                ref.prefill(w.q, w.q_start, kp, vp, w.block_tables, w.context_lens, block_size=w.block_size,
+                            num_kv_heads=w.num_kv_heads, window=w.window, scale=w.scale, dtype=w.dtype,
+                            seqs=[done])
+                C = int(w.q_start[done + 1] - w.q_start[done])
+                L = int(w.context_lens[done])
+                pairs = sum((L - C + i + 1) if w.window <= 0 else min(L - C + i + 1, w.window) for i in range(C))
+                units += 4 * w.head_dim * w.num_heads * pairs
+            elapsed += time.perf_counter() - t
+            done += 1
+    if w.kind == "decode":
+        value, unit = units / elapsed / 1e9, "GB/s"
+    else:
+        value, unit = units / elapsed / 1e12, "TFLOP/s"
+    return {"value": round(value, 4), "unit": unit, "cores": 1, "kind": "oracle",
+            "sample": f"first {done} of {w.num_seqs} sequences (all heads), fp64 NumPy oracle, "
+                      f"{elapsed:.2f} s, one BLAS thread"}
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5],
+                    help="workload: 1 tiny fp32 decode, 2 batched MHA decode (default), 3 long GQA decode, "
+                         "4 sliding-window decode, 5 chunked prefill over a shared prefix")
+    ap.add_argument("--seed", type=int, default=None)
+    ap.add_argument("--partition", type=int, default=0, help="decode partition length (0 = automatic)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the decode and prefill paths "
+              "shard by sequence or kv head with no exchange, which this build does not launch.",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    import workloads as wl
+    from paged_kv_cache_30_amd import session
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    torch.cuda.set_device(0)
+    w = wl.config(args.config, args.seed)
+    d = session.DeviceWorkload(w, partition_size=args.partition)
+    torch.cuda.synchronize()
+
+    for _ in range(args.warmup):
+        d.step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record()
+    for i in range(K):
+        ev[i][0].record()
+        d.write_step()
+        ev[i][1].record()
+        d.attend()
+        ev[i][2].record()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_total = start.elapsed_time(end)
+    ms_step = ms_total / K
+    write_ms = sorted(e[0].elapsed_time(e[1]) for e in ev)
+    attend_ms = sorted(e[1].elapsed_time(e[2]) for e in ev)
+    att_mean = sum(attend_ms) / K
+    att_med = attend_ms[K // 2]
+
+    if w.kind == "decode":
+        by = decode_bytes(w)
+        step_units = by["attend"] + by["write"]
+        value = step_units / (ms_step * 1e-3) / 1e9
+        unit = "GB/s"
+        achieved = by["attend"] / (att_mean * 1e-3) / 1e9
+        src = source_hash("decode.hip", "common.h")
+        key = f"paged_attn_decode|{w.name}"
+        roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_for(key, src)}
+        n_part_info = {"partition_size": args.partition or None}
+    else:
+        flop = prefill_flop(w)
+        value = flop / (ms_step * 1e-3) / 1e12
+        unit = "TFLOP/s"
+        achieved = flop / (att_mean * 1e-3) / 1e12
+        src = source_hash("prefill.hip", "common.h")
+        key = f"paged_attn_prefill|{w.name}"
+        peak = MFMA_PEAK_TFLOPS[w.dtype]
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4), "traffic": traffic_for(key, src)}
+        n_part_info = {}
+
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": unit,
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded, shapes and distributions of the workload)",
+        "config": {"workload": w.name, "kind": w.kind, "num_seqs": w.num_seqs, "num_heads": w.num_heads,
+                   "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "block_size": w.block_size,
+                   "window": w.window, "max_context_len": w.max_context_len,
+                   "total_context": int(w.context_lens.sum()), "seed": w.seed, **n_part_info},
+        "roofline": roof,
+        "timing": {"attend_ms_mean": round(att_mean, 5), "attend_ms_median": round(att_med, 5),
+                   "attend_ms_min": round(attend_ms[0], 5), "write_ms_mean": round(sum(write_ms) / K, 5),
+                   "wall_s_timed": round(wall, 4), "source_hash": src},
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,198 @@
+/*
+ * paged_attn.h - C ABI of the paged-KV attention library (gfx950 / MI355X).
+ *
+ * Scaled dot-product attention that reads keys and values through a block
+ * table from a paged KV cache: single-query decode (batched, ragged lengths,
+ * grouped query heads, optional sliding window) and causal chunked prefill
+ * over the same pages, plus the write of new tokens' keys/values into their
+ * pool slots.
+ *
+ * Sources (page title, section):
+ *  - "Build a Paged KV Cache in Pure Python": Step 1 (a block holds keys and
+ *    values of block_size positions for every head, shape
+ *    (block_size, num_heads, head_dim)), Step 2 (a pool of blocks handed out
+ *    from a free list), Step 3 (append: block = table[pos // block_size],
+ *    slot = pos % block_size; retrieve: blocks in table order, the last one
+ *    cut to the positions present), Step 4 (attention of one query per head
+ *    over the retrieved keys: scaled scores, max-subtracted softmax over the
+ *    keys, weighted sum of values; empty -> zeros), Step 5 (keys/values are
+ *    appended before the query attends).
+ *  - "Build a Minimal LLM Inference Engine with Paged Attention and Adaptive
+ *    KV Cache": Step 1 (block table: a sequence's list of physical page ids)
+ *    and Step 4 (gather through the table, then attend).
+ *  - "Building a Streaming Sliding-Window Attention Engine in Pure Python":
+ *    Step 3 (sliding window: the query at position i sees keys in
+ *    [i - w + 1, i]; prefill mask j <= i and i - j < w).
+ *
+ * Conventions shared by every entry point
+ *  - Every pointer argument except `geom` and `stream` is DEVICE memory
+ *    (allocated by the caller, e.g. through torch); `geom` is host memory.
+ *    The library never allocates, frees or keeps device memory and keeps no
+ *    state between calls.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream). All
+ *    work is enqueued on it; nothing synchronises. Results are valid once
+ *    the stream reaches them.
+ *  - Pools: K and V each [num_blocks, block_size, num_kv_heads, head_dim],
+ *    row-major, element type kv_dtype. Position t of sequence s lives in
+ *    block block_tables[s * max_blocks_per_seq + t / block_size], slot
+ *    t % block_size.
+ *  - block_tables: int32 [num_seqs, max_blocks_per_seq]; -1 = unmapped.
+ *  - Query head h reads kv head h / (num_heads / num_kv_heads).
+ *  - Outputs are float32.
+ *  - Return value: PKV_OK, or a negative status (pkv_status_string names it).
+ *    Argument checks are synchronous and enqueue nothing when they fail.
+ *    Device-resident contents (table entries, lengths) are not validated on
+ *    the host; see each call for what the kernels do with out-of-range
+ *    entries (they are skipped, never dereferenced).
+ */
+#ifndef PAGED_ATTN_H
+#define PAGED_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types of pools, queries and new keys/values. */
+enum { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2 };
+
+/* Status codes. */
+enum {
+  PKV_OK = 0,
+  PKV_EINVAL = -1,        /* bad argument (null pointer, negative size, ...) */
+  PKV_EUNSUPPORTED = -2,  /* valid but not built: head_dim, block_size, dtype, group size */
+  PKV_EWORKSPACE = -3,    /* workspace missing or smaller than the query says */
+  PKV_EHIP = -4           /* a HIP launch failed; pkv_last_hip_error() has the code */
+};
+
+/* Cache geometry (host struct).
+ *   num_blocks    NB, blocks in each pool (> 0)
+ *   block_size    B, positions per block: 16 or 32
+ *   num_heads     H, query heads
+ *   num_kv_heads  Hkv, key/value heads; H % Hkv == 0, H / Hkv in {1, 2, 4, 8}
+ *   head_dim      D: 64 or 128
+ *   kv_dtype      PKV_F32, PKV_F16 or PKV_BF16 (pools, q, k_new, v_new) */
+typedef struct pkv_geometry {
+  int32_t num_blocks;
+  int32_t block_size;
+  int32_t num_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t kv_dtype;
+} pkv_geometry_t;
+
+/* paged_kv_write - store new tokens' keys and values in their pool slots.
+ *
+ * "Build a Paged KV Cache in Pure Python", Step 3 (append): token n of
+ * sequence seq_idx[n] at position pos[n] goes to block
+ * block_tables[seq_idx[n]][pos[n] / B], slot pos[n] % B; its whole
+ * [num_kv_heads, head_dim] row of keys and of values is copied bit for bit.
+ * No other byte of either pool changes.
+ *
+ *   k_pool, v_pool   [NB, B, Hkv, D] kv_dtype, written in place
+ *   k_new, v_new     [num_tokens, Hkv, D] kv_dtype
+ *   seq_idx, pos     int32 [num_tokens]
+ *   block_tables     int32 [num_seqs, max_blocks_per_seq]
+ * A token whose sequence index is outside [0, num_seqs), whose position is
+ * negative or past max_blocks_per_seq * B, or whose table entry is outside
+ * [0, NB), is skipped (nothing is written for it). Two tokens mapping to the
+ * same slot race; callers give distinct slots. num_tokens == 0 is a no-op. */
+int paged_kv_write(const pkv_geometry_t* geom, void* k_pool, void* v_pool,
+                   const void* k_new, const void* v_new,
+                   const int32_t* seq_idx, const int32_t* pos, int32_t num_tokens,
+                   const int32_t* block_tables, int32_t num_seqs, int32_t max_blocks_per_seq,
+                   void* stream);
+
+/* Bytes of workspace paged_attn_decode needs for these sizes (0 when the
+ * call runs as one pass). partition_size as for paged_attn_decode.
+ * Returns 0 for invalid arguments too; paged_attn_decode reports those. */
+size_t paged_attn_decode_workspace_bytes(const pkv_geometry_t* geom, int32_t num_seqs,
+                                         int32_t max_context_len, int32_t window,
+                                         int32_t partition_size);
+
+/* The partition length (positions) paged_attn_decode uses for
+ * partition_size == 0 with these sizes. */
+int32_t paged_attn_decode_auto_partition(const pkv_geometry_t* geom, int32_t num_seqs,
+                                         int32_t max_context_len, int32_t window);
+
+/* paged_attn_decode - one query token per sequence attends its cached
+ * context through the block table.
+ *
+ * "Build a Paged KV Cache in Pure Python", Step 4, and "Building a Streaming
+ * Sliding-Window Attention Engine in Pure Python", Step 3: for sequence s
+ * with context length L = context_lens[s] (which includes the query token,
+ * already written: the query sits at position L - 1) and query head h,
+ *   lo = window > 0 ? max(0, L - window) : 0
+ *   score_t = scale * sum_d q[s,h,d] * K[t, h / G, d]      for t in [lo, L)
+ *   out[s,h,:] = sum_t softmax(score)_t * V[t, h / G, :]
+ *   lse[s,h]  = log(sum_t exp(score_t))   (natural log)
+ * L == 0 gives out = 0 and lse = -inf.
+ *
+ *   out           float32 [num_seqs, H, D]
+ *   lse           float32 [num_seqs, H], or NULL
+ *   q             kv_dtype [num_seqs, H, D]
+ *   k_pool/v_pool [NB, B, Hkv, D] kv_dtype
+ *   context_lens  int32 [num_seqs], each in [0, max_context_len]
+ *   max_context_len  host bound on context_lens (<= max_blocks_per_seq * B)
+ *   window        0 = attend everything, else the last `window` positions
+ *   scale         score scale, typically 1/sqrt(D)
+ *   partition_size  positions per split-K partition: 0 = automatic, else a
+ *                 positive multiple of block_size. The context is split into
+ *                 partitions attended independently (running max and sum per
+ *                 partition) and merged exactly by a second pass.
+ *   workspace     device scratch of >= paged_attn_decode_workspace_bytes()
+ *                 bytes (may be NULL when that is 0)
+ * Table entries of attended blocks that are -1 or >= NB are skipped: their
+ * positions contribute nothing. The partially covered first block of a
+ * window must stay mapped. */
+int paged_attn_decode(const pkv_geometry_t* geom, float* out, float* lse, const void* q,
+                      const void* k_pool, const void* v_pool,
+                      const int32_t* block_tables, int32_t max_blocks_per_seq,
+                      const int32_t* context_lens, int32_t num_seqs, int32_t max_context_len,
+                      int32_t window, float scale, int32_t partition_size,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* paged_attn_prefill - causal attention of a chunk of query tokens per
+ * sequence over everything cached before them and the chunk itself.
+ *
+ * "Building a Streaming Sliding-Window Attention Engine in Pure Python",
+ * Step 3 (prefill mask: causal, and i - j < w with a window) and Step 4
+ * (keys/values are in the cache before attention), read for a chunk that
+ * follows a cached prefix: sequence s owns query rows
+ * [q_start[s], q_start[s+1]); its chunk of C = q_start[s+1] - q_start[s]
+ * rows are its last C positions, so row i sits at p = L - C + i with
+ * L = context_lens[s] (the chunk's keys/values are already written). Row i
+ * of head h attends positions t with t <= p and, when window > 0,
+ * t > p - window; the result is the same softmax-weighted sum as decode.
+ *
+ *   out     float32 [q_start[num_seqs], H, D]
+ *   lse     float32 [q_start[num_seqs], H], or NULL
+ *   q       kv_dtype [q_start[num_seqs], H, D] (PKV_F16 or PKV_BF16 only)
+ *   q_start int32 [num_seqs + 1], non-decreasing, q_start[0] == 0
+ *   max_q_len        host bound on the chunk lengths
+ *   max_context_len  host bound on context_lens (<= max_blocks_per_seq * B)
+ * Requires C <= L for every sequence. Scores and outputs accumulate in
+ * float32; the softmax weights are rounded to kv_dtype before they multiply
+ * V on the matrix cores. */
+int paged_attn_prefill(const pkv_geometry_t* geom, float* out, float* lse, const void* q,
+                       const int32_t* q_start, const void* k_pool, const void* v_pool,
+                       const int32_t* block_tables, int32_t max_blocks_per_seq,
+                       const int32_t* context_lens, int32_t num_seqs, int32_t max_q_len,
+                       int32_t max_context_len, int32_t window, float scale, void* stream);
+
+/* Name of a status code (static string). */
+const char* pkv_status_string(int status);
+
+/* hipError_t of the most recent PKV_EHIP returned on the calling thread. */
+int pkv_last_hip_error(void);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int pkv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGED_ATTN_H */

@@ -1,0 +1,198 @@
+"""ctypes binding of ``libpagedattn.so`` (argument marshalling only).
+
+Every function here takes torch tensors for device memory, reads their data
+pointers, shapes and the current HIP stream, and calls the C entry point of
+the same name; the computation is entirely in the library's kernels.  A
+missing library raises at import time: there is no fallback.
+
+The library is loaded after torch so that the HIP runtime torch already
+mapped serves both (same soname).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.environ.get("PKV_LIBRARY", os.path.join(_HERE, "libpagedattn.so"))
+
+PKV_F32, PKV_F16, PKV_BF16 = 0, 1, 2
+PKV_OK, PKV_EINVAL, PKV_EUNSUPPORTED, PKV_EWORKSPACE, PKV_EHIP = 0, -1, -2, -3, -4
+
+_DTYPES = {torch.float32: PKV_F32, torch.float16: PKV_F16, torch.bfloat16: PKV_BF16}
+
+# Every symbol declared in include/paged_attn.h.
+EXPORTS = ("paged_kv_write", "paged_attn_decode_workspace_bytes", "paged_attn_decode_auto_partition",
+           "paged_attn_decode", "paged_attn_prefill", "pkv_status_string", "pkv_last_hip_error",
+           "pkv_version")
+
+
+class Geometry(ctypes.Structure):
+    _fields_ = [("num_blocks", ctypes.c_int32), ("block_size", ctypes.c_int32),
+                ("num_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("kv_dtype", ctypes.c_int32)]
+
+
+class PagedAttnError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python -m paged_kv_cache_30_amd.build` "
+            "(the HIP library is the only implementation)")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, SZ, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_float
+    G = ctypes.POINTER(Geometry)
+    lib.paged_kv_write.argtypes = [G, P, P, P, P, P, P, I32, P, I32, I32, P]
+    lib.paged_kv_write.restype = ctypes.c_int
+    lib.paged_attn_decode_workspace_bytes.argtypes = [G, I32, I32, I32, I32]
+    lib.paged_attn_decode_workspace_bytes.restype = SZ
+    lib.paged_attn_decode_auto_partition.argtypes = [G, I32, I32, I32]
+    lib.paged_attn_decode_auto_partition.restype = I32
+    lib.paged_attn_decode.argtypes = [G, P, P, P, P, P, P, I32, P, I32, I32, I32, F, I32, P, SZ, P]
+    lib.paged_attn_decode.restype = ctypes.c_int
+    lib.paged_attn_prefill.argtypes = [G, P, P, P, P, P, P, P, I32, P, I32, I32, I32, I32, F, P]
+    lib.paged_attn_prefill.restype = ctypes.c_int
+    lib.pkv_status_string.argtypes = [ctypes.c_int]
+    lib.pkv_status_string.restype = ctypes.c_char_p
+    lib.pkv_last_hip_error.argtypes = []
+    lib.pkv_last_hip_error.restype = ctypes.c_int
+    lib.pkv_version.argtypes = []
+    lib.pkv_version.restype = ctypes.c_int
+    return lib
+
+
+LIB = _load()
+
+
+def _check(status: int, what: str) -> None:
+    if status != PKV_OK:
+        msg = LIB.pkv_status_string(status).decode()
+        if status == PKV_EHIP:
+            msg += f" (hipError {LIB.pkv_last_hip_error()})"
+        raise PagedAttnError(status, f"{what}: {msg}")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None, ndim=None) -> torch.Tensor:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions")
+    return t
+
+
+def geometry(k_pool: torch.Tensor, num_heads: int) -> Geometry:
+    """Geometry of a [NB, B, Hkv, D] pool with ``num_heads`` query heads."""
+    if k_pool.dim() != 4:
+        raise ValueError("pool must be [num_blocks, block_size, num_kv_heads, head_dim]")
+    if k_pool.dtype not in _DTYPES:
+        raise ValueError(f"unsupported pool dtype {k_pool.dtype}")
+    nb, b, hkv, d = k_pool.shape
+    return Geometry(nb, b, num_heads, hkv, d, _DTYPES[k_pool.dtype])
+
+
+def paged_kv_write(k_pool, v_pool, k_new, v_new, seq_idx, pos, block_tables, stream=None) -> None:
+    """C ``paged_kv_write``: store k_new/v_new [T, Hkv, D] at (seq_idx, pos)."""
+    _dev(k_pool, "k_pool", ndim=4)
+    _dev(v_pool, "v_pool", dtype=k_pool.dtype)
+    if v_pool.shape != k_pool.shape:
+        raise ValueError("k_pool and v_pool differ in shape")
+    _dev(k_new, "k_new", dtype=k_pool.dtype, ndim=3)
+    _dev(v_new, "v_new", dtype=k_pool.dtype, ndim=3)
+    _dev(seq_idx, "seq_idx", dtype=torch.int32, ndim=1)
+    _dev(pos, "pos", dtype=torch.int32, ndim=1)
+    _dev(block_tables, "block_tables", dtype=torch.int32, ndim=2)
+    T = k_new.shape[0]
+    if k_new.shape[1:] != k_pool.shape[2:] or v_new.shape != k_new.shape:
+        raise ValueError("k_new/v_new must be [T, num_kv_heads, head_dim]")
+    if seq_idx.shape[0] != T or pos.shape[0] != T:
+        raise ValueError("seq_idx and pos need one entry per token")
+    g = geometry(k_pool, k_pool.shape[2])
+    _check(LIB.paged_kv_write(ctypes.byref(g), _ptr(k_pool), _ptr(v_pool), _ptr(k_new), _ptr(v_new),
+                              _ptr(seq_idx), _ptr(pos), T, _ptr(block_tables), block_tables.shape[0],
+                              block_tables.shape[1], _stream(stream)), "paged_kv_write")
+
+
+def paged_attn_decode_workspace_bytes(k_pool, num_heads, num_seqs, max_context_len, window=0,
+                                      partition_size=0) -> int:
+    g = geometry(k_pool, num_heads)
+    return int(LIB.paged_attn_decode_workspace_bytes(ctypes.byref(g), num_seqs, max_context_len, window,
+                                                     partition_size))
+
+
+def paged_attn_decode_auto_partition(k_pool, num_heads, num_seqs, max_context_len, window=0) -> int:
+    g = geometry(k_pool, num_heads)
+    return int(LIB.paged_attn_decode_auto_partition(ctypes.byref(g), num_seqs, max_context_len, window))
+
+
+def paged_attn_decode(out, q, k_pool, v_pool, block_tables, context_lens, max_context_len, *,
+                      window=0, scale, partition_size=0, workspace=None, lse=None, stream=None) -> None:
+    """C ``paged_attn_decode``: out[S, H, D] (fp32) for q[S, H, D]."""
+    _dev(q, "q", dtype=k_pool.dtype, ndim=3)
+    _dev(out, "out", dtype=torch.float32, ndim=3)
+    _dev(k_pool, "k_pool", ndim=4)
+    _dev(v_pool, "v_pool", dtype=k_pool.dtype)
+    _dev(block_tables, "block_tables", dtype=torch.int32, ndim=2)
+    _dev(context_lens, "context_lens", dtype=torch.int32, ndim=1)
+    S, H, D = q.shape
+    if out.shape != q.shape or context_lens.shape[0] != S or block_tables.shape[0] != S:
+        raise ValueError("shape mismatch between q, out, context_lens and block_tables")
+    if lse is not None:
+        _dev(lse, "lse", dtype=torch.float32, ndim=2)
+        if lse.shape != (S, H):
+            raise ValueError("lse must be [S, H]")
+    ws_bytes = 0
+    if workspace is not None:
+        _dev(workspace, "workspace")
+        ws_bytes = workspace.numel() * workspace.element_size()
+    g = geometry(k_pool, H)
+    _check(LIB.paged_attn_decode(ctypes.byref(g), _ptr(out), _ptr(lse), _ptr(q), _ptr(k_pool), _ptr(v_pool),
+                                 _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), S,
+                                 int(max_context_len), int(window), float(scale), int(partition_size),
+                                 _ptr(workspace), ws_bytes, _stream(stream)), "paged_attn_decode")
+
+
+def paged_attn_prefill(out, q, q_start, k_pool, v_pool, block_tables, context_lens, max_q_len,
+                       max_context_len, *, window=0, scale, lse=None, stream=None) -> None:
+    """C ``paged_attn_prefill``: out[T, H, D] (fp32) for chunk queries q[T, H, D]."""
+    _dev(q, "q", dtype=k_pool.dtype, ndim=3)
+    _dev(out, "out", dtype=torch.float32, ndim=3)
+    _dev(q_start, "q_start", dtype=torch.int32, ndim=1)
+    _dev(k_pool, "k_pool", ndim=4)
+    _dev(v_pool, "v_pool", dtype=k_pool.dtype)
+    _dev(block_tables, "block_tables", dtype=torch.int32, ndim=2)
+    _dev(context_lens, "context_lens", dtype=torch.int32, ndim=1)
+    T, H, D = q.shape
+    S = context_lens.shape[0]
+    if out.shape != q.shape or q_start.shape[0] != S + 1 or block_tables.shape[0] != S:
+        raise ValueError("shape mismatch between q, out, q_start, context_lens and block_tables")
+    if lse is not None:
+        _dev(lse, "lse", dtype=torch.float32, ndim=2)
+        if lse.shape != (T, H):
+            raise ValueError("lse must be [T, H]")
+    g = geometry(k_pool, H)
+    _check(LIB.paged_attn_prefill(ctypes.byref(g), _ptr(out), _ptr(lse), _ptr(q), _ptr(q_start), _ptr(k_pool),
+                                  _ptr(v_pool), _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), S,
+                                  int(max_q_len), int(max_context_len), int(window), float(scale),
+                                  _stream(stream)), "paged_attn_prefill")

@@ -1,0 +1,177 @@
+// C ABI of the library: argument checks, partition sizing, launches on the
+// caller's stream. Declarations and the contract are in paged_attn.h.
+#include "../../include/paged_attn.h"
+
+#include <math.h>
+
+#include "launch.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return PKV_OK;
+  g_last_hip_error = (int)e;
+  return PKV_EHIP;
+}
+
+int elem_bytes(int dtype) { return dtype == PKV_F32 ? 4 : 2; }
+
+// Geometry checks common to every call. Returns PKV_OK, PKV_EINVAL or
+// PKV_EUNSUPPORTED.
+int check_geometry(const pkv_geometry_t* g) {
+  if (!g) return PKV_EINVAL;
+  if (g->num_blocks <= 0 || g->block_size <= 0 || g->num_heads <= 0 || g->num_kv_heads <= 0 ||
+      g->head_dim <= 0)
+    return PKV_EINVAL;
+  if (g->num_heads % g->num_kv_heads) return PKV_EINVAL;
+  if (g->kv_dtype != PKV_F32 && g->kv_dtype != PKV_F16 && g->kv_dtype != PKV_BF16) return PKV_EUNSUPPORTED;
+  if (g->head_dim != 64 && g->head_dim != 128) return PKV_EUNSUPPORTED;
+  if (g->block_size != 16 && g->block_size != 32) return PKV_EUNSUPPORTED;
+  const int G = g->num_heads / g->num_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return PKV_EUNSUPPORTED;
+  return PKV_OK;
+}
+
+int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
+
+// Blocks one sequence's attended range can span.
+int span_blocks(const pkv_geometry_t* g, int max_context_len, int window) {
+  const int B = g->block_size;
+  int n = ceil_div(max_context_len, B);
+  if (window > 0) {
+    const int w = ceil_div(window, B) + 1;
+    if (w < n) n = w;
+  }
+  return n;
+}
+
+// Automatic partition length: aim for enough workgroups to fill 256 compute
+// units several times over, with partitions of at least 8 blocks, at most 64.
+int auto_partition_blocks(const pkv_geometry_t* g, int num_seqs, int max_context_len, int window) {
+  const int span = span_blocks(g, max_context_len, window);
+  const long long items = (long long)num_seqs * g->num_kv_heads;
+  const long long target_wg = 2048;
+  long long want = items > 0 ? (items * span + target_wg - 1) / target_wg : span;
+  int bpp = 8;
+  while (bpp < want && bpp < 64) bpp *= 2;
+  if (bpp > span) bpp = span > 0 ? span : 1;
+  return bpp;
+}
+
+int decode_split(const pkv_geometry_t* g, int num_seqs, int max_context_len, int window,
+                 int partition_size, int* bpp, int* n_part) {
+  if (partition_size < 0 || (partition_size % g->block_size)) return PKV_EINVAL;
+  *bpp = partition_size ? partition_size / g->block_size
+                        : auto_partition_blocks(g, num_seqs, max_context_len, window);
+  const int span = span_blocks(g, max_context_len, window);
+  *n_part = span > 0 ? ceil_div(span, *bpp) : 1;
+  if (*n_part < 1) *n_part = 1;
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int paged_kv_write(const pkv_geometry_t* geom, void* k_pool, void* v_pool, const void* k_new,
+                   const void* v_new, const int32_t* seq_idx, const int32_t* pos, int32_t num_tokens,
+                   const int32_t* block_tables, int32_t num_seqs, int32_t max_blocks_per_seq,
+                   void* stream) {
+  int st = check_geometry(geom);
+  if (st) return st;
+  if (num_tokens < 0 || num_seqs < 0 || max_blocks_per_seq <= 0) return PKV_EINVAL;
+  if (num_tokens == 0) return PKV_OK;
+  if (!k_pool || !v_pool || !k_new || !v_new || !seq_idx || !pos || !block_tables || num_seqs == 0)
+    return PKV_EINVAL;
+  pkv::WriteArgs a{k_pool, v_pool, k_new, v_new, seq_idx, pos, block_tables, num_tokens, num_seqs,
+                   max_blocks_per_seq, geom->num_blocks, geom->block_size, geom->num_kv_heads,
+                   geom->head_dim, elem_bytes(geom->kv_dtype)};
+  return hip_status(pkv::launch_kv_write(a, (hipStream_t)stream));
+}
+
+int32_t paged_attn_decode_auto_partition(const pkv_geometry_t* geom, int32_t num_seqs,
+                                         int32_t max_context_len, int32_t window) {
+  if (check_geometry(geom) || num_seqs < 0 || max_context_len < 0 || window < 0) return 0;
+  return auto_partition_blocks(geom, num_seqs, max_context_len, window) * geom->block_size;
+}
+
+size_t paged_attn_decode_workspace_bytes(const pkv_geometry_t* geom, int32_t num_seqs,
+                                         int32_t max_context_len, int32_t window,
+                                         int32_t partition_size) {
+  if (check_geometry(geom) || num_seqs < 0 || max_context_len < 0 || window < 0) return 0;
+  int bpp, n_part;
+  if (decode_split(geom, num_seqs, max_context_len, window, partition_size, &bpp, &n_part)) return 0;
+  if (n_part == 1) return 0;
+  return (size_t)num_seqs * geom->num_heads * n_part * (geom->head_dim + 2) * sizeof(float);
+}
+
+int paged_attn_decode(const pkv_geometry_t* geom, float* out, float* lse, const void* q,
+                      const void* k_pool, const void* v_pool, const int32_t* block_tables,
+                      int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
+                      int32_t max_context_len, int32_t window, float scale, int32_t partition_size,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_geometry(geom);
+  if (st) return st;
+  if (num_seqs < 0 || max_blocks_per_seq <= 0 || max_context_len < 0 || window < 0 || !isfinite(scale))
+    return PKV_EINVAL;
+  if ((long long)max_context_len > (long long)max_blocks_per_seq * geom->block_size) return PKV_EINVAL;
+  if (num_seqs == 0) return PKV_OK;
+  if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens) return PKV_EINVAL;
+  const int G = geom->num_heads / geom->num_kv_heads;
+  if (!pkv::decode_supported(geom->kv_dtype, geom->head_dim, geom->block_size, G)) return PKV_EUNSUPPORTED;
+  int bpp, n_part;
+  st = decode_split(geom, num_seqs, max_context_len, window, partition_size, &bpp, &n_part);
+  if (st) return st;
+  const size_t need = n_part == 1 ? 0
+                                  : (size_t)num_seqs * geom->num_heads * n_part * (geom->head_dim + 2) * sizeof(float);
+  if (need && (!workspace || workspace_bytes < need)) return PKV_EWORKSPACE;
+  float* ws_o = (float*)workspace;
+  float* ws_ml = need ? ws_o + (size_t)num_seqs * geom->num_heads * n_part * geom->head_dim : nullptr;
+  pkv::DecodeArgs a{out, lse, q, k_pool, v_pool, block_tables, context_lens, ws_o, ws_ml,
+                    num_seqs, geom->num_heads, geom->num_kv_heads, geom->head_dim, geom->block_size,
+                    max_blocks_per_seq, geom->num_blocks, window, geom->kv_dtype, max_context_len,
+                    bpp, n_part, scale};
+  return hip_status(pkv::launch_decode(a, (hipStream_t)stream));
+}
+
+int paged_attn_prefill(const pkv_geometry_t* geom, float* out, float* lse, const void* q,
+                       const int32_t* q_start, const void* k_pool, const void* v_pool,
+                       const int32_t* block_tables, int32_t max_blocks_per_seq,
+                       const int32_t* context_lens, int32_t num_seqs, int32_t max_q_len,
+                       int32_t max_context_len, int32_t window, float scale, void* stream) {
+  int st = check_geometry(geom);
+  if (st) return st;
+  if (num_seqs < 0 || max_blocks_per_seq <= 0 || max_q_len < 0 || max_context_len < 0 || window < 0 ||
+      !isfinite(scale))
+    return PKV_EINVAL;
+  if ((long long)max_context_len > (long long)max_blocks_per_seq * geom->block_size) return PKV_EINVAL;
+  if (max_q_len > max_context_len) return PKV_EINVAL;
+  if (num_seqs == 0 || max_q_len == 0) return PKV_OK;
+  if (!out || !q || !q_start || !k_pool || !v_pool || !block_tables || !context_lens) return PKV_EINVAL;
+  const int G = geom->num_heads / geom->num_kv_heads;
+  if (!pkv::prefill_supported(geom->kv_dtype, geom->head_dim, geom->block_size, G)) return PKV_EUNSUPPORTED;
+  pkv::PrefillArgs a{out, lse, q, q_start, k_pool, v_pool, block_tables, context_lens, num_seqs,
+                     geom->num_heads, geom->num_kv_heads, geom->head_dim, geom->block_size,
+                     max_blocks_per_seq, geom->num_blocks, window, geom->kv_dtype, max_q_len,
+                     max_context_len, scale};
+  return hip_status(pkv::launch_prefill(a, (hipStream_t)stream));
+}
+
+const char* pkv_status_string(int status) {
+  switch (status) {
+    case PKV_OK: return "PKV_OK";
+    case PKV_EINVAL: return "PKV_EINVAL: invalid argument";
+    case PKV_EUNSUPPORTED: return "PKV_EUNSUPPORTED: unsupported head_dim, block_size, dtype or group size";
+    case PKV_EWORKSPACE: return "PKV_EWORKSPACE: workspace missing or too small";
+    case PKV_EHIP: return "PKV_EHIP: HIP launch failed";
+  }
+  return "unknown status";
+}
+
+int pkv_last_hip_error(void) { return g_last_hip_error; }
+
+int pkv_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,57 @@
+// Internal interface between the C ABI (api.hip) and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pkv {
+
+struct WriteArgs {
+  void* k_pool;
+  void* v_pool;
+  const void* k_new;
+  const void* v_new;
+  const int32_t* seq_idx;
+  const int32_t* pos;
+  const int32_t* tables;
+  int32_t num_tokens, num_seqs, mb, nb, B, Hkv, D, elem_bytes;
+};
+
+struct DecodeArgs {
+  float* out;
+  float* lse;
+  const void* q;
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* tables;
+  const int32_t* lens;
+  float* ws_o;   // [S, H, n_part, D] partial outputs (split mode)
+  float* ws_ml;  // [S, H, n_part, 2] partial running max (log2 units) and sum
+  int32_t S, H, Hkv, D, B, mb, nb, window, dtype, max_context_len;
+  int32_t blocks_per_part, n_part;
+  float scale;
+};
+
+struct PrefillArgs {
+  float* out;
+  float* lse;
+  const void* q;
+  const int32_t* q_start;
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* tables;
+  const int32_t* lens;
+  int32_t S, H, Hkv, D, B, mb, nb, window, dtype, max_q_len, max_context_len;
+  float scale;
+};
+
+hipError_t launch_kv_write(const WriteArgs& a, hipStream_t st);
+
+bool decode_supported(int dtype, int D, int B, int G);
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
+
+bool prefill_supported(int dtype, int D, int B, int G);
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st);
+
+}  // namespace pkv

@@ -1,0 +1,359 @@
+// Causal chunked prefill through the block table on the matrix cores.
+//
+// What it computes ("Building a Streaming Sliding-Window Attention Engine in
+// Pure Python", Step 3 and Step 4, read for a chunk that follows a cached
+// prefix): query row i of sequence s sits at position p = L - C + i and
+// attends every cached position t <= p (and t > p - w with a window).
+//
+// How, on gfx950 (v_mfma_f32_32x32x16 on 16-bit inputs, fp32 accumulate):
+//  * Workgroup = 4 wavefronts; each wavefront owns 32 query rows of one query
+//    head. The wavefronts of a workgroup share one kv head, so each K/V tile
+//    is gathered once into LDS for up to 4 query heads of the group.
+//  * Tiles of 64 key positions are gathered through the block table into LDS
+//    (K and V both row-major, two buffers): the next tile's global loads are
+//    in flight while the current tile is computed, one barrier per tile.
+//  * Per tile and wavefront
+//      S^T (64 keys x 32 queries) = K_tile . Q^T        (16 MFMAs, D = 128)
+//    so each lane holds the scores of one query; the running maximum is
+//    exchanged between the two lane halves that hold the same query; then
+//      O^T (D x 32 queries) += V_tile^T . P^T
+//    keeps one query's output per lane, so the rescale never leaves the lane.
+//    The V^T operand is read from row-major V with the LDS transpose read
+//    (ds_read_b64_tr_b16): within 16 lanes, lane j reads 4 consecutive dims
+//    of key j/4 and lane i receives dim i of those 4 keys.
+//  * Weights for P.V: fp16 inputs use the weights rounded to fp16; bf16
+//    inputs split each weight into bf16 high and low parts (p = hi + lo to
+//    about 2^-17 relative) and multiply both, so the 8-bit bf16 mantissa
+//    does not limit the result. The normaliser sums the weights as used.
+//  * Rescaling of the output accumulators is skipped when no lane's running
+//    maximum grew (exact: the factor would be 1).
+//  * Masked keys (causal, window, unmapped blocks) are removed by selection
+//    (score -inf); K/V rows outside the loaded range are zero-filled so a
+//    zero weight never meets a NaN.
+#include "common.h"
+#include "launch.h"
+
+namespace pkv {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+template <class T> struct Mma;
+template <> struct Mma<BF16T> {
+  using V8 = bf16x8;
+  static constexpr bool kSplit = true;
+  static __device__ __forceinline__ f32x16 mma(V8 a, V8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ uint32_t bits(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
+  static __device__ __forceinline__ float value(uint32_t b) { return __builtin_bit_cast(float, b << 16); }
+};
+template <> struct Mma<F16T> {
+  using V8 = f16x8;
+  static constexpr bool kSplit = false;
+  static __device__ __forceinline__ f32x16 mma(V8 a, V8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ uint32_t bits(float x) { return __builtin_bit_cast(uint16_t, (_Float16)x); }
+  static __device__ __forceinline__ float value(uint32_t b) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
+  }
+};
+
+constexpr int kKT = 64;   // key positions per tile
+constexpr int kPad = 8;   // elements of padding per LDS row
+
+// Row index inside a 32x32 accumulator for register v of lane-half hf.
+__device__ __forceinline__ int acc_row(int v, int hf) { return 8 * (v >> 2) + 4 * hf + (v & 3); }
+
+__device__ __forceinline__ u32x2 lds_read_tr(const uint16_t* p) {
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+  return __builtin_bit_cast(u32x2, v);
+}
+
+template <class T, int D, int B, int G>
+__global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a, float scale_log2) {
+  using M = Mma<T>;
+  using V8 = typename M::V8;
+  constexpr int KC = D / 16;            // MFMA k-chunks over the head dim
+  constexpr int DT = D / 32;            // 32-wide output tiles over the head dim
+  constexpr int HPW = G < 4 ? G : 4;    // query heads per workgroup
+  constexpr int PSUB = 4 / HPW;         // 32-row query sub-tiles per workgroup
+  constexpr int QT = 32 * PSUB;         // query rows per workgroup
+  constexpr int ROW = D + kPad;         // LDS row, elements (16-byte multiple)
+  constexpr int NLD = kKT * D / 8 / 256;  // 16-byte pieces per thread per tile (each of K and V)
+  constexpr int TILE = kKT * ROW;
+
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][TILE];  // [buffer][K, V]
+  __shared__ int kvalid[2][kKT];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = uniform(tid >> 6);
+  const int hf = lane >> 5;
+  const int ql = lane & 31;
+  const int s = blockIdx.z;
+  const int g = blockIdx.y / (G / HPW);
+  const int hq = g * G + (blockIdx.y % (G / HPW)) * HPW + wave % HPW;
+  const int qt = gridDim.x - 1 - blockIdx.x;  // heaviest (latest) tiles first
+
+  const int r0 = a.q_start[s];
+  const int C = a.q_start[s + 1] - r0;
+  int L = a.lens[s];
+  L = L < 0 ? 0 : (L > a.max_context_len ? a.max_context_len : L);
+  if (qt * QT >= C || C > L) return;
+  const int row0 = qt * QT + (wave / HPW) * 32;   // first chunk row of this wavefront
+  const int wg_last = min(C, (qt + 1) * QT) - 1;  // last chunk row of the workgroup
+  const int base = L - C;                         // position of chunk row 0
+  const int kv_hi = base + wg_last + 1;
+  int kv_lo = 0;
+  if (a.window > 0) kv_lo = max(0, base + qt * QT - a.window + 1);
+  const int t_first = (kv_lo / kKT) * kKT;
+
+  // Query fragment of this lane: row ql of the wavefront, 8 elements per k-chunk.
+  const int my_row = row0 + ql;
+  const bool row_ok = my_row < C;
+  const int my_pos = base + my_row;
+  V8 qf[KC];
+  {
+    const char* qp = (const char*)a.q + ((size_t)(r0 + (row_ok ? my_row : 0)) * a.H + hq) * D * 2;
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+      u32x4 v = load16(qp + (size_t)(kc * 16 + 8 * hf) * 2);
+      if (!row_ok) v = u32x4{0, 0, 0, 0};
+      qf[kc] = __builtin_bit_cast(V8, v);
+    }
+  }
+
+  f32x16 o[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) o[dt] = f32x16{};
+  float m_run = -INFINITY;
+  float l_run = 0.f;  // sum of the weights as multiplied (normaliser)
+  float l_lse = 0.f;  // exact fp32 sum, for lse (differs when weights are rounded)
+
+  const int wave_pmin = base + row0;
+  const int wave_pmax = base + min(row0 + 31, C - 1);
+  const bool wave_has_rows = row0 < C;
+  const size_t row_stride = (size_t)a.Hkv * D * 2;
+  const char* kpool = (const char*)a.k_pool + (size_t)g * D * 2;
+  const char* vpool = (const char*)a.v_pool + (size_t)g * D * 2;
+  const int32_t* trow = a.tables + (size_t)s * a.mb;
+
+  // Staging registers for one tile: piece i is row (tid + 256 i) / (D/8),
+  // 16-byte column (tid + 256 i) % (D/8), of both K and V.
+  u32x4 kreg[NLD], vreg[NLD];
+  int okmask = 0;
+  auto load_tile = [&](int t0) {
+    okmask = 0;
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const int id = tid + 256 * i;
+      const int row = id / (D / 8);
+      const int ch = id % (D / 8);
+      const int t = t0 + row;
+      int pb = -1;
+      if (t >= kv_lo && t < kv_hi) pb = trow[t / B];
+      const bool ok = pb >= 0 && pb < a.nb;
+      kreg[i] = u32x4{0, 0, 0, 0};
+      vreg[i] = u32x4{0, 0, 0, 0};
+      if (ok) {
+        const size_t off = ((size_t)pb * B + t % B) * row_stride + ch * 16;
+        kreg[i] = load16(kpool + off);
+        vreg[i] = load16(vpool + off);
+      }
+      okmask |= (int)ok << i;
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const int id = tid + 256 * i;
+      const int row = id / (D / 8);
+      const int ch = id % (D / 8);
+      *reinterpret_cast<u32x4*>(&lds[buf][0][row * ROW + ch * 8]) = kreg[i];
+      *reinterpret_cast<u32x4*>(&lds[buf][1][row * ROW + ch * 8]) = vreg[i];
+      if (ch == 0) kvalid[buf][row] = (okmask >> i) & 1;
+    }
+  };
+
+  load_tile(t_first);
+  store_tile(0);
+  int tile_ok = __syncthreads_and(okmask == (1 << NLD) - 1);
+
+  // V^T operand addressing for the transpose read: 16-lane group gq = lane/16
+  // covers dims 16*(gq&1) .. +16 of a 32-dim tile and key half hf = gq>>1.
+  const int gq = lane >> 4, j16 = lane & 15;
+  const int tr_row = j16 >> 2;                       // key offset inside 4
+  const int tr_col = 16 * (gq & 1) + 4 * (j16 & 3);  // dim offset inside a 32-dim tile
+
+  int buf = 0;
+  for (int t0 = t_first; t0 < kv_hi; t0 += kKT, buf ^= 1) {
+    const bool has_next = t0 + kKT < kv_hi;
+    if (has_next) load_tile(t0 + kKT);
+
+    bool skip = !wave_has_rows || t0 > wave_pmax;
+    if (a.window > 0 && t0 + kKT - 1 <= wave_pmin - a.window) skip = true;
+    if (!skip) {
+      const uint16_t* Ks = lds[buf][0];
+      const uint16_t* Vs = lds[buf][1];
+      // S^T = K_tile . Q^T, two 32-key halves.
+      f32x16 sacc[2];
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh) {
+        sacc[kh] = f32x16{};
+        const uint16_t* kr = &Ks[(kh * 32 + ql) * ROW + 8 * hf];
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) {
+          V8 av = __builtin_bit_cast(V8, *reinterpret_cast<const u32x4*>(kr + kc * 16));
+          sacc[kh] = M::mma(av, qf[kc], sacc[kh]);
+        }
+      }
+      // Scale, mask, running maximum.
+      const bool need_mask = !tile_ok || wave_pmin < t0 + kKT - 1 || row0 + 31 >= C ||
+                             (a.window > 0 && t0 <= wave_pmax - a.window);
+      float mt = -INFINITY;
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          float x = sacc[kh][v] * scale_log2;
+          if (need_mask) {
+            const int kl = kh * 32 + acc_row(v, hf);
+            const int t = t0 + kl;
+            bool ok = row_ok && t <= my_pos && kvalid[buf][kl];
+            if (a.window > 0) ok = ok && t > my_pos - a.window;
+            x = ok ? x : -INFINITY;
+          }
+          sacc[kh][v] = x;
+          mt = fmaxf(mt, x);
+        }
+      }
+      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+      const float mn = fmaxf(m_run, mt);
+      const float ms = mn == -INFINITY ? 0.f : mn;
+      if (__any(mn > m_run)) {
+        const float alpha = __builtin_amdgcn_exp2f(m_run - ms);
+        l_run *= alpha;
+        if constexpr (!M::kSplit) l_lse *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+      }
+      m_run = mn;
+
+      // P^T operands: key chunk c = 16 keys; this lane supplies the weights of
+      // its accumulator registers 8*(c%2) .. +7 of half c/2, i.e. keys
+      // 16c + 8*(e/4) + 4*hf + e%4 for e = 0..7.
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int kh = c >> 1, sub = c & 1;
+        uint32_t hi[4], lo[4];
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) {
+          const float p0 = __builtin_amdgcn_exp2f(sacc[kh][8 * sub + 2 * e2] - ms);
+          const float p1 = __builtin_amdgcn_exp2f(sacc[kh][8 * sub + 2 * e2 + 1] - ms);
+          const uint32_t h0 = M::bits(p0), h1 = M::bits(p1);
+          hi[e2] = h0 | (h1 << 16);
+          if constexpr (M::kSplit) {
+            const float r0v = p0 - M::value(h0), r1v = p1 - M::value(h1);
+            lo[e2] = M::bits(r0v) | (M::bits(r1v) << 16);
+            l_run += p0 + p1;
+          } else {
+            l_run += M::value(h0) + M::value(h1);
+            l_lse += p0 + p1;
+          }
+        }
+        const V8 bhi = __builtin_bit_cast(V8, u32x4{hi[0], hi[1], hi[2], hi[3]});
+        const V8 blo = __builtin_bit_cast(V8, u32x4{lo[0], lo[1], lo[2], lo[3]});
+        const uint16_t* vb = Vs + (16 * c + 4 * hf + tr_row) * ROW + tr_col;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const u32x2 e03 = lds_read_tr(vb + dt * 32);
+          const u32x2 e47 = lds_read_tr(vb + 8 * ROW + dt * 32);
+          const V8 av = __builtin_bit_cast(V8, u32x4{e03.x, e03.y, e47.x, e47.y});
+          o[dt] = M::mma(av, bhi, o[dt]);
+          if constexpr (M::kSplit) o[dt] = M::mma(av, blo, o[dt]);
+        }
+      }
+    }
+    if (has_next) store_tile(buf ^ 1);
+    tile_ok = __syncthreads_and(okmask == (1 << NLD) - 1);
+  }
+
+  if (!row_ok) return;
+  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  float* op = a.out + ((size_t)(r0 + my_row) * a.H + hq) * D;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+    for (int v4 = 0; v4 < 4; ++v4) {
+      const int d = dt * 32 + 8 * v4 + 4 * hf;
+      float4 w = make_float4(o[dt][4 * v4] * inv, o[dt][4 * v4 + 1] * inv, o[dt][4 * v4 + 2] * inv,
+                             o[dt][4 * v4 + 3] * inv);
+      *reinterpret_cast<float4*>(op + d) = w;
+    }
+  }
+  if (a.lse) {
+    const float l_exact = M::kSplit ? l_tot : l_lse + __shfl_xor(l_lse, 32, 64);
+    if (hf == 0)
+      a.lse[(size_t)(r0 + my_row) * a.H + hq] = l_exact > 0.f ? (m_run + __log2f(l_exact)) * kLn2 : -INFINITY;
+  }
+}
+
+template <class T, int D, int B, int G>
+static hipError_t launch_typed(const PrefillArgs& a, hipStream_t st) {
+  constexpr int HPW = G < 4 ? G : 4;
+  constexpr int QT = 32 * (4 / HPW);
+  dim3 grid((a.max_q_len + QT - 1) / QT, a.Hkv * (G / HPW), a.S);
+  hipLaunchKernelGGL((prefill_kernel<T, D, B, G>), grid, dim3(256), 0, st, a, a.scale * kLog2e);
+  return hipGetLastError();
+}
+
+template <class T, int D, int B>
+static hipError_t by_group(const PrefillArgs& a, hipStream_t st) {
+  switch (a.H / a.Hkv) {
+    case 1: return launch_typed<T, D, B, 1>(a, st);
+    case 2: return launch_typed<T, D, B, 2>(a, st);
+    case 4: return launch_typed<T, D, B, 4>(a, st);
+    case 8: return launch_typed<T, D, B, 8>(a, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <class T, int D>
+static hipError_t by_block(const PrefillArgs& a, hipStream_t st) {
+  switch (a.B) {
+    case 16: return by_group<T, D, 16>(a, st);
+    case 32: return by_group<T, D, 32>(a, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <class T>
+static hipError_t by_dim(const PrefillArgs& a, hipStream_t st) {
+  switch (a.D) {
+    case 64: return by_block<T, 64>(a, st);
+    case 128: return by_block<T, 128>(a, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+bool prefill_supported(int dtype, int D, int B, int G) {
+  return (dtype == 1 || dtype == 2) && (D == 64 || D == 128) && (B == 16 || B == 32) &&
+         (G == 1 || G == 2 || G == 4 || G == 8);
+}
+
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
+  switch (a.dtype) {
+    case 1: return by_dim<F16T>(a, st);
+    case 2: return by_dim<BF16T>(a, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pkv

@@ -1,0 +1,105 @@
+"""Device staging of a workload for the library: pools, tables, lengths,
+queries and the tokens one step writes, as torch device tensors.
+
+Takes host arrays (anything with the fields of ``workloads.Workload``:
+storage-dtype numpy arrays, with bfloat16 held as uint16 bit patterns).  The
+cached history is written into the pools with the library's own
+``paged_kv_write``; one ``step()`` is the hot path: write the step's new
+tokens, then attend (decode or chunked prefill).
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional
+
+import numpy as np
+import torch
+
+from . import _lib
+
+TORCH_DTYPE = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+
+def to_device(a: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
+    """Host storage array -> device tensor of the storage dtype (bit copy)."""
+    a = np.ascontiguousarray(a)
+    if dtype == "bf16":
+        t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(a)
+    return t.to(device, non_blocking=False)
+
+
+def from_device(t: torch.Tensor) -> np.ndarray:
+    """Device tensor -> host storage array (bfloat16 as uint16 bits)."""
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def int_tensor(a, device="cuda") -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(np.asarray(a, dtype=np.int32))).to(device)
+
+
+class DeviceWorkload:
+    def __init__(self, w, device: str = "cuda", poison: bool = True, partition_size: int = 0,
+                 with_lse: bool = True, write_history: bool = True):
+        self.w = w
+        self.device = device
+        dt = TORCH_DTYPE[w.dtype]
+        shape = (w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim)
+        fill = math.nan if poison else 0.0
+        self.k_pool = torch.full(shape, fill, dtype=dt, device=device)
+        self.v_pool = torch.full(shape, fill, dtype=dt, device=device)
+        self.tables = int_tensor(w.block_tables, device)
+        self.lens = int_tensor(w.context_lens, device)
+        self.q = to_device(w.q, w.dtype, device)
+        self.q_start = int_tensor(w.q_start, device) if w.q_start is not None else None
+        self.out = torch.empty(self.q.shape, dtype=torch.float32, device=device)
+        self.lse = (torch.empty(self.q.shape[:2], dtype=torch.float32, device=device) if with_lse else None)
+        si, pos, k, v = w.step_tokens()
+        self.step_seq = int_tensor(si, device)
+        self.step_pos = int_tensor(pos, device)
+        self.step_k = to_device(k, w.dtype, device)
+        self.step_v = to_device(v, w.dtype, device)
+        self.partition_size = partition_size
+        self.workspace: Optional[torch.Tensor] = None
+        if w.kind == "decode":
+            nbytes = _lib.paged_attn_decode_workspace_bytes(self.k_pool, w.num_heads, w.num_seqs,
+                                                            w.max_context_len, w.window, partition_size)
+            if nbytes:
+                self.workspace = torch.empty(nbytes // 4, dtype=torch.float32, device=device)
+        if write_history:
+            self.write_history()
+
+    def write_history(self) -> None:
+        w = self.w
+        for s, p0, k, v in w.history_tokens():
+            n = k.shape[0]
+            _lib.paged_kv_write(self.k_pool, self.v_pool, to_device(k, w.dtype, self.device),
+                                to_device(v, w.dtype, self.device),
+                                torch.full((n,), s, dtype=torch.int32, device=self.device),
+                                torch.arange(p0, p0 + n, dtype=torch.int32, device=self.device),
+                                self.tables)
+
+    def write_step(self, stream=None) -> None:
+        _lib.paged_kv_write(self.k_pool, self.v_pool, self.step_k, self.step_v, self.step_seq,
+                            self.step_pos, self.tables, stream=stream)
+
+    def attend(self, stream=None) -> None:
+        w = self.w
+        if w.kind == "decode":
+            _lib.paged_attn_decode(self.out, self.q, self.k_pool, self.v_pool, self.tables, self.lens,
+                                   w.max_context_len, window=w.window, scale=w.scale,
+                                   partition_size=self.partition_size, workspace=self.workspace,
+                                   lse=self.lse, stream=stream)
+        else:
+            _lib.paged_attn_prefill(self.out, self.q, self.q_start, self.k_pool, self.v_pool, self.tables,
+                                    self.lens, w.max_q_len, w.max_context_len, window=w.window,
+                                    scale=w.scale, lse=self.lse, stream=stream)
+
+    def step(self, stream=None) -> None:
+        """One pass of the hot path: write the new tokens, then attend."""
+        self.write_step(stream)
+        self.attend(stream)

@@ -31,8 +31,10 @@ bfloat16 type).
 """
 from __future__ import annotations
 
+import concurrent.futures
 import dataclasses
 import math
+import os
 from typing import Dict, List, Optional, Tuple
 
 import numpy as np
@@ -55,9 +57,16 @@ def stream(seed: int, tag: int, index: int = 0) -> np.random.Generator:
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round float32 to bfloat16 (nearest, ties to even); return the uint16 bits."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    bias = ((u >> 16) & 1) + 0x7FFF
-    out = ((u + bias) >> 16).astype(np.uint16)
+    u = x.view(np.uint32)
+    # Finite inputs cannot carry past bit 31 (largest finite magnitude bits
+    # 0x7F7FFFFF plus the bias stay below 2^31 for each sign); NaNs are set
+    # afterwards.
+    t = u >> 16
+    t &= 1
+    t += 0x7FFF
+    t += u
+    t >>= 16
+    out = t.astype(np.uint16)
     nan = np.isnan(x)
     if nan.any():
         out[nan] = 0x7FC0
@@ -200,6 +209,18 @@ class Workload:
         return int(n.sum()) * self.num_kv_heads * self.head_dim * 2 * eb
 
 
+def _parallel_map(fn, items):
+    """Map over independent streams on host threads (NumPy's generators and
+    casts release the GIL); results keep their order, so the output does not
+    depend on the thread count."""
+    items = list(items)
+    if len(items) < 2:
+        return [fn(i) for i in items]
+    workers = min(len(items), max(1, min(16, len(os.sched_getaffinity(0)))))
+    with concurrent.futures.ThreadPoolExecutor(max_workers=workers) as ex:
+        return list(ex.map(fn, items))
+
+
 def _deal_tables(rng_perm, blocks_per_seq: List[int], first_block: List[int], mb: int,
                  num_blocks: int) -> np.ndarray:
     """Hand out shuffled physical ids in sequence order; -1 elsewhere."""
@@ -246,14 +267,14 @@ def make_decode(*, lens, num_heads, num_kv_heads, head_dim, block_size, dtype, s
     nb = int(sum(nblocks)) + int(spare_blocks)
     nb = max(nb, 1)
     tables = _deal_tables(stream(seed, TAG_PERM), nblocks, first_block, mb, nb)
-    seq_kv = []
-    for s in range(S):
-        L = int(lens[s])
-        n = L - starts[s]
+    def one(s):
+        n = int(lens[s]) - starts[s]
         rng = stream(seed, TAG_SEQ_KV, s)
         k = draw(rng, (n, num_kv_heads, head_dim), dtype, k_scale)
         v = draw(rng, (n, num_kv_heads, head_dim), dtype)
-        seq_kv.append(SeqKV(starts[s], k, v))
+        return SeqKV(starts[s], k, v)
+
+    seq_kv = _parallel_map(one, range(S))
     q = draw(stream(seed, TAG_QUERY), (S, num_heads, head_dim), dtype)
     if scale is None:
         scale = 1.0 / math.sqrt(head_dim)
@@ -293,12 +314,13 @@ def make_prefill(*, prefix_len, chunk_lens, num_heads, num_kv_heads, head_dim, b
     rng = stream(seed, TAG_PREFIX_KV)
     prefix = SeqKV(0, draw(rng, (prefix_len, num_kv_heads, head_dim), dtype),
                    draw(rng, (prefix_len, num_kv_heads, head_dim), dtype))
-    seq_kv = []
-    for s in range(S):
+    def one(s):
         rng = stream(seed, TAG_SEQ_KV, s)
         k = draw(rng, (chunk_lens[s], num_kv_heads, head_dim), dtype)
         v = draw(rng, (chunk_lens[s], num_kv_heads, head_dim), dtype)
-        seq_kv.append(SeqKV(prefix_len, k, v))
+        return SeqKV(prefix_len, k, v)
+
+    seq_kv = _parallel_map(one, range(S))
     q_start = np.zeros(S + 1, dtype=np.int32)
     q_start[1:] = np.cumsum(chunk_lens)
     q = draw(stream(seed, TAG_QUERY), (int(q_start[-1]), num_heads, head_dim), dtype)
