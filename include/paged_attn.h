@@ -105,17 +105,18 @@ int paged_kv_write(const pkv_geometry_t* geom, void* k_pool, void* v_pool,
                    const int32_t* block_tables, int32_t num_seqs, int32_t max_blocks_per_seq,
                    void* stream);
 
-/* Bytes of workspace paged_attn_decode needs for these sizes (0 when the
- * call runs as one pass). partition_size as for paged_attn_decode.
- * Returns 0 for invalid arguments too; paged_attn_decode reports those. */
+/* Bytes of device workspace paged_attn_decode needs for these sizes and
+ * num_workers (as for paged_attn_decode). The automatic worker count
+ * depends on the current device, so query on the device that runs the call.
+ * Returns 0 for invalid arguments; paged_attn_decode reports those. */
 size_t paged_attn_decode_workspace_bytes(const pkv_geometry_t* geom, int32_t num_seqs,
                                          int32_t max_context_len, int32_t window,
-                                         int32_t partition_size);
+                                         int32_t num_workers);
 
-/* The partition length (positions) paged_attn_decode uses for
- * partition_size == 0 with these sizes. */
-int32_t paged_attn_decode_auto_partition(const pkv_geometry_t* geom, int32_t num_seqs,
-                                         int32_t max_context_len, int32_t window);
+/* The worker count paged_attn_decode uses for num_workers == 0 with these
+ * sizes on the current device (0 for invalid arguments). */
+int32_t paged_attn_decode_workers(const pkv_geometry_t* geom, int32_t num_seqs,
+                                  int32_t max_context_len, int32_t window);
 
 /* paged_attn_decode - one query token per sequence attends its cached
  * context through the block table.
@@ -138,12 +139,17 @@ int32_t paged_attn_decode_auto_partition(const pkv_geometry_t* geom, int32_t num
  *   max_context_len  host bound on context_lens (<= max_blocks_per_seq * B)
  *   window        0 = attend everything, else the last `window` positions
  *   scale         score scale, typically 1/sqrt(D)
- *   partition_size  positions per split-K partition: 0 = automatic, else a
- *                 positive multiple of block_size. The context is split into
- *                 partitions attended independently (running max and sum per
- *                 partition) and merged exactly by a second pass.
+ *   num_workers   wavefronts the attended (sequence, kv head, block) triples
+ *                 are divided among, in equal contiguous shares: 0 = an
+ *                 automatic count for the current device (whole workgroups
+ *                 per compute unit, capped by the number of blocks); any
+ *                 positive count is valid (workers beyond the number of
+ *                 attended blocks stay idle). Each wavefront keeps
+ *                 a running max and sum over its share; a second pass merges
+ *                 the shares of every (sequence, head) exactly.
  *   workspace     device scratch of >= paged_attn_decode_workspace_bytes()
- *                 bytes (may be NULL when that is 0)
+ *                 bytes, 16-byte aligned; overwritten by the call, so two
+ *                 calls in flight at once need different workspaces
  * Table entries of attended blocks that are -1 or >= NB are skipped: their
  * positions contribute nothing. The partially covered first block of a
  * window must stay mapped. */
@@ -151,7 +157,7 @@ int paged_attn_decode(const pkv_geometry_t* geom, float* out, float* lse, const 
                       const void* k_pool, const void* v_pool,
                       const int32_t* block_tables, int32_t max_blocks_per_seq,
                       const int32_t* context_lens, int32_t num_seqs, int32_t max_context_len,
-                      int32_t window, float scale, int32_t partition_size,
+                      int32_t window, float scale, int32_t num_workers,
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /* paged_attn_prefill - causal attention of a chunk of query tokens per

@@ -1,6 +1,6 @@
 """Build ``libpagedattn.so`` (HIP, gfx950) in-tree with hipcc.
 
-    python -m paged_kv_cache_30_amd.build
+    python paged_kv_cache_30_amd/build.py
 
 Each ``csrc/*.hip`` is compiled to an object in ``_build/`` (in parallel),
 then linked into ``paged_kv_cache_30_amd/libpagedattn.so``.  Packed FP32

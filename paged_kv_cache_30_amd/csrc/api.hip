@@ -1,8 +1,9 @@
 // C ABI of the library: argument checks, partition sizing, launches on the
 // caller's stream. Declarations and the contract are in paged_attn.h.
-#include "../../include/paged_attn.h"
+#include "paged_attn.h"
 
 #include <math.h>
+#include <stdint.h>
 
 #include "launch.h"
 
@@ -47,27 +48,29 @@ int span_blocks(const pkv_geometry_t* g, int max_context_len, int window) {
   return n;
 }
 
-// Automatic partition length: aim for enough workgroups to fill 256 compute
-// units several times over, with partitions of at least 8 blocks, at most 64.
-int auto_partition_blocks(const pkv_geometry_t* g, int num_seqs, int max_context_len, int window) {
-  const int span = span_blocks(g, max_context_len, window);
-  const long long items = (long long)num_seqs * g->num_kv_heads;
-  const long long target_wg = 2048;
-  long long want = items > 0 ? (items * span + target_wg - 1) / target_wg : span;
-  int bpp = 8;
-  while (bpp < want && bpp < 64) bpp *= 2;
-  if (bpp > span) bpp = span > 0 ? span : 1;
-  return bpp;
-}
+// Decode work split: num_workers wavefronts (0 = automatic, but no more than
+// the attended blocks could occupy) and the workspace layout for them.
+struct DecodeSplit {
+  int workers;
+  size_t cum_bytes, ml_bytes, o_bytes;
+  size_t total() const { return cum_bytes + ml_bytes + o_bytes; }
+};
 
-int decode_split(const pkv_geometry_t* g, int num_seqs, int max_context_len, int window,
-                 int partition_size, int* bpp, int* n_part) {
-  if (partition_size < 0 || (partition_size % g->block_size)) return PKV_EINVAL;
-  *bpp = partition_size ? partition_size / g->block_size
-                        : auto_partition_blocks(g, num_seqs, max_context_len, window);
-  const int span = span_blocks(g, max_context_len, window);
-  *n_part = span > 0 ? ceil_div(span, *bpp) : 1;
-  if (*n_part < 1) *n_part = 1;
+int decode_split(const pkv_geometry_t* g, int num_seqs, int max_context_len, int window, int num_workers,
+                 DecodeSplit* out) {
+  if (num_workers < 0) return PKV_EINVAL;
+  const int G = g->num_heads / g->num_kv_heads;
+  int nw = num_workers;
+  if (nw == 0) {
+    const long long bound = (long long)num_seqs * g->num_kv_heads * span_blocks(g, max_context_len, window);
+    nw = pkv::decode_auto_workers(g->kv_dtype, g->head_dim, g->block_size, G);
+    if (bound < nw) nw = bound > 0 ? (int)bound : 1;
+  }
+  const size_t slots = (size_t)nw + (size_t)num_seqs * g->num_kv_heads;
+  out->workers = nw;
+  out->cum_bytes = (((size_t)num_seqs + 1) * sizeof(int32_t) + 255) / 256 * 256;
+  out->ml_bytes = (slots * G * 2 * sizeof(float) + 255) / 256 * 256;
+  out->o_bytes = slots * G * g->head_dim * sizeof(float);
   return PKV_OK;
 }
 
@@ -91,48 +94,47 @@ int paged_kv_write(const pkv_geometry_t* geom, void* k_pool, void* v_pool, const
   return hip_status(pkv::launch_kv_write(a, (hipStream_t)stream));
 }
 
-int32_t paged_attn_decode_auto_partition(const pkv_geometry_t* geom, int32_t num_seqs,
-                                         int32_t max_context_len, int32_t window) {
+int32_t paged_attn_decode_workers(const pkv_geometry_t* geom, int32_t num_seqs, int32_t max_context_len,
+                                  int32_t window) {
   if (check_geometry(geom) || num_seqs < 0 || max_context_len < 0 || window < 0) return 0;
-  return auto_partition_blocks(geom, num_seqs, max_context_len, window) * geom->block_size;
+  DecodeSplit sp;
+  if (decode_split(geom, num_seqs, max_context_len, window, 0, &sp)) return 0;
+  return sp.workers;
 }
 
 size_t paged_attn_decode_workspace_bytes(const pkv_geometry_t* geom, int32_t num_seqs,
-                                         int32_t max_context_len, int32_t window,
-                                         int32_t partition_size) {
-  if (check_geometry(geom) || num_seqs < 0 || max_context_len < 0 || window < 0) return 0;
-  int bpp, n_part;
-  if (decode_split(geom, num_seqs, max_context_len, window, partition_size, &bpp, &n_part)) return 0;
-  if (n_part == 1) return 0;
-  return (size_t)num_seqs * geom->num_heads * n_part * (geom->head_dim + 2) * sizeof(float);
+                                         int32_t max_context_len, int32_t window, int32_t num_workers) {
+  if (check_geometry(geom) || num_seqs <= 0 || max_context_len < 0 || window < 0) return 0;
+  DecodeSplit sp;
+  if (decode_split(geom, num_seqs, max_context_len, window, num_workers, &sp)) return 0;
+  return sp.total();
 }
 
 int paged_attn_decode(const pkv_geometry_t* geom, float* out, float* lse, const void* q,
                       const void* k_pool, const void* v_pool, const int32_t* block_tables,
                       int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
-                      int32_t max_context_len, int32_t window, float scale, int32_t partition_size,
+                      int32_t max_context_len, int32_t window, float scale, int32_t num_workers,
                       void* workspace, size_t workspace_bytes, void* stream) {
   int st = check_geometry(geom);
   if (st) return st;
-  if (num_seqs < 0 || max_blocks_per_seq <= 0 || max_context_len < 0 || window < 0 || !isfinite(scale))
+  if (num_seqs < 0 || max_blocks_per_seq <= 0 || max_context_len < 0 || window < 0 || num_workers < 0 ||
+      !isfinite(scale))
     return PKV_EINVAL;
   if ((long long)max_context_len > (long long)max_blocks_per_seq * geom->block_size) return PKV_EINVAL;
   if (num_seqs == 0) return PKV_OK;
   if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens) return PKV_EINVAL;
   const int G = geom->num_heads / geom->num_kv_heads;
   if (!pkv::decode_supported(geom->kv_dtype, geom->head_dim, geom->block_size, G)) return PKV_EUNSUPPORTED;
-  int bpp, n_part;
-  st = decode_split(geom, num_seqs, max_context_len, window, partition_size, &bpp, &n_part);
+  DecodeSplit sp;
+  st = decode_split(geom, num_seqs, max_context_len, window, num_workers, &sp);
   if (st) return st;
-  const size_t need = n_part == 1 ? 0
-                                  : (size_t)num_seqs * geom->num_heads * n_part * (geom->head_dim + 2) * sizeof(float);
-  if (need && (!workspace || workspace_bytes < need)) return PKV_EWORKSPACE;
-  float* ws_o = (float*)workspace;
-  float* ws_ml = need ? ws_o + (size_t)num_seqs * geom->num_heads * n_part * geom->head_dim : nullptr;
-  pkv::DecodeArgs a{out, lse, q, k_pool, v_pool, block_tables, context_lens, ws_o, ws_ml,
+  if (!workspace || workspace_bytes < sp.total() || ((uintptr_t)workspace & 15)) return PKV_EWORKSPACE;
+  char* ws = (char*)workspace;
+  pkv::DecodeArgs a{out, lse, q, k_pool, v_pool, block_tables, context_lens,
+                    (int32_t*)ws, (float*)(ws + sp.cum_bytes), (float*)(ws + sp.cum_bytes + sp.ml_bytes),
                     num_seqs, geom->num_heads, geom->num_kv_heads, geom->head_dim, geom->block_size,
                     max_blocks_per_seq, geom->num_blocks, window, geom->kv_dtype, max_context_len,
-                    bpp, n_part, scale};
+                    sp.workers, scale};
   return hip_status(pkv::launch_decode(a, (hipStream_t)stream));
 }
 

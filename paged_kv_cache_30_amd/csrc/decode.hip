@@ -1,269 +1,480 @@
-// Single-query decode through the block table (split-K over blocks).
+// Single-query decode through the block table, split evenly over wavefronts.
 //
 // What it computes ("Build a Paged KV Cache in Pure Python", Step 4; "Building
 // a Streaming Sliding-Window Attention Engine in Pure Python", Step 3): for
 // every sequence s and query head h, softmax(scale * q.K^T) V over positions
 // [lo, L) of the sequence, fetched through its block table.
 //
-// How, on gfx950:
-//  * Work item = (sequence, kv head, partition of consecutive blocks). One
-//    256-thread workgroup (4 wavefronts) per item; wavefront w takes blocks
-//    w, w+4, ... of the partition. Every query head of the kv head's group is
-//    processed with each loaded page, so a K/V page is read from HBM once per
-//    group.
-//  * Lane layout: a K or V row (D elements of one position and kv head) is
-//    D*bytes/16 lanes x 16 bytes. A wavefront load covers 64/(lanes per row)
-//    consecutive slots of a block; the lanes of one row hold a slice of the
-//    head dimension. Scores are a dot product on each lane's slice followed by
-//    a DPP reduction across the row's lanes.
-//  * Each row group of lanes keeps its own running maximum and sum (online
-//    softmax in base 2: scores are scaled by scale*log2(e)), so nothing is
-//    exchanged between row groups inside the block loop. At the end the
-//    wavefronts' and row groups' states are merged through LDS.
-//  * One partition per (sequence, kv head) writes the output directly;
-//    otherwise each partition writes its unnormalised partial output with its
-//    maximum and sum, and a second kernel merges the partitions:
-//      M = max_i m_i,  out = sum_i 2^(m_i-M) o_i / sum_i 2^(m_i-M) l_i.
-//  * Positions outside [lo, L) (the partial first block of a window, the
-//    partial last block) are removed by selection, never by multiplying with
-//    zero, so whatever the unused slots hold cannot leak in.
+// How, on gfx950 (two launches on the caller's stream):
+//  1. plan: every wavefront (batches under 64 sequences, in a register) or
+//     every workgroup (up to 4096, in LDS) prefix-sums the attended block
+//     count of every sequence (cum[s]; a separate one-workgroup launch writes
+//     it to the workspace instead for larger batches); the
+//     attended (sequence, kv head, block) triples, flattened in that order,
+//     number T = Hkv * cum[S].
+//  2. split: wavefront w of NW takes the flattened range
+//     [w*T/NW, (w+1)*T/NW) - every wavefront gets the same number of blocks
+//     (+-1) however ragged the lengths are, so no wavefront is left running
+//     alone at the end. The range falls into one or a few (sequence, kv head)
+//     segments. For each, the wavefront streams the segment's K/V pages
+//     (16-byte loads; the next chunk's loads are issued before the current
+//     chunk is processed), computes the scores of every query head of the kv
+//     head's group with each page (a page is read from HBM once per group),
+//     keeps a running maximum and sum (online softmax in base 2), merges the
+//     states of its row groups with lane shuffles and writes one partial
+//     (max, sum, unnormalised output) per head.
+//  3. merge: per (sequence, query head) the partials of the wavefronts whose
+//     ranges cover it are combined exactly:
+//       M = max_i m_i,  out = sum_i 2^(m_i-M) o_i / sum_i 2^(m_i-M) l_i.
+//  Lane layout: a K or V row (D elements of one position and kv head) is
+//  D*bytes/16 lanes x 16 bytes; one wavefront load covers 64/(lanes per row)
+//  consecutive slots of a block. Scores are a dot product on each lane's
+//  slice (v_dot2 for 16-bit types) and a DPP reduction across the row.
+//  Positions outside [lo, L) (the partial first block of a window, the
+//  partial last block) are removed by selection, never by multiplying with
+//  zero, so whatever unused slots hold cannot leak in.
 #include "common.h"
 #include "launch.h"
+
+#ifndef PKV_DECODE_CHUNK_LOADS
+#define PKV_DECODE_CHUNK_LOADS(G) 4
+#endif
 
 namespace pkv {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
+constexpr int kPlanThreads = 1024;
 
 template <class T, int D, int B, int G>
 struct DecodeShape {
   static constexpr int EB = T::BYTES;
-  static constexpr int E = 16 / EB;            // elements per lane chunk
-  static constexpr int LPR = D * EB / 16;      // lanes per K/V row
-  static constexpr int RPL = 64 / LPR;         // rows per wavefront load
-  static constexpr int STEPS = B / RPL;        // wavefront loads per block
-  static constexpr int STATES = kWaves * RPL;  // softmax states per workgroup
-  static_assert(LPR >= 4 && LPR <= 32 && B % RPL == 0, "shape");
+  static constexpr int E = 16 / EB;                    // elements per lane chunk
+  static constexpr int LPR = D * EB / 16;              // lanes per K/V row
+  static constexpr int RPL = 64 / LPR;                 // rows per wavefront load
+  static constexpr int STEPS = B / RPL;                // wavefront loads per block
+  // Wavefront loads per chunk (of K and of V); two chunks are in registers at
+  // a time (16 KB in flight per wavefront).
+  static constexpr int CWANT = PKV_DECODE_CHUNK_LOADS(G);
+  static constexpr int CSTEPS = STEPS < CWANT ? STEPS : CWANT;
+  static constexpr int CHUNK = RPL * CSTEPS;           // slots per chunk
+  static constexpr int CPB = B / CHUNK;                // chunks per block
+  static_assert(LPR >= 4 && LPR <= 32 && B % CHUNK == 0, "shape");
 };
 
+// Attended blocks of a sequence: [lo / B, ceil(L / B)), L clamped to
+// [0, max_ctx], lo = max(0, L - window) with a window.
+__device__ __forceinline__ void attended(int L, int max_ctx, int window, int B, int& L_out, int& lo,
+                                         int& blk_lo, int& nblk) {
+  L = L < 0 ? 0 : (L > max_ctx ? max_ctx : L);
+  lo = window > 0 ? max(0, L - window) : 0;
+  blk_lo = lo / B;
+  nblk = L > 0 ? (L + B - 1) / B - blk_lo : 0;
+  L_out = L;
+}
+
+// cum[s] = attended blocks of sequences 0 .. s-1 for s <= S, computed by all
+// NT threads of the workgroup (a block-wide scan, NT/64 wavefronts).
+template <int NT>
+__device__ void prefix_blocks(const DecodeArgs& a, int32_t* cum) {
+  __shared__ int wave_sum[NT / 64];
+  __shared__ int carry_sh;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  if (tid == 0) carry_sh = 0;
+  __syncthreads();
+  for (int base = 0; base < a.S; base += NT) {
+    const int s = base + tid;
+    int v = 0;
+    if (s < a.S) {
+      int L, lo, b0, n;
+      attended(a.lens[s], a.max_context_len, a.window, a.B, L, lo, b0, n);
+      v = n;
+    }
+    int x = v;  // inclusive scan inside the wavefront
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(x, off, 64);
+      if (lane >= off) x += y;
+    }
+    if (lane == 63) wave_sum[wv] = x;
+    __syncthreads();
+    int before = carry_sh;
+    for (int i = 0; i < wv; ++i) before += wave_sum[i];
+    if (s < a.S) cum[s] = before + x - v;
+    __syncthreads();
+    if (tid == NT - 1) carry_sh = before + x;
+    __syncthreads();
+  }
+  if (tid == 0) cum[a.S] = carry_sh;
+  __syncthreads();
+}
+
+// Batches of more than kLdsSeqs sequences get their prefix from a separate
+// one-workgroup launch; smaller ones compute it in every workgroup (LDS).
+constexpr int kLdsSeqs = 4096;
+
+__global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(DecodeArgs a) {
+  prefix_blocks<kPlanThreads>(a, a.ws_cum);
+}
+
 template <class T, int D, int B, int G>
-__global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a, int max_ctx, float scale_log2) {
+__global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, float scale_log2) {
   using Sh = DecodeShape<T, D, B, G>;
-  constexpr int E = Sh::E, LPR = Sh::LPR, RPL = Sh::RPL, STEPS = Sh::STEPS, EB = Sh::EB;
-  __shared__ float sh_o[Sh::STATES][G][D];
-  __shared__ float sh_m[Sh::STATES][G];
-  __shared__ float sh_l[Sh::STATES][G];
+  constexpr int E = Sh::E, LPR = Sh::LPR, RPL = Sh::RPL, CSTEPS = Sh::CSTEPS, CHUNK = Sh::CHUNK,
+                CPB = Sh::CPB, EB = Sh::EB;
 
   const int lane = threadIdx.x & 63;
-  const int wave = uniform(threadIdx.x >> 6);
+  // Prefix of attended blocks, in one of three places: batches of fewer than
+  // 64 sequences keep it in a register of every wavefront (lane i holds
+  // cum[i] and the length of sequence i; no LDS, no barrier), batches up to
+  // kLdsSeqs in LDS, larger ones in the workspace (separate launch).
+  __shared__ int32_t cum_sh[kLdsSeqs + 1];
+  const bool in_reg = a.S < 64;
+  const int32_t* cum_mem = a.ws_cum;
+  int cum_reg = 0, len_reg = 0;
+  if (in_reg) {
+    int v = 0;
+    if (lane < a.S) {
+      len_reg = a.lens[lane];
+      int L, lo, b0, n;
+      attended(len_reg, a.max_context_len, a.window, B, L, lo, b0, n);
+      v = n;
+    }
+    int x = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(x, off, 64);
+      if (lane >= off) x += y;
+    }
+    cum_reg = x - v;  // exclusive: lane S holds the total
+    if (blockIdx.x == 0 && threadIdx.x < 64 && lane <= a.S) a.ws_cum[lane] = cum_reg;  // for the merge pass
+  } else if (a.S <= kLdsSeqs) {
+    prefix_blocks<kThreads>(a, cum_sh);
+    cum_mem = cum_sh;
+    if (blockIdx.x == 0)  // the merge pass reads the prefix from the workspace
+      for (int i = threadIdx.x; i <= a.S; i += kThreads) a.ws_cum[i] = cum_sh[i];
+  }
+  // cum[i] and lens[i] for a wavefront-uniform i.
+  auto cum = [&](int i) -> int { return in_reg ? __builtin_amdgcn_readlane(cum_reg, i) : cum_mem[i]; };
+  auto len_of = [&](int i) -> int { return in_reg ? __builtin_amdgcn_readlane(len_reg, i) : a.lens[i]; };
+
+  const int w = blockIdx.x * kWaves + uniform(threadIdx.x >> 6);  // worker index
   const int c = lane % LPR;
   const int r = lane / LPR;
-  const int part = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
-  const int H = a.Hkv * G;
+  const int Hkv = a.Hkv, H = Hkv * G;
+  const long long total = (long long)Hkv * cum(a.S);
+  // Workers beyond the number of blocks stay idle, so every active worker
+  // has at least one block.
+  const long long nw = total < a.n_workers ? total : a.n_workers;
+  if (w >= nw) return;
+  const long long start = (long long)w * total / nw;
+  const long long end = (long long)(w + 1) * total / nw;
 
-  int L = a.lens[s];
-  L = L < 0 ? 0 : (L > max_ctx ? max_ctx : L);
-  const int lo = a.window > 0 ? max(0, L - a.window) : 0;
-  const int blk_lo = lo / B;
-  const int blk_hi = (L + B - 1) / B;
-  const int b0 = blk_lo + part * a.blocks_per_part;
-  const int b1 = min(b0 + a.blocks_per_part, blk_hi);
-  const bool direct = a.n_part == 1;
-  if (!direct && b0 >= b1) return;  // the merge pass knows this partition is empty
-
-  // Query rows of the group, this lane's slice.
-  const char* qb = (const char*)a.q + ((size_t)(s * H + g * G) * D + c * E) * EB;
-  u32x4 qv[G];
-#pragma unroll
-  for (int h = 0; h < G; ++h) qv[h] = load16(qb + (size_t)h * D * EB);
-
-  float m[G], l[G], o[G][E];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    m[h] = -INFINITY;
-    l[h] = 0.f;
-#pragma unroll
-    for (int e = 0; e < E; ++e) o[h][e] = 0.f;
+  // Sequence holding flattened index `start`: the largest s with
+  // Hkv*cum[s] <= start.
+  int s;
+  if (in_reg) {
+    const unsigned long long msk = __ballot(lane < a.S && (long long)Hkv * cum_reg <= start);
+    s = 63 - __builtin_clzll(msk);  // lane 0 always qualifies
+  } else {  // 64 candidates at a time
+    int s_lo = 0, s_hi = a.S;  // invariant: Hkv*cum[s_lo] <= start < Hkv*cum[s_hi]
+    while (s_hi - s_lo > 1) {
+      const int step = (s_hi - s_lo + 63) / 64;
+      const int probe = s_lo + lane * step;
+      const bool le = probe < s_hi && (long long)Hkv * cum_mem[probe] <= start;
+      const unsigned long long msk = __ballot(le);
+      const int k = 63 - __builtin_clzll(msk);  // lane 0 always qualifies
+      s_lo = s_lo + k * step;
+      s_hi = min(s_hi, s_lo + step);
+    }
+    s = s_lo;
   }
 
-  const size_t row_stride = (size_t)a.Hkv * D * EB;  // bytes between slots
+  const size_t row_stride = (size_t)Hkv * D * EB;  // bytes between slots
   const size_t blk_stride = row_stride * B;
-  const size_t lane_off = (size_t)g * D * EB + (size_t)c * 16 + (size_t)r * row_stride;
-  const char* kbase = (const char*)a.k_pool + lane_off;
-  const char* vbase = (const char*)a.v_pool + lane_off;
-  const int32_t* trow = a.tables + (size_t)s * a.mb;
+  float m[G], l[G], o[G][E];
 
-  for (int b = b0 + wave; b < b1; b += kWaves) {
-    const int pb = trow[b];
-    if (pb < 0 || pb >= a.nb) continue;
-    const char* kp = kbase + (size_t)pb * blk_stride;
-    const char* vp = vbase + (size_t)pb * blk_stride;
-    u32x4 kr[STEPS], vr[STEPS];
-#pragma unroll
-    for (int j = 0; j < STEPS; ++j) kr[j] = load16(kp + (size_t)j * RPL * row_stride);
-#pragma unroll
-    for (int j = 0; j < STEPS; ++j) vr[j] = load16(vp + (size_t)j * RPL * row_stride);
+  for (long long pos = start; pos < end;) {
+    while ((long long)Hkv * cum(s + 1) <= pos) ++s;
+    const int c0 = cum(s);
+    const int nblk = cum(s + 1) - c0;
+    const long long rel = pos - (long long)Hkv * c0;
+    const int g = (int)(rel / nblk);
+    const int b_first = (int)(rel - (long long)g * nblk);
+    const long long seg_end = min(end, (long long)Hkv * c0 + (long long)(g + 1) * nblk);
+    const int n = (int)(seg_end - pos);
 
-    const int t0 = b * B;
-    const bool full = t0 >= lo && t0 + B <= L;
-    float sc[STEPS][G];
+    int L, lo, blk_lo, nb_unused;
+    attended(len_of(s), a.max_context_len, a.window, B, L, lo, blk_lo, nb_unused);
+    const int32_t* trow = a.tables + (size_t)s * a.mb + blk_lo + b_first;
+    const int blk0 = blk_lo + b_first;  // first logical block of the segment
+    int tv = lane < n ? trow[lane] : -1;  // table entries of blocks 0..63 of the segment
+
+    const char* qb = (const char*)a.q + ((size_t)(s * H + g * G) * D + c * E) * EB;
+    u32x4 qv[G];
 #pragma unroll
-    for (int j = 0; j < STEPS; ++j) {
-#pragma unroll
-      for (int h = 0; h < G; ++h) sc[j][h] = group_sum<LPR>(dot_chunk<T>(qv[h], kr[j], 0.f)) * scale_log2;
-    }
-    if (!full) {
-#pragma unroll
-      for (int j = 0; j < STEPS; ++j) {
-        const int t = t0 + j * RPL + r;
-        const bool ok = t >= lo && t < L;
-#pragma unroll
-        for (int h = 0; h < G; ++h) sc[j][h] = ok ? sc[j][h] : -INFINITY;
-      }
-    }
-    // Online softmax update, one state per (row group, head).
+    for (int h = 0; h < G; ++h) qv[h] = load16(qb + (size_t)h * D * EB);
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      float mb = sc[0][h];
+      m[h] = -INFINITY;
+      l[h] = 0.f;
 #pragma unroll
-      for (int j = 1; j < STEPS; ++j) mb = fmaxf(mb, sc[j][h]);
-      const float mn = fmaxf(m[h], mb);
-      const float ms = mn == -INFINITY ? 0.f : mn;
-      const float alpha = __builtin_amdgcn_exp2f(m[h] - ms);
-      l[h] *= alpha;
-#pragma unroll
-      for (int e = 0; e < E; ++e) o[h][e] *= alpha;
-      m[h] = mn;
-#pragma unroll
-      for (int j = 0; j < STEPS; ++j) {
-        const float p = __builtin_amdgcn_exp2f(sc[j][h] - ms);
-        sc[j][h] = p;
-        l[h] += p;
-      }
+      for (int e = 0; e < E; ++e) o[h][e] = 0.f;
     }
+    const size_t lane_off = (size_t)g * D * EB + (size_t)c * 16 + (size_t)r * row_stride;
+    const char* kbase = (const char*)a.k_pool + lane_off;
+    const char* vbase = (const char*)a.v_pool + lane_off;
+
+    // Loads of chunk k of the segment; false when its table entry is out of
+    // range (the chunk is skipped).
+    auto issue = [&](int k, u32x4* kr, u32x4* vr) -> bool {
+      const int bi = k / CPB;
+      const int sub = k - bi * CPB;
+      if ((bi & 63) == 0 && bi > 0 && sub == 0) tv = bi + lane < n ? trow[bi + lane] : -1;
+      const int pb = __builtin_amdgcn_readlane(tv, bi & 63);
+      if (pb < 0 || pb >= a.nb) return false;
+      const size_t off = (size_t)pb * blk_stride + (size_t)sub * CHUNK * row_stride;
 #pragma unroll
-    for (int j = 0; j < STEPS; ++j) {
-      float vf[E];
-      chunk_to_f32<T>(vr[j], vf);
+      for (int j = 0; j < CSTEPS; ++j) kr[j] = load_stream(kbase + off + (size_t)j * RPL * row_stride);
+#pragma unroll
+      for (int j = 0; j < CSTEPS; ++j) vr[j] = load_stream(vbase + off + (size_t)j * RPL * row_stride);
+      return true;
+    };
+
+    // Scores, online-softmax update and P.V for chunk k.
+    auto process = [&](int k, const u32x4* kr, const u32x4* vr) {
+      const int bi = k / CPB;
+      const int sub = k - bi * CPB;
+      const int t0 = (blk0 + bi) * B + sub * CHUNK;
+      const bool full = t0 >= lo && t0 + CHUNK <= L;
+      float sc[CSTEPS][G];
+#pragma unroll
+      for (int j = 0; j < CSTEPS; ++j) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) sc[j][h] = group_sum<LPR>(dot_chunk<T>(qv[h], kr[j], 0.f)) * scale_log2;
+      }
       if (!full) {
-        const int t = t0 + j * RPL + r;
-        const bool ok = t >= lo && t < L;
 #pragma unroll
-        for (int e = 0; e < E; ++e) vf[e] = ok ? vf[e] : 0.f;
+        for (int j = 0; j < CSTEPS; ++j) {
+          const int t = t0 + j * RPL + r;
+          const bool ok = t >= lo && t < L;
+#pragma unroll
+          for (int h = 0; h < G; ++h) sc[j][h] = ok ? sc[j][h] : -INFINITY;
+        }
       }
 #pragma unroll
       for (int h = 0; h < G; ++h) {
+        float mb = sc[0][h];
 #pragma unroll
-        for (int e = 0; e < E; ++e) o[h][e] = __builtin_fmaf(sc[j][h], vf[e], o[h][e]);
+        for (int j = 1; j < CSTEPS; ++j) mb = fmaxf(mb, sc[j][h]);
+        const float mn = fmaxf(m[h], mb);
+        const float ms = mn == -INFINITY ? 0.f : mn;
+        const float alpha = __builtin_amdgcn_exp2f(m[h] - ms);
+        l[h] *= alpha;
+#pragma unroll
+        for (int e = 0; e < E; ++e) o[h][e] *= alpha;
+        m[h] = mn;
+#pragma unroll
+        for (int j = 0; j < CSTEPS; ++j) {
+          const float p = __builtin_amdgcn_exp2f(sc[j][h] - ms);
+          sc[j][h] = p;
+          l[h] += p;
+        }
       }
-    }
-  }
+#pragma unroll
+      for (int j = 0; j < CSTEPS; ++j) {
+        float vf[E];
+        chunk_to_f32<T>(vr[j], vf);
+        if (!full) {
+          const int t = t0 + j * RPL + r;
+          const bool ok = t >= lo && t < L;
+#pragma unroll
+          for (int e = 0; e < E; ++e) vf[e] = ok ? vf[e] : 0.f;
+        }
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+#pragma unroll
+          for (int e = 0; e < E; ++e) o[h][e] = __builtin_fmaf(sc[j][h], vf[e], o[h][e]);
+        }
+      }
+    };
 
-  // Merge the STATES = waves x row-groups states of this workgroup.
-  const int st = wave * RPL + r;
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-#pragma unroll
-    for (int e = 0; e < E; ++e) sh_o[st][h][c * E + e] = o[h][e];
-    if (c == 0) {
-      sh_m[st][h] = m[h];
-      sh_l[st][h] = l[h];
+    // Two register sets: the next chunk's loads are in flight while the
+    // current chunk is processed.
+    const int nchunks = n * CPB;
+    u32x4 ka[CSTEPS], va[CSTEPS], kb[CSTEPS], vb[CSTEPS];
+    bool oka = issue(0, ka, va);
+    for (int k = 0; k < nchunks; k += 2) {
+      const bool okb = k + 1 < nchunks && issue(k + 1, kb, vb);
+      if (oka) process(k, ka, va);
+      oka = k + 2 < nchunks && issue(k + 2, ka, va);
+      if (okb) process(k + 1, kb, vb);
     }
-  }
-  __syncthreads();
-  for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
-    const int h = idx / D;
-    const int d = idx - h * D;
-    float M = -INFINITY;
+
+    // Merge the row groups' states (lanes r*LPR + c, same c) with shuffles.
 #pragma unroll
-    for (int i = 0; i < Sh::STATES; ++i) M = fmaxf(M, sh_m[i][h]);
-    const float Ms = M == -INFINITY ? 0.f : M;
-    float sl = 0.f, so = 0.f;
+    for (int off = LPR; off < 64; off <<= 1) {
 #pragma unroll
-    for (int i = 0; i < Sh::STATES; ++i) {
-      const float w = __builtin_amdgcn_exp2f(sh_m[i][h] - Ms);
-      sl = __builtin_fmaf(w, sh_l[i][h], sl);
-      so = __builtin_fmaf(w, sh_o[i][h][d], so);
-    }
-    const size_t row = (size_t)s * H + g * G + h;
-    if (direct) {
-      a.out[row * D + d] = sl > 0.f ? so / sl : 0.f;
-      if (a.lse && d == 0) a.lse[row] = sl > 0.f ? (M + __log2f(sl)) * kLn2 : -INFINITY;
-    } else {
-      const size_t slot = row * a.n_part + part;
-      a.ws_o[slot * D + d] = so;
-      if (d == 0) {
-        a.ws_ml[slot * 2] = M;
-        a.ws_ml[slot * 2 + 1] = sl;
+      for (int h = 0; h < G; ++h) {
+        const float mo = __shfl_xor(m[h], off, 64);
+        const float lo_ = __shfl_xor(l[h], off, 64);
+        const float M = fmaxf(m[h], mo);
+        const float Ms = M == -INFINITY ? 0.f : M;
+        const float fa = __builtin_amdgcn_exp2f(m[h] - Ms);
+        const float fb = __builtin_amdgcn_exp2f(mo - Ms);
+        l[h] = fa * l[h] + fb * lo_;
+#pragma unroll
+        for (int e = 0; e < E; ++e) o[h][e] = fa * o[h][e] + fb * __shfl_xor(o[h][e], off, 64);
+        m[h] = M;
       }
     }
+    // One partial per head, slot w + s*Hkv + g (unique: see the merge).
+    const size_t slot = (size_t)w + (size_t)s * Hkv + g;
+    if (r == 0) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float* dst = a.ws_o + (slot * G + h) * D + c * E;
+#pragma unroll
+        for (int e = 0; e < E; e += 4)
+          *reinterpret_cast<float4*>(dst + e) = make_float4(o[h][e], o[h][e + 1], o[h][e + 2], o[h][e + 3]);
+        if (c == 0) *reinterpret_cast<float2*>(a.ws_ml + (slot * G + h) * 2) = make_float2(m[h], l[h]);
+      }
+    }
+    pos = seg_end;
   }
 }
 
-// Merge of the partitions of one (sequence, query head): one thread per
-// output element of the head.
-template <int D, int B>
-__global__ __launch_bounds__(D) void decode_merge_kernel(DecodeArgs a, int max_ctx) {
+// Merge of the partials of one (sequence, query head): one thread per output
+// element. With NW = min(workers, T) active wavefronts, wavefront w holds
+// [w*T/NW, (w+1)*T/NW) (never empty), so flattened index i lies in wavefront
+// ((i + 1) * NW - 1) / T and the range [x, y) of (s, g) is covered by
+// wavefronts w_lo .. w_hi, each of which wrote its partial of (s, g) in slot
+// w + s*Hkv + g. Within a wavefront those slots are distinct, and a later
+// wavefront's (s, g) is never earlier, so no two writers share a slot.
+template <int D, int G>
+__global__ __launch_bounds__(D) void decode_merge_kernel(DecodeArgs a) {
   const int hq = blockIdx.x, s = blockIdx.y, d = threadIdx.x;
-  int L = a.lens[s];
-  L = L < 0 ? 0 : (L > max_ctx ? max_ctx : L);
-  const int lo = a.window > 0 ? max(0, L - a.window) : 0;
-  const int nblk = (L + B - 1) / B - lo / B;
-  const int nvalid = nblk > 0 ? (nblk + a.blocks_per_part - 1) / a.blocks_per_part : 0;
+  const int g = hq / G, hh = hq - g * G;
+  const int Hkv = a.Hkv;
   const size_t row = (size_t)s * a.H + hq;
-  const float* ml = a.ws_ml + row * a.n_part * 2;
-  const float* po = a.ws_o + row * a.n_part * D;
-  float M = -INFINITY;
-  for (int i = 0; i < nvalid; ++i) M = fmaxf(M, ml[2 * i]);
-  const float Ms = M == -INFINITY ? 0.f : M;
-  float sl = 0.f, so = 0.f;
-  for (int i = 0; i < nvalid; ++i) {
-    const float w = __builtin_amdgcn_exp2f(ml[2 * i] - Ms);
-    sl = __builtin_fmaf(w, ml[2 * i + 1], sl);
-    so = __builtin_fmaf(w, po[(size_t)i * D + d], so);
+  const int c0 = a.ws_cum[s];
+  const int nblk = a.ws_cum[s + 1] - c0;
+  float M = -INFINITY, sl = 0.f, so = 0.f;
+  if (nblk > 0) {
+    const long long total = (long long)Hkv * a.ws_cum[a.S];
+    const long long NW = total < a.n_workers ? total : a.n_workers;
+    const long long x = (long long)Hkv * c0 + (long long)g * nblk;
+    const long long y = x + nblk;
+    const int w_lo = (int)(((x + 1) * NW - 1) / total);
+    const int w_hi = (int)((y * NW - 1) / total);
+    const size_t base = ((size_t)s * Hkv + g) * G + hh;  // slot of worker 0, head hh
+    // Eight partials at a time, their loads issued together.
+    constexpr int U = 8;
+    for (int w0 = w_lo; w0 <= w_hi; w0 += U) {
+      float mv[U];
+#pragma unroll
+      for (int j = 0; j < U; ++j)
+        mv[j] = w0 + j <= w_hi ? a.ws_ml[(base + (size_t)(w0 + j) * G) * 2] : -INFINITY;
+#pragma unroll
+      for (int j = 0; j < U; ++j) M = fmaxf(M, mv[j]);
+    }
+    const float Ms = M == -INFINITY ? 0.f : M;
+    for (int w0 = w_lo; w0 <= w_hi; w0 += U) {
+      float2 ml[U];
+      float ov[U];
+#pragma unroll
+      for (int j = 0; j < U; ++j) {
+        const size_t slot = base + (size_t)(w0 + j) * G;
+        const bool ok = w0 + j <= w_hi;
+        ml[j] = ok ? *reinterpret_cast<const float2*>(a.ws_ml + slot * 2) : make_float2(-INFINITY, 0.f);
+        ov[j] = ok ? a.ws_o[slot * D + d] : 0.f;
+      }
+#pragma unroll
+      for (int j = 0; j < U; ++j) {
+        const float f = __builtin_amdgcn_exp2f(ml[j].x - Ms);
+        sl = __builtin_fmaf(f, ml[j].y, sl);
+        so = __builtin_fmaf(f, ov[j], so);
+      }
+    }
   }
   a.out[row * D + d] = sl > 0.f ? so / sl : 0.f;
   if (a.lse && d == 0) a.lse[row] = sl > 0.f ? (M + __log2f(sl)) * kLn2 : -INFINITY;
 }
 
 template <class T, int D, int B, int G>
-static hipError_t launch_typed(const DecodeArgs& a, int max_ctx, hipStream_t st) {
-  const float scale_log2 = a.scale * kLog2e;
-  dim3 grid(a.n_part, a.Hkv, a.S);
-  hipLaunchKernelGGL((decode_partition_kernel<T, D, B, G>), grid, dim3(kThreads), 0, st, a, max_ctx, scale_log2);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.n_part == 1) return e;
-  hipLaunchKernelGGL((decode_merge_kernel<D, B>), dim3(a.H, a.S), dim3(D), 0, st, a, max_ctx);
-  return hipGetLastError();
-}
-
-template <class T, int D, int B>
-static hipError_t by_group(const DecodeArgs& a, int max_ctx, hipStream_t st) {
-  switch (a.H / a.Hkv) {
-    case 1: return launch_typed<T, D, B, 1>(a, max_ctx, st);
-    case 2: return launch_typed<T, D, B, 2>(a, max_ctx, st);
-    case 4: return launch_typed<T, D, B, 4>(a, max_ctx, st);
-    case 8: return launch_typed<T, D, B, 8>(a, max_ctx, st);
+struct DecodeKernels {
+  static hipError_t launch(const DecodeArgs& a, hipStream_t st) {
+    hipError_t e;
+    if (a.S > kLdsSeqs) {
+      hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(kPlanThreads), 0, st, a);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    const int grid = (a.n_workers + kWaves - 1) / kWaves;
+    hipLaunchKernelGGL((decode_split_kernel<T, D, B, G>), dim3(grid), dim3(kThreads), 0, st, a, a.scale * kLog2e);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((decode_merge_kernel<D, G>), dim3(a.H, a.S), dim3(D), 0, st, a);
+    return hipGetLastError();
   }
-  return hipErrorInvalidValue;
-}
-
-template <class T, int D>
-static hipError_t by_block(const DecodeArgs& a, int max_ctx, hipStream_t st) {
-  switch (a.B) {
-    case 16: return by_group<T, D, 16>(a, max_ctx, st);
-    case 32: return by_group<T, D, 32>(a, max_ctx, st);
+  // Workgroups of the split kernel resident per compute unit.
+  static int blocks_per_cu() {
+    static int cached = 0;
+    if (!cached) {
+      int n = 0;
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_split_kernel<T, D, B, G>, kThreads, 0) !=
+              hipSuccess ||
+          n <= 0) {
+        (void)hipGetLastError();
+        n = 2;
+      }
+      cached = n;
+    }
+    return cached;
   }
-  return hipErrorInvalidValue;
-}
+};
 
-template <class T>
-static hipError_t by_dim(const DecodeArgs& a, int max_ctx, hipStream_t st) {
-  switch (a.D) {
-    case 64: return by_block<T, 64>(a, max_ctx, st);
-    case 128: return by_block<T, 128>(a, max_ctx, st);
+template <class T, int D, int B, int G>
+struct LaunchOp {
+  static hipError_t run(const DecodeArgs& a, hipStream_t st) { return DecodeKernels<T, D, B, G>::launch(a, st); }
+};
+template <class T, int D, int B, int G>
+struct OccupancyOp {
+  static int run() { return DecodeKernels<T, D, B, G>::blocks_per_cu(); }
+};
+
+// Runtime (dtype, head dim, block size, group size) -> template instance.
+template <template <class, int, int, int> class Op, class R, class... Args>
+static R dispatch(int dtype, int D, int B, int G, R bad, const Args&... args) {
+#define PKV_G(T_, D_, B_)                               \
+  switch (G) {                                          \
+    case 1: return Op<T_, D_, B_, 1>::run(args...);     \
+    case 2: return Op<T_, D_, B_, 2>::run(args...);     \
+    case 4: return Op<T_, D_, B_, 4>::run(args...);     \
+    case 8: return Op<T_, D_, B_, 8>::run(args...);     \
+  }                                                     \
+  return bad;
+#define PKV_B(T_, D_)            \
+  switch (B) {                   \
+    case 16: { PKV_G(T_, D_, 16) } \
+    case 32: { PKV_G(T_, D_, 32) } \
+  }                              \
+  return bad;
+#define PKV_D(T_)                \
+  switch (D) {                   \
+    case 64: { PKV_B(T_, 64) }   \
+    case 128: { PKV_B(T_, 128) } \
+  }                              \
+  return bad;
+  switch (dtype) {
+    case 0: { PKV_D(F32T) }
+    case 1: { PKV_D(F16T) }
+    case 2: { PKV_D(BF16T) }
   }
-  return hipErrorInvalidValue;
+  return bad;
+#undef PKV_D
+#undef PKV_B
+#undef PKV_G
 }
 
 bool decode_supported(int dtype, int D, int B, int G) {
@@ -271,17 +482,26 @@ bool decode_supported(int dtype, int D, int B, int G) {
          (G == 1 || G == 2 || G == 4 || G == 8);
 }
 
-// Launch. Device-side lengths are clamped to [0, max_context_len], which
-// the host has checked against the table width, so no read leaves the
-// sequence's table row or the partition workspace.
-hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
-  const int max_ctx = a.max_context_len;
-  switch (a.dtype) {
-    case 0: return by_dim<F32T>(a, max_ctx, st);
-    case 1: return by_dim<F16T>(a, max_ctx, st);
-    case 2: return by_dim<BF16T>(a, max_ctx, st);
+// Automatic worker count: whole workgroups per compute unit (an uneven
+// spread leaves some units with more work), enough wavefronts in flight to
+// cover HBM latency (16 KB of loads each; groups of 4 or more query heads
+// spend longer on each chunk, so they get twice as many), within what the
+// unit holds at once.
+int decode_auto_workers(int dtype, int D, int B, int G) {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) {
+    (void)hipGetLastError();
+    cus = 256;
   }
-  return hipErrorInvalidValue;
+  const int resident = dispatch<OccupancyOp, int>(dtype, D, B, G, 2);
+  int per_cu = G >= 4 ? 2 : 1;
+  if (per_cu > resident) per_cu = resident;
+  return cus * per_cu * kWaves;
+}
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
+  return dispatch<LaunchOp, hipError_t>(a.dtype, a.D, a.B, a.H / a.Hkv, hipErrorInvalidValue, a, st);
 }
 
 }  // namespace pkv

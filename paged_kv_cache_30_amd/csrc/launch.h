@@ -26,10 +26,11 @@ struct DecodeArgs {
   const void* v_pool;
   const int32_t* tables;
   const int32_t* lens;
-  float* ws_o;   // [S, H, n_part, D] partial outputs (split mode)
-  float* ws_ml;  // [S, H, n_part, 2] partial running max (log2 units) and sum
+  int32_t* ws_cum;  // [S + 1] attended blocks before each sequence
+  float* ws_ml;     // [slots, G, 2] partial running max (log2 units) and sum
+  float* ws_o;      // [slots, G, D] partial unnormalised outputs
   int32_t S, H, Hkv, D, B, mb, nb, window, dtype, max_context_len;
-  int32_t blocks_per_part, n_part;
+  int32_t n_workers;  // wavefronts the attended blocks are divided among
   float scale;
 };
 
@@ -48,7 +49,11 @@ struct PrefillArgs {
 
 hipError_t launch_kv_write(const WriteArgs& a, hipStream_t st);
 
+
+
 bool decode_supported(int dtype, int D, int B, int G);
+// Decode worker (wavefront) count used when the caller passes 0.
+int decode_auto_workers(int dtype, int D, int B, int G);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
 
 bool prefill_supported(int dtype, int D, int B, int G);

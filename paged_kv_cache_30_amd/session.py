@@ -43,7 +43,7 @@ def int_tensor(a, device="cuda") -> torch.Tensor:
 
 
 class DeviceWorkload:
-    def __init__(self, w, device: str = "cuda", poison: bool = True, partition_size: int = 0,
+    def __init__(self, w, device: str = "cuda", poison: bool = True, num_workers: int = 0,
                  with_lse: bool = True, write_history: bool = True):
         self.w = w
         self.device = device
@@ -63,15 +63,18 @@ class DeviceWorkload:
         self.step_pos = int_tensor(pos, device)
         self.step_k = to_device(k, w.dtype, device)
         self.step_v = to_device(v, w.dtype, device)
-        self.partition_size = partition_size
         self.workspace: Optional[torch.Tensor] = None
-        if w.kind == "decode":
-            nbytes = _lib.paged_attn_decode_workspace_bytes(self.k_pool, w.num_heads, w.num_seqs,
-                                                            w.max_context_len, w.window, partition_size)
-            if nbytes:
-                self.workspace = torch.empty(nbytes // 4, dtype=torch.float32, device=device)
+        self.set_workers(num_workers)
         if write_history:
             self.write_history()
+
+    def set_workers(self, num_workers: int) -> None:
+        """Decode worker count (0 = automatic) and a workspace sized for it."""
+        self.num_workers = num_workers
+        w = self.w
+        if w.kind == "decode":
+            self.workspace = _lib.decode_workspace(self.k_pool, w.num_heads, w.num_seqs, w.max_context_len,
+                                                   w.window, num_workers)
 
     def write_history(self) -> None:
         w = self.w
@@ -92,7 +95,7 @@ class DeviceWorkload:
         if w.kind == "decode":
             _lib.paged_attn_decode(self.out, self.q, self.k_pool, self.v_pool, self.tables, self.lens,
                                    w.max_context_len, window=w.window, scale=w.scale,
-                                   partition_size=self.partition_size, workspace=self.workspace,
+                                   num_workers=self.num_workers, workspace=self.workspace,
                                    lse=self.lse, stream=stream)
         else:
             _lib.paged_attn_prefill(self.out, self.q, self.q_start, self.k_pool, self.v_pool, self.tables,

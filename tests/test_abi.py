@@ -47,18 +47,19 @@ def geo(nb=64, B=16, H=32, Hkv=8, D=128, dt=pkv.PKV_BF16):
 
 def test_workspace_query_matches_split():
     g = geo()
-    # 64 seqs, max 32768 positions, partition of 512 positions (32 blocks)
-    n_part = -(-32768 // 16 // 32)
-    want = 64 * 32 * n_part * (128 + 2) * 4
-    assert pkv.LIB.paged_attn_decode_workspace_bytes(ctypes.byref(g), 64, 32768, 0, 512) == want
-    # window 4096: a sequence spans at most 4096/16 + 1 blocks
-    n_part = -(-(4096 // 16 + 1) // 16)
-    assert pkv.LIB.paged_attn_decode_workspace_bytes(ctypes.byref(g), 16, 32768, 4096, 256) == \
-        16 * 32 * n_part * 130 * 4
-    # one partition -> no workspace
-    assert pkv.LIB.paged_attn_decode_workspace_bytes(ctypes.byref(g), 1, 100, 0, 512) == 0
-    auto = pkv.LIB.paged_attn_decode_auto_partition(ctypes.byref(g), 64, 32768, 0)
-    assert auto > 0 and auto % 16 == 0
+    def expect(S, nw, G=4, D=128):
+        slots = nw + S * 8
+        cum = -(-(S + 1) * 4 // 256) * 256
+        ml = -(-slots * G * 2 * 4 // 256) * 256
+        return cum + ml + slots * G * D * 4
+    assert pkv.LIB.paged_attn_decode_workspace_bytes(ctypes.byref(g), 64, 32768, 0, 512) == expect(64, 512)
+    assert pkv.LIB.paged_attn_decode_workspace_bytes(ctypes.byref(g), 1, 100, 0, 1) == expect(1, 1)
+    # automatic: never more workers than the attended blocks could occupy
+    auto = pkv.LIB.paged_attn_decode_workers(ctypes.byref(g), 1, 100, 0)
+    assert 1 <= auto <= 8 * 7
+    assert pkv.LIB.paged_attn_decode_workspace_bytes(ctypes.byref(g), 1, 100, 0, 0) == expect(1, auto)
+    big = pkv.LIB.paged_attn_decode_workers(ctypes.byref(g), 64, 32768, 0)
+    assert big >= 1
 
 
 def call_decode(g, **over):
@@ -78,15 +79,18 @@ def test_argument_errors_before_any_launch():
     assert call_decode(g, out=None) == pkv.PKV_EINVAL
     assert call_decode(g, window=-1) == pkv.PKV_EINVAL
     assert call_decode(g, maxc=8 * 16 + 1) == pkv.PKV_EINVAL
-    assert call_decode(g, part=24) == pkv.PKV_EINVAL
+    assert call_decode(g, part=-1) == pkv.PKV_EINVAL
     assert call_decode(g, scale=float("nan")) == pkv.PKV_EINVAL
     assert call_decode(geo(D=96)) == pkv.PKV_EUNSUPPORTED
     assert call_decode(geo(B=8)) == pkv.PKV_EUNSUPPORTED
     assert call_decode(geo(H=24, Hkv=8)) == pkv.PKV_EUNSUPPORTED
     assert call_decode(geo(H=30, Hkv=8)) == pkv.PKV_EINVAL
     assert call_decode(geo(dt=7)) == pkv.PKV_EUNSUPPORTED
-    # split needed but no workspace
+    # workspace missing, too small or misaligned
     assert call_decode(g, S=64, maxc=128, mb=8, part=16) == pkv.PKV_EWORKSPACE
+    need = pkv.LIB.paged_attn_decode_workspace_bytes(ctypes.byref(g), 2, 100, 0, 4)
+    assert call_decode(g, part=4, ws=4096, wsb=need - 1) == pkv.PKV_EWORKSPACE
+    assert call_decode(g, part=4, ws=4100, wsb=need) == pkv.PKV_EWORKSPACE
     assert call_decode(g, S=0) == pkv.PKV_OK
     P = ctypes.c_void_p
     # prefill: fp32 is not built, chunk longer than context is invalid

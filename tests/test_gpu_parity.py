@@ -112,19 +112,21 @@ def test_write_skips_invalid_tokens(lib):
 # ----------------------------------------------------------------- decode
 
 DECODE_CASES = [
-    # (dtype, H, Hkv, D, B, lens, window, partition)
+    # (dtype, H, Hkv, D, B, lens, window, workers)
     ("f32", 4, 4, 64, 16, [100, 1, 33, 0], 0, 0),
-    ("f32", 8, 2, 128, 32, [77, 300, 5], 0, 64),
+    ("f32", 8, 2, 128, 32, [77, 300, 5], 0, 7),
     ("f16", 8, 8, 128, 16, [1, 17, 250, 513, 0], 0, 0),
-    ("f16", 8, 8, 128, 16, [1, 17, 250, 513, 1000], 0, 32),
+    ("f16", 8, 8, 128, 16, [1, 17, 250, 513, 1000], 0, 33),
     ("bf16", 16, 4, 128, 32, [31, 32, 33, 640, 2000], 0, 0),
-    ("bf16", 16, 4, 128, 32, [31, 32, 33, 640, 2000], 0, 128),
+    ("bf16", 16, 4, 128, 32, [31, 32, 33, 640, 2000], 0, 2),
     ("bf16", 8, 1, 64, 16, [5, 64, 700], 0, 48),
     ("f16", 4, 2, 64, 32, [3, 90, 129], 0, 0),
     ("bf16", 16, 2, 128, 16, [40, 600, 1500], 100, 0),
-    ("bf16", 16, 2, 128, 16, [40, 600, 1500], 100, 16),
+    ("bf16", 16, 2, 128, 16, [40, 600, 1500], 100, 1),
     ("f16", 8, 8, 128, 32, [1, 2, 500], 1, 0),
-    ("f32", 4, 2, 64, 16, [10, 70], 16, 16),
+    ("f32", 4, 2, 64, 16, [10, 70], 16, 3),
+    ("bf16", 32, 8, 128, 16, [0, 0, 2000, 0, 4100, 1], 0, 0),
+    ("f16", 64, 8, 128, 16, [300, 20000, 7], 0, 0),
 ]
 
 
@@ -137,7 +139,7 @@ def test_decode_small(lib, case):
     w = wl.make_decode(lens=lens, num_heads=H, num_kv_heads=Hkv, head_dim=D, block_size=B, dtype=dtype,
                        seed=sum(lens) + H, window=window, k_scale=3.0 if dtype == "bf16" else 1.0,
                        spare_blocks=3)
-    d = run(session, w, partition_size=part)
+    d = run(session, w, num_workers=part)
     kp, vp = ref.build_pools(w)
     out, lse = oracle_decode(w, kp, vp)
     assert_close(d.out.cpu().numpy(), out, dtype, str(case))
@@ -196,7 +198,7 @@ def test_decode_permutation_bitwise(lib):
     outs = []
     for ps in (0, 1, 2):
         w = wl.repermute(base, ps)
-        d = run(session, w, partition_size=128)
+        d = run(session, w, num_workers=16)
         outs.append(d.out.cpu().numpy())
     assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
 
@@ -208,7 +210,7 @@ def test_decode_split_count_independent(lib):
                        dtype="bf16", seed=8, k_scale=3.0)
     res = []
     for part in (16, 64, 256, 4096):
-        d = run(session, w, partition_size=part)
+        d = run(session, w, num_workers=part)
         res.append(d.out.cpu().numpy())
     for r in res[1:]:
         assert np.abs(r - res[0]).max() <= 1e-5
@@ -220,15 +222,18 @@ def test_decode_gqa_equals_replicated_mha(lib):
     w = wl.make_decode(lens=[70, 513, 1024], num_heads=16, num_kv_heads=4, head_dim=128, block_size=32,
                        dtype="bf16", seed=9)
     G = 4
-    d = run(session, w, partition_size=128)
+    d = run(session, w, num_workers=16)
     m = wl.make_decode(lens=[70, 513, 1024], num_heads=16, num_kv_heads=16, head_dim=128, block_size=32,
                        dtype="bf16", seed=9)
     for s in range(3):
         m.seq_kv[s].k = np.repeat(w.seq_kv[s].k, G, axis=1)
         m.seq_kv[s].v = np.repeat(w.seq_kv[s].v, G, axis=1)
     m.q = w.q.copy()
-    dm = run(session, m, partition_size=128)
-    assert np.array_equal(d.out.cpu().numpy(), dm.out.cpu().numpy())
+    dm = run(session, m, num_workers=16)
+    # Same arithmetic per head; the group kernel may process a partition in
+    # smaller chunks (less register state per query), so only the fp32
+    # rounding of the online softmax may differ.
+    assert np.abs(d.out.cpu().numpy() - dm.out.cpu().numpy()).max() <= 1e-5
 
 
 def test_decode_unit_cases(lib):
@@ -254,7 +259,7 @@ def test_decode_unit_cases(lib):
                         dtype="f16", seed=13)
     for e in wc.seq_kv:
         e.v[:] = np.float16(0.75)
-    dc = run(session, wc, partition_size=64)
+    dc = run(session, wc, num_workers=5)
     assert np.abs(dc.out.cpu().numpy() - 0.75).max() <= 1e-6
 
 
@@ -327,8 +332,8 @@ def test_prefill_rows_match_decode(lib):
         qd = torch.from_numpy(w.q[i:i + 1].view(np.int16)).view(torch.bfloat16).cuda()
         outd = torch.empty((1, 8, 128), dtype=torch.float32, device="cuda")
         lens = torch.tensor([L - C + i + 1], dtype=torch.int32, device="cuda")
-        pkv.paged_attn_decode(outd, qd, d.k_pool, d.v_pool, d.tables, lens, L, scale=w.scale,
-                              partition_size=16 * ((L + 15) // 16), workspace=None)
+        ws = pkv.decode_workspace(d.k_pool, 8, 1, L)
+        pkv.paged_attn_decode(outd, qd, d.k_pool, d.v_pool, d.tables, lens, L, scale=w.scale, workspace=ws)
         torch.cuda.synchronize()
         assert np.abs(outd.cpu().numpy()[0] - got[i]).max() <= TOL_ABS_16
 
@@ -340,10 +345,15 @@ def test_abi_errors_on_device(lib):
     note("abi errors")
     w = wl.make_decode(lens=[100, 40], num_heads=8, num_kv_heads=2, head_dim=128, block_size=16, dtype="bf16",
                        seed=1)
-    d = session.DeviceWorkload(w, partition_size=16)
+    d = session.DeviceWorkload(w, num_workers=16)
     with pytest.raises(pkv.PagedAttnError) as e:
         pkv.paged_attn_decode(d.out, d.q, d.k_pool, d.v_pool, d.tables, d.lens, 100, scale=0.1,
-                              partition_size=16, workspace=None)
+                              num_workers=16, workspace=None)
+    assert e.value.status == pkv.PKV_EWORKSPACE
+    small = d.workspace[:-16]
+    with pytest.raises(pkv.PagedAttnError) as e:
+        pkv.paged_attn_decode(d.out, d.q, d.k_pool, d.v_pool, d.tables, d.lens, 100, scale=0.1,
+                              num_workers=16, workspace=small)
     assert e.value.status == pkv.PKV_EWORKSPACE
     with pytest.raises(pkv.PagedAttnError) as e:
         pkv.paged_attn_decode(d.out, d.q, d.k_pool, d.v_pool, d.tables, d.lens, 10 ** 6, scale=0.1)
