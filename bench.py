@@ -7,7 +7,8 @@ their pool slots through the block table (``paged_kv_write``), then attend
 (``paged_attn_decode`` for the decode workloads, ``paged_attn_prefill`` for
 the chunked-prefill one).  W untimed warm-up steps, then exactly K timed
 steps between two device synchronisations; HIP events on the launch stream
-also time the write and the attention call of every step.
+also time the write and the attention call of every step (called eagerly:
+the host enqueues ahead of the GPU; ``--graph`` replays them as HIP graphs).
 
 Prints one JSON line.  ``value`` is the algorithmic bytes one step must move
 (decode: every attended K/V row once per kv head, queries, outputs, table
@@ -134,6 +135,74 @@ def cpu_baseline(w, target_s: float):
                       f"{elapsed:.2f} s, one BLAS thread"}
 
 
+KERNELS = {"decode": ("decode_split_kernel", "decode_merge_kernel", "decode_plan_kernel"),
+           "prefill": ("prefill_kernel",)}
+
+
+def summarize_pmc(args, fetch_dir, write_dir, copy_mib) -> int:
+    """HBM bytes per attention call from rocprofv3 counter runs.
+
+    Each run's counter CSV has one row per dispatch with FETCH_SIZE or
+    WRITE_SIZE (KiB). The calibration copy (a torch elementwise copy of
+    COPY_MIB MiB) gives the scale of each counter: bytes it should read or
+    write / what the counter reports for it. The attention call's kernels are
+    summed per launch and averaged over launches."""
+    import csv
+    import glob
+    import workloads as wl
+    w = wl.config(args.config, args.seed)
+    kind = w.kind
+    copy_bytes = int(copy_mib) << 20
+
+    def per_dispatch(d, counter):
+        files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        if not files:
+            raise SystemExit(f"no counter_collection.csv under {d}")
+        vals, grids = {}, {}
+        for row in csv.DictReader(open(files[0])):
+            if row.get("Counter_Name") != counter:
+                continue
+            key = (int(row["Dispatch_Id"]), row["Kernel_Name"])
+            vals[key] = vals.get(key, 0.0) + float(row["Counter_Value"])
+            grids[key] = int(row["Grid_Size"])
+        return vals, grids
+
+    out = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        vals, grids = per_dispatch(d, counter)
+        # The calibration copy is the device-to-device copy-buffer dispatch
+        # with the largest grid (torch's copy_ of COPY_MIB MiB).
+        copies = [(grids[k], v) for k, v in vals.items() if "copyBuffer" in k[1]]
+        copy_val = max(copies)[1] if copies else None
+        scale = copy_bytes / (copy_val * 1024.0) if copy_val else 1.0
+        ours = sorted((i, k, v) for (i, k), v in vals.items() if any(n in k for n in KERNELS[kind]))
+        # group consecutive dispatches of one call: the split/prefill kernel starts a call
+        calls, cur = [], None
+        for i, k, v in ours:
+            if KERNELS[kind][0] in k:
+                cur = [v]
+                calls.append(cur)
+            elif cur is not None:
+                cur.append(v)
+        per_call = [sum(c) * 1024.0 * scale for c in calls]
+        out[counter] = {"kib_per_call_raw": round(sum(sum(c) for c in calls) / max(len(calls), 1), 1),
+                        "calls": len(calls), "copy_kib_raw": copy_val, "scale": round(scale, 4),
+                        "bytes_per_call": round(sum(per_call) / max(len(per_call), 1))}
+    src = source_hash("decode.hip", "common.h") if kind == "decode" else source_hash("prefill.hip", "common.h")
+    key = f"paged_attn_{kind}|{w.name}"
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        db = json.load(open(path))
+    except (OSError, ValueError):
+        db = {}
+    db[key] = {"source_hash": src, "fetch": out["FETCH_SIZE"], "write": out["WRITE_SIZE"],
+               "bytes_per_launch": out["FETCH_SIZE"]["bytes_per_call"] + out["WRITE_SIZE"]["bytes_per_call"]}
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    json.dump(db, open(path, "w"), indent=1, sort_keys=True)
+    print(json.dumps({key: db[key]}))
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -146,7 +215,16 @@ def main(argv=None) -> int:
     ap.add_argument("--workers", type=int, default=0, help="decode wavefront workers (0 = automatic)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay the step's two calls as HIP graphs instead of calling the library per step")
+    ap.add_argument("--calibration-copy-mib", type=int, default=0,
+                    help="copy this many MiB once before the timed steps (scale for HBM byte counters)")
+    ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_MIB"),
+                    help="turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this command into "
+                         "profiles/traffic.json entries and exit")
     args = ap.parse_args(argv)
+    if args.summarize_pmc:
+        return summarize_pmc(args, *args.summarize_pmc)
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the decode and prefill paths "
@@ -165,10 +243,35 @@ def main(argv=None) -> int:
     w = wl.config(args.config, args.seed)
     d = session.DeviceWorkload(w, num_workers=args.workers)
     torch.cuda.synchronize()
+    if args.calibration_copy_mib:
+        # A plain device copy of known size, for scaling HBM byte counters.
+        n = args.calibration_copy_mib << 20
+        src_t = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst_t = torch.empty_like(src_t)
+        dst_t.copy_(src_t)
+        torch.cuda.synchronize()
+        del src_t, dst_t
 
     for _ in range(args.warmup):
         d.step()
     torch.cuda.synchronize()
+
+    # The step's two calls, replayed as HIP graphs (no host launch gaps) or
+    # called eagerly.
+    if not args.graph:
+        do_write, do_attend = d.write_step, d.attend
+    else:
+        g_write, g_attend = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_write):
+            d.write_step()
+        with torch.cuda.graph(g_attend):
+            d.attend()
+        torch.cuda.synchronize()
+        for _ in range(2):
+            g_write.replay()
+            g_attend.replay()
+        torch.cuda.synchronize()
+        do_write, do_attend = g_write.replay, g_attend.replay
 
     K = args.steps
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
@@ -179,9 +282,9 @@ def main(argv=None) -> int:
     start.record()
     for i in range(K):
         ev[i][0].record()
-        d.write_step()
+        do_write()
         ev[i][1].record()
-        d.attend()
+        do_attend()
         ev[i][2].record()
     end.record()
     torch.cuda.synchronize()
@@ -216,6 +319,7 @@ def main(argv=None) -> int:
                 "frac": round(achieved / peak, 4), "traffic": traffic_for(key, src)}
         n_part_info = {}
 
+    timing_mode = "hip_graph" if args.graph else "eager"
     rec = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -236,7 +340,7 @@ def main(argv=None) -> int:
         "roofline": roof,
         "timing": {"attend_ms_mean": round(att_mean, 5), "attend_ms_median": round(att_med, 5),
                    "attend_ms_min": round(attend_ms[0], 5), "write_ms_mean": round(sum(write_ms) / K, 5),
-                   "wall_s_timed": round(wall, 4), "source_hash": src},
+                   "wall_s_timed": round(wall, 4), "mode": timing_mode, "source_hash": src},
     }
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)

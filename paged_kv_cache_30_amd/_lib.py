@@ -112,8 +112,9 @@ def geometry(k_pool: torch.Tensor, num_heads: int) -> Geometry:
     return Geometry(nb, b, num_heads, hkv, d, _DTYPES[k_pool.dtype])
 
 
-def paged_kv_write(k_pool, v_pool, k_new, v_new, seq_idx, pos, block_tables, stream=None) -> None:
-    """C ``paged_kv_write``: store k_new/v_new [T, Hkv, D] at (seq_idx, pos)."""
+def bind_kv_write(k_pool, v_pool, k_new, v_new, seq_idx, pos, block_tables):
+    """Check and marshal the arguments of ``paged_kv_write`` once; returns a
+    callable ``f(stream=None)`` that makes the C call with them."""
     _dev(k_pool, "k_pool", ndim=4)
     _dev(v_pool, "v_pool", dtype=k_pool.dtype)
     if v_pool.shape != k_pool.shape:
@@ -129,9 +130,19 @@ def paged_kv_write(k_pool, v_pool, k_new, v_new, seq_idx, pos, block_tables, str
     if seq_idx.shape[0] != T or pos.shape[0] != T:
         raise ValueError("seq_idx and pos need one entry per token")
     g = geometry(k_pool, k_pool.shape[2])
-    _check(LIB.paged_kv_write(ctypes.byref(g), _ptr(k_pool), _ptr(v_pool), _ptr(k_new), _ptr(v_new),
-                              _ptr(seq_idx), _ptr(pos), T, _ptr(block_tables), block_tables.shape[0],
-                              block_tables.shape[1], _stream(stream)), "paged_kv_write")
+    args = (ctypes.byref(g), _ptr(k_pool), _ptr(v_pool), _ptr(k_new), _ptr(v_new), _ptr(seq_idx), _ptr(pos), T,
+            _ptr(block_tables), block_tables.shape[0], block_tables.shape[1])
+    keep = (g, k_pool, v_pool, k_new, v_new, seq_idx, pos, block_tables)
+
+    def call(stream=None):
+        _check(LIB.paged_kv_write(*args, _stream(stream)), "paged_kv_write")
+    call.keep = keep
+    return call
+
+
+def paged_kv_write(k_pool, v_pool, k_new, v_new, seq_idx, pos, block_tables, stream=None) -> None:
+    """C ``paged_kv_write``: store k_new/v_new [T, Hkv, D] at (seq_idx, pos)."""
+    bind_kv_write(k_pool, v_pool, k_new, v_new, seq_idx, pos, block_tables)(stream)
 
 
 def paged_attn_decode_workspace_bytes(k_pool, num_heads, num_seqs, max_context_len, window=0,
@@ -152,9 +163,10 @@ def decode_workspace(k_pool, num_heads, num_seqs, max_context_len, window=0, num
     return torch.empty(max(n, 16), dtype=torch.uint8, device=k_pool.device)
 
 
-def paged_attn_decode(out, q, k_pool, v_pool, block_tables, context_lens, max_context_len, *,
-                      window=0, scale, num_workers=0, workspace=None, lse=None, stream=None) -> None:
-    """C ``paged_attn_decode``: out[S, H, D] (fp32) for q[S, H, D]."""
+def bind_decode(out, q, k_pool, v_pool, block_tables, context_lens, max_context_len, *,
+                window=0, scale, num_workers=0, workspace=None, lse=None):
+    """Check and marshal the arguments of ``paged_attn_decode`` once; returns
+    a callable ``f(stream=None)`` that makes the C call with them."""
     _dev(q, "q", dtype=k_pool.dtype, ndim=3)
     _dev(out, "out", dtype=torch.float32, ndim=3)
     _dev(k_pool, "k_pool", ndim=4)
@@ -173,15 +185,28 @@ def paged_attn_decode(out, q, k_pool, v_pool, block_tables, context_lens, max_co
         _dev(workspace, "workspace")
         ws_bytes = workspace.numel() * workspace.element_size()
     g = geometry(k_pool, H)
-    _check(LIB.paged_attn_decode(ctypes.byref(g), _ptr(out), _ptr(lse), _ptr(q), _ptr(k_pool), _ptr(v_pool),
-                                 _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), S,
-                                 int(max_context_len), int(window), float(scale), int(num_workers),
-                                 _ptr(workspace), ws_bytes, _stream(stream)), "paged_attn_decode")
+    args = (ctypes.byref(g), _ptr(out), _ptr(lse), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables),
+            block_tables.shape[1], _ptr(context_lens), S, int(max_context_len), int(window), float(scale),
+            int(num_workers), _ptr(workspace), ws_bytes)
+    keep = (g, out, q, k_pool, v_pool, block_tables, context_lens, workspace, lse)
+
+    def call(stream=None):
+        _check(LIB.paged_attn_decode(*args, _stream(stream)), "paged_attn_decode")
+    call.keep = keep
+    return call
 
 
-def paged_attn_prefill(out, q, q_start, k_pool, v_pool, block_tables, context_lens, max_q_len,
-                       max_context_len, *, window=0, scale, lse=None, stream=None) -> None:
-    """C ``paged_attn_prefill``: out[T, H, D] (fp32) for chunk queries q[T, H, D]."""
+def paged_attn_decode(out, q, k_pool, v_pool, block_tables, context_lens, max_context_len, *,
+                      window=0, scale, num_workers=0, workspace=None, lse=None, stream=None) -> None:
+    """C ``paged_attn_decode``: out[S, H, D] (fp32) for q[S, H, D]."""
+    bind_decode(out, q, k_pool, v_pool, block_tables, context_lens, max_context_len, window=window,
+                scale=scale, num_workers=num_workers, workspace=workspace, lse=lse)(stream)
+
+
+def bind_prefill(out, q, q_start, k_pool, v_pool, block_tables, context_lens, max_q_len, max_context_len, *,
+                 window=0, scale, lse=None):
+    """Check and marshal the arguments of ``paged_attn_prefill`` once; returns
+    a callable ``f(stream=None)`` that makes the C call with them."""
     _dev(q, "q", dtype=k_pool.dtype, ndim=3)
     _dev(out, "out", dtype=torch.float32, ndim=3)
     _dev(q_start, "q_start", dtype=torch.int32, ndim=1)
@@ -198,7 +223,19 @@ def paged_attn_prefill(out, q, q_start, k_pool, v_pool, block_tables, context_le
         if lse.shape != (T, H):
             raise ValueError("lse must be [T, H]")
     g = geometry(k_pool, H)
-    _check(LIB.paged_attn_prefill(ctypes.byref(g), _ptr(out), _ptr(lse), _ptr(q), _ptr(q_start), _ptr(k_pool),
-                                  _ptr(v_pool), _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), S,
-                                  int(max_q_len), int(max_context_len), int(window), float(scale),
-                                  _stream(stream)), "paged_attn_prefill")
+    args = (ctypes.byref(g), _ptr(out), _ptr(lse), _ptr(q), _ptr(q_start), _ptr(k_pool), _ptr(v_pool),
+            _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), S, int(max_q_len), int(max_context_len),
+            int(window), float(scale))
+    keep = (g, out, q, q_start, k_pool, v_pool, block_tables, context_lens, lse)
+
+    def call(stream=None):
+        _check(LIB.paged_attn_prefill(*args, _stream(stream)), "paged_attn_prefill")
+    call.keep = keep
+    return call
+
+
+def paged_attn_prefill(out, q, q_start, k_pool, v_pool, block_tables, context_lens, max_q_len,
+                       max_context_len, *, window=0, scale, lse=None, stream=None) -> None:
+    """C ``paged_attn_prefill``: out[T, H, D] (fp32) for chunk queries q[T, H, D]."""
+    bind_prefill(out, q, q_start, k_pool, v_pool, block_tables, context_lens, max_q_len, max_context_len,
+                 window=window, scale=scale, lse=lse)(stream)

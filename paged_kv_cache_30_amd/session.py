@@ -64,6 +64,7 @@ class DeviceWorkload:
         self.step_k = to_device(k, w.dtype, device)
         self.step_v = to_device(v, w.dtype, device)
         self.workspace: Optional[torch.Tensor] = None
+        self._bound_write = self._bound_attend = None
         self.set_workers(num_workers)
         if write_history:
             self.write_history()
@@ -71,6 +72,7 @@ class DeviceWorkload:
     def set_workers(self, num_workers: int) -> None:
         """Decode worker count (0 = automatic) and a workspace sized for it."""
         self.num_workers = num_workers
+        self._bound_attend = None
         w = self.w
         if w.kind == "decode":
             self.workspace = _lib.decode_workspace(self.k_pool, w.num_heads, w.num_seqs, w.max_context_len,
@@ -87,20 +89,24 @@ class DeviceWorkload:
                                 self.tables)
 
     def write_step(self, stream=None) -> None:
-        _lib.paged_kv_write(self.k_pool, self.v_pool, self.step_k, self.step_v, self.step_seq,
-                            self.step_pos, self.tables, stream=stream)
+        if self._bound_write is None:
+            self._bound_write = _lib.bind_kv_write(self.k_pool, self.v_pool, self.step_k, self.step_v,
+                                                   self.step_seq, self.step_pos, self.tables)
+        self._bound_write(stream)
 
     def attend(self, stream=None) -> None:
         w = self.w
-        if w.kind == "decode":
-            _lib.paged_attn_decode(self.out, self.q, self.k_pool, self.v_pool, self.tables, self.lens,
-                                   w.max_context_len, window=w.window, scale=w.scale,
-                                   num_workers=self.num_workers, workspace=self.workspace,
-                                   lse=self.lse, stream=stream)
-        else:
-            _lib.paged_attn_prefill(self.out, self.q, self.q_start, self.k_pool, self.v_pool, self.tables,
-                                    self.lens, w.max_q_len, w.max_context_len, window=w.window,
-                                    scale=w.scale, lse=self.lse, stream=stream)
+        if self._bound_attend is None:
+            if w.kind == "decode":
+                self._bound_attend = _lib.bind_decode(
+                    self.out, self.q, self.k_pool, self.v_pool, self.tables, self.lens, w.max_context_len,
+                    window=w.window, scale=w.scale, num_workers=self.num_workers, workspace=self.workspace,
+                    lse=self.lse)
+            else:
+                self._bound_attend = _lib.bind_prefill(
+                    self.out, self.q, self.q_start, self.k_pool, self.v_pool, self.tables, self.lens,
+                    w.max_q_len, w.max_context_len, window=w.window, scale=w.scale, lse=self.lse)
+        self._bound_attend(stream)
 
     def step(self, stream=None) -> None:
         """One pass of the hot path: write the new tokens, then attend."""

@@ -360,3 +360,38 @@ def test_abi_errors_on_device(lib):
     assert e.value.status == pkv.PKV_EINVAL
     with pytest.raises(ValueError):
         pkv.paged_attn_decode(d.out, d.q.float(), d.k_pool, d.v_pool, d.tables, d.lens, 100, scale=0.1)
+
+
+# ------------------------------------------------------------ HIP graphs
+
+@pytest.mark.parametrize("kind", ["decode", "prefill"])
+def test_graph_replay_matches_eager(lib, kind):
+    """The step's calls captured in a HIP graph: every replay, with eager work
+    and synchronisations between replays, gives the eager result bit for bit."""
+    pkv, session = lib
+    note(f"graph replay {kind}")
+    if kind == "decode":
+        w = wl.make_decode(lens=[33, 700, 1500, 4], num_heads=16, num_kv_heads=4, head_dim=128, block_size=16,
+                           dtype="bf16", seed=23)
+    else:
+        w = wl.make_prefill(prefix_len=64, chunk_lens=[50, 20], num_heads=8, num_kv_heads=2, head_dim=128,
+                            block_size=16, dtype="bf16", seed=24)
+    d = session.DeviceWorkload(w)
+    d.step()
+    torch.cuda.synchronize()
+    eager = d.out.clone()
+    eager_lse = d.lse.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        d.step()
+    torch.cuda.synchronize()
+    for i in range(4):
+        d.out.zero_()
+        d.lse.fill_(1.0)
+        junk = torch.randn(1 << 20, device="cuda").sum()  # unrelated eager work
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(d.out, eager), f"replay {i} differs"
+        assert torch.equal(d.lse, eager_lse), f"replay {i} lse differs"
+        del junk
