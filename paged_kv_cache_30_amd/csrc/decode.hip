@@ -49,13 +49,17 @@ constexpr int kPlanThreads = 1024;
 template <class T, int D, int B, int G>
 struct DecodeShape {
   static constexpr int EB = T::BYTES;
-  static constexpr int E = 16 / EB;                    // elements per lane chunk
-  static constexpr int LPR = D * EB / 16;              // lanes per K/V row
-  static constexpr int RPL = 64 / LPR;                 // rows per wavefront load
-  static constexpr int STEPS = B / RPL;                // wavefront loads per block
-  // Wavefront loads per chunk (of K and of V); two chunks are in registers at
-  // a time (16 KB in flight per wavefront).
-  static constexpr int CWANT = PKV_DECODE_CHUNK_LOADS(G);
+  static constexpr int E = 16 / EB;                    // elements per 16-byte piece
+  // Pieces of a K/V row per lane: with 4 or more query heads per kv head the
+  // per-position softmax work, done redundantly by every lane of a row, is
+  // halved by giving each lane two pieces (fewer lanes per row).
+  static constexpr int PIECES = (G >= 4 && D * EB / 16 >= 16) ? 2 : 1;
+  static constexpr int LPR = D * EB / 16 / PIECES;     // lanes per K/V row
+  static constexpr int RPL = 64 / LPR;                 // rows per step
+  static constexpr int STEPS = B / RPL;                // steps per block
+  // Loads per chunk (of K and of V); two chunks are in registers at a time
+  // (16 KB in flight per wavefront).
+  static constexpr int CWANT = PKV_DECODE_CHUNK_LOADS(G) / PIECES;
   static constexpr int CSTEPS = STEPS < CWANT ? STEPS : CWANT;
   static constexpr int CHUNK = RPL * CSTEPS;           // slots per chunk
   static constexpr int CPB = B / CHUNK;                // chunks per block
@@ -121,7 +125,8 @@ template <class T, int D, int B, int G>
 __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, float scale_log2) {
   using Sh = DecodeShape<T, D, B, G>;
   constexpr int E = Sh::E, LPR = Sh::LPR, RPL = Sh::RPL, CSTEPS = Sh::CSTEPS, CHUNK = Sh::CHUNK,
-                CPB = Sh::CPB, EB = Sh::EB;
+                CPB = Sh::CPB, EB = Sh::EB, PC = Sh::PIECES;
+  constexpr int PSTRIDE = LPR * 16;  // bytes between a lane's pieces of one row
 
   const int lane = threadIdx.x & 63;
   // Prefix of attended blocks, in one of three places: batches of fewer than
@@ -192,7 +197,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, fl
 
   const size_t row_stride = (size_t)Hkv * D * EB;  // bytes between slots
   const size_t blk_stride = row_stride * B;
-  float m[G], l[G], o[G][E];
+  float m[G], l[G], o[G][PC * E];
 
   for (long long pos = start; pos < end;) {
     while ((long long)Hkv * cum(s + 1) <= pos) ++s;
@@ -211,15 +216,17 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, fl
     int tv = lane < n ? trow[lane] : -1;  // table entries of blocks 0..63 of the segment
 
     const char* qb = (const char*)a.q + ((size_t)(s * H + g * G) * D + c * E) * EB;
-    u32x4 qv[G];
+    u32x4 qv[G][PC];
 #pragma unroll
-    for (int h = 0; h < G; ++h) qv[h] = load16(qb + (size_t)h * D * EB);
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int pc = 0; pc < PC; ++pc) qv[h][pc] = load16(qb + (size_t)h * D * EB + pc * PSTRIDE);
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       m[h] = -INFINITY;
       l[h] = 0.f;
 #pragma unroll
-      for (int e = 0; e < E; ++e) o[h][e] = 0.f;
+      for (int e = 0; e < PC * E; ++e) o[h][e] = 0.f;
     }
     const size_t lane_off = (size_t)g * D * EB + (size_t)c * 16 + (size_t)r * row_stride;
     const char* kbase = (const char*)a.k_pool + lane_off;
@@ -227,7 +234,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, fl
 
     // Loads of chunk k of the segment; false when its table entry is out of
     // range (the chunk is skipped).
-    auto issue = [&](int k, u32x4* kr, u32x4* vr) -> bool {
+    auto issue = [&](int k, u32x4 (*kr)[PC], u32x4 (*vr)[PC]) -> bool {
       const int bi = k / CPB;
       const int sub = k - bi * CPB;
       if ((bi & 63) == 0 && bi > 0 && sub == 0) tv = bi + lane < n ? trow[bi + lane] : -1;
@@ -235,14 +242,20 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, fl
       if (pb < 0 || pb >= a.nb) return false;
       const size_t off = (size_t)pb * blk_stride + (size_t)sub * CHUNK * row_stride;
 #pragma unroll
-      for (int j = 0; j < CSTEPS; ++j) kr[j] = load_stream(kbase + off + (size_t)j * RPL * row_stride);
+      for (int j = 0; j < CSTEPS; ++j)
 #pragma unroll
-      for (int j = 0; j < CSTEPS; ++j) vr[j] = load_stream(vbase + off + (size_t)j * RPL * row_stride);
+        for (int pc = 0; pc < PC; ++pc)
+          kr[j][pc] = load_stream(kbase + off + (size_t)j * RPL * row_stride + pc * PSTRIDE);
+#pragma unroll
+      for (int j = 0; j < CSTEPS; ++j)
+#pragma unroll
+        for (int pc = 0; pc < PC; ++pc)
+          vr[j][pc] = load_stream(vbase + off + (size_t)j * RPL * row_stride + pc * PSTRIDE);
       return true;
     };
 
     // Scores, online-softmax update and P.V for chunk k.
-    auto process = [&](int k, const u32x4* kr, const u32x4* vr) {
+    auto process = [&](int k, const u32x4 (*kr)[PC], const u32x4 (*vr)[PC]) {
       const int bi = k / CPB;
       const int sub = k - bi * CPB;
       const int t0 = (blk0 + bi) * B + sub * CHUNK;
@@ -251,7 +264,12 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, fl
 #pragma unroll
       for (int j = 0; j < CSTEPS; ++j) {
 #pragma unroll
-        for (int h = 0; h < G; ++h) sc[j][h] = group_sum<LPR>(dot_chunk<T>(qv[h], kr[j], 0.f)) * scale_log2;
+        for (int h = 0; h < G; ++h) {
+          float x = 0.f;
+#pragma unroll
+          for (int pc = 0; pc < PC; ++pc) x = dot_chunk<T>(qv[h][pc], kr[j][pc], x);
+          sc[j][h] = group_sum<LPR>(x) * scale_log2;
+        }
       }
       if (!full) {
 #pragma unroll
@@ -269,10 +287,13 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, fl
         for (int j = 1; j < CSTEPS; ++j) mb = fmaxf(mb, sc[j][h]);
         const float mn = fmaxf(m[h], mb);
         const float ms = mn == -INFINITY ? 0.f : mn;
-        const float alpha = __builtin_amdgcn_exp2f(m[h] - ms);
-        l[h] *= alpha;
+        // Rescale only when some lane's maximum grew (otherwise the factor is 1).
+        if (__any(mn > m[h])) {
+          const float alpha = __builtin_amdgcn_exp2f(m[h] - ms);
+          l[h] *= alpha;
 #pragma unroll
-        for (int e = 0; e < E; ++e) o[h][e] *= alpha;
+          for (int e = 0; e < PC * E; ++e) o[h][e] *= alpha;
+        }
         m[h] = mn;
 #pragma unroll
         for (int j = 0; j < CSTEPS; ++j) {
@@ -283,18 +304,21 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, fl
       }
 #pragma unroll
       for (int j = 0; j < CSTEPS; ++j) {
-        float vf[E];
-        chunk_to_f32<T>(vr[j], vf);
-        if (!full) {
-          const int t = t0 + j * RPL + r;
-          const bool ok = t >= lo && t < L;
+        const int t = t0 + j * RPL + r;
+        const bool ok = full || (t >= lo && t < L);
 #pragma unroll
-          for (int e = 0; e < E; ++e) vf[e] = ok ? vf[e] : 0.f;
-        }
+        for (int pc = 0; pc < PC; ++pc) {
+          float vf[E];
+          chunk_to_f32<T>(vr[j][pc], vf);
+          if (!full) {
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
+            for (int e = 0; e < E; ++e) vf[e] = ok ? vf[e] : 0.f;
+          }
 #pragma unroll
-          for (int e = 0; e < E; ++e) o[h][e] = __builtin_fmaf(sc[j][h], vf[e], o[h][e]);
+          for (int h = 0; h < G; ++h) {
+#pragma unroll
+            for (int e = 0; e < E; ++e) o[h][pc * E + e] = __builtin_fmaf(sc[j][h], vf[e], o[h][pc * E + e]);
+          }
         }
       }
     };
@@ -302,7 +326,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, fl
     // Two register sets: the next chunk's loads are in flight while the
     // current chunk is processed.
     const int nchunks = n * CPB;
-    u32x4 ka[CSTEPS], va[CSTEPS], kb[CSTEPS], vb[CSTEPS];
+    u32x4 ka[CSTEPS][PC], va[CSTEPS][PC], kb[CSTEPS][PC], vb[CSTEPS][PC];
     bool oka = issue(0, ka, va);
     for (int k = 0; k < nchunks; k += 2) {
       const bool okb = k + 1 < nchunks && issue(k + 1, kb, vb);
@@ -324,7 +348,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, fl
         const float fb = __builtin_amdgcn_exp2f(mo - Ms);
         l[h] = fa * l[h] + fb * lo_;
 #pragma unroll
-        for (int e = 0; e < E; ++e) o[h][e] = fa * o[h][e] + fb * __shfl_xor(o[h][e], off, 64);
+        for (int e = 0; e < PC * E; ++e) o[h][e] = fa * o[h][e] + fb * __shfl_xor(o[h][e], off, 64);
         m[h] = M;
       }
     }
@@ -333,10 +357,14 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, fl
     if (r == 0) {
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        float* dst = a.ws_o + (slot * G + h) * D + c * E;
 #pragma unroll
-        for (int e = 0; e < E; e += 4)
-          *reinterpret_cast<float4*>(dst + e) = make_float4(o[h][e], o[h][e + 1], o[h][e + 2], o[h][e + 3]);
+        for (int pc = 0; pc < PC; ++pc) {
+          float* dst = a.ws_o + (slot * G + h) * D + pc * LPR * E + c * E;
+#pragma unroll
+          for (int e = 0; e < E; e += 4)
+            *reinterpret_cast<float4*>(dst + e) =
+                make_float4(o[h][pc * E + e], o[h][pc * E + e + 1], o[h][pc * E + e + 2], o[h][pc * E + e + 3]);
+        }
         if (c == 0) *reinterpret_cast<float2*>(a.ws_ml + (slot * G + h) * 2) = make_float2(m[h], l[h]);
       }
     }
@@ -483,10 +511,9 @@ bool decode_supported(int dtype, int D, int B, int G) {
 }
 
 // Automatic worker count: whole workgroups per compute unit (an uneven
-// spread leaves some units with more work), enough wavefronts in flight to
-// cover HBM latency (16 KB of loads each; groups of 4 or more query heads
-// spend longer on each chunk, so they get twice as many), within what the
-// unit holds at once.
+// spread leaves some units with more work); two per unit keep 128 KB of
+// loads in flight per unit (16 KB per wavefront), which covers HBM latency,
+// within what the unit holds at once.
 int decode_auto_workers(int dtype, int D, int B, int G) {
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
@@ -495,7 +522,7 @@ int decode_auto_workers(int dtype, int D, int B, int G) {
     cus = 256;
   }
   const int resident = dispatch<OccupancyOp, int>(dtype, D, B, G, 2);
-  int per_cu = G >= 4 ? 2 : 1;
+  int per_cu = 2;
   if (per_cu > resident) per_cu = resident;
   return cus * per_cu * kWaves;
 }

@@ -64,7 +64,14 @@ template <> struct Mma<F16T> {
 };
 
 constexpr int kKT = 64;   // key positions per tile
-constexpr int kPad = 8;   // elements of padding per LDS row
+// LDS row strides (elements). K rows are read 16 bytes per lane down 32
+// consecutive rows: a stride of 4 dwords mod 64 banks spreads 16 rows over
+// all banks. V rows are read by the transpose load, 4 rows x 32 bytes per
+// 16 lanes: a stride of 16 dwords mod 64 puts those 4 rows in disjoint banks.
+template <int D> struct LdsRows {
+  static constexpr int K = D + 8;
+  static constexpr int V = D + 32;
+};
 
 // Row index inside a 32x32 accumulator for register v of lane-half hf.
 __device__ __forceinline__ int acc_row(int v, int hf) { return 8 * (v >> 2) + 4 * hf + (v & 3); }
@@ -84,12 +91,12 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a, float sc
   constexpr int HPW = G < 4 ? G : 4;    // query heads per workgroup
   constexpr int PSUB = 4 / HPW;         // 32-row query sub-tiles per workgroup
   constexpr int QT = 32 * PSUB;         // query rows per workgroup
-  constexpr int ROW = D + kPad;         // LDS row, elements (16-byte multiple)
+  constexpr int KROW = LdsRows<D>::K, VROW = LdsRows<D>::V;
   constexpr int NLD = kKT * D / 8 / 256;  // 16-byte pieces per thread per tile (each of K and V)
-  constexpr int TILE = kKT * ROW;
 
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][TILE];  // [buffer][K, V]
-  __shared__ int kvalid[2][kKT];
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][kKT * KROW];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][kKT * VROW];
+  __shared__ unsigned long long kvalid[2];  // bit t: key t0 + t of the tile is mapped
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -132,9 +139,9 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a, float sc
   f32x16 o[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) o[dt] = f32x16{};
-  float m_run = -INFINITY;
-  float l_run = 0.f;  // sum of the weights as multiplied (normaliser)
-  float l_lse = 0.f;  // exact fp32 sum, for lse (differs when weights are rounded)
+  float m_run = -INFINITY;  // running max of the scaled scores (base 2)
+  float l_run = 0.f;        // sum of the weights as multiplied (normaliser)
+  float l_lse = 0.f;        // exact fp32 sum, for lse (differs when weights are rounded)
 
   const int wave_pmin = base + row0;
   const int wave_pmax = base + min(row0 + 31, C - 1);
@@ -145,7 +152,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a, float sc
   const int32_t* trow = a.tables + (size_t)s * a.mb;
 
   // Staging registers for one tile: piece i is row (tid + 256 i) / (D/8),
-  // 16-byte column (tid + 256 i) % (D/8), of both K and V.
+  // 16-byte column (tid + 256 i) % (D/8), of both K and V. Rows outside the
+  // loaded range or unmapped read block 0 and are zeroed.
   u32x4 kreg[NLD], vreg[NLD];
   int okmask = 0;
   auto load_tile = [&](int t0) {
@@ -156,34 +164,44 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a, float sc
       const int row = id / (D / 8);
       const int ch = id % (D / 8);
       const int t = t0 + row;
-      int pb = -1;
-      if (t >= kv_lo && t < kv_hi) pb = trow[t / B];
-      const bool ok = pb >= 0 && pb < a.nb;
-      kreg[i] = u32x4{0, 0, 0, 0};
-      vreg[i] = u32x4{0, 0, 0, 0};
-      if (ok) {
-        const size_t off = ((size_t)pb * B + t % B) * row_stride + ch * 16;
-        kreg[i] = load16(kpool + off);
-        vreg[i] = load16(vpool + off);
-      }
+      const bool in = t >= kv_lo && t < kv_hi;
+      int pb = in ? trow[t / B] : 0;
+      const bool ok = in && pb >= 0 && pb < a.nb;
+      pb = ok ? pb : 0;
+      const size_t off = ((size_t)pb * B + (ok ? t % B : 0)) * row_stride + ch * 16;
+      kreg[i] = load16(kpool + off);
+      vreg[i] = load16(vpool + off);
       okmask |= (int)ok << i;
     }
   };
-  auto store_tile = [&](int buf) {
+  auto store_tile = [&](int b) {
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
       const int id = tid + 256 * i;
       const int row = id / (D / 8);
       const int ch = id % (D / 8);
-      *reinterpret_cast<u32x4*>(&lds[buf][0][row * ROW + ch * 8]) = kreg[i];
-      *reinterpret_cast<u32x4*>(&lds[buf][1][row * ROW + ch * 8]) = vreg[i];
-      if (ch == 0) kvalid[buf][row] = (okmask >> i) & 1;
+      const bool ok = (okmask >> i) & 1;
+      *reinterpret_cast<u32x4*>(&k_lds[b][row * KROW + ch * 8]) = ok ? kreg[i] : u32x4{0, 0, 0, 0};
+      *reinterpret_cast<u32x4*>(&v_lds[b][row * VROW + ch * 8]) = ok ? vreg[i] : u32x4{0, 0, 0, 0};
     }
+  };
+
+  // Key validity bitmask of a tile, computed from the table directly by
+  // wavefront 0 (64 lanes = 64 keys).
+  auto tile_valid = [&](int t0) -> unsigned long long {
+    const int t = t0 + lane;
+    const bool in = t >= kv_lo && t < kv_hi;
+    const int pb = in ? trow[t / B] : -1;
+    return __ballot(in && pb >= 0 && pb < a.nb);
   };
 
   load_tile(t_first);
   store_tile(0);
-  int tile_ok = __syncthreads_and(okmask == (1 << NLD) - 1);
+  if (wave == 0) {
+    const unsigned long long vm = tile_valid(t_first);
+    if (lane == 0) kvalid[0] = vm;
+  }
+  __syncthreads();
 
   // V^T operand addressing for the transpose read: 16-lane group gq = lane/16
   // covers dims 16*(gq&1) .. +16 of a 32-dim tile and key half hf = gq>>1.
@@ -199,41 +217,44 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a, float sc
     bool skip = !wave_has_rows || t0 > wave_pmax;
     if (a.window > 0 && t0 + kKT - 1 <= wave_pmin - a.window) skip = true;
     if (!skip) {
-      const uint16_t* Ks = lds[buf][0];
-      const uint16_t* Vs = lds[buf][1];
+      const uint16_t* Ks = k_lds[buf];
+      const uint16_t* Vs = v_lds[buf];
+      const unsigned long long vmask = kvalid[buf];
       // S^T = K_tile . Q^T, two 32-key halves.
       f32x16 sacc[2];
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh) {
         sacc[kh] = f32x16{};
-        const uint16_t* kr = &Ks[(kh * 32 + ql) * ROW + 8 * hf];
+        const uint16_t* kr = &Ks[(kh * 32 + ql) * KROW + 8 * hf];
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc) {
           V8 av = __builtin_bit_cast(V8, *reinterpret_cast<const u32x4*>(kr + kc * 16));
           sacc[kh] = M::mma(av, qf[kc], sacc[kh]);
         }
       }
-      // Scale, mask, running maximum.
-      const bool need_mask = !tile_ok || wave_pmin < t0 + kKT - 1 || row0 + 31 >= C ||
+      // Mask (selection, branch-free), running maximum of the raw scores.
+      const bool need_mask = vmask != ~0ull || wave_pmin < t0 + kKT - 1 || row0 + 31 >= C ||
                              (a.window > 0 && t0 <= wave_pmax - a.window);
+      if (need_mask) {
+        const int lim_hi = row_ok ? my_pos - t0 : -1;  // key offsets <= lim_hi
+        const int lim_lo = a.window > 0 ? my_pos - a.window + 1 - t0 : -(1 << 30);
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh) {
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int kl = kh * 32 + acc_row(v, hf);
+            const bool ok = kl <= lim_hi && kl >= lim_lo && ((vmask >> kl) & 1);
+            sacc[kh][v] = ok ? sacc[kh][v] : -INFINITY;
+          }
+        }
+      }
       float mt = -INFINITY;
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh) {
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          float x = sacc[kh][v] * scale_log2;
-          if (need_mask) {
-            const int kl = kh * 32 + acc_row(v, hf);
-            const int t = t0 + kl;
-            bool ok = row_ok && t <= my_pos && kvalid[buf][kl];
-            if (a.window > 0) ok = ok && t > my_pos - a.window;
-            x = ok ? x : -INFINITY;
-          }
-          sacc[kh][v] = x;
-          mt = fmaxf(mt, x);
-        }
+        for (int v = 0; v < 16; ++v) mt = fmaxf(mt, sacc[kh][v]);
       }
-      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+      mt = fmaxf(mt, __shfl_xor(mt, 32, 64)) * scale_log2;
       const float mn = fmaxf(m_run, mt);
       const float ms = mn == -INFINITY ? 0.f : mn;
       if (__any(mn > m_run)) {
@@ -254,8 +275,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a, float sc
         uint32_t hi[4], lo[4];
 #pragma unroll
         for (int e2 = 0; e2 < 4; ++e2) {
-          const float p0 = __builtin_amdgcn_exp2f(sacc[kh][8 * sub + 2 * e2] - ms);
-          const float p1 = __builtin_amdgcn_exp2f(sacc[kh][8 * sub + 2 * e2 + 1] - ms);
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kh][8 * sub + 2 * e2], scale_log2, -ms));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kh][8 * sub + 2 * e2 + 1], scale_log2, -ms));
           const uint32_t h0 = M::bits(p0), h1 = M::bits(p1);
           hi[e2] = h0 | (h1 << 16);
           if constexpr (M::kSplit) {
@@ -269,19 +290,25 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a, float sc
         }
         const V8 bhi = __builtin_bit_cast(V8, u32x4{hi[0], hi[1], hi[2], hi[3]});
         const V8 blo = __builtin_bit_cast(V8, u32x4{lo[0], lo[1], lo[2], lo[3]});
-        const uint16_t* vb = Vs + (16 * c + 4 * hf + tr_row) * ROW + tr_col;
+        const uint16_t* vb = Vs + (16 * c + 4 * hf + tr_row) * VROW + tr_col;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
           const u32x2 e03 = lds_read_tr(vb + dt * 32);
-          const u32x2 e47 = lds_read_tr(vb + 8 * ROW + dt * 32);
+          const u32x2 e47 = lds_read_tr(vb + 8 * VROW + dt * 32);
           const V8 av = __builtin_bit_cast(V8, u32x4{e03.x, e03.y, e47.x, e47.y});
           o[dt] = M::mma(av, bhi, o[dt]);
           if constexpr (M::kSplit) o[dt] = M::mma(av, blo, o[dt]);
         }
       }
     }
-    if (has_next) store_tile(buf ^ 1);
-    tile_ok = __syncthreads_and(okmask == (1 << NLD) - 1);
+    if (has_next) {
+      store_tile(buf ^ 1);
+      if (wave == 0) {
+        const unsigned long long vm = tile_valid(t0 + kKT);
+        if (lane == 0) kvalid[buf ^ 1] = vm;
+      }
+    }
+    __syncthreads();
   }
 
   if (!row_ok) return;
