@@ -73,7 +73,9 @@ enum {
  *   num_heads     H, query heads
  *   num_kv_heads  Hkv, key/value heads; H % Hkv == 0, H / Hkv in {1, 2, 4, 8}
  *   head_dim      D: 64 or 128
- *   kv_dtype      PKV_F32, PKV_F16 or PKV_BF16 (pools, q, k_new, v_new) */
+ *   kv_dtype      PKV_F32, PKV_F16 or PKV_BF16 (pools, q, k_new, v_new)
+ * One block (B * Hkv * D elements) must hold fewer than 2^31 bytes
+ * (PKV_EUNSUPPORTED otherwise). */
 typedef struct pkv_geometry {
   int32_t num_blocks;
   int32_t block_size;

@@ -32,6 +32,9 @@ int check_geometry(const pkv_geometry_t* g) {
   if (g->block_size != 16 && g->block_size != 32) return PKV_EUNSUPPORTED;
   const int G = g->num_heads / g->num_kv_heads;
   if (G != 1 && G != 2 && G != 4 && G != 8) return PKV_EUNSUPPORTED;
+  // Kernels address inside a block with 32-bit offsets.
+  if ((long long)g->block_size * g->num_kv_heads * g->head_dim * elem_bytes(g->kv_dtype) > INT32_MAX)
+    return PKV_EUNSUPPORTED;
   return PKV_OK;
 }
 

@@ -28,7 +28,7 @@
 //  * Rescaling of the output accumulators is skipped when no lane's running
 //    maximum grew (exact: the factor would be 1).
 //  * Masked keys (causal, window, unmapped blocks) are removed by selection
-//    (score -inf); K/V rows outside the loaded range are zero-filled so a
+//    (score -inf); V rows outside the loaded range are zero-filled so a
 //    zero weight never meets a NaN.
 #include "common.h"
 #include "launch.h"
@@ -41,6 +41,10 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// pack(a, b): a and b rounded to nearest (even) in the 16-bit type, a in the
+// low half; lo(u), hi(u): the halves of a packed pair back in fp32 (exact).
 template <class T> struct Mma;
 template <> struct Mma<BF16T> {
   using V8 = bf16x8;
@@ -48,8 +52,11 @@ template <> struct Mma<BF16T> {
   static __device__ __forceinline__ f32x16 mma(V8 a, V8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
   }
-  static __device__ __forceinline__ uint32_t bits(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
-  static __device__ __forceinline__ float value(uint32_t b) { return __builtin_bit_cast(float, b << 16); }
+  static __device__ __forceinline__ uint32_t pack(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{a, b}), bf16x2));
+  }
+  static __device__ __forceinline__ float lo(uint32_t u) { return __builtin_bit_cast(float, u << 16); }
+  static __device__ __forceinline__ float hi(uint32_t u) { return __builtin_bit_cast(float, u & 0xffff0000u); }
 };
 template <> struct Mma<F16T> {
   using V8 = f16x8;
@@ -57,10 +64,11 @@ template <> struct Mma<F16T> {
   static __device__ __forceinline__ f32x16 mma(V8 a, V8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
   }
-  static __device__ __forceinline__ uint32_t bits(float x) { return __builtin_bit_cast(uint16_t, (_Float16)x); }
-  static __device__ __forceinline__ float value(uint32_t b) {
-    return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
+  static __device__ __forceinline__ uint32_t pack(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{a, b}), f16x2));
   }
+  static __device__ __forceinline__ float lo(uint32_t u) { return (float)as_h2(u).x; }
+  static __device__ __forceinline__ float hi(uint32_t u) { return (float)as_h2(u).y; }
 };
 
 constexpr int kKT = 64;   // key positions per tile
@@ -146,14 +154,16 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a, float sc
   const int wave_pmin = base + row0;
   const int wave_pmax = base + min(row0 + 31, C - 1);
   const bool wave_has_rows = row0 < C;
-  const size_t row_stride = (size_t)a.Hkv * D * 2;
+  const uint32_t row_stride = (uint32_t)a.Hkv * D * 2;
+  const uint32_t block_stride = (uint32_t)B * row_stride;
   const char* kpool = (const char*)a.k_pool + (size_t)g * D * 2;
   const char* vpool = (const char*)a.v_pool + (size_t)g * D * 2;
   const int32_t* trow = a.tables + (size_t)s * a.mb;
 
   // Staging registers for one tile: piece i is row (tid + 256 i) / (D/8),
   // 16-byte column (tid + 256 i) % (D/8), of both K and V. Rows outside the
-  // loaded range or unmapped read block 0 and are zeroed.
+  // loaded range or unmapped read block 0; their V rows are stored as zeros
+  // (their K rows only reach scores that the mask replaces).
   u32x4 kreg[NLD], vreg[NLD];
   int okmask = 0;
   auto load_tile = [&](int t0) {
@@ -165,10 +175,10 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a, float sc
       const int ch = id % (D / 8);
       const int t = t0 + row;
       const bool in = t >= kv_lo && t < kv_hi;
-      int pb = in ? trow[t / B] : 0;
+      int pb = trow[min(t / B, a.mb - 1)];  // in range of the table row even when t is not
       const bool ok = in && pb >= 0 && pb < a.nb;
       pb = ok ? pb : 0;
-      const size_t off = ((size_t)pb * B + (ok ? t % B : 0)) * row_stride + ch * 16;
+      const size_t off = (size_t)(uint32_t)pb * block_stride + (uint32_t)((t % B) * row_stride + ch * 16);
       kreg[i] = load16(kpool + off);
       vreg[i] = load16(vpool + off);
       okmask |= (int)ok << i;
@@ -181,7 +191,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a, float sc
       const int row = id / (D / 8);
       const int ch = id % (D / 8);
       const bool ok = (okmask >> i) & 1;
-      *reinterpret_cast<u32x4*>(&k_lds[b][row * KROW + ch * 8]) = ok ? kreg[i] : u32x4{0, 0, 0, 0};
+      *reinterpret_cast<u32x4*>(&k_lds[b][row * KROW + ch * 8]) = kreg[i];
       *reinterpret_cast<u32x4*>(&v_lds[b][row * VROW + ch * 8]) = ok ? vreg[i] : u32x4{0, 0, 0, 0};
     }
   };
@@ -191,7 +201,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a, float sc
   auto tile_valid = [&](int t0) -> unsigned long long {
     const int t = t0 + lane;
     const bool in = t >= kv_lo && t < kv_hi;
-    const int pb = in ? trow[t / B] : -1;
+    const int pb = trow[min(t / B, a.mb - 1)];
     return __ballot(in && pb >= 0 && pb < a.nb);
   };
 
@@ -221,14 +231,13 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a, float sc
       const uint16_t* Vs = v_lds[buf];
       const unsigned long long vmask = kvalid[buf];
       // S^T = K_tile . Q^T, two 32-key halves.
-      f32x16 sacc[2];
+      f32x16 sacc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-      for (int kh = 0; kh < 2; ++kh) {
-        sacc[kh] = f32x16{};
-        const uint16_t* kr = &Ks[(kh * 32 + ql) * KROW + 8 * hf];
+      for (int kc = 0; kc < KC; ++kc) {
 #pragma unroll
-        for (int kc = 0; kc < KC; ++kc) {
-          V8 av = __builtin_bit_cast(V8, *reinterpret_cast<const u32x4*>(kr + kc * 16));
+        for (int kh = 0; kh < 2; ++kh) {
+          const V8 av = __builtin_bit_cast(
+              V8, *reinterpret_cast<const u32x4*>(&Ks[(kh * 32 + ql) * KROW + 8 * hf + kc * 16]));
           sacc[kh] = M::mma(av, qf[kc], sacc[kh]);
         }
       }
@@ -277,14 +286,14 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a, float sc
         for (int e2 = 0; e2 < 4; ++e2) {
           const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kh][8 * sub + 2 * e2], scale_log2, -ms));
           const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kh][8 * sub + 2 * e2 + 1], scale_log2, -ms));
-          const uint32_t h0 = M::bits(p0), h1 = M::bits(p1);
-          hi[e2] = h0 | (h1 << 16);
+          const uint32_t h = M::pack(p0, p1);
+          hi[e2] = h;
           if constexpr (M::kSplit) {
-            const float r0v = p0 - M::value(h0), r1v = p1 - M::value(h1);
-            lo[e2] = M::bits(r0v) | (M::bits(r1v) << 16);
+            lo[e2] = M::pack(p0 - M::lo(h), p1 - M::hi(h));
             l_run += p0 + p1;
           } else {
-            l_run += M::value(h0) + M::value(h1);
+            lo[e2] = 0;
+            l_run += M::lo(h) + M::hi(h);
             l_lse += p0 + p1;
           }
         }

@@ -86,6 +86,8 @@ def test_argument_errors_before_any_launch():
     assert call_decode(geo(H=24, Hkv=8)) == pkv.PKV_EUNSUPPORTED
     assert call_decode(geo(H=30, Hkv=8)) == pkv.PKV_EINVAL
     assert call_decode(geo(dt=7)) == pkv.PKV_EUNSUPPORTED
+    # one block of 32 x 2^17 x 128 fp32 elements is 2^31 bytes: too large
+    assert call_decode(geo(B=32, H=1 << 17, Hkv=1 << 17, dt=pkv.PKV_F32)) == pkv.PKV_EUNSUPPORTED
     # workspace missing, too small or misaligned
     assert call_decode(g, S=64, maxc=128, mb=8, part=16) == pkv.PKV_EWORKSPACE
     need = pkv.LIB.paged_attn_decode_workspace_bytes(ctypes.byref(g), 2, 100, 0, 4)
