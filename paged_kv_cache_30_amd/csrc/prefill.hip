@@ -72,23 +72,71 @@ template <> struct Mma<F16T> {
 };
 
 constexpr int kKT = 64;   // key positions per tile
-// LDS row strides (elements). K rows are read 16 bytes per lane down 32
-// consecutive rows: a stride of 4 dwords mod 64 banks spreads 16 rows over
-// all banks. V rows are read by the transpose load, 4 rows x 32 bytes per
-// 16 lanes: a stride of 16 dwords mod 64 puts those 4 rows in disjoint banks.
-template <int D> struct LdsRows {
-  static constexpr int K = D + 8;
-  static constexpr int V = D + 32;
+
+// LDS layout of a K or V tile: key row r takes D*2 bytes at r*D*2, as D/8
+// units of 16 bytes, and logical unit c of row r is stored at unit
+// c ^ swizzle(r). The tiles are filled by direct global->LDS loads, which
+// write 64 consecutive units per wavefront instruction, so rows cannot be
+// padded; the XOR keeps the reads free of bank conflicts instead:
+//  * K (MFMA A operand): 16 lanes read one logical unit of 16 consecutive
+//    rows, which land in 16 distinct units modulo 256 bytes (all 64 banks).
+//  * V (transpose read): 32 lanes read 4 consecutive rows (first one a
+//    multiple of 4) x logical units 4dt .. 4dt+3: again 16 distinct units.
+template <int D> struct Swz;
+template <> struct Swz<128> {
+  static __device__ __forceinline__ int k(int r) { return r & 15; }
+  static __device__ __forceinline__ int v(int r) { return 4 * (r & 3); }
 };
+template <> struct Swz<64> {
+  static __device__ __forceinline__ int k(int r) { return (r >> 1) & 7; }
+  static __device__ __forceinline__ int v(int r) { return 4 * ((r >> 1) & 1); }
+};
+
+// Source of the 16 bytes loaded for a key row that is outside the range or
+// unmapped: zeros, so a zero weight never meets a NaN in V.
+__device__ __attribute__((aligned(16))) uint32_t g_zero16[4];
+
+// One 16-byte direct load per lane from global memory into LDS: lane l of
+// the wavefront writes bytes [16 l, 16 l + 16) after `lds` (which must be
+// the same for every lane).
+__device__ __forceinline__ void dma16(const void* src, uint16_t* lds) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                   (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+}
+// Wait for this wavefront's direct loads (vmcnt 0). The compiler does not
+// see LDS change under a direct load: the empty asm with a memory clobber
+// stops it from keeping or assuming LDS values across the wait.
+__device__ __forceinline__ void dma_wait() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __asm__ volatile("" ::: "memory");
+}
 
 // Row index inside a 32x32 accumulator for register v of lane-half hf.
 __device__ __forceinline__ int acc_row(int v, int hf) { return 8 * (v >> 2) + 4 * hf + (v & 3); }
 
-__device__ __forceinline__ u32x2 lds_read_tr(const uint16_t* p) {
-  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-  s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
-  return __builtin_bit_cast(u32x2, v);
+// Byte offset of an LDS location (a __shared__ pointer) in the LDS space.
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
+
+// Transposing 8-byte LDS read (ds_read_b64_tr_b16) of byte addr + OFF:
+// within 16 lanes, lane j reads 4 consecutive 16-bit elements of row j/4 and
+// lane i receives element i of those 4 rows. Issued as inline asm because
+// the compiler makes each such read that it emits itself wait for every
+// direct load in flight (it cannot tell which LDS buffer the builtin reads),
+// which would stall on the gather of the next tile. The compiler does not
+// track these reads: lds_wait() waits for them and settle() orders each
+// result after that wait.
+template <int OFF>
+__device__ __forceinline__ u32x2 lds_read_tr(uint32_t addr) {
+  u32x2 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+  return r;
+}
+__device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)"); }
+__device__ __forceinline__ void settle(u32x2& x) { asm volatile("" : "+v"(x)); }
+
+template <int N> struct IntC { static constexpr int value = N; };
 
 template <class T, int D, int B, int G>
 __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a, float scale_log2) {
@@ -99,11 +147,16 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a, float sc
   constexpr int HPW = G < 4 ? G : 4;    // query heads per workgroup
   constexpr int PSUB = 4 / HPW;         // 32-row query sub-tiles per workgroup
   constexpr int QT = 32 * PSUB;         // query rows per workgroup
-  constexpr int KROW = LdsRows<D>::K, VROW = LdsRows<D>::V;
-  constexpr int NLD = kKT * D / 8 / 256;  // 16-byte pieces per thread per tile (each of K and V)
+  constexpr int U = D / 8;              // 16-byte units per key row
+  constexpr int NLD = kKT * U / 256;    // direct loads per thread per tile (each of K and V)
 
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][kKT * KROW];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][kKT * VROW];
+  // Two buffers of each of K and V, as separate arrays: the compiler then
+  // knows that reads of one buffer do not depend on direct loads in flight
+  // into the other.
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds0[kKT * D];
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds1[kKT * D];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds0[kKT * D];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds1[kKT * D];
   __shared__ unsigned long long kvalid[2];  // bit t: key t0 + t of the tile is mapped
 
   const int tid = threadIdx.x;
@@ -159,77 +212,78 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a, float sc
   const char* kpool = (const char*)a.k_pool + (size_t)g * D * 2;
   const char* vpool = (const char*)a.v_pool + (size_t)g * D * 2;
   const int32_t* trow = a.tables + (size_t)s * a.mb;
+  const char* zero = (const char*)g_zero16;
 
-  // Staging registers for one tile: piece i is row (tid + 256 i) / (D/8),
-  // 16-byte column (tid + 256 i) % (D/8), of both K and V. Rows outside the
-  // loaded range or unmapped read block 0; their V rows are stored as zeros
-  // (their K rows only reach scores that the mask replaces).
-  u32x4 kreg[NLD], vreg[NLD];
-  int okmask = 0;
-  auto load_tile = [&](int t0) {
-    okmask = 0;
+  // Tile gather. Load j of thread (wave, lane) fills unit P = 64 (4 j + wave)
+  // + lane of the tile: row P / U, stored unit P % U, holding the logical
+  // unit that the swizzle puts there. The table entries of a tile are read
+  // one tile ahead (`fetch_table`), so that no wait for them also waits for
+  // the direct loads in flight.
+  int pb_row[NLD];  // table entry of each of this thread's rows in the next tile
+  int pb_key;       // table entry of key t0 + lane of the next tile
+  auto fetch_table = [&](int t0) {
 #pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      const int id = tid + 256 * i;
-      const int row = id / (D / 8);
-      const int ch = id % (D / 8);
-      const int t = t0 + row;
-      const bool in = t >= kv_lo && t < kv_hi;
-      int pb = trow[min(t / B, a.mb - 1)];  // in range of the table row even when t is not
-      const bool ok = in && pb >= 0 && pb < a.nb;
-      pb = ok ? pb : 0;
-      const size_t off = (size_t)(uint32_t)pb * block_stride + (uint32_t)((t % B) * row_stride + ch * 16);
-      kreg[i] = load16(kpool + off);
-      vreg[i] = load16(vpool + off);
-      okmask |= (int)ok << i;
+    for (int j = 0; j < NLD; ++j) {
+      const int t = t0 + ((4 * j + wave) * 64 + lane) / U;
+      pb_row[j] = trow[min(t / B, a.mb - 1)];  // in range of the table row even when t is not
+    }
+    pb_key = trow[min((t0 + lane) / B, a.mb - 1)];
+  };
+  auto gather = [&](int t0, uint16_t* kd, uint16_t* vd) {
+#pragma unroll
+    for (int j = 0; j < NLD; ++j) {
+      const int P = (4 * j + wave) * 64 + lane;
+      const int r = P / U, cs = P % U;
+      const int t = t0 + r;
+      const int pb = pb_row[j];
+      const bool ok = t >= kv_lo && t < kv_hi && pb >= 0 && pb < a.nb;
+      const size_t roff = (size_t)(uint32_t)pb * block_stride + (uint32_t)((t % B) * row_stride);
+      dma16(ok ? kpool + roff + 16 * (cs ^ Swz<D>::k(r)) : zero, kd + (4 * j + wave) * 512);
+      dma16(ok ? vpool + roff + 16 * (cs ^ Swz<D>::v(r)) : zero, vd + (4 * j + wave) * 512);
     }
   };
-  auto store_tile = [&](int b) {
-#pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      const int id = tid + 256 * i;
-      const int row = id / (D / 8);
-      const int ch = id % (D / 8);
-      const bool ok = (okmask >> i) & 1;
-      *reinterpret_cast<u32x4*>(&k_lds[b][row * KROW + ch * 8]) = kreg[i];
-      *reinterpret_cast<u32x4*>(&v_lds[b][row * VROW + ch * 8]) = ok ? vreg[i] : u32x4{0, 0, 0, 0};
+  // Key validity bitmask of a tile (64 lanes = 64 keys), by wavefront 0.
+  auto put_valid = [&](int t0, int slot) {
+    if (wave == 0) {
+      const int t = t0 + lane;
+      const unsigned long long vm = __ballot(t >= kv_lo && t < kv_hi && pb_key >= 0 && pb_key < a.nb);
+      if (lane == 0) kvalid[slot] = vm;
     }
   };
-
-  // Key validity bitmask of a tile, computed from the table directly by
-  // wavefront 0 (64 lanes = 64 keys).
-  auto tile_valid = [&](int t0) -> unsigned long long {
-    const int t = t0 + lane;
-    const bool in = t >= kv_lo && t < kv_hi;
-    const int pb = trow[min(t / B, a.mb - 1)];
-    return __ballot(in && pb >= 0 && pb < a.nb);
-  };
-
-  load_tile(t_first);
-  store_tile(0);
-  if (wave == 0) {
-    const unsigned long long vm = tile_valid(t_first);
-    if (lane == 0) kvalid[0] = vm;
-  }
-  __syncthreads();
 
   // V^T operand addressing for the transpose read: 16-lane group gq = lane/16
   // covers dims 16*(gq&1) .. +16 of a 32-dim tile and key half hf = gq>>1.
   const int gq = lane >> 4, j16 = lane & 15;
-  const int tr_row = j16 >> 2;                       // key offset inside 4
-  const int tr_col = 16 * (gq & 1) + 4 * (j16 & 3);  // dim offset inside a 32-dim tile
+  const int tr_row = j16 >> 2;                          // key offset inside 4
+  const int tr_unit = 2 * (gq & 1) + ((j16 & 3) >> 1);  // 16-byte unit inside a 32-dim tile
+  const int tr_sw = Swz<D>::v(tr_row) >> 2;             // swizzle of rows 4i + tr_row, in 4-unit steps
+  const int tr_elem = 4 * (j16 & 1);                    // element inside the unit
+  // Byte offset, inside a V buffer, of this lane's transpose read for key
+  // chunk 0 and dim tile dt (other key chunks add constants).
+  uint32_t tr_addr[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+    tr_addr[dt] = 2 * ((4 * hf + tr_row) * D + tr_elem + 8 * (4 * (dt ^ tr_sw) + tr_unit));
+  // K operand: row kh*32 + ql, logical unit 2 kc + hf, stored at
+  // (2 kc) ^ (hf ^ swizzle(ql)) (the swizzle is the same for both halves).
+  const int k_sw = hf ^ Swz<D>::k(ql);
 
-  int buf = 0;
-  for (int t0 = t_first; t0 < kv_hi; t0 += kKT, buf ^= 1) {
+  // One tile: gather the next tile into the other buffers, compute this one
+  // from (Ks, Vs, kvalid[slot]), wait for the gather, barrier. Returns
+  // whether a next tile exists.
+  auto step = [&](int t0, const uint16_t* Ks, const uint16_t* Vs, uint16_t* Kn, uint16_t* Vn,
+                  int slot) -> bool {
     const bool has_next = t0 + kKT < kv_hi;
-    if (has_next) load_tile(t0 + kKT);
+    if (has_next) {
+      gather(t0 + kKT, Kn, Vn);
+      put_valid(t0 + kKT, slot ^ 1);
+      if (t0 + 2 * kKT < kv_hi) fetch_table(t0 + 2 * kKT);
+    }
 
     bool skip = !wave_has_rows || t0 > wave_pmax;
     if (a.window > 0 && t0 + kKT - 1 <= wave_pmin - a.window) skip = true;
     if (!skip) {
-      const uint16_t* Ks = k_lds[buf];
-      const uint16_t* Vs = v_lds[buf];
-      const unsigned long long vmask = kvalid[buf];
+      const unsigned long long vmask = kvalid[slot];
       // S^T = K_tile . Q^T, two 32-key halves.
       f32x16 sacc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
@@ -237,7 +291,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a, float sc
 #pragma unroll
         for (int kh = 0; kh < 2; ++kh) {
           const V8 av = __builtin_bit_cast(
-              V8, *reinterpret_cast<const u32x4*>(&Ks[(kh * 32 + ql) * KROW + 8 * hf + kc * 16]));
+              V8, *reinterpret_cast<const u32x4*>(&Ks[(kh * 32 + ql) * D + 8 * ((2 * kc) ^ k_sw)]));
           sacc[kh] = M::mma(av, qf[kc], sacc[kh]);
         }
       }
@@ -278,9 +332,18 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a, float sc
       // P^T operands: key chunk c = 16 keys; this lane supplies the weights of
       // its accumulator registers 8*(c%2) .. +7 of half c/2, i.e. keys
       // 16c + 8*(e/4) + 4*hf + e%4 for e = 0..7.
+      const uint32_t vbase = lds_offset(Vs);
+      auto chunk = [&](auto cc) {
+        constexpr int c = decltype(cc)::value;
+        constexpr int kh = c >> 1, sub = c & 1;
+        // V^T operands of this chunk: keys 16c .. 16c+15, loaded first so the
+        // LDS latency overlaps the weights below.
+        u32x2 e03[DT], e47[DT];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int kh = c >> 1, sub = c & 1;
+        for (int dt = 0; dt < DT; ++dt) {
+          e03[dt] = lds_read_tr<16 * c * D * 2>(vbase + tr_addr[dt]);
+          e47[dt] = lds_read_tr<(16 * c + 8) * D * 2>(vbase + tr_addr[dt]);
+        }
         uint32_t hi[4], lo[4];
 #pragma unroll
         for (int e2 = 0; e2 < 4; ++e2) {
@@ -299,25 +362,39 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a, float sc
         }
         const V8 bhi = __builtin_bit_cast(V8, u32x4{hi[0], hi[1], hi[2], hi[3]});
         const V8 blo = __builtin_bit_cast(V8, u32x4{lo[0], lo[1], lo[2], lo[3]});
-        const uint16_t* vb = Vs + (16 * c + 4 * hf + tr_row) * VROW + tr_col;
+        lds_wait();
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-          const u32x2 e03 = lds_read_tr(vb + dt * 32);
-          const u32x2 e47 = lds_read_tr(vb + 8 * VROW + dt * 32);
-          const V8 av = __builtin_bit_cast(V8, u32x4{e03.x, e03.y, e47.x, e47.y});
+          settle(e03[dt]);
+          settle(e47[dt]);
+        }
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const V8 av = __builtin_bit_cast(V8, u32x4{e03[dt].x, e03[dt].y, e47[dt].x, e47[dt].y});
           o[dt] = M::mma(av, bhi, o[dt]);
           if constexpr (M::kSplit) o[dt] = M::mma(av, blo, o[dt]);
         }
-      }
+      };
+      chunk(IntC<0>{});
+      chunk(IntC<1>{});
+      chunk(IntC<2>{});
+      chunk(IntC<3>{});
     }
-    if (has_next) {
-      store_tile(buf ^ 1);
-      if (wave == 0) {
-        const unsigned long long vm = tile_valid(t0 + kKT);
-        if (lane == 0) kvalid[buf ^ 1] = vm;
-      }
-    }
+    dma_wait();
     __syncthreads();
+    return has_next;
+  };
+
+  fetch_table(t_first);
+  dma_wait();  // table entries in registers
+  gather(t_first, k_lds0, v_lds0);
+  put_valid(t_first, 0);
+  if (t_first + kKT < kv_hi) fetch_table(t_first + kKT);
+  dma_wait();
+  __syncthreads();
+  for (int t0 = t_first;; t0 += 2 * kKT) {
+    if (!step(t0, k_lds0, v_lds0, k_lds1, v_lds1, 0)) break;
+    if (!step(t0 + kKT, k_lds1, v_lds1, k_lds0, v_lds0, 1)) break;
   }
 
   if (!row_ok) return;
