@@ -25,8 +25,11 @@
 //    inputs split each weight into bf16 high and low parts (p = hi + lo to
 //    about 2^-17 relative) and multiply both, so the 8-bit bf16 mantissa
 //    does not limit the result. The normaliser sums the weights as used.
-//  * Rescaling of the output accumulators is skipped when no lane's running
-//    maximum grew (exact: the factor would be 1).
+//  * The weights are taken relative to a reference maximum that moves only
+//    when some row's maximum grows by more than a factor 2^8 (weights then
+//    stay <= 256, well inside fp32 and the 16-bit formats); the output is
+//    rescaled only then. The result o / l and lse = m + log l do not depend
+//    on the reference, so this is exact up to rounding.
 //  * Masked keys (causal, window, unmapped blocks) are removed by selection
 //    (score -inf); V rows outside the loaded range are zero-filled so a
 //    zero weight never meets a NaN.
@@ -72,6 +75,9 @@ template <> struct Mma<F16T> {
 };
 
 constexpr int kKT = 64;   // key positions per tile
+// Headroom (base-2 exponent) that a row's maximum may gain over the
+// reference maximum before the output is rescaled: weights stay <= 256.
+constexpr float kSlackLog2 = 8.f;
 
 // LDS layout of a K or V tile: key row r takes D*2 bytes at r*D*2, as D/8
 // units of 16 bytes, and logical unit c of row r is stored at unit
@@ -216,30 +222,32 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a, float sc
 
   // Tile gather. Load j of thread (wave, lane) fills unit P = 64 (4 j + wave)
   // + lane of the tile: row P / U, stored unit P % U, holding the logical
-  // unit that the swizzle puts there. The table entries of a tile are read
-  // one tile ahead (`fetch_table`), so that no wait for them also waits for
-  // the direct loads in flight.
-  int pb_row[NLD];  // table entry of each of this thread's rows in the next tile
-  int pb_key;       // table entry of key t0 + lane of the next tile
+  // unit that the swizzle puts there. The 64 / U rows of one wavefront
+  // instruction start at a multiple of 64 / U, so they lie in one block: the
+  // table entry of instruction j is uniform over the wavefront and is read
+  // with a scalar load. Entries are read one tile ahead (`fetch_table`).
+  constexpr int RPI = 64 / U;  // rows per wavefront instruction
+  static_assert(B % RPI == 0, "a wavefront instruction must not straddle blocks");
+  int pb_ins[NLD];  // table entry of instruction j of this wavefront, next tile
+  int pb_key = -1;  // wavefront 0: table entry of key t0 + lane, next tile
   auto fetch_table = [&](int t0) {
 #pragma unroll
-    for (int j = 0; j < NLD; ++j) {
-      const int t = t0 + ((4 * j + wave) * 64 + lane) / U;
-      pb_row[j] = trow[min(t / B, a.mb - 1)];  // in range of the table row even when t is not
-    }
-    pb_key = trow[min((t0 + lane) / B, a.mb - 1)];
+    for (int j = 0; j < NLD; ++j)  // in range of the table row even past the context
+      pb_ins[j] = trow[min((t0 + (4 * j + wave) * RPI) / B, a.mb - 1)];
+    if (wave == 0) pb_key = trow[min((t0 + lane) / B, a.mb - 1)];
   };
   auto gather = [&](int t0, uint16_t* kd, uint16_t* vd) {
 #pragma unroll
     for (int j = 0; j < NLD; ++j) {
-      const int P = (4 * j + wave) * 64 + lane;
-      const int r = P / U, cs = P % U;
+      const int pb = pb_ins[j];
+      const bool blk_ok = pb >= 0 && pb < a.nb;
+      const size_t boff = (size_t)(uint32_t)(blk_ok ? pb : 0) * block_stride;
+      const int r = (4 * j + wave) * RPI + lane / U, cs = lane % U;
       const int t = t0 + r;
-      const int pb = pb_row[j];
-      const bool ok = t >= kv_lo && t < kv_hi && pb >= 0 && pb < a.nb;
-      const size_t roff = (size_t)(uint32_t)pb * block_stride + (uint32_t)((t % B) * row_stride);
-      dma16(ok ? kpool + roff + 16 * (cs ^ Swz<D>::k(r)) : zero, kd + (4 * j + wave) * 512);
-      dma16(ok ? vpool + roff + 16 * (cs ^ Swz<D>::v(r)) : zero, vd + (4 * j + wave) * 512);
+      const bool ok = blk_ok && t >= kv_lo && t < kv_hi;
+      const uint32_t roff = (uint32_t)((t % B) * row_stride);
+      dma16(ok ? kpool + boff + roff + 16 * (cs ^ Swz<D>::k(r)) : zero, kd + (4 * j + wave) * 512);
+      dma16(ok ? vpool + boff + roff + 16 * (cs ^ Swz<D>::v(r)) : zero, vd + (4 * j + wave) * 512);
     }
   };
   // Key validity bitmask of a tile (64 lanes = 64 keys), by wavefront 0.
@@ -318,16 +326,19 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a, float sc
         for (int v = 0; v < 16; ++v) mt = fmaxf(mt, sacc[kh][v]);
       }
       mt = fmaxf(mt, __shfl_xor(mt, 32, 64)) * scale_log2;
-      const float mn = fmaxf(m_run, mt);
-      const float ms = mn == -INFINITY ? 0.f : mn;
-      if (__any(mn > m_run)) {
-        const float alpha = __builtin_amdgcn_exp2f(m_run - ms);
+      // The reference maximum m_run moves only when some row's tile maximum
+      // exceeds it by more than kSlackLog2, so weights are at most
+      // 2^kSlackLog2 and the output rescale (exact either way) is rare.
+      if (__any(mt > m_run + kSlackLog2)) {
+        const float mn = fmaxf(m_run, mt);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - (mn == -INFINITY ? 0.f : mn));
         l_run *= alpha;
         if constexpr (!M::kSplit) l_lse *= alpha;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+        m_run = mn;
       }
-      m_run = mn;
+      const float ms = m_run == -INFINITY ? 0.f : m_run;
 
       // P^T operands: key chunk c = 16 keys; this lane supplies the weights of
       // its accumulator registers 8*(c%2) .. +7 of half c/2, i.e. keys
