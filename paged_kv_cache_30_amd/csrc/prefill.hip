@@ -142,6 +142,20 @@ __device__ __forceinline__ u32x2 lds_read_tr(uint32_t addr) {
 __device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)"); }
 __device__ __forceinline__ void settle(u32x2& x) { asm volatile("" : "+v"(x)); }
 
+// 16-byte LDS read at byte addr + OFF as inline asm (MFMA K operand), so the
+// reads of the next k-chunk can be kept in flight under this chunk's MFMAs:
+// lds_wait_n<N>() returns once at most N LDS reads are outstanding (they
+// complete in order).
+template <int OFF>
+__device__ __forceinline__ u32x4 lds_read16(uint32_t addr) {
+  u32x4 r;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+  return r;
+}
+template <int N>
+__device__ __forceinline__ void lds_wait_n() { asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(N)); }
+__device__ __forceinline__ void settle(u32x4& x) { asm volatile("" : "+v"(x)); }
+
 template <int N> struct IntC { static constexpr int value = N; };
 
 template <class T, int D, int B, int G>
@@ -293,15 +307,27 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a, float sc
     if (!skip) {
       const unsigned long long vmask = kvalid[slot];
       // S^T = K_tile . Q^T, two 32-key halves.
+      // The K fragments of chunk kc+1 are read while chunk kc multiplies.
       f32x16 sacc[2] = {f32x16{}, f32x16{}};
+      const uint32_t kbase = lds_offset(Ks) + 2 * ql * D;
+      auto kaddr = [&](int kc) { return kbase + 16 * ((2 * kc) ^ k_sw); };
+      u32x4 ka[2][2];  // [chunk parity][key half]
+      ka[0][0] = lds_read16<0>(kaddr(0));
+      ka[0][1] = lds_read16<32 * D * 2>(kaddr(0));
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) {
-#pragma unroll
-        for (int kh = 0; kh < 2; ++kh) {
-          const V8 av = __builtin_bit_cast(
-              V8, *reinterpret_cast<const u32x4*>(&Ks[(kh * 32 + ql) * D + 8 * ((2 * kc) ^ k_sw)]));
-          sacc[kh] = M::mma(av, qf[kc], sacc[kh]);
+        const int cur = kc & 1;
+        if (kc + 1 < KC) {
+          ka[cur ^ 1][0] = lds_read16<0>(kaddr(kc + 1));
+          ka[cur ^ 1][1] = lds_read16<32 * D * 2>(kaddr(kc + 1));
+          lds_wait_n<2>();
+        } else {
+          lds_wait_n<0>();
         }
+        settle(ka[cur][0]);
+        settle(ka[cur][1]);
+        sacc[0] = M::mma(__builtin_bit_cast(V8, ka[cur][0]), qf[kc], sacc[0]);
+        sacc[1] = M::mma(__builtin_bit_cast(V8, ka[cur][1]), qf[kc], sacc[1]);
       }
       // Mask (selection, branch-free), running maximum of the raw scores.
       const bool need_mask = vmask != ~0ull || wave_pmin < t0 + kKT - 1 || row0 + 31 >= C ||
