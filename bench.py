@@ -217,6 +217,9 @@ def main(argv=None) -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true",
                     help="replay the step's two calls as HIP graphs instead of calling the library per step")
+    ap.add_argument("--flush-mib", type=int, default=0,
+                    help="before every step, overwrite a buffer of this many MiB (evicts L2 and the 256 MiB "
+                         "MALL); ms_per_step then sums the per-step events, which exclude the flush")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="copy this many MiB once before the timed steps (scale for HBM byte counters)")
     ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_MIB"),
@@ -274,6 +277,8 @@ def main(argv=None) -> int:
         do_write, do_attend = g_write.replay, g_attend.replay
 
     K = args.steps
+    flush_buf = (torch.empty(args.flush_mib << 20, dtype=torch.uint8, device="cuda")
+                 if args.flush_mib > 0 else None)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
@@ -281,6 +286,8 @@ def main(argv=None) -> int:
     wall0 = time.perf_counter()
     start.record()
     for i in range(K):
+        if flush_buf is not None:
+            flush_buf.fill_(i & 0xFF)
         ev[i][0].record()
         do_write()
         ev[i][1].record()
@@ -291,6 +298,8 @@ def main(argv=None) -> int:
     wall = time.perf_counter() - wall0
     ms_total = start.elapsed_time(end)
     ms_step = ms_total / K
+    if flush_buf is not None:
+        ms_step = sum(e[0].elapsed_time(e[2]) for e in ev) / K
     write_ms = sorted(e[0].elapsed_time(e[1]) for e in ev)
     attend_ms = sorted(e[1].elapsed_time(e[2]) for e in ev)
     att_mean = sum(attend_ms) / K
@@ -340,7 +349,8 @@ def main(argv=None) -> int:
         "roofline": roof,
         "timing": {"attend_ms_mean": round(att_mean, 5), "attend_ms_median": round(att_med, 5),
                    "attend_ms_min": round(attend_ms[0], 5), "write_ms_mean": round(sum(write_ms) / K, 5),
-                   "wall_s_timed": round(wall, 4), "mode": timing_mode, "source_hash": src},
+                   "wall_s_timed": round(wall, 4), "mode": timing_mode, "flush_mib": args.flush_mib,
+                   "source_hash": src},
     }
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)

@@ -46,9 +46,12 @@ def assert_close(got, want, dtype, what=""):
         err = np.abs(g2 - w2).max(axis=1)
         bound = TOL_REL_32 * np.maximum(np.abs(w2).max(axis=1), 1e-30)
         bad = err > bound
-        assert not bad.any(), f"{what}: fp32 rel err {float((err / bound).max()) * TOL_REL_32:.3g}"
+        rel = float((err / bound).max()) * TOL_REL_32
+        note(f"{what}: fp32 max row-relative err {rel:.3g}")
+        assert not bad.any(), f"{what}: fp32 rel err {rel:.3g}"
     else:
         err = float(np.abs(got - want).max())
+        note(f"{what}: max abs err {err:.3g}")
         assert err <= TOL_ABS_16, f"{what}: max abs err {err:.3g}"
 
 
