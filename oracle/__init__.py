@@ -15,6 +15,8 @@ Two independent implementations:
   weighted sum of values; window and causal masks).
 * ``oracle.brute`` - scalar pure Python (``math.exp``/``math.fsum``) for tiny
   inputs, used to cross-check ``oracle.ref``.
+* ``oracle.quant`` - the 8-bit (INT8 / FP8 E4M3) row encoding of KV pages and
+  decode over the decoded pools (float32 encoding steps, float64 attention).
 
 Sources (the pages these follow, by title and section):
 
@@ -36,5 +38,6 @@ Sources (the pages these follow, by title and section):
 Parity-unpinned: none of the oracle's functions.  Every function is pinned by
 ``tests/test_oracle.py`` against closed forms, invariants, a library routine
 (``torch.nn.functional.scaled_dot_product_attention`` in float64) and the
-scalar brute force.
+scalar brute force; the 8-bit encoding by ``tests/test_oracle_quant.py``
+(torch's float8_e4m3fn conversion, round-trip bounds, exact cases).
 """

@@ -117,12 +117,15 @@ def attended_range(L: int, window: int):
 
 
 def decode(q, k_pool, v_pool, block_tables, context_lens, *, block_size, num_kv_heads,
-           window, scale, dtype, seqs=None, heads=None):
+           window, scale, dtype, seqs=None, heads=None, kv_dtype=None):
     """Single-query decode through the block table, every (seq, head).
 
     q [S, H, D].  Returns (out [S, H, D], lse [S, H]) float64; with ``seqs`` /
-    ``heads`` only those rows are computed (others stay NaN).
+    ``heads`` only those rows are computed (others stay NaN).  ``kv_dtype``
+    (default ``dtype``) is the storage type of the pools when it differs from
+    the queries' ("f64": already decoded values).
     """
+    kv_dtype = dtype if kv_dtype is None else kv_dtype
     S, H, D = q.shape
     out = np.full((S, H, D), np.nan)
     lse = np.full((S, H), np.nan)
@@ -137,8 +140,8 @@ def decode(q, k_pool, v_pool, block_tables, context_lens, *, block_size, num_kv_
         for h in heads:
             by_group.setdefault(kv_head_of(h, H, num_kv_heads), []).append(h)
         for g, hs in by_group.items():
-            K = gather(k_pool, block_tables[s], pos, g, block_size, dtype)
-            V = gather(v_pool, block_tables[s], pos, g, block_size, dtype)
+            K = gather(k_pool, block_tables[s], pos, g, block_size, kv_dtype)
+            V = gather(v_pool, block_tables[s], pos, g, block_size, kv_dtype)
             o, l = attend(qf[s, hs], K, V, scale)
             out[s, hs] = o
             lse[s, hs] = l
