@@ -37,19 +37,24 @@ HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0}
 
 
-def decode_bytes(w) -> dict:
-    """Algorithmic bytes of one decode call and of the step's write."""
+def decode_bytes(w, kv: str = "native") -> dict:
+    """Algorithmic bytes of one decode call and of the step's write.  With
+    8-bit pools (kv "i8" / "fp8") a K or V row is D code bytes plus its
+    4-byte scale."""
     import numpy as np
     eb = {"f32": 4, "f16": 2, "bf16": 2}[w.dtype]
     S, H, D, B = w.num_seqs, w.num_heads, w.head_dim, w.block_size
     L = w.context_lens.astype(np.int64)
     lo = np.maximum(0, L - w.window) if w.window > 0 else np.zeros_like(L)
     blocks = np.where(L > 0, (L + B - 1) // B - lo // B, 0)
-    attend = (w.kv_bytes_attended() + S * H * D * eb + S * H * D * 4 + S * H * 4
-              + int(blocks.sum()) * 4 + S * 4)
+    kv_bytes = w.kv_bytes_attended()
+    if kv != "native":
+        kv_bytes = kv_bytes // (D * eb) * (D + 4)
+    attend = (kv_bytes + S * H * D * eb + S * H * D * 4 + S * H * 4 + int(blocks.sum()) * 4 + S * 4)
     T = int((L > 0).sum())
-    write = T * w.num_kv_heads * D * eb * 2 * 2 + T * 8 + T * 4
-    return {"attend": attend, "write": write, "kv": w.kv_bytes_attended()}
+    stored = D * eb if kv == "native" else D + 4
+    write = T * w.num_kv_heads * 2 * (D * eb + stored) + T * 8 + T * 4
+    return {"attend": attend, "write": write, "kv": kv_bytes}
 
 
 def prefill_flop(w) -> int:
@@ -189,7 +194,7 @@ def summarize_pmc(args, fetch_dir, write_dir, copy_mib) -> int:
                         "calls": len(calls), "copy_kib_raw": copy_val, "scale": round(scale, 4),
                         "bytes_per_call": round(sum(per_call) / max(len(per_call), 1))}
     src = source_hash("decode.hip", "common.h") if kind == "decode" else source_hash("prefill.hip", "common.h")
-    key = f"paged_attn_{kind}|{w.name}"
+    key = f"paged_attn_{kind}|{w.name}" + ("" if args.kv == "native" else f"|{args.kv}")
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         db = json.load(open(path))
@@ -213,6 +218,9 @@ def main(argv=None) -> int:
                          "4 sliding-window decode, 5 chunked prefill over a shared prefix")
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--workers", type=int, default=0, help="decode wavefront workers (0 = automatic)")
+    ap.add_argument("--kv", choices=["native", "i8", "fp8"], default="native",
+                    help="decode pools: the workload's dtype (default) or 8-bit INT8 / FP8 E4M3 codes with row "
+                         "scales, encoded from the workload's rows on write")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true",
@@ -244,7 +252,10 @@ def main(argv=None) -> int:
         return 1
     torch.cuda.set_device(0)
     w = wl.config(args.config, args.seed)
-    d = session.DeviceWorkload(w, num_workers=args.workers)
+    if args.kv != "native" and w.kind != "decode":
+        print("8-bit pools (--kv) are decode only", file=sys.stderr)
+        return 2
+    d = session.DeviceWorkload(w, num_workers=args.workers, kv_format=args.kv)
     torch.cuda.synchronize()
     if args.calibration_copy_mib:
         # A plain device copy of known size, for scaling HBM byte counters.
@@ -306,16 +317,16 @@ def main(argv=None) -> int:
     att_med = attend_ms[K // 2]
 
     if w.kind == "decode":
-        by = decode_bytes(w)
+        by = decode_bytes(w, args.kv)
         step_units = by["attend"] + by["write"]
         value = step_units / (ms_step * 1e-3) / 1e9
         unit = "GB/s"
         achieved = by["attend"] / (att_mean * 1e-3) / 1e9
         src = source_hash("decode.hip", "common.h")
-        key = f"paged_attn_decode|{w.name}"
+        key = f"paged_attn_decode|{w.name}" + ("" if args.kv == "native" else f"|{args.kv}")
         roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_for(key, src)}
-        n_part_info = {"decode_workers": d.num_workers or pkv_workers(d)}
+        n_part_info = {"decode_workers": d.num_workers or pkv_workers(d), "kv_pool": args.kv}
     else:
         flop = prefill_flop(w)
         value = flop / (ms_step * 1e-3) / 1e12
@@ -340,7 +351,7 @@ def main(argv=None) -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": w.dtype,
+        "dtype": w.dtype if args.kv == "native" else f"{args.kv}+{w.dtype}",
         "data": "synthetic (seeded, shapes and distributions of the workload)",
         "config": {"workload": w.name, "kind": w.kind, "num_seqs": w.num_seqs, "num_heads": w.num_heads,
                    "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "block_size": w.block_size,

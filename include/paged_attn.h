@@ -55,8 +55,10 @@
 extern "C" {
 #endif
 
-/* Element types of pools, queries and new keys/values. */
-enum { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2 };
+/* Element types of pools, queries and new keys/values. PKV_I8 and PKV_FP8
+ * are 8-bit pools (codes with one float32 scale per row), used only through
+ * paged_kv_write_quant and paged_attn_decode_quant. */
+enum { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2, PKV_I8 = 3, PKV_FP8 = 4 };
 
 /* Status codes. */
 enum {
@@ -73,7 +75,8 @@ enum {
  *   num_heads     H, query heads
  *   num_kv_heads  Hkv, key/value heads; H % Hkv == 0, H / Hkv in {1, 2, 4, 8}
  *   head_dim      D: 64 or 128
- *   kv_dtype      PKV_F32, PKV_F16 or PKV_BF16 (pools, q, k_new, v_new)
+ *   kv_dtype      PKV_F32, PKV_F16 or PKV_BF16 (pools, q, k_new, v_new), or
+ *                 PKV_I8 / PKV_FP8 for 8-bit pools (the *_quant calls)
  * One block (B * Hkv * D elements) must hold fewer than 2^31 bytes
  * (PKV_EUNSUPPORTED otherwise). */
 typedef struct pkv_geometry {
@@ -85,7 +88,8 @@ typedef struct pkv_geometry {
   int32_t kv_dtype;
 } pkv_geometry_t;
 
-/* paged_kv_write - store new tokens' keys and values in their pool slots.
+/* paged_kv_write - store new tokens' keys and values in their pool slots
+ * (16-bit and fp32 pools; 8-bit pools use paged_kv_write_quant).
  *
  * "Build a Paged KV Cache in Pure Python", Step 3 (append): token n of
  * sequence seq_idx[n] at position pos[n] goes to block
@@ -182,13 +186,69 @@ int paged_attn_decode(const pkv_geometry_t* geom, float* out, float* lse, const 
  *   max_q_len        host bound on the chunk lengths
  *   max_context_len  host bound on context_lens (<= max_blocks_per_seq * B)
  * Requires C <= L for every sequence. Scores and outputs accumulate in
- * float32; the softmax weights are rounded to kv_dtype before they multiply
- * V on the matrix cores. */
+ * float32. The softmax weights multiply V on the matrix cores: rounded to
+ * fp16 for PKV_F16; for PKV_BF16 each weight is split into two bf16 parts
+ * (high part and rounded remainder) that are both multiplied, which keeps
+ * about 16 significant bits. */
 int paged_attn_prefill(const pkv_geometry_t* geom, float* out, float* lse, const void* q,
                        const int32_t* q_start, const void* k_pool, const void* v_pool,
                        const int32_t* block_tables, int32_t max_blocks_per_seq,
                        const int32_t* context_lens, int32_t num_seqs, int32_t max_q_len,
                        int32_t max_context_len, int32_t window, float scale, void* stream);
+
+/* 8-bit key/value pages.
+ *
+ * "Build a Memory-Compressed Attention Engine with KV Caching from
+ * Scratch", section "Extending It: Your Roadmap to Senior-Level", item 2
+ * (quantized KV cache: INT8 or FP8 keys and values cut the bytes a decode
+ * step reads). Encoding of one row x (the D values of one block slot and kv
+ * head), all in float32 with correctly rounded division:
+ *   amax = max_d |x_d|, scale = amax / QMAX, inv = QMAX / amax (0 if amax 0)
+ *   PKV_I8:  code_d = round-half-even(x_d * inv) clamped to [-127, 127]
+ *            (QMAX 127), two's complement
+ *   PKV_FP8: code_d = x_d * inv rounded to the nearest OCP FP8 E4M3 value
+ *            (bias 7, largest 448 = QMAX, ties to even)
+ *   decoded value = code_d * scale.
+ * Pools hold codes, uint8 [NB, B, Hkv, D] (the 16-bit layout); scale pools
+ * hold the row scales, float32 [NB, Hkv, B]. */
+
+/* paged_kv_write_quant - encode new tokens' keys and values into 8-bit
+ * pools. Slot rule, skipping of invalid tokens and races as paged_kv_write
+ * ("Build a Paged KV Cache in Pure Python", Step 3); each (token, kv head)
+ * row is encoded as above and its scale stored at
+ * scale[block][kv head][slot]. Rows never written keep whatever the caller
+ * put there.
+ *
+ *   geom->kv_dtype   PKV_I8 or PKV_FP8
+ *   k_pool, v_pool   [NB, B, Hkv, D] codes, written in place
+ *   k_scale, v_scale float32 [NB, Hkv, B], written in place
+ *   k_new, v_new     [num_tokens, Hkv, D] new_dtype (PKV_F32, PKV_F16 or
+ *                    PKV_BF16)
+ *   seq_idx, pos, block_tables, num_seqs, max_blocks_per_seq: as
+ *                    paged_kv_write */
+int paged_kv_write_quant(const pkv_geometry_t* geom, void* k_pool, void* v_pool, float* k_scale,
+                         float* v_scale, const void* k_new, const void* v_new, int32_t new_dtype,
+                         const int32_t* seq_idx, const int32_t* pos, int32_t num_tokens,
+                         const int32_t* block_tables, int32_t num_seqs, int32_t max_blocks_per_seq,
+                         void* stream);
+
+/* paged_attn_decode_quant - paged_attn_decode over 8-bit pools: the same
+ * attention with every key and value replaced by its decoded value
+ * code * scale. Scores and outputs accumulate in float32 (the row scales
+ * factor out of each dot product).
+ *
+ *   geom->kv_dtype    PKV_I8 or PKV_FP8; num_heads / num_kv_heads in {1, 2, 4}
+ *   q                 q_dtype [num_seqs, H, D], q_dtype PKV_F16 or PKV_BF16
+ *   k_pool, v_pool    codes [NB, B, Hkv, D]
+ *   k_scale, v_scale  float32 [NB, Hkv, B]
+ *   all other arguments, the workspace (paged_attn_decode_workspace_bytes
+ *   with this geometry) and the worker count as paged_attn_decode. */
+int paged_attn_decode_quant(const pkv_geometry_t* geom, float* out, float* lse, const void* q,
+                            int32_t q_dtype, const void* k_pool, const void* v_pool,
+                            const float* k_scale, const float* v_scale, const int32_t* block_tables,
+                            int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
+                            int32_t max_context_len, int32_t window, float scale, int32_t num_workers,
+                            void* workspace, size_t workspace_bytes, void* stream);
 
 /* Name of a status code (static string). */
 const char* pkv_status_string(int status);

@@ -19,15 +19,19 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("PKV_LIBRARY", os.path.join(_HERE, "libpagedattn.so"))
 
-PKV_F32, PKV_F16, PKV_BF16 = 0, 1, 2
+PKV_F32, PKV_F16, PKV_BF16, PKV_I8, PKV_FP8 = 0, 1, 2, 3, 4
 PKV_OK, PKV_EINVAL, PKV_EUNSUPPORTED, PKV_EWORKSPACE, PKV_EHIP = 0, -1, -2, -3, -4
 
-_DTYPES = {torch.float32: PKV_F32, torch.float16: PKV_F16, torch.bfloat16: PKV_BF16}
+# 8-bit pools are torch.int8 (INT8 codes) or torch.float8_e4m3fn (FP8 E4M3
+# codes); their row scales are separate float32 tensors.
+_DTYPES = {torch.float32: PKV_F32, torch.float16: PKV_F16, torch.bfloat16: PKV_BF16,
+           torch.int8: PKV_I8, torch.float8_e4m3fn: PKV_FP8}
+_QUANT = (torch.int8, torch.float8_e4m3fn)
 
 # Every symbol declared in include/paged_attn.h.
 EXPORTS = ("paged_kv_write", "paged_attn_decode_workspace_bytes", "paged_attn_decode_workers",
-           "paged_attn_decode", "paged_attn_prefill", "pkv_status_string", "pkv_last_hip_error",
-           "pkv_version")
+           "paged_attn_decode", "paged_attn_prefill", "paged_kv_write_quant", "paged_attn_decode_quant",
+           "pkv_status_string", "pkv_last_hip_error", "pkv_version")
 
 
 class Geometry(ctypes.Structure):
@@ -60,6 +64,11 @@ def _load() -> ctypes.CDLL:
     lib.paged_attn_decode.restype = ctypes.c_int
     lib.paged_attn_prefill.argtypes = [G, P, P, P, P, P, P, P, I32, P, I32, I32, I32, I32, F, P]
     lib.paged_attn_prefill.restype = ctypes.c_int
+    lib.paged_kv_write_quant.argtypes = [G, P, P, P, P, P, P, I32, P, P, I32, P, I32, I32, P]
+    lib.paged_kv_write_quant.restype = ctypes.c_int
+    lib.paged_attn_decode_quant.argtypes = [G, P, P, P, I32, P, P, P, P, P, I32, P, I32, I32, I32, F, I32, P, SZ,
+                                            P]
+    lib.paged_attn_decode_quant.restype = ctypes.c_int
     lib.pkv_status_string.argtypes = [ctypes.c_int]
     lib.pkv_status_string.restype = ctypes.c_char_p
     lib.pkv_last_hip_error.argtypes = []
@@ -239,3 +248,95 @@ def paged_attn_prefill(out, q, q_start, k_pool, v_pool, block_tables, context_le
     """C ``paged_attn_prefill``: out[T, H, D] (fp32) for chunk queries q[T, H, D]."""
     bind_prefill(out, q, q_start, k_pool, v_pool, block_tables, context_lens, max_q_len, max_context_len,
                  window=window, scale=scale, lse=lse)(stream)
+
+
+# ------------------------------------------------------------- 8-bit pools
+
+def _check_quant_pools(k_pool, v_pool, k_scale, v_scale):
+    _dev(k_pool, "k_pool", ndim=4)
+    if k_pool.dtype not in _QUANT:
+        raise ValueError("8-bit pools are torch.int8 (INT8) or torch.float8_e4m3fn (FP8)")
+    _dev(v_pool, "v_pool", dtype=k_pool.dtype)
+    if v_pool.shape != k_pool.shape:
+        raise ValueError("k_pool and v_pool differ in shape")
+    nb, b, hkv, _ = k_pool.shape
+    for name, t in (("k_scale", k_scale), ("v_scale", v_scale)):
+        _dev(t, name, dtype=torch.float32, ndim=3)
+        if tuple(t.shape) != (nb, hkv, b):
+            raise ValueError(f"{name} must be [num_blocks, num_kv_heads, block_size]")
+
+
+def bind_kv_write_quant(k_pool, v_pool, k_scale, v_scale, k_new, v_new, seq_idx, pos, block_tables):
+    """Check and marshal the arguments of ``paged_kv_write_quant`` once;
+    returns a callable ``f(stream=None)``."""
+    _check_quant_pools(k_pool, v_pool, k_scale, v_scale)
+    _dev(k_new, "k_new", ndim=3)
+    _dev(v_new, "v_new", dtype=k_new.dtype, ndim=3)
+    if k_new.dtype not in (torch.float32, torch.float16, torch.bfloat16):
+        raise ValueError("k_new/v_new must be float32, float16 or bfloat16")
+    _dev(seq_idx, "seq_idx", dtype=torch.int32, ndim=1)
+    _dev(pos, "pos", dtype=torch.int32, ndim=1)
+    _dev(block_tables, "block_tables", dtype=torch.int32, ndim=2)
+    T = k_new.shape[0]
+    if k_new.shape[1:] != k_pool.shape[2:] or v_new.shape != k_new.shape:
+        raise ValueError("k_new/v_new must be [T, num_kv_heads, head_dim]")
+    if seq_idx.shape[0] != T or pos.shape[0] != T:
+        raise ValueError("seq_idx and pos need one entry per token")
+    g = geometry(k_pool, k_pool.shape[2])
+    args = (ctypes.byref(g), _ptr(k_pool), _ptr(v_pool), _ptr(k_scale), _ptr(v_scale), _ptr(k_new), _ptr(v_new),
+            _DTYPES[k_new.dtype], _ptr(seq_idx), _ptr(pos), T, _ptr(block_tables), block_tables.shape[0],
+            block_tables.shape[1])
+    keep = (g, k_pool, v_pool, k_scale, v_scale, k_new, v_new, seq_idx, pos, block_tables)
+
+    def call(stream=None):
+        _check(LIB.paged_kv_write_quant(*args, _stream(stream)), "paged_kv_write_quant")
+    call.keep = keep
+    return call
+
+
+def paged_kv_write_quant(k_pool, v_pool, k_scale, v_scale, k_new, v_new, seq_idx, pos, block_tables,
+                         stream=None) -> None:
+    """C ``paged_kv_write_quant``: encode k_new/v_new [T, Hkv, D] into 8-bit pools."""
+    bind_kv_write_quant(k_pool, v_pool, k_scale, v_scale, k_new, v_new, seq_idx, pos, block_tables)(stream)
+
+
+def bind_decode_quant(out, q, k_pool, v_pool, k_scale, v_scale, block_tables, context_lens, max_context_len, *,
+                      window=0, scale, num_workers=0, workspace=None, lse=None):
+    """Check and marshal the arguments of ``paged_attn_decode_quant`` once;
+    returns a callable ``f(stream=None)``."""
+    _check_quant_pools(k_pool, v_pool, k_scale, v_scale)
+    _dev(q, "q", ndim=3)
+    if q.dtype not in (torch.float16, torch.bfloat16):
+        raise ValueError("q must be float16 or bfloat16 for 8-bit pools")
+    _dev(out, "out", dtype=torch.float32, ndim=3)
+    _dev(block_tables, "block_tables", dtype=torch.int32, ndim=2)
+    _dev(context_lens, "context_lens", dtype=torch.int32, ndim=1)
+    S, H, D = q.shape
+    if out.shape != q.shape or context_lens.shape[0] != S or block_tables.shape[0] != S:
+        raise ValueError("shape mismatch between q, out, context_lens and block_tables")
+    if lse is not None:
+        _dev(lse, "lse", dtype=torch.float32, ndim=2)
+        if lse.shape != (S, H):
+            raise ValueError("lse must be [S, H]")
+    ws_bytes = 0
+    if workspace is not None:
+        _dev(workspace, "workspace")
+        ws_bytes = workspace.numel() * workspace.element_size()
+    g = geometry(k_pool, H)
+    args = (ctypes.byref(g), _ptr(out), _ptr(lse), _ptr(q), _DTYPES[q.dtype], _ptr(k_pool), _ptr(v_pool),
+            _ptr(k_scale), _ptr(v_scale), _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), S,
+            int(max_context_len), int(window), float(scale), int(num_workers), _ptr(workspace), ws_bytes)
+    keep = (g, out, q, k_pool, v_pool, k_scale, v_scale, block_tables, context_lens, workspace, lse)
+
+    def call(stream=None):
+        _check(LIB.paged_attn_decode_quant(*args, _stream(stream)), "paged_attn_decode_quant")
+    call.keep = keep
+    return call
+
+
+def paged_attn_decode_quant(out, q, k_pool, v_pool, k_scale, v_scale, block_tables, context_lens,
+                            max_context_len, *, window=0, scale, num_workers=0, workspace=None, lse=None,
+                            stream=None) -> None:
+    """C ``paged_attn_decode_quant``: decode over 8-bit pools with row scales."""
+    bind_decode_quant(out, q, k_pool, v_pool, k_scale, v_scale, block_tables, context_lens, max_context_len,
+                      window=window, scale=scale, num_workers=num_workers, workspace=workspace, lse=lse)(stream)

@@ -17,7 +17,12 @@ int hip_status(hipError_t e) {
   return PKV_EHIP;
 }
 
-int elem_bytes(int dtype) { return dtype == PKV_F32 ? 4 : 2; }
+int elem_bytes(int dtype) { return dtype == PKV_F32 ? 4 : (dtype == PKV_I8 || dtype == PKV_FP8) ? 1 : 2; }
+bool is_quant(int dtype) { return dtype == PKV_I8 || dtype == PKV_FP8; }
+// The query type that sizes the automatic decode split: the pools' own for
+// 16-bit and fp32 pools, bf16 for 8-bit pools (both query types of an 8-bit
+// pool use the same count, so workspace queries need no query type).
+int split_q_dtype(int kv_dtype) { return is_quant(kv_dtype) ? PKV_BF16 : kv_dtype; }
 
 // Geometry checks common to every call. Returns PKV_OK, PKV_EINVAL or
 // PKV_EUNSUPPORTED.
@@ -27,7 +32,8 @@ int check_geometry(const pkv_geometry_t* g) {
       g->head_dim <= 0)
     return PKV_EINVAL;
   if (g->num_heads % g->num_kv_heads) return PKV_EINVAL;
-  if (g->kv_dtype != PKV_F32 && g->kv_dtype != PKV_F16 && g->kv_dtype != PKV_BF16) return PKV_EUNSUPPORTED;
+  if (g->kv_dtype != PKV_F32 && g->kv_dtype != PKV_F16 && g->kv_dtype != PKV_BF16 && !is_quant(g->kv_dtype))
+    return PKV_EUNSUPPORTED;
   if (g->head_dim != 64 && g->head_dim != 128) return PKV_EUNSUPPORTED;
   if (g->block_size != 16 && g->block_size != 32) return PKV_EUNSUPPORTED;
   const int G = g->num_heads / g->num_kv_heads;
@@ -66,7 +72,7 @@ int decode_split(const pkv_geometry_t* g, int num_seqs, int max_context_len, int
   int nw = num_workers;
   if (nw == 0) {
     const long long bound = (long long)num_seqs * g->num_kv_heads * span_blocks(g, max_context_len, window);
-    nw = pkv::decode_auto_workers(g->kv_dtype, g->head_dim, g->block_size, G);
+    nw = pkv::decode_auto_workers(g->kv_dtype, split_q_dtype(g->kv_dtype), g->head_dim, g->block_size, G);
     if (bound < nw) nw = bound > 0 ? (int)bound : 1;
   }
   const size_t slots = (size_t)nw + (size_t)num_seqs * g->num_kv_heads;
@@ -87,6 +93,7 @@ int paged_kv_write(const pkv_geometry_t* geom, void* k_pool, void* v_pool, const
                    void* stream) {
   int st = check_geometry(geom);
   if (st) return st;
+  if (is_quant(geom->kv_dtype)) return PKV_EUNSUPPORTED;  // paged_kv_write_quant
   if (num_tokens < 0 || num_seqs < 0 || max_blocks_per_seq <= 0) return PKV_EINVAL;
   if (num_tokens == 0) return PKV_OK;
   if (!k_pool || !v_pool || !k_new || !v_new || !seq_idx || !pos || !block_tables || num_seqs == 0)
@@ -113,6 +120,42 @@ size_t paged_attn_decode_workspace_bytes(const pkv_geometry_t* geom, int32_t num
   return sp.total();
 }
 
+}  // extern "C"
+
+namespace {
+
+int decode_common(const pkv_geometry_t* geom, float* out, float* lse, const void* q, int q_dtype,
+                  const void* k_pool, const void* v_pool, const float* k_scale, const float* v_scale,
+                  const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                  int32_t num_seqs, int32_t max_context_len, int32_t window, float scale, int32_t num_workers,
+                  void* workspace, size_t workspace_bytes, void* stream) {
+  if (num_seqs < 0 || max_blocks_per_seq <= 0 || max_context_len < 0 || window < 0 || num_workers < 0 ||
+      !isfinite(scale))
+    return PKV_EINVAL;
+  if ((long long)max_context_len > (long long)max_blocks_per_seq * geom->block_size) return PKV_EINVAL;
+  if (num_seqs == 0) return PKV_OK;
+  if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens) return PKV_EINVAL;
+  if (is_quant(geom->kv_dtype) && (!k_scale || !v_scale)) return PKV_EINVAL;
+  const int G = geom->num_heads / geom->num_kv_heads;
+  if (!pkv::decode_supported(geom->kv_dtype, q_dtype, geom->head_dim, geom->block_size, G))
+    return PKV_EUNSUPPORTED;
+  DecodeSplit sp;
+  int st = decode_split(geom, num_seqs, max_context_len, window, num_workers, &sp);
+  if (st) return st;
+  if (!workspace || workspace_bytes < sp.total() || ((uintptr_t)workspace & 15)) return PKV_EWORKSPACE;
+  char* ws = (char*)workspace;
+  pkv::DecodeArgs a{out, lse, q, k_pool, v_pool, block_tables, context_lens, k_scale, v_scale, q_dtype,
+                    (int32_t*)ws, (float*)(ws + sp.cum_bytes), (float*)(ws + sp.cum_bytes + sp.ml_bytes),
+                    num_seqs, geom->num_heads, geom->num_kv_heads, geom->head_dim, geom->block_size,
+                    max_blocks_per_seq, geom->num_blocks, window, geom->kv_dtype, max_context_len,
+                    sp.workers, scale};
+  return hip_status(pkv::launch_decode(a, (hipStream_t)stream));
+}
+
+}  // namespace
+
+extern "C" {
+
 int paged_attn_decode(const pkv_geometry_t* geom, float* out, float* lse, const void* q,
                       const void* k_pool, const void* v_pool, const int32_t* block_tables,
                       int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
@@ -120,25 +163,45 @@ int paged_attn_decode(const pkv_geometry_t* geom, float* out, float* lse, const 
                       void* workspace, size_t workspace_bytes, void* stream) {
   int st = check_geometry(geom);
   if (st) return st;
-  if (num_seqs < 0 || max_blocks_per_seq <= 0 || max_context_len < 0 || window < 0 || num_workers < 0 ||
-      !isfinite(scale))
-    return PKV_EINVAL;
-  if ((long long)max_context_len > (long long)max_blocks_per_seq * geom->block_size) return PKV_EINVAL;
-  if (num_seqs == 0) return PKV_OK;
-  if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens) return PKV_EINVAL;
-  const int G = geom->num_heads / geom->num_kv_heads;
-  if (!pkv::decode_supported(geom->kv_dtype, geom->head_dim, geom->block_size, G)) return PKV_EUNSUPPORTED;
-  DecodeSplit sp;
-  st = decode_split(geom, num_seqs, max_context_len, window, num_workers, &sp);
+  if (is_quant(geom->kv_dtype)) return PKV_EUNSUPPORTED;  // paged_attn_decode_quant
+  return decode_common(geom, out, lse, q, geom->kv_dtype, k_pool, v_pool, nullptr, nullptr, block_tables,
+                       max_blocks_per_seq, context_lens, num_seqs, max_context_len, window, scale, num_workers,
+                       workspace, workspace_bytes, stream);
+}
+
+int paged_attn_decode_quant(const pkv_geometry_t* geom, float* out, float* lse, const void* q, int32_t q_dtype,
+                            const void* k_pool, const void* v_pool, const float* k_scale, const float* v_scale,
+                            const int32_t* block_tables, int32_t max_blocks_per_seq,
+                            const int32_t* context_lens, int32_t num_seqs, int32_t max_context_len,
+                            int32_t window, float scale, int32_t num_workers, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  int st = check_geometry(geom);
   if (st) return st;
-  if (!workspace || workspace_bytes < sp.total() || ((uintptr_t)workspace & 15)) return PKV_EWORKSPACE;
-  char* ws = (char*)workspace;
-  pkv::DecodeArgs a{out, lse, q, k_pool, v_pool, block_tables, context_lens,
-                    (int32_t*)ws, (float*)(ws + sp.cum_bytes), (float*)(ws + sp.cum_bytes + sp.ml_bytes),
-                    num_seqs, geom->num_heads, geom->num_kv_heads, geom->head_dim, geom->block_size,
-                    max_blocks_per_seq, geom->num_blocks, window, geom->kv_dtype, max_context_len,
-                    sp.workers, scale};
-  return hip_status(pkv::launch_decode(a, (hipStream_t)stream));
+  if (!is_quant(geom->kv_dtype)) return PKV_EINVAL;
+  if (q_dtype != PKV_F16 && q_dtype != PKV_BF16) return PKV_EUNSUPPORTED;
+  return decode_common(geom, out, lse, q, q_dtype, k_pool, v_pool, k_scale, v_scale, block_tables,
+                       max_blocks_per_seq, context_lens, num_seqs, max_context_len, window, scale, num_workers,
+                       workspace, workspace_bytes, stream);
+}
+
+int paged_kv_write_quant(const pkv_geometry_t* geom, void* k_pool, void* v_pool, float* k_scale, float* v_scale,
+                         const void* k_new, const void* v_new, int32_t new_dtype, const int32_t* seq_idx,
+                         const int32_t* pos, int32_t num_tokens, const int32_t* block_tables, int32_t num_seqs,
+                         int32_t max_blocks_per_seq, void* stream) {
+  int st = check_geometry(geom);
+  if (st) return st;
+  if (!is_quant(geom->kv_dtype)) return PKV_EINVAL;
+  if (new_dtype != PKV_F32 && new_dtype != PKV_F16 && new_dtype != PKV_BF16) return PKV_EUNSUPPORTED;
+  if (num_tokens < 0 || num_seqs < 0 || max_blocks_per_seq <= 0) return PKV_EINVAL;
+  if (num_tokens == 0) return PKV_OK;
+  if (!k_pool || !v_pool || !k_scale || !v_scale || !k_new || !v_new || !seq_idx || !pos || !block_tables ||
+      num_seqs == 0)
+    return PKV_EINVAL;
+  if (!pkv::kv_write_quant_supported(geom->kv_dtype, new_dtype, geom->head_dim)) return PKV_EUNSUPPORTED;
+  pkv::WriteQuantArgs a{k_pool, v_pool, k_scale, v_scale, k_new, v_new, seq_idx, pos, block_tables,
+                        num_tokens, num_seqs, max_blocks_per_seq, geom->num_blocks, geom->block_size,
+                        geom->num_kv_heads, geom->head_dim, geom->kv_dtype, new_dtype};
+  return hip_status(pkv::launch_kv_write_quant(a, (hipStream_t)stream));
 }
 
 int paged_attn_prefill(const pkv_geometry_t* geom, float* out, float* lse, const void* q,
@@ -156,7 +219,9 @@ int paged_attn_prefill(const pkv_geometry_t* geom, float* out, float* lse, const
   if (num_seqs == 0 || max_q_len == 0) return PKV_OK;
   if (!out || !q || !q_start || !k_pool || !v_pool || !block_tables || !context_lens) return PKV_EINVAL;
   const int G = geom->num_heads / geom->num_kv_heads;
-  if (!pkv::prefill_supported(geom->kv_dtype, geom->head_dim, geom->block_size, G)) return PKV_EUNSUPPORTED;
+  if (is_quant(geom->kv_dtype) ||
+      !pkv::prefill_supported(geom->kv_dtype, geom->head_dim, geom->block_size, G))
+    return PKV_EUNSUPPORTED;
   pkv::PrefillArgs a{out, lse, q, q_start, k_pool, v_pool, block_tables, context_lens, num_seqs,
                      geom->num_heads, geom->num_kv_heads, geom->head_dim, geom->block_size,
                      max_blocks_per_seq, geom->num_blocks, window, geom->kv_dtype, max_q_len,
@@ -177,6 +242,6 @@ const char* pkv_status_string(int status) {
 
 int pkv_last_hip_error(void) { return g_last_hip_error; }
 
-int pkv_version(void) { return 100; }
+int pkv_version(void) { return 200; }
 
 }  // extern "C"

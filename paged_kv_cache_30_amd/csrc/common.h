@@ -1,6 +1,7 @@
-// Internal helpers shared by the gfx950 kernels: element traits for the three
-// storage types, 16-byte chunk dot products and conversions, and DPP lane
-// reductions inside rows of 16 lanes.
+// Internal helpers shared by the gfx950 kernels: element traits for the
+// storage types (fp32, fp16, bf16 and the 8-bit INT8 / FP8 E4M3 codes),
+// 16-byte chunk dot products and conversions, and DPP lane reductions inside
+// rows of 16 lanes.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -16,10 +17,26 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
 // Storage type tags. BYTES is the element size; one 16-byte chunk holds
-// 16 / BYTES elements.
-struct F32T { static constexpr int BYTES = 4; };
-struct F16T { static constexpr int BYTES = 2; };
-struct BF16T { static constexpr int BYTES = 2; };
+// 16 / BYTES elements. QUANT: 8-bit codes with one fp32 scale per row.
+struct F32T { static constexpr int BYTES = 4; static constexpr bool QUANT = false; static constexpr float BIAS = 0.f; };
+struct F16T { static constexpr int BYTES = 2; static constexpr bool QUANT = false; static constexpr float BIAS = 0.f; };
+struct BF16T { static constexpr int BYTES = 2; static constexpr bool QUANT = false; static constexpr float BIAS = 0.f; };
+// INT8 codes (two's complement, -127..127) and OCP FP8 E4M3 codes. QMAX is
+// the code magnitude a row's largest element maps to. The kernels widen INT8
+// codes as unsigned bytes of (code ^ 0x80) = code + 128 and subtract BIAS =
+// 128 once per sum; FP8 codes widen exactly (BIAS 0).
+struct I8T {
+  static constexpr int BYTES = 1;
+  static constexpr bool QUANT = true;
+  static constexpr float QMAX = 127.f;
+  static constexpr float BIAS = 128.f;
+};
+struct FP8T {
+  static constexpr int BYTES = 1;
+  static constexpr bool QUANT = true;
+  static constexpr float QMAX = 448.f;
+  static constexpr float BIAS = 0.f;
+};
 
 // Reinterpret one 32-bit word. The word is taken by value: bit-casting an
 // ext-vector element in place (q.y) reads the vector's first element.
@@ -82,6 +99,25 @@ template <> __device__ __forceinline__ void chunk_to_f32<BF16T>(const u32x4& v, 
   }
 }
 
+// Four 8-bit codes of one word as fp32 values code + BIAS (exact): INT8 as
+// the unsigned byte code ^ 0x80 = code + 128, FP8 as the code's value.
+template <class T> __device__ __forceinline__ void codes4_to_f32(uint32_t w, float* f);
+
+template <> __device__ __forceinline__ void codes4_to_f32<I8T>(uint32_t w, float* f) {
+  const uint32_t u = w ^ 0x80808080u;
+  f[0] = (float)(u & 0xffu);
+  f[1] = (float)((u >> 8) & 0xffu);
+  f[2] = (float)((u >> 16) & 0xffu);
+  f[3] = (float)(u >> 24);
+}
+
+template <> __device__ __forceinline__ void codes4_to_f32<FP8T>(uint32_t w, float* f) {
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+  const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+  f[0] = lo.x; f[1] = lo.y; f[2] = hi.x; f[3] = hi.y;
+}
+
 // DPP lane permutations (GFX9 encodings): quad_perm, half-row and row mirror.
 template <int CTRL> __device__ __forceinline__ float dpp(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
@@ -100,6 +136,17 @@ template <int N> __device__ __forceinline__ float group_sum(float x) {
   if constexpr (N >= 8) x += dpp<kHalfMirror>(x);
   if constexpr (N >= 16) x += dpp<kRowMirror>(x);
   if constexpr (N >= 32) x += __shfl_xor(x, 16, 64);
+  return x;
+}
+
+// Maximum over aligned groups of N lanes (N in 4, 8, 16, 32).
+template <int N> __device__ __forceinline__ float group_max(float x) {
+  static_assert(N == 4 || N == 8 || N == 16 || N == 32, "group size");
+  x = fmaxf(x, dpp<kQuadSwap1>(x));
+  x = fmaxf(x, dpp<kQuadSwap2>(x));
+  if constexpr (N >= 8) x = fmaxf(x, dpp<kHalfMirror>(x));
+  if constexpr (N >= 16) x = fmaxf(x, dpp<kRowMirror>(x));
+  if constexpr (N >= 32) x = fmaxf(x, __shfl_xor(x, 16, 64));
   return x;
 }
 

@@ -46,6 +46,39 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kPlanThreads = 1024;
 
+// 8-bit K against 16-bit q: acc + sum_e q_e * (code_e + BIAS) over one
+// 16-byte piece of 16 codes; q2 holds the 16 matching q values (two 16-byte
+// words). Codes are widened to fp32, packed in pairs into q's 16-bit type
+// (exact: 0..255 and every E4M3 value fit) and multiplied with v_dot2.
+template <class Q> __device__ __forceinline__ uint32_t pack_pair(float a, float b);
+template <> __device__ __forceinline__ uint32_t pack_pair<BF16T>(float a, float b) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2{a, b}), bf16x2));
+}
+template <> __device__ __forceinline__ uint32_t pack_pair<F16T>(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a, b));
+}
+template <class Q> __device__ __forceinline__ float dot2(uint32_t q, uint32_t k, float acc);
+template <> __device__ __forceinline__ float dot2<BF16T>(uint32_t q, uint32_t k, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(as_b2(q), as_b2(k), acc, false);
+}
+template <> __device__ __forceinline__ float dot2<F16T>(uint32_t q, uint32_t k, float acc) {
+  return __builtin_amdgcn_fdot2(as_h2(q), as_h2(k), acc, false);
+}
+template <class T, class Q>
+__device__ __forceinline__ float dot_codes(const u32x4* q2, const u32x4& k, float acc) {
+  const uint32_t kw[4] = {k.x, k.y, k.z, k.w};
+  const uint32_t qw[8] = {q2[0].x, q2[0].y, q2[0].z, q2[0].w, q2[1].x, q2[1].y, q2[1].z, q2[1].w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float f[4];
+    codes4_to_f32<T>(kw[i], f);
+    acc = dot2<Q>(qw[2 * i], pack_pair<Q>(f[0], f[1]), acc);
+    acc = dot2<Q>(qw[2 * i + 1], pack_pair<Q>(f[2], f[3]), acc);
+  }
+  return acc;
+}
+
 template <class T, int D, int B, int G>
 struct DecodeShape {
   static constexpr int EB = T::BYTES;
@@ -59,7 +92,9 @@ struct DecodeShape {
   static constexpr int STEPS = B / RPL;                // steps per block
   // Loads per chunk (of K and of V); two chunks are in registers at a time
   // (16 KB in flight per wavefront).
-  static constexpr int CWANT = PKV_DECODE_CHUNK_LOADS(G) / PIECES;
+  // 8-bit rows with 4 query heads keep two steps per chunk: their per-lane
+  // state (16 outputs per head) leaves room for fewer loads in flight.
+  static constexpr int CWANT = (T::QUANT && G >= 4) ? 2 : PKV_DECODE_CHUNK_LOADS(G) / PIECES;
   static constexpr int CSTEPS = STEPS < CWANT ? STEPS : CWANT;
   static constexpr int CHUNK = RPL * CSTEPS;           // slots per chunk
   static constexpr int CPB = B / CHUNK;                // chunks per block
@@ -121,12 +156,19 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(DecodeArgs a)
   prefix_blocks<kPlanThreads>(a, a.ws_cum);
 }
 
-template <class T, int D, int B, int G>
+// T: storage type of the pools; Q: type of q (T itself, or fp16/bf16 for the
+// 8-bit pools, whose rows also carry a scale each).
+template <class T, class Q, int D, int B, int G>
 __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, float scale_log2) {
   using Sh = DecodeShape<T, D, B, G>;
   constexpr int E = Sh::E, LPR = Sh::LPR, RPL = Sh::RPL, CSTEPS = Sh::CSTEPS, CHUNK = Sh::CHUNK,
                 CPB = Sh::CPB, EB = Sh::EB, PC = Sh::PIECES;
   constexpr int PSTRIDE = LPR * 16;  // bytes between a lane's pieces of one row
+  constexpr bool QU = T::QUANT;
+  constexpr int QB = Q::BYTES;
+  constexpr int QW = E * QB / 16;    // 16-byte words of q per piece
+  constexpr float BIAS = T::BIAS;
+  static_assert(QU || (QB == EB && QW == 1), "q has the pools' type unless the pools are 8-bit");
 
   const int lane = threadIdx.x & 63;
   // Prefix of attended blocks, in one of three places: batches of fewer than
@@ -215,18 +257,37 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, fl
     const int blk0 = blk_lo + b_first;  // first logical block of the segment
     int tv = lane < n ? trow[lane] : -1;  // table entries of blocks 0..63 of the segment
 
-    const char* qb = (const char*)a.q + ((size_t)(s * H + g * G) * D + c * E) * EB;
-    u32x4 qv[G][PC];
+    const char* qb = (const char*)a.q + ((size_t)(s * H + g * G) * D + c * E) * QB;
+    u32x4 qv[G][PC][QW];
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int pc = 0; pc < PC; ++pc) qv[h][pc] = load16(qb + (size_t)h * D * EB + pc * PSTRIDE);
+      for (int pc = 0; pc < PC; ++pc)
+#pragma unroll
+        for (int qw = 0; qw < QW; ++qw)
+          qv[h][pc][qw] = load16(qb + (size_t)h * D * QB + (size_t)pc * LPR * E * QB + qw * 16);
+    // INT8: the sum of this lane's q values, for the BIAS correction of its
+    // partial dot products; lvb: the running sum of the V weights (same role).
+    float qsum[G], lvb[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       m[h] = -INFINITY;
       l[h] = 0.f;
+      lvb[h] = 0.f;
 #pragma unroll
       for (int e = 0; e < PC * E; ++e) o[h][e] = 0.f;
+      qsum[h] = 0.f;
+      if constexpr (BIAS != 0.f) {
+#pragma unroll
+        for (int pc = 0; pc < PC; ++pc)
+#pragma unroll
+          for (int qw = 0; qw < QW; ++qw) {
+            float f[16 / QB];
+            chunk_to_f32<Q>(qv[h][pc][qw], f);
+#pragma unroll
+            for (int e = 0; e < 16 / QB; ++e) qsum[h] += f[e];
+          }
+      }
     }
     const size_t lane_off = (size_t)g * D * EB + (size_t)c * 16 + (size_t)r * row_stride;
     const char* kbase = (const char*)a.k_pool + lane_off;
@@ -234,13 +295,21 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, fl
 
     // Loads of chunk k of the segment; false when its table entry is out of
     // range (the chunk is skipped).
-    auto issue = [&](int k, u32x4 (*kr)[PC], u32x4 (*vr)[PC]) -> bool {
+    auto issue = [&](int k, u32x4 (*kr)[PC], u32x4 (*vr)[PC], float* ks, float* vs) -> bool {
       const int bi = k / CPB;
       const int sub = k - bi * CPB;
       if ((bi & 63) == 0 && bi > 0 && sub == 0) tv = bi + lane < n ? trow[bi + lane] : -1;
       const int pb = __builtin_amdgcn_readlane(tv, bi & 63);
       if (pb < 0 || pb >= a.nb) return false;
       const size_t off = (size_t)pb * blk_stride + (size_t)sub * CHUNK * row_stride;
+      if constexpr (QU) {  // this lane's row scales, [NB, Hkv, B]
+        const size_t sidx = ((size_t)pb * Hkv + g) * B + sub * CHUNK + r;
+#pragma unroll
+        for (int j = 0; j < CSTEPS; ++j) {
+          ks[j] = a.k_scale[sidx + j * RPL];
+          vs[j] = a.v_scale[sidx + j * RPL];
+        }
+      }
 #pragma unroll
       for (int j = 0; j < CSTEPS; ++j)
 #pragma unroll
@@ -255,7 +324,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, fl
     };
 
     // Scores, online-softmax update and P.V for chunk k.
-    auto process = [&](int k, const u32x4 (*kr)[PC], const u32x4 (*vr)[PC]) {
+    auto process = [&](int k, const u32x4 (*kr)[PC], const u32x4 (*vr)[PC], const float* ks, const float* vs) {
       const int bi = k / CPB;
       const int sub = k - bi * CPB;
       const int t0 = (blk0 + bi) * B + sub * CHUNK;
@@ -266,9 +335,16 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, fl
 #pragma unroll
         for (int h = 0; h < G; ++h) {
           float x = 0.f;
+          if constexpr (QU) {
 #pragma unroll
-          for (int pc = 0; pc < PC; ++pc) x = dot_chunk<T>(qv[h][pc], kr[j][pc], x);
-          sc[j][h] = group_sum<LPR>(x) * scale_log2;
+            for (int pc = 0; pc < PC; ++pc) x = dot_codes<T, Q>(qv[h][pc], kr[j][pc], x);
+            if constexpr (BIAS != 0.f) x = __builtin_fmaf(-BIAS, qsum[h], x);
+            sc[j][h] = group_sum<LPR>(x) * (ks[j] * scale_log2);
+          } else {
+#pragma unroll
+            for (int pc = 0; pc < PC; ++pc) x = dot_chunk<T>(qv[h][pc][0], kr[j][pc], x);
+            sc[j][h] = group_sum<LPR>(x) * scale_log2;
+          }
         }
       }
       if (!full) {
@@ -291,6 +367,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, fl
         if (__any(mn > m[h])) {
           const float alpha = __builtin_amdgcn_exp2f(m[h] - ms);
           l[h] *= alpha;
+          if constexpr (BIAS != 0.f) lvb[h] *= alpha;
 #pragma unroll
           for (int e = 0; e < PC * E; ++e) o[h][e] *= alpha;
         }
@@ -306,18 +383,47 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, fl
       for (int j = 0; j < CSTEPS; ++j) {
         const int t = t0 + j * RPL + r;
         const bool ok = full || (t >= lo && t < L);
-#pragma unroll
-        for (int pc = 0; pc < PC; ++pc) {
-          float vf[E];
-          chunk_to_f32<T>(vr[j][pc], vf);
-          if (!full) {
-#pragma unroll
-            for (int e = 0; e < E; ++e) vf[e] = ok ? vf[e] : 0.f;
-          }
+        if constexpr (QU) {
+          // Weight of the row times its V scale (0 for a masked row, whose
+          // scale may be unset); codes widened to code + BIAS.
 #pragma unroll
           for (int h = 0; h < G; ++h) {
+            const float pw = sc[j][h] * vs[j];
+            sc[j][h] = full ? pw : (ok ? pw : 0.f);
+            if constexpr (BIAS != 0.f) lvb[h] += sc[j][h];
+          }
 #pragma unroll
-            for (int e = 0; e < E; ++e) o[h][pc * E + e] = __builtin_fmaf(sc[j][h], vf[e], o[h][pc * E + e]);
+          for (int pc = 0; pc < PC; ++pc) {
+            const uint32_t vw[4] = {vr[j][pc].x, vr[j][pc].y, vr[j][pc].z, vr[j][pc].w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              float vf[4];
+              codes4_to_f32<T>(vw[i], vf);
+              if (!full) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) vf[e] = ok ? vf[e] : 0.f;
+              }
+#pragma unroll
+              for (int h = 0; h < G; ++h)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                  o[h][pc * E + 4 * i + e] = __builtin_fmaf(sc[j][h], vf[e], o[h][pc * E + 4 * i + e]);
+            }
+          }
+        } else {
+#pragma unroll
+          for (int pc = 0; pc < PC; ++pc) {
+            float vf[E];
+            chunk_to_f32<T>(vr[j][pc], vf);
+            if (!full) {
+#pragma unroll
+              for (int e = 0; e < E; ++e) vf[e] = ok ? vf[e] : 0.f;
+            }
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+#pragma unroll
+              for (int e = 0; e < E; ++e) o[h][pc * E + e] = __builtin_fmaf(sc[j][h], vf[e], o[h][pc * E + e]);
+            }
           }
         }
       }
@@ -327,12 +433,21 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, fl
     // current chunk is processed.
     const int nchunks = n * CPB;
     u32x4 ka[CSTEPS][PC], va[CSTEPS][PC], kb[CSTEPS][PC], vb[CSTEPS][PC];
-    bool oka = issue(0, ka, va);
+    float ksa[CSTEPS], vsa[CSTEPS], ksb[CSTEPS], vsb[CSTEPS];  // row scales (8-bit pools)
+    bool oka = issue(0, ka, va, ksa, vsa);
     for (int k = 0; k < nchunks; k += 2) {
-      const bool okb = k + 1 < nchunks && issue(k + 1, kb, vb);
-      if (oka) process(k, ka, va);
-      oka = k + 2 < nchunks && issue(k + 2, ka, va);
-      if (okb) process(k + 1, kb, vb);
+      const bool okb = k + 1 < nchunks && issue(k + 1, kb, vb, ksb, vsb);
+      if (oka) process(k, ka, va, ksa, vsa);
+      oka = k + 2 < nchunks && issue(k + 2, ka, va, ksa, vsa);
+      if (okb) process(k + 1, kb, vb, ksb, vsb);
+    }
+    // INT8: the widened codes were code + BIAS; take BIAS times the weights
+    // off once.
+    if constexpr (BIAS != 0.f) {
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < PC * E; ++e) o[h][e] = __builtin_fmaf(-BIAS, lvb[h], o[h][e]);
     }
 
     // Merge the row groups' states (lanes r*LPR + c, same c) with shuffles.
@@ -429,7 +544,7 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(DecodeArgs a) {
   if (a.lse && d == 0) a.lse[row] = sl > 0.f ? (M + __log2f(sl)) * kLn2 : -INFINITY;
 }
 
-template <class T, int D, int B, int G>
+template <class T, class Q, int D, int B, int G>
 struct DecodeKernels {
   static hipError_t launch(const DecodeArgs& a, hipStream_t st) {
     hipError_t e;
@@ -439,7 +554,8 @@ struct DecodeKernels {
       if (e != hipSuccess) return e;
     }
     const int grid = (a.n_workers + kWaves - 1) / kWaves;
-    hipLaunchKernelGGL((decode_split_kernel<T, D, B, G>), dim3(grid), dim3(kThreads), 0, st, a, a.scale * kLog2e);
+    hipLaunchKernelGGL((decode_split_kernel<T, Q, D, B, G>), dim3(grid), dim3(kThreads), 0, st, a,
+                       a.scale * kLog2e);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((decode_merge_kernel<D, G>), dim3(a.H, a.S), dim3(D), 0, st, a);
@@ -450,7 +566,7 @@ struct DecodeKernels {
     static int cached = 0;
     if (!cached) {
       int n = 0;
-      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_split_kernel<T, D, B, G>, kThreads, 0) !=
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_split_kernel<T, Q, D, B, G>, kThreads, 0) !=
               hipSuccess ||
           n <= 0) {
         (void)hipGetLastError();
@@ -462,42 +578,61 @@ struct DecodeKernels {
   }
 };
 
-template <class T, int D, int B, int G>
+template <class T, class Q, int D, int B, int G>
 struct LaunchOp {
-  static hipError_t run(const DecodeArgs& a, hipStream_t st) { return DecodeKernels<T, D, B, G>::launch(a, st); }
+  static hipError_t run(const DecodeArgs& a, hipStream_t st) { return DecodeKernels<T, Q, D, B, G>::launch(a, st); }
 };
-template <class T, int D, int B, int G>
+template <class T, class Q, int D, int B, int G>
 struct OccupancyOp {
-  static int run() { return DecodeKernels<T, D, B, G>::blocks_per_cu(); }
+  static int run() { return DecodeKernels<T, Q, D, B, G>::blocks_per_cu(); }
 };
 
-// Runtime (dtype, head dim, block size, group size) -> template instance.
-template <template <class, int, int, int> class Op, class R, class... Args>
-static R dispatch(int dtype, int D, int B, int G, R bad, const Args&... args) {
-#define PKV_G(T_, D_, B_)                               \
-  switch (G) {                                          \
-    case 1: return Op<T_, D_, B_, 1>::run(args...);     \
-    case 2: return Op<T_, D_, B_, 2>::run(args...);     \
-    case 4: return Op<T_, D_, B_, 4>::run(args...);     \
-    case 8: return Op<T_, D_, B_, 8>::run(args...);     \
-  }                                                     \
+// Kernel instance of a (pool dtype, q dtype) pair: 16-bit and fp32 pools take
+// q of their own type; 8-bit pools (3 INT8, 4 FP8) take fp16 or bf16 q.
+constexpr int kInstF32 = 0, kInstF16 = 1, kInstBF16 = 2, kInstI8F16 = 3, kInstI8BF16 = 4, kInstFP8F16 = 5,
+              kInstFP8BF16 = 6;
+static int instance_of(int dtype, int q_dtype) {
+  if (dtype <= 2) return dtype;
+  if (q_dtype != 1 && q_dtype != 2) return -1;
+  if (dtype == 3) return q_dtype == 1 ? kInstI8F16 : kInstI8BF16;
+  if (dtype == 4) return q_dtype == 1 ? kInstFP8F16 : kInstFP8BF16;
+  return -1;
+}
+
+// Runtime (instance, head dim, block size, group size) -> template instance.
+// 8-bit pools are built for groups of up to 4 query heads.
+template <template <class, class, int, int, int> class Op, class R, class... Args>
+static R dispatch(int inst, int D, int B, int G, R bad, const Args&... args) {
+#define PKV_G(T_, Q_, D_, B_)                               \
+  switch (G) {                                              \
+    case 1: return Op<T_, Q_, D_, B_, 1>::run(args...);     \
+    case 2: return Op<T_, Q_, D_, B_, 2>::run(args...);     \
+    case 4: return Op<T_, Q_, D_, B_, 4>::run(args...);     \
+    case 8:                                                 \
+      if constexpr (!T_::QUANT) return Op<T_, Q_, D_, B_, 8>::run(args...); \
+      return bad;                                           \
+  }                                                         \
   return bad;
-#define PKV_B(T_, D_)            \
-  switch (B) {                   \
-    case 16: { PKV_G(T_, D_, 16) } \
-    case 32: { PKV_G(T_, D_, 32) } \
-  }                              \
+#define PKV_B(T_, Q_, D_)                \
+  switch (B) {                           \
+    case 16: { PKV_G(T_, Q_, D_, 16) }   \
+    case 32: { PKV_G(T_, Q_, D_, 32) }   \
+  }                                      \
   return bad;
-#define PKV_D(T_)                \
-  switch (D) {                   \
-    case 64: { PKV_B(T_, 64) }   \
-    case 128: { PKV_B(T_, 128) } \
-  }                              \
+#define PKV_D(T_, Q_)                    \
+  switch (D) {                           \
+    case 64: { PKV_B(T_, Q_, 64) }       \
+    case 128: { PKV_B(T_, Q_, 128) }     \
+  }                                      \
   return bad;
-  switch (dtype) {
-    case 0: { PKV_D(F32T) }
-    case 1: { PKV_D(F16T) }
-    case 2: { PKV_D(BF16T) }
+  switch (inst) {
+    case kInstF32: { PKV_D(F32T, F32T) }
+    case kInstF16: { PKV_D(F16T, F16T) }
+    case kInstBF16: { PKV_D(BF16T, BF16T) }
+    case kInstI8F16: { PKV_D(I8T, F16T) }
+    case kInstI8BF16: { PKV_D(I8T, BF16T) }
+    case kInstFP8F16: { PKV_D(FP8T, F16T) }
+    case kInstFP8BF16: { PKV_D(FP8T, BF16T) }
   }
   return bad;
 #undef PKV_D
@@ -505,30 +640,33 @@ static R dispatch(int dtype, int D, int B, int G, R bad, const Args&... args) {
 #undef PKV_G
 }
 
-bool decode_supported(int dtype, int D, int B, int G) {
-  return (dtype == 0 || dtype == 1 || dtype == 2) && (D == 64 || D == 128) && (B == 16 || B == 32) &&
-         (G == 1 || G == 2 || G == 4 || G == 8);
+bool decode_supported(int dtype, int q_dtype, int D, int B, int G) {
+  const int inst = instance_of(dtype, q_dtype);
+  if (inst < 0 || (D != 64 && D != 128) || (B != 16 && B != 32)) return false;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return false;
+  return dtype <= 2 || G <= 4;
 }
 
 // Automatic worker count: whole workgroups per compute unit (an uneven
 // spread leaves some units with more work); two per unit keep 128 KB of
 // loads in flight per unit (16 KB per wavefront), which covers HBM latency,
 // within what the unit holds at once.
-int decode_auto_workers(int dtype, int D, int B, int G) {
+int decode_auto_workers(int dtype, int q_dtype, int D, int B, int G) {
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) {
     (void)hipGetLastError();
     cus = 256;
   }
-  const int resident = dispatch<OccupancyOp, int>(dtype, D, B, G, 2);
+  const int resident = dispatch<OccupancyOp, int>(instance_of(dtype, q_dtype), D, B, G, 2);
   int per_cu = 2;
   if (per_cu > resident) per_cu = resident;
   return cus * per_cu * kWaves;
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
-  return dispatch<LaunchOp, hipError_t>(a.dtype, a.D, a.B, a.H / a.Hkv, hipErrorInvalidValue, a, st);
+  return dispatch<LaunchOp, hipError_t>(instance_of(a.dtype, a.q_dtype), a.D, a.B, a.H / a.Hkv,
+                                        hipErrorInvalidValue, a, st);
 }
 
 }  // namespace pkv

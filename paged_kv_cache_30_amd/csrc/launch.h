@@ -18,6 +18,21 @@ struct WriteArgs {
   int32_t num_tokens, num_seqs, mb, nb, B, Hkv, D, elem_bytes;
 };
 
+// Quantising write: rows of k_new/v_new (in_dtype) become 8-bit codes in the
+// pools and one fp32 scale per row in the [NB, Hkv, B] scale pools.
+struct WriteQuantArgs {
+  void* k_pool;
+  void* v_pool;
+  float* k_scale;
+  float* v_scale;
+  const void* k_new;
+  const void* v_new;
+  const int32_t* seq_idx;
+  const int32_t* pos;
+  const int32_t* tables;
+  int32_t num_tokens, num_seqs, mb, nb, B, Hkv, D, kv_dtype, in_dtype;
+};
+
 struct DecodeArgs {
   float* out;
   float* lse;
@@ -26,6 +41,9 @@ struct DecodeArgs {
   const void* v_pool;
   const int32_t* tables;
   const int32_t* lens;
+  const float* k_scale;  // 8-bit pools only: [NB, Hkv, B] row scales
+  const float* v_scale;
+  int32_t q_dtype;       // 8-bit pools only: type of q (fp16 or bf16)
   int32_t* ws_cum;  // [S + 1] attended blocks before each sequence
   float* ws_ml;     // [slots, G, 2] partial running max (log2 units) and sum
   float* ws_o;      // [slots, G, D] partial unnormalised outputs
@@ -48,12 +66,15 @@ struct PrefillArgs {
 };
 
 hipError_t launch_kv_write(const WriteArgs& a, hipStream_t st);
+bool kv_write_quant_supported(int kv_dtype, int in_dtype, int D);
+hipError_t launch_kv_write_quant(const WriteQuantArgs& a, hipStream_t st);
 
 
 
-bool decode_supported(int dtype, int D, int B, int G);
+// q_dtype is the type of q (equal to dtype for the 16-bit and fp32 pools).
+bool decode_supported(int dtype, int q_dtype, int D, int B, int G);
 // Decode worker (wavefront) count used when the caller passes 0.
-int decode_auto_workers(int dtype, int D, int B, int G);
+int decode_auto_workers(int dtype, int q_dtype, int D, int B, int G);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
 
 bool prefill_supported(int dtype, int D, int B, int G);

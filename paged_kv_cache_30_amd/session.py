@@ -18,6 +18,8 @@ import torch
 from . import _lib
 
 TORCH_DTYPE = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+# 8-bit pool formats: code tensor dtype.
+QUANT_DTYPE = {"i8": torch.int8, "fp8": torch.float8_e4m3fn}
 
 
 def to_device(a: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
@@ -43,15 +45,32 @@ def int_tensor(a, device="cuda") -> torch.Tensor:
 
 
 class DeviceWorkload:
+    """``kv_format``: "native" (pools in the workload's dtype) or "i8" / "fp8"
+    (8-bit pools with row scales; keys and values are encoded on write from
+    the workload's 16-bit or fp32 rows; decode only)."""
+
     def __init__(self, w, device: str = "cuda", poison: bool = True, num_workers: int = 0,
-                 with_lse: bool = True, write_history: bool = True):
+                 with_lse: bool = True, write_history: bool = True, kv_format: str = "native"):
         self.w = w
         self.device = device
-        dt = TORCH_DTYPE[w.dtype]
+        self.kv_format = kv_format
         shape = (w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim)
         fill = math.nan if poison else 0.0
-        self.k_pool = torch.full(shape, fill, dtype=dt, device=device)
-        self.v_pool = torch.full(shape, fill, dtype=dt, device=device)
+        self.k_scale = self.v_scale = None
+        if kv_format == "native":
+            dt = TORCH_DTYPE[w.dtype]
+            self.k_pool = torch.full(shape, fill, dtype=dt, device=device)
+            self.v_pool = torch.full(shape, fill, dtype=dt, device=device)
+        else:
+            if w.kind != "decode":
+                raise ValueError("8-bit pools are decode only")
+            # unwritten rows: code 0xFF (NaN for FP8) and scale NaN (or zeros)
+            code = 0xFF if poison else 0
+            self.k_pool = torch.full(shape, code, dtype=torch.uint8, device=device).view(QUANT_DTYPE[kv_format])
+            self.v_pool = torch.full(shape, code, dtype=torch.uint8, device=device).view(QUANT_DTYPE[kv_format])
+            sshape = (w.num_blocks, w.num_kv_heads, w.block_size)
+            self.k_scale = torch.full(sshape, fill, dtype=torch.float32, device=device)
+            self.v_scale = torch.full(sshape, fill, dtype=torch.float32, device=device)
         self.tables = int_tensor(w.block_tables, device)
         self.lens = int_tensor(w.context_lens, device)
         self.q = to_device(w.q, w.dtype, device)
@@ -78,26 +97,34 @@ class DeviceWorkload:
             self.workspace = _lib.decode_workspace(self.k_pool, w.num_heads, w.num_seqs, w.max_context_len,
                                                    w.window, num_workers)
 
+    def _write(self, k, v, seq, pos):
+        if self.kv_format == "native":
+            return _lib.bind_kv_write(self.k_pool, self.v_pool, k, v, seq, pos, self.tables)
+        return _lib.bind_kv_write_quant(self.k_pool, self.v_pool, self.k_scale, self.v_scale, k, v, seq, pos,
+                                        self.tables)
+
     def write_history(self) -> None:
         w = self.w
         for s, p0, k, v in w.history_tokens():
             n = k.shape[0]
-            _lib.paged_kv_write(self.k_pool, self.v_pool, to_device(k, w.dtype, self.device),
-                                to_device(v, w.dtype, self.device),
-                                torch.full((n,), s, dtype=torch.int32, device=self.device),
-                                torch.arange(p0, p0 + n, dtype=torch.int32, device=self.device),
-                                self.tables)
+            self._write(to_device(k, w.dtype, self.device), to_device(v, w.dtype, self.device),
+                        torch.full((n,), s, dtype=torch.int32, device=self.device),
+                        torch.arange(p0, p0 + n, dtype=torch.int32, device=self.device))()
 
     def write_step(self, stream=None) -> None:
         if self._bound_write is None:
-            self._bound_write = _lib.bind_kv_write(self.k_pool, self.v_pool, self.step_k, self.step_v,
-                                                   self.step_seq, self.step_pos, self.tables)
+            self._bound_write = self._write(self.step_k, self.step_v, self.step_seq, self.step_pos)
         self._bound_write(stream)
 
     def attend(self, stream=None) -> None:
         w = self.w
         if self._bound_attend is None:
-            if w.kind == "decode":
+            if w.kind == "decode" and self.kv_format != "native":
+                self._bound_attend = _lib.bind_decode_quant(
+                    self.out, self.q, self.k_pool, self.v_pool, self.k_scale, self.v_scale, self.tables, self.lens,
+                    w.max_context_len, window=w.window, scale=w.scale, num_workers=self.num_workers,
+                    workspace=self.workspace, lse=self.lse)
+            elif w.kind == "decode":
                 self._bound_attend = _lib.bind_decode(
                     self.out, self.q, self.k_pool, self.v_pool, self.tables, self.lens, w.max_context_len,
                     window=w.window, scale=w.scale, num_workers=self.num_workers, workspace=self.workspace,

@@ -108,3 +108,42 @@ def test_argument_errors_before_any_launch():
                                   None) == pkv.PKV_EINVAL
     assert pkv.LIB.paged_kv_write(ctypes.byref(g), None, P(1), P(1), P(1), P(1), P(1), 3, P(1), 1, 8,
                                   None) == pkv.PKV_EINVAL
+
+
+def test_quant_argument_errors_before_any_launch():
+    """8-bit pools: the plain entry points refuse them, the *_quant ones
+    refuse 16-bit pools, unsupported query types, missing scales and groups
+    of 8 -- all before anything is enqueued."""
+    P = ctypes.c_void_p
+    gi8 = geo(dt=pkv.PKV_I8)
+    gfp8 = geo(dt=pkv.PKV_FP8)
+    g16 = geo(dt=pkv.PKV_BF16)
+    # plain calls on 8-bit pools
+    assert call_decode(gi8) == pkv.PKV_EUNSUPPORTED
+    assert pkv.LIB.paged_kv_write(ctypes.byref(gi8), P(1), P(1), P(1), P(1), P(1), P(1), 3, P(1), 1, 8,
+                                  None) == pkv.PKV_EUNSUPPORTED
+    assert pkv.LIB.paged_attn_prefill(ctypes.byref(gfp8), P(1), None, P(1), P(1), P(1), P(1), P(1), 8, P(1), 1, 4,
+                                      100, 0, 0.1, None) == pkv.PKV_EUNSUPPORTED
+
+    def dq(g, q_dtype=pkv.PKV_BF16, ks=P(1), H=None, ws=P(4096), wsb=1 << 30):
+        if H is not None:
+            g = geo(H=H, Hkv=g.num_kv_heads, dt=g.kv_dtype)
+        return pkv.LIB.paged_attn_decode_quant(ctypes.byref(g), P(1), None, P(1), q_dtype, P(1), P(1), ks, P(1),
+                                               P(1), 8, P(1), 2, 100, 0, 0.1, 0, ws, wsb, None)
+    assert dq(g16) == pkv.PKV_EINVAL                               # not an 8-bit pool
+    assert dq(gi8, q_dtype=pkv.PKV_F32) == pkv.PKV_EUNSUPPORTED    # query type
+    assert dq(gi8, ks=None) == pkv.PKV_EINVAL                      # missing scales
+    assert dq(gi8, H=64) == pkv.PKV_EUNSUPPORTED                   # 8 query heads per kv head
+    assert dq(gfp8, ws=None) == pkv.PKV_EWORKSPACE
+
+    def wq(g, new_dtype=pkv.PKV_BF16, n=3, ks=P(1)):
+        return pkv.LIB.paged_kv_write_quant(ctypes.byref(g), P(1), P(1), ks, P(1), P(1), P(1), new_dtype, P(1),
+                                            P(1), n, P(1), 1, 8, None)
+    assert wq(g16) == pkv.PKV_EINVAL
+    assert wq(gi8, new_dtype=pkv.PKV_I8) == pkv.PKV_EUNSUPPORTED
+    assert wq(gi8, ks=None) == pkv.PKV_EINVAL
+    assert wq(gfp8, n=0) == pkv.PKV_OK
+    assert wq(gfp8, n=-1) == pkv.PKV_EINVAL
+    # the workspace size of an 8-bit pool is that of any pool
+    assert (pkv.LIB.paged_attn_decode_workspace_bytes(ctypes.byref(gi8), 2, 100, 0, 4) ==
+            pkv.LIB.paged_attn_decode_workspace_bytes(ctypes.byref(g16), 2, 100, 0, 4))
