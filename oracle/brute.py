@@ -56,8 +56,9 @@ def softmax_weighted(q, keys, vals, scale):
     return out, m + math.log(z)
 
 
-def decode(q, k_pool, v_pool, tables, lens, B, Hkv, window, scale, dtype):
-    """Nested lists out[s][h][d], lse[s][h]."""
+def decode(q, k_pool, v_pool, tables, lens, B, Hkv, window, scale, dtype, sinks=0):
+    """Nested lists out[s][h][d], lse[s][h].  With a window, positions below
+    ``sinks`` are attended as well."""
     S, H, D = len(q), len(q[0]), len(q[0][0])
     out, lse = [], []
     for s in range(S):
@@ -69,7 +70,9 @@ def decode(q, k_pool, v_pool, tables, lens, B, Hkv, window, scale, dtype):
         for h in range(H):
             g = head_group(h, H, Hkv)
             keys, vals = [], []
-            for t in range(lo, L):
+            for t in range(0, L):
+                if t < lo and not (window > 0 and t < sinks):
+                    continue
                 pb, off = slot(tables[s], t, B)
                 keys.append([value(k_pool[pb][off][g][d], dtype) for d in range(D)])
                 vals.append([value(v_pool[pb][off][g][d], dtype) for d in range(D)])
@@ -82,7 +85,7 @@ def decode(q, k_pool, v_pool, tables, lens, B, Hkv, window, scale, dtype):
     return out, lse
 
 
-def prefill(q, q_start, k_pool, v_pool, tables, lens, B, Hkv, window, scale, dtype):
+def prefill(q, q_start, k_pool, v_pool, tables, lens, B, Hkv, window, scale, dtype, sinks=0):
     """Nested lists out[row][h][d] for every query row of every chunk."""
     H, D = len(q[0]), len(q[0][0])
     out = [None] * len(q)
@@ -97,7 +100,7 @@ def prefill(q, q_start, k_pool, v_pool, tables, lens, B, Hkv, window, scale, dty
                 g = head_group(h, H, Hkv)
                 keys, vals = [], []
                 for t in range(0, p + 1):
-                    if window > 0 and not (p - t < window):
+                    if window > 0 and not (p - t < window) and not t < sinks:
                         continue
                     pb, off = slot(tables[s], t, B)
                     keys.append([value(k_pool[pb][off][g][d], dtype) for d in range(D)])

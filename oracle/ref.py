@@ -116,12 +116,29 @@ def attended_range(L: int, window: int):
     return lo, L
 
 
+def attended_positions(L: int, window: int, sinks: int = 0) -> np.ndarray:
+    """Positions a decode query at position L-1 attends, in increasing order:
+    ``attended_range`` and, with a window, also the first ``sinks`` positions.
+
+    "Building a Streaming Sliding-Window Attention Engine in Pure Python",
+    Step 4 (eviction policies that keep the first few tokens, the "attention
+    sinks", when the middle is dropped) and the roadmap's attention-sinks
+    item (keep the first 4 tokens regardless of the window).
+    """
+    lo, hi = attended_range(L, window)
+    pos = np.arange(lo, hi)
+    if window > 0 and sinks > 0:
+        pos = np.union1d(np.arange(min(sinks, L)), pos)
+    return pos
+
+
 def decode(q, k_pool, v_pool, block_tables, context_lens, *, block_size, num_kv_heads,
-           window, scale, dtype, seqs=None, heads=None, kv_dtype=None):
+           window, scale, dtype, seqs=None, heads=None, kv_dtype=None, sinks=0):
     """Single-query decode through the block table, every (seq, head).
 
     q [S, H, D].  Returns (out [S, H, D], lse [S, H]) float64; with ``seqs`` /
-    ``heads`` only those rows are computed (others stay NaN).  ``kv_dtype``
+    ``heads`` only those rows are computed (others stay NaN).  ``sinks``: see
+    ``attended_positions``.  ``kv_dtype``
     (default ``dtype``) is the storage type of the pools when it differs from
     the queries' ("f64": already decoded values).
     """
@@ -134,8 +151,7 @@ def decode(q, k_pool, v_pool, block_tables, context_lens, *, block_size, num_kv_
     heads = range(H) if heads is None else heads
     for s in seqs:
         L = int(context_lens[s])
-        lo, hi = attended_range(L, window)
-        pos = np.arange(lo, hi)
+        pos = attended_positions(L, window, sinks) if sinks else np.arange(*attended_range(L, window))
         by_group = {}
         for h in heads:
             by_group.setdefault(kv_head_of(h, H, num_kv_heads), []).append(h)
@@ -148,7 +164,7 @@ def decode(q, k_pool, v_pool, block_tables, context_lens, *, block_size, num_kv_
     return out, lse
 
 
-def contiguous_decode(q_s, k_log, v_log, first_pos, L, *, num_kv_heads, window, scale, dtype):
+def contiguous_decode(q_s, k_log, v_log, first_pos, L, *, num_kv_heads, window, scale, dtype, sinks=0):
     """The same decode over a contiguous (never paged) cache of one sequence.
 
     "Building a Streaming Sliding-Window Attention Engine in Pure Python",
@@ -157,27 +173,29 @@ def contiguous_decode(q_s, k_log, v_log, first_pos, L, *, num_kv_heads, window, 
     equal for any physical block assignment.
 
     q_s [H, D]; k_log/v_log [L - first_pos, Hkv, D].  Returns (out, lse).
+    With ``sinks`` the first positions are kept as well (``attended_positions``).
     """
     H, D = q_s.shape
-    lo, hi = attended_range(L, window)
-    if lo < first_pos:
-        raise ValueError("window reaches before the first stored position")
+    pos = attended_positions(L, window, sinks)
+    if pos.size and pos[0] < first_pos:
+        raise ValueError("attended positions reach before the first stored position")
     qf = to_f64(q_s, dtype)
     out = np.zeros((H, D))
     lse = np.zeros(H)
     for h in range(H):
         g = kv_head_of(h, H, num_kv_heads)
-        K = to_f64(k_log[lo - first_pos:hi - first_pos, g], dtype)
-        V = to_f64(v_log[lo - first_pos:hi - first_pos, g], dtype)
+        K = to_f64(k_log[pos - first_pos, g], dtype)
+        V = to_f64(v_log[pos - first_pos, g], dtype)
         o, l = attend(qf[h:h + 1], K, V, scale)
         out[h] = o[0]
         lse[h] = l[0]
     return out, lse
 
 
-def prefill_keys(L: int, C: int, window: int):
+def prefill_keys(L: int, C: int, window: int, sinks: int = 0):
     """Query row i of a chunk of C rows that ends at position L-1 sits at
-    position p = L - C + i; it attends t <= p, and t > p - w when w > 0.
+    position p = L - C + i; it attends t <= p, and t > p - w when w > 0
+    (with ``sinks``, also every t < sinks, t <= p: see ``attended_positions``).
 
     "Building a Streaming Sliding-Window Attention Engine in Pure Python",
     Step 3 (``prefill_attention``: causal and sliding-window mask); the chunk
@@ -188,12 +206,15 @@ def prefill_keys(L: int, C: int, window: int):
     t = np.arange(L)[None, :]
     mask = t <= p
     if window > 0:
-        mask &= t > p - window
+        keep = t > p - window
+        if sinks > 0:
+            keep |= t < sinks
+        mask &= keep
     return mask
 
 
 def prefill(q, q_start, k_pool, v_pool, block_tables, context_lens, *, block_size,
-            num_kv_heads, window, scale, dtype, seqs=None, heads=None):
+            num_kv_heads, window, scale, dtype, seqs=None, heads=None, sinks=0):
     """Causal chunked prefill through the block table.
 
     q [sum C, H, D] with sequence s owning rows q_start[s]:q_start[s+1] (its
@@ -213,7 +234,7 @@ def prefill(q, q_start, k_pool, v_pool, block_tables, context_lens, *, block_siz
         L = int(context_lens[s])
         if C == 0:
             continue
-        mask = prefill_keys(L, C, window)
+        mask = prefill_keys(L, C, window, sinks) if sinks else prefill_keys(L, C, window)
         lo = int(np.argmax(mask[0])) if window > 0 else 0
         pos = np.arange(lo, L)
         mask = mask[:, lo:]

@@ -31,14 +31,14 @@ def small_decode(seed, *, S=3, H=4, Hkv=2, D=8, B=4, dtype="f32", window=0, lens
 def ref_decode(w, k_pool, v_pool, tables=None):
     return ref.decode(w.q, k_pool, v_pool, w.block_tables if tables is None else tables,
                       w.context_lens, block_size=w.block_size, num_kv_heads=w.num_kv_heads,
-                      window=w.window, scale=w.scale, dtype=w.dtype)
+                      window=w.window, scale=w.scale, dtype=w.dtype, sinks=w.sinks)
 
 
-def ref_prefill(w, k_pool, v_pool, window=None):
+def ref_prefill(w, k_pool, v_pool, window=None, sinks=0):
     return ref.prefill(w.q, w.q_start, k_pool, v_pool, w.block_tables, w.context_lens,
                        block_size=w.block_size, num_kv_heads=w.num_kv_heads,
                        window=w.window if window is None else window, scale=w.scale,
-                       dtype=w.dtype)
+                       dtype=w.dtype, sinks=sinks)
 
 
 def contiguous(w, s):
@@ -317,9 +317,75 @@ def pin_write_round_trip():
     return bool(ok)
 
 
+def pin_sinks():
+    """Window plus attention sinks: attention over exactly the positions
+    [0, min(s, L-w)) and [L-w, L) (explicit slices of the contiguous keys),
+    the scalar brute force, torch SDPA with the explicit prefill mask, prefill
+    rows equal to decodes, and sinks covering everything before the window
+    give the unwindowed result.  The generator frees the blocks between the
+    sink blocks and the window."""
+    ok = True
+    lens = [9, 30, 4, 50]
+    base = wl.make_decode(lens=lens, num_heads=4, num_kv_heads=2, head_dim=8, block_size=4,
+                          dtype="f32", seed=41, spare_blocks=2)
+    kpb, vpb = ref.build_pools(base)
+    full, _ = ref_decode(base, kpb, vpb)
+    for wsz in (3, 8):
+        for sk in (1, 4, 6, 64):
+            w = wl.make_decode(lens=lens, num_heads=4, num_kv_heads=2, head_dim=8, block_size=4,
+                               dtype="f32", seed=41, window=wsz, sinks=sk, spare_blocks=2)
+            kp, vp = ref.build_pools(w)
+            out, lse = ref_decode(w, kp, vp)
+            bo, bl = brute.decode(w.q, kp, vp, w.block_tables, w.context_lens, 4, 2, wsz, w.scale, "f32",
+                                  sinks=sk)
+            ok &= np.max(np.abs(out - np.array(bo))) <= 1e-12
+            for s in range(len(lens)):
+                L = int(w.context_lens[s])
+                lo = max(0, L - wsz)
+                first, k, v = w.logical_kv(s)
+                pos = np.concatenate([np.arange(min(sk, lo)), np.arange(lo, L)])
+                # freed blocks: nothing between the sink blocks and the window is mapped
+                nsb = -(-min(sk, lo) // 4)
+                ok &= bool(np.all(w.block_tables[s, nsb:lo // 4] == -1))
+                for h in range(4):
+                    g = ref.kv_head_of(h, 4, 2)
+                    o, _ = ref.attend(ref.to_f64(w.q[s, h:h + 1], "f32"), k[pos - first, g].astype(np.float64),
+                                      v[pos - first, g].astype(np.float64), w.scale)
+                    ok &= np.max(np.abs(out[s, h] - o[0])) <= 1e-13
+                    if sk >= lo:
+                        ok &= np.max(np.abs(out[s, h] - full[s, h])) <= 1e-13
+    p = wl.make_prefill(prefix_len=12, chunk_lens=[6, 9, 1], num_heads=4, num_kv_heads=2, head_dim=8,
+                        block_size=4, dtype="f32", seed=42, window=4)
+    kp, vp = ref.build_pools(p)
+    for sk in (2, 5):
+        out, lse = ref_prefill(p, kp, vp, sinks=sk)
+        bo = brute.prefill(p.q, p.q_start, kp, vp, p.block_tables, p.context_lens, 4, 2, 4, p.scale, "f32",
+                           sinks=sk)
+        ok &= np.max(np.abs(out - np.array(bo))) <= 1e-12
+        for s in range(p.num_seqs):
+            r0, r1 = int(p.q_start[s]), int(p.q_start[s + 1])
+            L = int(p.context_lens[s])
+            C = r1 - r0
+            first, k, v = p.logical_kv(s)
+            pp = L - C + np.arange(C)[:, None]
+            t = np.arange(L)[None, :]
+            mask = torch.from_numpy((t <= pp) & ((pp - t < 4) | (t < sk)))
+            q = torch.from_numpy(ref.to_f64(p.q[r0:r1], "f32")).permute(1, 0, 2)[None]
+            K = torch.from_numpy(ref.to_f64(k, "f32")).permute(1, 0, 2)[None]
+            V = torch.from_numpy(ref.to_f64(v, "f32")).permute(1, 0, 2)[None]
+            lib = torch.nn.functional.scaled_dot_product_attention(q, K, V, attn_mask=mask, scale=p.scale,
+                                                                   enable_gqa=True)
+            ok &= np.max(np.abs(out[r0:r1] - lib[0].permute(1, 0, 2).numpy())) <= 1e-12
+            for i in range(C):
+                d, dl = ref.decode(p.q[r0 + i][None], kp, vp, p.block_tables[s:s + 1], np.array([L - C + i + 1]),
+                                   block_size=4, num_kv_heads=2, window=4, scale=p.scale, dtype="f32", sinks=sk)
+                ok &= np.max(np.abs(out[r0 + i] - d[0])) <= 1e-13
+    return bool(ok)
+
+
 PINS = [pin_brute_decode, pin_brute_prefill, pin_library_sdpa, pin_closed_forms,
         pin_permutation_invariance, pin_window, pin_prefill_rows_are_decodes, pin_shared_prefix,
-        pin_gqa_equals_replicated_mha, pin_write_round_trip]
+        pin_gqa_equals_replicated_mha, pin_write_round_trip, pin_sinks]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -413,6 +479,11 @@ def _mutants():
             m &= t >= p - window
         return m
 
+    orig_positions = ref.attended_positions
+
+    def sinks_one_too_many(L, window, sinks=0):
+        return orig_positions(L, window, sinks + 1 if sinks else 0)
+
     def write_off_by_block(k_pool, v_pool, k_new, v_new, seq_idx, pos, tables, B):
         return ref_kv_write(k_pool, v_pool, k_new, v_new, seq_idx, np.asarray(pos) + 1, tables, B)
 
@@ -426,6 +497,7 @@ def _mutants():
         "causal_excludes_self": ("prefill_keys", keys_strict),
         "window_one_too_wide": ("prefill_keys", keys_window_inclusive),
         "write_shifted": ("kv_write", write_off_by_block),
+        "sinks_one_too_many": ("attended_positions", sinks_one_too_many),
     }
 
 

@@ -100,10 +100,13 @@ def draw(rng: np.random.Generator, shape, dtype: str, scale: float = 1.0) -> np.
 
 @dataclasses.dataclass
 class SeqKV:
-    """Keys/values of one sequence for positions [start, start + len(k))."""
+    """Keys/values of one sequence for positions [start, start + len(k)).
+    ``runs``: the position ranges [p0, p1) held in the cache (mapped blocks),
+    when not the whole range (attention sinks plus a window)."""
     start: int
     k: np.ndarray  # (n, Hkv, D) storage dtype
     v: np.ndarray
+    runs: Optional[List[Tuple[int, int]]] = None
 
 
 @dataclasses.dataclass
@@ -129,6 +132,7 @@ class Workload:
     prefix: Optional[SeqKV] = None  # prefill: shared prefix tokens [0, P)
     prefix_len: int = 0
     shared_prefix_blocks: int = 0
+    sinks: int = 0  # with a window: the first `sinks` positions are attended too
 
     @property
     def max_context_len(self) -> int:
@@ -161,9 +165,11 @@ class Workload:
         if self.kind == "decode":
             for s in range(self.num_seqs):
                 e = self.seq_kv[s]
-                n = e.k.shape[0] - 1
-                if n > 0:
-                    yield s, e.start, e.k[:n], e.v[:n]
+                last = e.start + e.k.shape[0] - 1  # the step writes this one
+                for p0, p1 in (e.runs if e.runs is not None else [(e.start, last + 1)]):
+                    p1 = min(p1, last)
+                    if p1 > p0:
+                        yield s, p0, e.k[p0 - e.start:p1 - e.start], e.v[p0 - e.start:p1 - e.start]
         elif self.prefix is not None and self.prefix_len > 0:
             owners = [0] if self.shared_prefix_blocks > 0 else range(self.num_seqs)
             for s in owners:
@@ -203,7 +209,8 @@ class Workload:
         eb = ELEM_BYTES[self.dtype]
         L = self.context_lens.astype(np.int64)
         if self.window > 0:
-            n = np.minimum(L, self.window)
+            lo = np.maximum(0, L - self.window)
+            n = (L - lo) + np.minimum(self.sinks, lo)
         else:
             n = L
         return int(n.sum()) * self.num_kv_heads * self.head_dim * 2 * eb
@@ -222,12 +229,17 @@ def _parallel_map(fn, items):
 
 
 def _deal_tables(rng_perm, blocks_per_seq: List[int], first_block: List[int], mb: int,
-                 num_blocks: int) -> np.ndarray:
-    """Hand out shuffled physical ids in sequence order; -1 elsewhere."""
+                 num_blocks: int, sink_blocks: Optional[List[int]] = None) -> np.ndarray:
+    """Hand out shuffled physical ids in sequence order; -1 elsewhere.  A
+    sequence's logical blocks [0, sink_blocks[s]) come first, then
+    [first_block[s], first_block[s] + blocks_per_seq[s])."""
     perm = rng_perm.permutation(num_blocks).astype(np.int32)
     tables = np.full((len(blocks_per_seq), mb), -1, dtype=np.int32)
     at = 0
     for s, (n, b0) in enumerate(zip(blocks_per_seq, first_block)):
+        sb = sink_blocks[s] if sink_blocks is not None else 0
+        tables[s, 0:sb] = perm[at:at + sb]
+        at += sb
         tables[s, b0:b0 + n] = perm[at:at + n]
         at += n
     return tables
@@ -235,44 +247,51 @@ def _deal_tables(rng_perm, blocks_per_seq: List[int], first_block: List[int], mb
 
 def make_decode(*, lens, num_heads, num_kv_heads, head_dim, block_size, dtype, seed,
                 window=0, scale=None, k_scale=1.0, max_blocks_per_seq=None,
-                spare_blocks=0, name="decode") -> Workload:
+                spare_blocks=0, sinks=0, name="decode") -> Workload:
     """A batched single-query decode workload.
 
     ``lens[s]`` is the context length of sequence s including the query token.
     With ``window > 0`` only blocks that hold a position in ``[L-window, L)``
     are mapped; table entries of blocks that end at or before ``L-window``
-    are -1 (freed).
+    are -1 (freed).  With ``sinks > 0`` as well, the blocks holding the first
+    ``sinks`` positions stay mapped too (attention sinks); the blocks between
+    them and the window are freed.
     """
     lens = np.asarray(lens, dtype=np.int64)
     S = len(lens)
     B = block_size
-    first_block, nblocks, starts = [], [], []
+    first_block, nblocks, starts, sink_blocks, runs = [], [], [], [], []
     for L in lens:
         L = int(L)
         if L == 0:
             first_block.append(0)
             nblocks.append(0)
             starts.append(0)
+            sink_blocks.append(0)
+            runs.append(None)
             continue
         lo = max(0, L - window) if window > 0 else 0
         b0 = lo // B
         b1 = (L + B - 1) // B
+        sb = min((min(sinks, lo) + B - 1) // B, b0) if window > 0 else 0
         first_block.append(b0)
         nblocks.append(b1 - b0)
-        starts.append(b0 * B)
+        sink_blocks.append(sb)
+        starts.append(0 if sb else b0 * B)
+        runs.append([(0, sb * B), (b0 * B, L)] if sb else None)
     need_mb = max([b + n for b, n in zip(first_block, nblocks)] + [1])
     mb = max_blocks_per_seq if max_blocks_per_seq is not None else need_mb
     if mb < need_mb:
         raise ValueError("max_blocks_per_seq too small")
-    nb = int(sum(nblocks)) + int(spare_blocks)
+    nb = int(sum(nblocks)) + int(sum(sink_blocks)) + int(spare_blocks)
     nb = max(nb, 1)
-    tables = _deal_tables(stream(seed, TAG_PERM), nblocks, first_block, mb, nb)
+    tables = _deal_tables(stream(seed, TAG_PERM), nblocks, first_block, mb, nb, sink_blocks)
     def one(s):
         n = int(lens[s]) - starts[s]
         rng = stream(seed, TAG_SEQ_KV, s)
         k = draw(rng, (n, num_kv_heads, head_dim), dtype, k_scale)
         v = draw(rng, (n, num_kv_heads, head_dim), dtype)
-        return SeqKV(starts[s], k, v)
+        return SeqKV(starts[s], k, v, runs[s])
 
     seq_kv = _parallel_map(one, range(S))
     q = draw(stream(seed, TAG_QUERY), (S, num_heads, head_dim), dtype)
@@ -281,12 +300,13 @@ def make_decode(*, lens, num_heads, num_kv_heads, head_dim, block_size, dtype, s
     return Workload(name=name, kind="decode", seed=seed, num_seqs=S, num_heads=num_heads,
                     num_kv_heads=num_kv_heads, head_dim=head_dim, block_size=B, dtype=dtype,
                     num_blocks=nb, max_blocks_per_seq=mb, window=window, scale=float(scale),
-                    context_lens=lens.astype(np.int32), block_tables=tables, q=q, seq_kv=seq_kv)
+                    context_lens=lens.astype(np.int32), block_tables=tables, q=q, seq_kv=seq_kv,
+                    sinks=int(sinks) if window > 0 else 0)
 
 
 def make_prefill(*, prefix_len, chunk_lens, num_heads, num_kv_heads, head_dim, block_size,
                  dtype, seed, window=0, scale=None, share_prefix=True, max_blocks_per_seq=None,
-                 name="prefill") -> Workload:
+                 sinks=0, name="prefill") -> Workload:
     """Chunked prefill: every sequence has a common prefix of ``prefix_len``
     tokens (already cached) followed by its own chunk of ``chunk_lens[s]``
     query tokens.  With ``share_prefix`` the prefix blocks are one set of
@@ -331,7 +351,7 @@ def make_prefill(*, prefix_len, chunk_lens, num_heads, num_kv_heads, head_dim, b
                     num_blocks=nb, max_blocks_per_seq=mb, window=window, scale=float(scale),
                     context_lens=lens.astype(np.int32), block_tables=tables, q=q, seq_kv=seq_kv,
                     q_start=q_start, prefix=prefix, prefix_len=prefix_len,
-                    shared_prefix_blocks=pb)
+                    shared_prefix_blocks=pb, sinks=int(sinks) if window > 0 else 0)
 
 
 def private_prefix_copy(w: Workload, seed_perm: int = 7) -> Workload:
