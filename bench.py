@@ -73,7 +73,7 @@ def prefill_flop(w) -> int:
 def pkv_workers(d) -> int:
     from paged_kv_cache_30_amd import paged_attn_decode_workers
     w = d.w
-    return paged_attn_decode_workers(d.k_pool, w.num_heads, w.num_seqs, w.max_context_len, w.window)
+    return paged_attn_decode_workers(d.k_pool, w.num_heads, w.num_seqs, w.max_context_len, w.window, w.sinks)
 
 
 def source_hash(*names) -> str:

@@ -117,12 +117,12 @@ int paged_kv_write(const pkv_geometry_t* geom, void* k_pool, void* v_pool,
  * Returns 0 for invalid arguments; paged_attn_decode reports those. */
 size_t paged_attn_decode_workspace_bytes(const pkv_geometry_t* geom, int32_t num_seqs,
                                          int32_t max_context_len, int32_t window,
-                                         int32_t num_workers);
+                                         int32_t num_sinks, int32_t num_workers);
 
 /* The worker count paged_attn_decode uses for num_workers == 0 with these
  * sizes on the current device (0 for invalid arguments). */
 int32_t paged_attn_decode_workers(const pkv_geometry_t* geom, int32_t num_seqs,
-                                  int32_t max_context_len, int32_t window);
+                                  int32_t max_context_len, int32_t window, int32_t num_sinks);
 
 /* paged_attn_decode - one query token per sequence attends its cached
  * context through the block table.
@@ -132,10 +132,14 @@ int32_t paged_attn_decode_workers(const pkv_geometry_t* geom, int32_t num_seqs,
  * with context length L = context_lens[s] (which includes the query token,
  * already written: the query sits at position L - 1) and query head h,
  *   lo = window > 0 ? max(0, L - window) : 0
- *   score_t = scale * sum_d q[s,h,d] * K[t, h / G, d]      for t in [lo, L)
+ *   attended t: lo <= t < L, and with a window also t < num_sinks
+ *   score_t = scale * sum_d q[s,h,d] * K[t, h / G, d]      for attended t
  *   out[s,h,:] = sum_t softmax(score)_t * V[t, h / G, :]
  *   lse[s,h]  = log(sum_t exp(score_t))   (natural log)
- * L == 0 gives out = 0 and lse = -inf.
+ * L == 0 gives out = 0 and lse = -inf. The sink positions follow "Building a
+ * Streaming Sliding-Window Attention Engine in Pure Python", Step 4 (keeping
+ * the first tokens when the middle is evicted) and its roadmap's attention
+ * sinks item (the first 4 tokens kept regardless of the window).
  *
  *   out           float32 [num_seqs, H, D]
  *   lse           float32 [num_seqs, H], or NULL
@@ -144,6 +148,9 @@ int32_t paged_attn_decode_workers(const pkv_geometry_t* geom, int32_t num_seqs,
  *   context_lens  int32 [num_seqs], each in [0, max_context_len]
  *   max_context_len  host bound on context_lens (<= max_blocks_per_seq * B)
  *   window        0 = attend everything, else the last `window` positions
+ *   num_sinks     with window > 0: also attend positions [0, num_sinks)
+ *                 (0 = none; ignored without a window); the blocks between
+ *                 the sink blocks and the window may be unmapped (-1)
  *   scale         score scale, typically 1/sqrt(D)
  *   num_workers   wavefronts the attended (sequence, kv head, block) triples
  *                 are divided among, in equal contiguous shares: 0 = an
@@ -158,12 +165,12 @@ int32_t paged_attn_decode_workers(const pkv_geometry_t* geom, int32_t num_seqs,
  *                 calls in flight at once need different workspaces
  * Table entries of attended blocks that are -1 or >= NB are skipped: their
  * positions contribute nothing. The partially covered first block of a
- * window must stay mapped. */
+ * window (and the blocks holding sink positions) must stay mapped. */
 int paged_attn_decode(const pkv_geometry_t* geom, float* out, float* lse, const void* q,
                       const void* k_pool, const void* v_pool,
                       const int32_t* block_tables, int32_t max_blocks_per_seq,
                       const int32_t* context_lens, int32_t num_seqs, int32_t max_context_len,
-                      int32_t window, float scale, int32_t num_workers,
+                      int32_t window, int32_t num_sinks, float scale, int32_t num_workers,
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /* paged_attn_prefill - causal attention of a chunk of query tokens per
@@ -177,7 +184,8 @@ int paged_attn_decode(const pkv_geometry_t* geom, float* out, float* lse, const 
  * rows are its last C positions, so row i sits at p = L - C + i with
  * L = context_lens[s] (the chunk's keys/values are already written). Row i
  * of head h attends positions t with t <= p and, when window > 0,
- * t > p - window; the result is the same softmax-weighted sum as decode.
+ * t > p - window or t < num_sinks; the result is the same softmax-weighted
+ * sum as decode.
  *
  *   out     float32 [q_start[num_seqs], H, D]
  *   lse     float32 [q_start[num_seqs], H], or NULL
@@ -194,7 +202,8 @@ int paged_attn_prefill(const pkv_geometry_t* geom, float* out, float* lse, const
                        const int32_t* q_start, const void* k_pool, const void* v_pool,
                        const int32_t* block_tables, int32_t max_blocks_per_seq,
                        const int32_t* context_lens, int32_t num_seqs, int32_t max_q_len,
-                       int32_t max_context_len, int32_t window, float scale, void* stream);
+                       int32_t max_context_len, int32_t window, int32_t num_sinks, float scale,
+                       void* stream);
 
 /* 8-bit key/value pages.
  *
@@ -247,8 +256,8 @@ int paged_attn_decode_quant(const pkv_geometry_t* geom, float* out, float* lse, 
                             int32_t q_dtype, const void* k_pool, const void* v_pool,
                             const float* k_scale, const float* v_scale, const int32_t* block_tables,
                             int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
-                            int32_t max_context_len, int32_t window, float scale, int32_t num_workers,
-                            void* workspace, size_t workspace_bytes, void* stream);
+                            int32_t max_context_len, int32_t window, int32_t num_sinks, float scale,
+                            int32_t num_workers, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Name of a status code (static string). */
 const char* pkv_status_string(int status);

@@ -56,18 +56,18 @@ def _load() -> ctypes.CDLL:
     G = ctypes.POINTER(Geometry)
     lib.paged_kv_write.argtypes = [G, P, P, P, P, P, P, I32, P, I32, I32, P]
     lib.paged_kv_write.restype = ctypes.c_int
-    lib.paged_attn_decode_workspace_bytes.argtypes = [G, I32, I32, I32, I32]
+    lib.paged_attn_decode_workspace_bytes.argtypes = [G, I32, I32, I32, I32, I32]
     lib.paged_attn_decode_workspace_bytes.restype = SZ
-    lib.paged_attn_decode_workers.argtypes = [G, I32, I32, I32]
+    lib.paged_attn_decode_workers.argtypes = [G, I32, I32, I32, I32]
     lib.paged_attn_decode_workers.restype = I32
-    lib.paged_attn_decode.argtypes = [G, P, P, P, P, P, P, I32, P, I32, I32, I32, F, I32, P, SZ, P]
+    lib.paged_attn_decode.argtypes = [G, P, P, P, P, P, P, I32, P, I32, I32, I32, I32, F, I32, P, SZ, P]
     lib.paged_attn_decode.restype = ctypes.c_int
-    lib.paged_attn_prefill.argtypes = [G, P, P, P, P, P, P, P, I32, P, I32, I32, I32, I32, F, P]
+    lib.paged_attn_prefill.argtypes = [G, P, P, P, P, P, P, P, I32, P, I32, I32, I32, I32, I32, F, P]
     lib.paged_attn_prefill.restype = ctypes.c_int
     lib.paged_kv_write_quant.argtypes = [G, P, P, P, P, P, P, I32, P, P, I32, P, I32, I32, P]
     lib.paged_kv_write_quant.restype = ctypes.c_int
-    lib.paged_attn_decode_quant.argtypes = [G, P, P, P, I32, P, P, P, P, P, I32, P, I32, I32, I32, F, I32, P, SZ,
-                                            P]
+    lib.paged_attn_decode_quant.argtypes = [G, P, P, P, I32, P, P, P, P, P, I32, P, I32, I32, I32, I32, F, I32, P,
+                                            SZ, P]
     lib.paged_attn_decode_quant.restype = ctypes.c_int
     lib.pkv_status_string.argtypes = [ctypes.c_int]
     lib.pkv_status_string.restype = ctypes.c_char_p
@@ -155,25 +155,26 @@ def paged_kv_write(k_pool, v_pool, k_new, v_new, seq_idx, pos, block_tables, str
 
 
 def paged_attn_decode_workspace_bytes(k_pool, num_heads, num_seqs, max_context_len, window=0,
-                                      num_workers=0) -> int:
+                                      num_workers=0, sinks=0) -> int:
     g = geometry(k_pool, num_heads)
-    return int(LIB.paged_attn_decode_workspace_bytes(ctypes.byref(g), num_seqs, max_context_len, window,
+    return int(LIB.paged_attn_decode_workspace_bytes(ctypes.byref(g), num_seqs, max_context_len, window, sinks,
                                                      num_workers))
 
 
-def paged_attn_decode_workers(k_pool, num_heads, num_seqs, max_context_len, window=0) -> int:
+def paged_attn_decode_workers(k_pool, num_heads, num_seqs, max_context_len, window=0, sinks=0) -> int:
     g = geometry(k_pool, num_heads)
-    return int(LIB.paged_attn_decode_workers(ctypes.byref(g), num_seqs, max_context_len, window))
+    return int(LIB.paged_attn_decode_workers(ctypes.byref(g), num_seqs, max_context_len, window, sinks))
 
 
-def decode_workspace(k_pool, num_heads, num_seqs, max_context_len, window=0, num_workers=0):
+def decode_workspace(k_pool, num_heads, num_seqs, max_context_len, window=0, num_workers=0, sinks=0):
     """A device workspace tensor of the size paged_attn_decode needs."""
-    n = paged_attn_decode_workspace_bytes(k_pool, num_heads, num_seqs, max_context_len, window, num_workers)
+    n = paged_attn_decode_workspace_bytes(k_pool, num_heads, num_seqs, max_context_len, window, num_workers,
+                                          sinks)
     return torch.empty(max(n, 16), dtype=torch.uint8, device=k_pool.device)
 
 
 def bind_decode(out, q, k_pool, v_pool, block_tables, context_lens, max_context_len, *,
-                window=0, scale, num_workers=0, workspace=None, lse=None):
+                window=0, scale, num_workers=0, workspace=None, lse=None, sinks=0):
     """Check and marshal the arguments of ``paged_attn_decode`` once; returns
     a callable ``f(stream=None)`` that makes the C call with them."""
     _dev(q, "q", dtype=k_pool.dtype, ndim=3)
@@ -195,8 +196,8 @@ def bind_decode(out, q, k_pool, v_pool, block_tables, context_lens, max_context_
         ws_bytes = workspace.numel() * workspace.element_size()
     g = geometry(k_pool, H)
     args = (ctypes.byref(g), _ptr(out), _ptr(lse), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables),
-            block_tables.shape[1], _ptr(context_lens), S, int(max_context_len), int(window), float(scale),
-            int(num_workers), _ptr(workspace), ws_bytes)
+            block_tables.shape[1], _ptr(context_lens), S, int(max_context_len), int(window), int(sinks),
+            float(scale), int(num_workers), _ptr(workspace), ws_bytes)
     keep = (g, out, q, k_pool, v_pool, block_tables, context_lens, workspace, lse)
 
     def call(stream=None):
@@ -206,14 +207,14 @@ def bind_decode(out, q, k_pool, v_pool, block_tables, context_lens, max_context_
 
 
 def paged_attn_decode(out, q, k_pool, v_pool, block_tables, context_lens, max_context_len, *,
-                      window=0, scale, num_workers=0, workspace=None, lse=None, stream=None) -> None:
+                      window=0, scale, num_workers=0, workspace=None, lse=None, stream=None, sinks=0) -> None:
     """C ``paged_attn_decode``: out[S, H, D] (fp32) for q[S, H, D]."""
     bind_decode(out, q, k_pool, v_pool, block_tables, context_lens, max_context_len, window=window,
-                scale=scale, num_workers=num_workers, workspace=workspace, lse=lse)(stream)
+                scale=scale, num_workers=num_workers, workspace=workspace, lse=lse, sinks=sinks)(stream)
 
 
 def bind_prefill(out, q, q_start, k_pool, v_pool, block_tables, context_lens, max_q_len, max_context_len, *,
-                 window=0, scale, lse=None):
+                 window=0, scale, lse=None, sinks=0):
     """Check and marshal the arguments of ``paged_attn_prefill`` once; returns
     a callable ``f(stream=None)`` that makes the C call with them."""
     _dev(q, "q", dtype=k_pool.dtype, ndim=3)
@@ -234,7 +235,7 @@ def bind_prefill(out, q, q_start, k_pool, v_pool, block_tables, context_lens, ma
     g = geometry(k_pool, H)
     args = (ctypes.byref(g), _ptr(out), _ptr(lse), _ptr(q), _ptr(q_start), _ptr(k_pool), _ptr(v_pool),
             _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), S, int(max_q_len), int(max_context_len),
-            int(window), float(scale))
+            int(window), int(sinks), float(scale))
     keep = (g, out, q, q_start, k_pool, v_pool, block_tables, context_lens, lse)
 
     def call(stream=None):
@@ -244,10 +245,10 @@ def bind_prefill(out, q, q_start, k_pool, v_pool, block_tables, context_lens, ma
 
 
 def paged_attn_prefill(out, q, q_start, k_pool, v_pool, block_tables, context_lens, max_q_len,
-                       max_context_len, *, window=0, scale, lse=None, stream=None) -> None:
+                       max_context_len, *, window=0, scale, lse=None, stream=None, sinks=0) -> None:
     """C ``paged_attn_prefill``: out[T, H, D] (fp32) for chunk queries q[T, H, D]."""
     bind_prefill(out, q, q_start, k_pool, v_pool, block_tables, context_lens, max_q_len, max_context_len,
-                 window=window, scale=scale, lse=lse)(stream)
+                 window=window, scale=scale, lse=lse, sinks=sinks)(stream)
 
 
 # ------------------------------------------------------------- 8-bit pools
@@ -301,7 +302,7 @@ def paged_kv_write_quant(k_pool, v_pool, k_scale, v_scale, k_new, v_new, seq_idx
 
 
 def bind_decode_quant(out, q, k_pool, v_pool, k_scale, v_scale, block_tables, context_lens, max_context_len, *,
-                      window=0, scale, num_workers=0, workspace=None, lse=None):
+                      window=0, scale, num_workers=0, workspace=None, lse=None, sinks=0):
     """Check and marshal the arguments of ``paged_attn_decode_quant`` once;
     returns a callable ``f(stream=None)``."""
     _check_quant_pools(k_pool, v_pool, k_scale, v_scale)
@@ -325,7 +326,8 @@ def bind_decode_quant(out, q, k_pool, v_pool, k_scale, v_scale, block_tables, co
     g = geometry(k_pool, H)
     args = (ctypes.byref(g), _ptr(out), _ptr(lse), _ptr(q), _DTYPES[q.dtype], _ptr(k_pool), _ptr(v_pool),
             _ptr(k_scale), _ptr(v_scale), _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), S,
-            int(max_context_len), int(window), float(scale), int(num_workers), _ptr(workspace), ws_bytes)
+            int(max_context_len), int(window), int(sinks), float(scale), int(num_workers), _ptr(workspace),
+            ws_bytes)
     keep = (g, out, q, k_pool, v_pool, k_scale, v_scale, block_tables, context_lens, workspace, lse)
 
     def call(stream=None):
@@ -336,7 +338,8 @@ def bind_decode_quant(out, q, k_pool, v_pool, k_scale, v_scale, block_tables, co
 
 def paged_attn_decode_quant(out, q, k_pool, v_pool, k_scale, v_scale, block_tables, context_lens,
                             max_context_len, *, window=0, scale, num_workers=0, workspace=None, lse=None,
-                            stream=None) -> None:
+                            stream=None, sinks=0) -> None:
     """C ``paged_attn_decode_quant``: decode over 8-bit pools with row scales."""
     bind_decode_quant(out, q, k_pool, v_pool, k_scale, v_scale, block_tables, context_lens, max_context_len,
-                      window=window, scale=scale, num_workers=num_workers, workspace=workspace, lse=lse)(stream)
+                      window=window, scale=scale, num_workers=num_workers, workspace=workspace, lse=lse,
+                      sinks=sinks)(stream)

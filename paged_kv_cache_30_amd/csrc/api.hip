@@ -46,13 +46,13 @@ int check_geometry(const pkv_geometry_t* g) {
 
 int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
 
-// Blocks one sequence's attended range can span.
-int span_blocks(const pkv_geometry_t* g, int max_context_len, int window) {
+// Blocks one sequence's attended positions can span.
+int span_blocks(const pkv_geometry_t* g, int max_context_len, int window, int sinks) {
   const int B = g->block_size;
   int n = ceil_div(max_context_len, B);
   if (window > 0) {
-    const int w = ceil_div(window, B) + 1;
-    if (w < n) n = w;
+    const long long w = (long long)ceil_div(window, B) + 1 + ceil_div(sinks, B);
+    if (w < n) n = (int)w;
   }
   return n;
 }
@@ -65,13 +65,14 @@ struct DecodeSplit {
   size_t total() const { return cum_bytes + ml_bytes + o_bytes; }
 };
 
-int decode_split(const pkv_geometry_t* g, int num_seqs, int max_context_len, int window, int num_workers,
-                 DecodeSplit* out) {
+int decode_split(const pkv_geometry_t* g, int num_seqs, int max_context_len, int window, int sinks,
+                 int num_workers, DecodeSplit* out) {
   if (num_workers < 0) return PKV_EINVAL;
   const int G = g->num_heads / g->num_kv_heads;
   int nw = num_workers;
   if (nw == 0) {
-    const long long bound = (long long)num_seqs * g->num_kv_heads * span_blocks(g, max_context_len, window);
+    const long long bound =
+        (long long)num_seqs * g->num_kv_heads * span_blocks(g, max_context_len, window, sinks);
     nw = pkv::decode_auto_workers(g->kv_dtype, split_q_dtype(g->kv_dtype), g->head_dim, g->block_size, G);
     if (bound < nw) nw = bound > 0 ? (int)bound : 1;
   }
@@ -105,18 +106,20 @@ int paged_kv_write(const pkv_geometry_t* geom, void* k_pool, void* v_pool, const
 }
 
 int32_t paged_attn_decode_workers(const pkv_geometry_t* geom, int32_t num_seqs, int32_t max_context_len,
-                                  int32_t window) {
-  if (check_geometry(geom) || num_seqs < 0 || max_context_len < 0 || window < 0) return 0;
+                                  int32_t window, int32_t num_sinks) {
+  if (check_geometry(geom) || num_seqs < 0 || max_context_len < 0 || window < 0 || num_sinks < 0) return 0;
   DecodeSplit sp;
-  if (decode_split(geom, num_seqs, max_context_len, window, 0, &sp)) return 0;
+  if (decode_split(geom, num_seqs, max_context_len, window, window > 0 ? num_sinks : 0, 0, &sp)) return 0;
   return sp.workers;
 }
 
 size_t paged_attn_decode_workspace_bytes(const pkv_geometry_t* geom, int32_t num_seqs,
-                                         int32_t max_context_len, int32_t window, int32_t num_workers) {
-  if (check_geometry(geom) || num_seqs <= 0 || max_context_len < 0 || window < 0) return 0;
+                                         int32_t max_context_len, int32_t window, int32_t num_sinks,
+                                         int32_t num_workers) {
+  if (check_geometry(geom) || num_seqs <= 0 || max_context_len < 0 || window < 0 || num_sinks < 0) return 0;
   DecodeSplit sp;
-  if (decode_split(geom, num_seqs, max_context_len, window, num_workers, &sp)) return 0;
+  if (decode_split(geom, num_seqs, max_context_len, window, window > 0 ? num_sinks : 0, num_workers, &sp))
+    return 0;
   return sp.total();
 }
 
@@ -127,11 +130,12 @@ namespace {
 int decode_common(const pkv_geometry_t* geom, float* out, float* lse, const void* q, int q_dtype,
                   const void* k_pool, const void* v_pool, const float* k_scale, const float* v_scale,
                   const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
-                  int32_t num_seqs, int32_t max_context_len, int32_t window, float scale, int32_t num_workers,
-                  void* workspace, size_t workspace_bytes, void* stream) {
-  if (num_seqs < 0 || max_blocks_per_seq <= 0 || max_context_len < 0 || window < 0 || num_workers < 0 ||
-      !isfinite(scale))
+                  int32_t num_seqs, int32_t max_context_len, int32_t window, int32_t num_sinks, float scale,
+                  int32_t num_workers, void* workspace, size_t workspace_bytes, void* stream) {
+  if (num_seqs < 0 || max_blocks_per_seq <= 0 || max_context_len < 0 || window < 0 || num_sinks < 0 ||
+      num_workers < 0 || !isfinite(scale))
     return PKV_EINVAL;
+  if (window == 0) num_sinks = 0;  // without a window every position is attended
   if ((long long)max_context_len > (long long)max_blocks_per_seq * geom->block_size) return PKV_EINVAL;
   if (num_seqs == 0) return PKV_OK;
   if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens) return PKV_EINVAL;
@@ -140,7 +144,7 @@ int decode_common(const pkv_geometry_t* geom, float* out, float* lse, const void
   if (!pkv::decode_supported(geom->kv_dtype, q_dtype, geom->head_dim, geom->block_size, G))
     return PKV_EUNSUPPORTED;
   DecodeSplit sp;
-  int st = decode_split(geom, num_seqs, max_context_len, window, num_workers, &sp);
+  int st = decode_split(geom, num_seqs, max_context_len, window, num_sinks, num_workers, &sp);
   if (st) return st;
   if (!workspace || workspace_bytes < sp.total() || ((uintptr_t)workspace & 15)) return PKV_EWORKSPACE;
   char* ws = (char*)workspace;
@@ -148,7 +152,7 @@ int decode_common(const pkv_geometry_t* geom, float* out, float* lse, const void
                     (int32_t*)ws, (float*)(ws + sp.cum_bytes), (float*)(ws + sp.cum_bytes + sp.ml_bytes),
                     num_seqs, geom->num_heads, geom->num_kv_heads, geom->head_dim, geom->block_size,
                     max_blocks_per_seq, geom->num_blocks, window, geom->kv_dtype, max_context_len,
-                    sp.workers, scale};
+                    sp.workers, scale, num_sinks};
   return hip_status(pkv::launch_decode(a, (hipStream_t)stream));
 }
 
@@ -159,29 +163,29 @@ extern "C" {
 int paged_attn_decode(const pkv_geometry_t* geom, float* out, float* lse, const void* q,
                       const void* k_pool, const void* v_pool, const int32_t* block_tables,
                       int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
-                      int32_t max_context_len, int32_t window, float scale, int32_t num_workers,
-                      void* workspace, size_t workspace_bytes, void* stream) {
+                      int32_t max_context_len, int32_t window, int32_t num_sinks, float scale,
+                      int32_t num_workers, void* workspace, size_t workspace_bytes, void* stream) {
   int st = check_geometry(geom);
   if (st) return st;
   if (is_quant(geom->kv_dtype)) return PKV_EUNSUPPORTED;  // paged_attn_decode_quant
   return decode_common(geom, out, lse, q, geom->kv_dtype, k_pool, v_pool, nullptr, nullptr, block_tables,
-                       max_blocks_per_seq, context_lens, num_seqs, max_context_len, window, scale, num_workers,
-                       workspace, workspace_bytes, stream);
+                       max_blocks_per_seq, context_lens, num_seqs, max_context_len, window, num_sinks, scale,
+                       num_workers, workspace, workspace_bytes, stream);
 }
 
 int paged_attn_decode_quant(const pkv_geometry_t* geom, float* out, float* lse, const void* q, int32_t q_dtype,
                             const void* k_pool, const void* v_pool, const float* k_scale, const float* v_scale,
                             const int32_t* block_tables, int32_t max_blocks_per_seq,
                             const int32_t* context_lens, int32_t num_seqs, int32_t max_context_len,
-                            int32_t window, float scale, int32_t num_workers, void* workspace,
-                            size_t workspace_bytes, void* stream) {
+                            int32_t window, int32_t num_sinks, float scale, int32_t num_workers,
+                            void* workspace, size_t workspace_bytes, void* stream) {
   int st = check_geometry(geom);
   if (st) return st;
   if (!is_quant(geom->kv_dtype)) return PKV_EINVAL;
   if (q_dtype != PKV_F16 && q_dtype != PKV_BF16) return PKV_EUNSUPPORTED;
   return decode_common(geom, out, lse, q, q_dtype, k_pool, v_pool, k_scale, v_scale, block_tables,
-                       max_blocks_per_seq, context_lens, num_seqs, max_context_len, window, scale, num_workers,
-                       workspace, workspace_bytes, stream);
+                       max_blocks_per_seq, context_lens, num_seqs, max_context_len, window, num_sinks, scale,
+                       num_workers, workspace, workspace_bytes, stream);
 }
 
 int paged_kv_write_quant(const pkv_geometry_t* geom, void* k_pool, void* v_pool, float* k_scale, float* v_scale,
@@ -208,12 +212,13 @@ int paged_attn_prefill(const pkv_geometry_t* geom, float* out, float* lse, const
                        const int32_t* q_start, const void* k_pool, const void* v_pool,
                        const int32_t* block_tables, int32_t max_blocks_per_seq,
                        const int32_t* context_lens, int32_t num_seqs, int32_t max_q_len,
-                       int32_t max_context_len, int32_t window, float scale, void* stream) {
+                       int32_t max_context_len, int32_t window, int32_t num_sinks, float scale, void* stream) {
   int st = check_geometry(geom);
   if (st) return st;
   if (num_seqs < 0 || max_blocks_per_seq <= 0 || max_q_len < 0 || max_context_len < 0 || window < 0 ||
-      !isfinite(scale))
+      num_sinks < 0 || !isfinite(scale))
     return PKV_EINVAL;
+  if (window == 0) num_sinks = 0;
   if ((long long)max_context_len > (long long)max_blocks_per_seq * geom->block_size) return PKV_EINVAL;
   if (max_q_len > max_context_len) return PKV_EINVAL;
   if (num_seqs == 0 || max_q_len == 0) return PKV_OK;
@@ -225,7 +230,7 @@ int paged_attn_prefill(const pkv_geometry_t* geom, float* out, float* lse, const
   pkv::PrefillArgs a{out, lse, q, q_start, k_pool, v_pool, block_tables, context_lens, num_seqs,
                      geom->num_heads, geom->num_kv_heads, geom->head_dim, geom->block_size,
                      max_blocks_per_seq, geom->num_blocks, window, geom->kv_dtype, max_q_len,
-                     max_context_len, scale};
+                     max_context_len, scale, num_sinks};
   return hip_status(pkv::launch_prefill(a, (hipStream_t)stream));
 }
 
@@ -242,6 +247,6 @@ const char* pkv_status_string(int status) {
 
 int pkv_last_hip_error(void) { return g_last_hip_error; }
 
-int pkv_version(void) { return 200; }
+int pkv_version(void) { return 300; }
 
 }  // extern "C"

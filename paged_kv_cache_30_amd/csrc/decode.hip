@@ -101,15 +101,24 @@ struct DecodeShape {
   static_assert(LPR >= 4 && LPR <= 32 && B % CHUNK == 0, "shape");
 };
 
-// Attended blocks of a sequence: [lo / B, ceil(L / B)), L clamped to
-// [0, max_ctx], lo = max(0, L - window) with a window.
-__device__ __forceinline__ void attended(int L, int max_ctx, int window, int B, int& L_out, int& lo,
-                                         int& blk_lo, int& nblk) {
+// Attended blocks of a sequence, L clamped to [0, max_ctx] and
+// lo = max(0, L - window) with a window: sb sink blocks [0, sb) (those
+// holding positions below min(sinks, lo) that lie before the window's first
+// block), then the window's blocks [wb0, ceil(L / B)), wb0 = lo / B.
+// Entry i of this list is logical block i < sb ? i : wb0 + (i - sb).
+struct Attended {
+  int L, lo, sb, wb0, nblk;
+  __device__ __forceinline__ int block(int i) const { return i < sb ? i : wb0 + (i - sb); }
+};
+__device__ __forceinline__ Attended attended(int L, int max_ctx, int window, int sinks, int B) {
+  Attended r;
   L = L < 0 ? 0 : (L > max_ctx ? max_ctx : L);
-  lo = window > 0 ? max(0, L - window) : 0;
-  blk_lo = lo / B;
-  nblk = L > 0 ? (L + B - 1) / B - blk_lo : 0;
-  L_out = L;
+  r.L = L;
+  r.lo = window > 0 ? max(0, L - window) : 0;
+  r.wb0 = r.lo / B;
+  r.sb = (window > 0 && sinks > 0 && L > 0) ? min((min(sinks, r.lo) + B - 1) / B, r.wb0) : 0;
+  r.nblk = L > 0 ? (L + B - 1) / B - r.wb0 + r.sb : 0;
+  return r;
 }
 
 // cum[s] = attended blocks of sequences 0 .. s-1 for s <= S, computed by all
@@ -124,11 +133,7 @@ __device__ void prefix_blocks(const DecodeArgs& a, int32_t* cum) {
   for (int base = 0; base < a.S; base += NT) {
     const int s = base + tid;
     int v = 0;
-    if (s < a.S) {
-      int L, lo, b0, n;
-      attended(a.lens[s], a.max_context_len, a.window, a.B, L, lo, b0, n);
-      v = n;
-    }
+    if (s < a.S) v = attended(a.lens[s], a.max_context_len, a.window, a.sinks, a.B).nblk;
     int x = v;  // inclusive scan inside the wavefront
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -183,9 +188,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, fl
     int v = 0;
     if (lane < a.S) {
       len_reg = a.lens[lane];
-      int L, lo, b0, n;
-      attended(len_reg, a.max_context_len, a.window, B, L, lo, b0, n);
-      v = n;
+      v = attended(len_reg, a.max_context_len, a.window, a.sinks, B).nblk;
     }
     int x = v;
 #pragma unroll
@@ -251,11 +254,11 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, fl
     const long long seg_end = min(end, (long long)Hkv * c0 + (long long)(g + 1) * nblk);
     const int n = (int)(seg_end - pos);
 
-    int L, lo, blk_lo, nb_unused;
-    attended(len_of(s), a.max_context_len, a.window, B, L, lo, blk_lo, nb_unused);
-    const int32_t* trow = a.tables + (size_t)s * a.mb + blk_lo + b_first;
-    const int blk0 = blk_lo + b_first;  // first logical block of the segment
-    int tv = lane < n ? trow[lane] : -1;  // table entries of blocks 0..63 of the segment
+    const Attended at = attended(len_of(s), a.max_context_len, a.window, a.sinks, B);
+    const int L = at.L, lo = at.lo;
+    const int32_t* trow = a.tables + (size_t)s * a.mb;
+    // table entries of attended blocks b_first .. b_first + 63 of the segment
+    int tv = lane < n ? trow[at.block(b_first + lane)] : -1;
 
     const char* qb = (const char*)a.q + ((size_t)(s * H + g * G) * D + c * E) * QB;
     u32x4 qv[G][PC][QW];
@@ -298,7 +301,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, fl
     auto issue = [&](int k, u32x4 (*kr)[PC], u32x4 (*vr)[PC], float* ks, float* vs) -> bool {
       const int bi = k / CPB;
       const int sub = k - bi * CPB;
-      if ((bi & 63) == 0 && bi > 0 && sub == 0) tv = bi + lane < n ? trow[bi + lane] : -1;
+      if ((bi & 63) == 0 && bi > 0 && sub == 0) tv = bi + lane < n ? trow[at.block(b_first + bi + lane)] : -1;
       const int pb = __builtin_amdgcn_readlane(tv, bi & 63);
       if (pb < 0 || pb >= a.nb) return false;
       const size_t off = (size_t)pb * blk_stride + (size_t)sub * CHUNK * row_stride;
@@ -327,8 +330,9 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, fl
     auto process = [&](int k, const u32x4 (*kr)[PC], const u32x4 (*vr)[PC], const float* ks, const float* vs) {
       const int bi = k / CPB;
       const int sub = k - bi * CPB;
-      const int t0 = (blk0 + bi) * B + sub * CHUNK;
-      const bool full = t0 >= lo && t0 + CHUNK <= L;
+      const int t0 = at.block(b_first + bi) * B + sub * CHUNK;
+      // attended: t in [lo, L), or t < sinks (below lo only with a window)
+      const bool full = (t0 >= lo || t0 + CHUNK <= a.sinks) && t0 + CHUNK <= L;
       float sc[CSTEPS][G];
 #pragma unroll
       for (int j = 0; j < CSTEPS; ++j) {
@@ -351,7 +355,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, fl
 #pragma unroll
         for (int j = 0; j < CSTEPS; ++j) {
           const int t = t0 + j * RPL + r;
-          const bool ok = t >= lo && t < L;
+          const bool ok = (t >= lo || t < a.sinks) && t < L;
 #pragma unroll
           for (int h = 0; h < G; ++h) sc[j][h] = ok ? sc[j][h] : -INFINITY;
         }
@@ -382,7 +386,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, fl
 #pragma unroll
       for (int j = 0; j < CSTEPS; ++j) {
         const int t = t0 + j * RPL + r;
-        const bool ok = full || (t >= lo && t < L);
+        const bool ok = full || ((t >= lo || t < a.sinks) && t < L);
         if constexpr (QU) {
           // Weight of the row times its V scale (0 for a masked row, whose
           // scale may be unset); codes widened to code + BIAS.

@@ -50,6 +50,7 @@ struct DecodeArgs {
   int32_t S, H, Hkv, D, B, mb, nb, window, dtype, max_context_len;
   int32_t n_workers;  // wavefronts the attended blocks are divided among
   float scale;
+  int32_t sinks;      // with a window: positions below this are attended too
 };
 
 struct PrefillArgs {
@@ -63,6 +64,7 @@ struct PrefillArgs {
   const int32_t* lens;
   int32_t S, H, Hkv, D, B, mb, nb, window, dtype, max_q_len, max_context_len;
   float scale;
+  int32_t sinks;      // with a window: positions below this are attended too
 };
 
 hipError_t launch_kv_write(const WriteArgs& a, hipStream_t st);

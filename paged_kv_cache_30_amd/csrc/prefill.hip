@@ -3,7 +3,8 @@
 // What it computes ("Building a Streaming Sliding-Window Attention Engine in
 // Pure Python", Step 3 and Step 4, read for a chunk that follows a cached
 // prefix): query row i of sequence s sits at position p = L - C + i and
-// attends every cached position t <= p (and t > p - w with a window).
+// attends every cached position t <= p (with a window: t > p - w, or
+// t < sinks for the attention sinks of the same page's Step 4 and roadmap).
 //
 // How, on gfx950 (v_mfma_f32_32x32x16 on 16-bit inputs, fp32 accumulate):
 //  * Workgroup = 4 wavefronts; each wavefront owns 32 query rows of one query
@@ -201,6 +202,14 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a, float sc
   int kv_lo = 0;
   if (a.window > 0) kv_lo = max(0, base + qt * QT - a.window + 1);
   const int t_first = (kv_lo / kKT) * kKT;
+  // Key tiles in processing order: with attention sinks, first the tiles
+  // holding positions below min(sinks, kv_lo) that lie before the window's
+  // first tile (ns of them), then the window's tiles from t_first.
+  const int ns = min((min(a.sinks, kv_lo) + kKT - 1) / kKT, t_first / kKT);
+  const int ntiles = ns + (kv_hi - t_first + kKT - 1) / kKT;
+  auto tile_t0 = [&](int i) { return i < ns ? i * kKT : t_first + (i - ns) * kKT; };
+  // A key position the workgroup's rows may attend.
+  auto in_range = [&](int t) { return (t >= kv_lo || t < a.sinks) && t < kv_hi; };
 
   // Query fragment of this lane: row ql of the wavefront, 8 elements per k-chunk.
   const int my_row = row0 + ql;
@@ -258,7 +267,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a, float sc
       const size_t boff = (size_t)(uint32_t)(blk_ok ? pb : 0) * block_stride;
       const int r = (4 * j + wave) * RPI + lane / U, cs = lane % U;
       const int t = t0 + r;
-      const bool ok = blk_ok && t >= kv_lo && t < kv_hi;
+      const bool ok = blk_ok && in_range(t);
       const uint32_t roff = (uint32_t)((t % B) * row_stride);
       dma16(ok ? kpool + boff + roff + 16 * (cs ^ Swz<D>::k(r)) : zero, kd + (4 * j + wave) * 512);
       dma16(ok ? vpool + boff + roff + 16 * (cs ^ Swz<D>::v(r)) : zero, vd + (4 * j + wave) * 512);
@@ -268,7 +277,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a, float sc
   auto put_valid = [&](int t0, int slot) {
     if (wave == 0) {
       const int t = t0 + lane;
-      const unsigned long long vm = __ballot(t >= kv_lo && t < kv_hi && pb_key >= 0 && pb_key < a.nb);
+      const unsigned long long vm = __ballot(in_range(t) && pb_key >= 0 && pb_key < a.nb);
       if (lane == 0) kvalid[slot] = vm;
     }
   };
@@ -293,17 +302,20 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a, float sc
   // One tile: gather the next tile into the other buffers, compute this one
   // from (Ks, Vs, kvalid[slot]), wait for the gather, barrier. Returns
   // whether a next tile exists.
-  auto step = [&](int t0, const uint16_t* Ks, const uint16_t* Vs, uint16_t* Kn, uint16_t* Vn,
+  auto step = [&](int i, const uint16_t* Ks, const uint16_t* Vs, uint16_t* Kn, uint16_t* Vn,
                   int slot) -> bool {
-    const bool has_next = t0 + kKT < kv_hi;
+    const int t0 = tile_t0(i);
+    const bool has_next = i + 1 < ntiles;
     if (has_next) {
-      gather(t0 + kKT, Kn, Vn);
-      put_valid(t0 + kKT, slot ^ 1);
-      if (t0 + 2 * kKT < kv_hi) fetch_table(t0 + 2 * kKT);
+      gather(tile_t0(i + 1), Kn, Vn);
+      put_valid(tile_t0(i + 1), slot ^ 1);
+      if (i + 2 < ntiles) fetch_table(tile_t0(i + 2));
     }
 
+    // Skip a tile whose keys all follow the wavefront's last row, or all
+    // precede its first row's window without holding a sink position.
     bool skip = !wave_has_rows || t0 > wave_pmax;
-    if (a.window > 0 && t0 + kKT - 1 <= wave_pmin - a.window) skip = true;
+    if (a.window > 0 && t0 + kKT - 1 <= wave_pmin - a.window && t0 >= a.sinks) skip = true;
     if (!skip) {
       const unsigned long long vmask = kvalid[slot];
       // S^T = K_tile . Q^T, two 32-key halves.
@@ -340,7 +352,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a, float sc
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
             const int kl = kh * 32 + acc_row(v, hf);
-            const bool ok = kl <= lim_hi && kl >= lim_lo && ((vmask >> kl) & 1);
+            const bool ok = kl <= lim_hi && (kl >= lim_lo || kl + t0 < a.sinks) && ((vmask >> kl) & 1);
             sacc[kh][v] = ok ? sacc[kh][v] : -INFINITY;
           }
         }
@@ -422,16 +434,16 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a, float sc
     return has_next;
   };
 
-  fetch_table(t_first);
+  fetch_table(tile_t0(0));
   dma_wait();  // table entries in registers
-  gather(t_first, k_lds0, v_lds0);
-  put_valid(t_first, 0);
-  if (t_first + kKT < kv_hi) fetch_table(t_first + kKT);
+  gather(tile_t0(0), k_lds0, v_lds0);
+  put_valid(tile_t0(0), 0);
+  if (ntiles > 1) fetch_table(tile_t0(1));
   dma_wait();
   __syncthreads();
-  for (int t0 = t_first;; t0 += 2 * kKT) {
-    if (!step(t0, k_lds0, v_lds0, k_lds1, v_lds1, 0)) break;
-    if (!step(t0 + kKT, k_lds1, v_lds1, k_lds0, v_lds0, 1)) break;
+  for (int i = 0;; i += 2) {
+    if (!step(i, k_lds0, v_lds0, k_lds1, v_lds1, 0)) break;
+    if (!step(i + 1, k_lds1, v_lds1, k_lds0, v_lds0, 1)) break;
   }
 
   if (!row_ok) return;

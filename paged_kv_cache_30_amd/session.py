@@ -95,7 +95,7 @@ class DeviceWorkload:
         w = self.w
         if w.kind == "decode":
             self.workspace = _lib.decode_workspace(self.k_pool, w.num_heads, w.num_seqs, w.max_context_len,
-                                                   w.window, num_workers)
+                                                   w.window, num_workers, sinks=w.sinks)
 
     def _write(self, k, v, seq, pos):
         if self.kv_format == "native":
@@ -123,16 +123,16 @@ class DeviceWorkload:
                 self._bound_attend = _lib.bind_decode_quant(
                     self.out, self.q, self.k_pool, self.v_pool, self.k_scale, self.v_scale, self.tables, self.lens,
                     w.max_context_len, window=w.window, scale=w.scale, num_workers=self.num_workers,
-                    workspace=self.workspace, lse=self.lse)
+                    workspace=self.workspace, lse=self.lse, sinks=w.sinks)
             elif w.kind == "decode":
                 self._bound_attend = _lib.bind_decode(
                     self.out, self.q, self.k_pool, self.v_pool, self.tables, self.lens, w.max_context_len,
                     window=w.window, scale=w.scale, num_workers=self.num_workers, workspace=self.workspace,
-                    lse=self.lse)
+                    lse=self.lse, sinks=w.sinks)
             else:
                 self._bound_attend = _lib.bind_prefill(
                     self.out, self.q, self.q_start, self.k_pool, self.v_pool, self.tables, self.lens,
-                    w.max_q_len, w.max_context_len, window=w.window, scale=w.scale, lse=self.lse)
+                    w.max_q_len, w.max_context_len, window=w.window, scale=w.scale, lse=self.lse, sinks=w.sinks)
         self._bound_attend(stream)
 
     def step(self, stream=None) -> None:

@@ -52,24 +52,25 @@ def test_workspace_query_matches_split():
         cum = -(-(S + 1) * 4 // 256) * 256
         ml = -(-slots * G * 2 * 4 // 256) * 256
         return cum + ml + slots * G * D * 4
-    assert pkv.LIB.paged_attn_decode_workspace_bytes(ctypes.byref(g), 64, 32768, 0, 512) == expect(64, 512)
-    assert pkv.LIB.paged_attn_decode_workspace_bytes(ctypes.byref(g), 1, 100, 0, 1) == expect(1, 1)
+    assert pkv.LIB.paged_attn_decode_workspace_bytes(ctypes.byref(g), 64, 32768, 0, 0, 512) == expect(64, 512)
+    assert pkv.LIB.paged_attn_decode_workspace_bytes(ctypes.byref(g), 1, 100, 0, 0, 1) == expect(1, 1)
     # automatic: never more workers than the attended blocks could occupy
-    auto = pkv.LIB.paged_attn_decode_workers(ctypes.byref(g), 1, 100, 0)
+    auto = pkv.LIB.paged_attn_decode_workers(ctypes.byref(g), 1, 100, 0, 0)
     assert 1 <= auto <= 8 * 7
-    assert pkv.LIB.paged_attn_decode_workspace_bytes(ctypes.byref(g), 1, 100, 0, 0) == expect(1, auto)
-    big = pkv.LIB.paged_attn_decode_workers(ctypes.byref(g), 64, 32768, 0)
+    assert pkv.LIB.paged_attn_decode_workspace_bytes(ctypes.byref(g), 1, 100, 0, 0, 0) == expect(1, auto)
+    big = pkv.LIB.paged_attn_decode_workers(ctypes.byref(g), 64, 32768, 0, 0)
     assert big >= 1
 
 
 def call_decode(g, **over):
-    args = dict(out=1, lse=None, q=1, k=1, v=1, t=1, mb=8, lens=1, S=2, maxc=100, window=0, scale=0.1,
+    args = dict(out=1, lse=None, q=1, k=1, v=1, t=1, mb=8, lens=1, S=2, maxc=100, window=0, sinks=0, scale=0.1,
                 part=0, ws=None, wsb=0)
     args.update(over)
     P = lambda x: None if x is None else ctypes.c_void_p(x)
     return pkv.LIB.paged_attn_decode(ctypes.byref(g) if g is not None else None, P(args["out"]), P(args["lse"]),
                                      P(args["q"]), P(args["k"]), P(args["v"]), P(args["t"]), args["mb"],
-                                     P(args["lens"]), args["S"], args["maxc"], args["window"], args["scale"],
+                                     P(args["lens"]), args["S"], args["maxc"], args["window"], args["sinks"],
+                                     args["scale"],
                                      args["part"], P(args["ws"]), args["wsb"], None)
 
 
@@ -80,6 +81,7 @@ def test_argument_errors_before_any_launch():
     assert call_decode(g, window=-1) == pkv.PKV_EINVAL
     assert call_decode(g, maxc=8 * 16 + 1) == pkv.PKV_EINVAL
     assert call_decode(g, part=-1) == pkv.PKV_EINVAL
+    assert call_decode(g, window=16, sinks=-1) == pkv.PKV_EINVAL
     assert call_decode(g, scale=float("nan")) == pkv.PKV_EINVAL
     assert call_decode(geo(D=96)) == pkv.PKV_EUNSUPPORTED
     assert call_decode(geo(B=8)) == pkv.PKV_EUNSUPPORTED
@@ -90,7 +92,7 @@ def test_argument_errors_before_any_launch():
     assert call_decode(geo(B=32, H=1 << 17, Hkv=1 << 17, dt=pkv.PKV_F32)) == pkv.PKV_EUNSUPPORTED
     # workspace missing, too small or misaligned
     assert call_decode(g, S=64, maxc=128, mb=8, part=16) == pkv.PKV_EWORKSPACE
-    need = pkv.LIB.paged_attn_decode_workspace_bytes(ctypes.byref(g), 2, 100, 0, 4)
+    need = pkv.LIB.paged_attn_decode_workspace_bytes(ctypes.byref(g), 2, 100, 0, 0, 4)
     assert call_decode(g, part=4, ws=4096, wsb=need - 1) == pkv.PKV_EWORKSPACE
     assert call_decode(g, part=4, ws=4100, wsb=need) == pkv.PKV_EWORKSPACE
     assert call_decode(g, S=0) == pkv.PKV_OK
@@ -98,9 +100,9 @@ def test_argument_errors_before_any_launch():
     # prefill: fp32 is not built, chunk longer than context is invalid
     g32 = geo(dt=pkv.PKV_F32)
     assert pkv.LIB.paged_attn_prefill(ctypes.byref(g32), P(1), None, P(1), P(1), P(1), P(1), P(1), 8, P(1), 1, 4,
-                                      100, 0, 0.1, None) == pkv.PKV_EUNSUPPORTED
+                                      100, 0, 0, 0.1, None) == pkv.PKV_EUNSUPPORTED
     assert pkv.LIB.paged_attn_prefill(ctypes.byref(g), P(1), None, P(1), P(1), P(1), P(1), P(1), 8, P(1), 1, 101,
-                                      100, 0, 0.1, None) == pkv.PKV_EINVAL
+                                      100, 0, 0, 0.1, None) == pkv.PKV_EINVAL
     # write: nothing to do / bad sizes
     assert pkv.LIB.paged_kv_write(ctypes.byref(g), P(1), P(1), P(1), P(1), P(1), P(1), 0, P(1), 1, 8,
                                   None) == pkv.PKV_OK
@@ -123,13 +125,13 @@ def test_quant_argument_errors_before_any_launch():
     assert pkv.LIB.paged_kv_write(ctypes.byref(gi8), P(1), P(1), P(1), P(1), P(1), P(1), 3, P(1), 1, 8,
                                   None) == pkv.PKV_EUNSUPPORTED
     assert pkv.LIB.paged_attn_prefill(ctypes.byref(gfp8), P(1), None, P(1), P(1), P(1), P(1), P(1), 8, P(1), 1, 4,
-                                      100, 0, 0.1, None) == pkv.PKV_EUNSUPPORTED
+                                      100, 0, 0, 0.1, None) == pkv.PKV_EUNSUPPORTED
 
     def dq(g, q_dtype=pkv.PKV_BF16, ks=P(1), H=None, ws=P(4096), wsb=1 << 30):
         if H is not None:
             g = geo(H=H, Hkv=g.num_kv_heads, dt=g.kv_dtype)
         return pkv.LIB.paged_attn_decode_quant(ctypes.byref(g), P(1), None, P(1), q_dtype, P(1), P(1), ks, P(1),
-                                               P(1), 8, P(1), 2, 100, 0, 0.1, 0, ws, wsb, None)
+                                               P(1), 8, P(1), 2, 100, 0, 0, 0.1, 0, ws, wsb, None)
     assert dq(g16) == pkv.PKV_EINVAL                               # not an 8-bit pool
     assert dq(gi8, q_dtype=pkv.PKV_F32) == pkv.PKV_EUNSUPPORTED    # query type
     assert dq(gi8, ks=None) == pkv.PKV_EINVAL                      # missing scales
@@ -145,5 +147,5 @@ def test_quant_argument_errors_before_any_launch():
     assert wq(gfp8, n=0) == pkv.PKV_OK
     assert wq(gfp8, n=-1) == pkv.PKV_EINVAL
     # the workspace size of an 8-bit pool is that of any pool
-    assert (pkv.LIB.paged_attn_decode_workspace_bytes(ctypes.byref(gi8), 2, 100, 0, 4) ==
-            pkv.LIB.paged_attn_decode_workspace_bytes(ctypes.byref(g16), 2, 100, 0, 4))
+    assert (pkv.LIB.paged_attn_decode_workspace_bytes(ctypes.byref(gi8), 2, 100, 0, 0, 4) ==
+            pkv.LIB.paged_attn_decode_workspace_bytes(ctypes.byref(g16), 2, 100, 0, 0, 4))

@@ -398,3 +398,106 @@ def test_graph_replay_matches_eager(lib, kind):
         assert torch.equal(d.out, eager), f"replay {i} differs"
         assert torch.equal(d.lse, eager_lse), f"replay {i} lse differs"
         del junk
+
+
+# ------------------------------------------------------- attention sinks
+
+SINK_CASES = [
+    # (dtype, H, Hkv, D, B, lens, window, sinks, workers)
+    ("bf16", 16, 4, 128, 16, [40, 600, 1500, 3], 100, 4, 0),
+    ("f16", 8, 8, 128, 32, [70, 1000, 333], 64, 4, 7),
+    ("bf16", 8, 1, 64, 16, [5, 64, 700], 30, 20, 3),
+    ("f32", 4, 2, 64, 16, [10, 170, 90], 16, 40, 0),
+    ("bf16", 32, 8, 128, 16, [2000, 4100, 1], 256, 1, 48),
+]
+
+
+def poison_freed_middle(w):
+    """Point the freed table entries between the sink blocks and the window
+    at a spare (never written, NaN) block: reading them would show."""
+    used = set(w.block_tables[w.block_tables >= 0].tolist())
+    spare = next(i for i in range(w.num_blocks) if i not in used)
+    t = w.block_tables.copy()
+    for s in range(w.num_seqs):
+        L = int(w.context_lens[s])
+        lo = max(0, L - w.window)
+        sb = min(-(-min(w.sinks, lo) // w.block_size), lo // w.block_size)
+        t[s, sb:lo // w.block_size] = spare
+    w.block_tables = t
+
+
+@pytest.mark.parametrize("case", SINK_CASES, ids=[f"{c[0]}-g{c[1] // c[2]}-d{c[3]}-b{c[4]}-w{c[6]}-s{c[7]}-p{c[8]}"
+                                                  for c in SINK_CASES])
+def test_decode_sinks(lib, case):
+    pkv, session = lib
+    dtype, H, Hkv, D, B, lens, window, sinks, workers = case
+    note(f"decode sinks {case}")
+    w = wl.make_decode(lens=lens, num_heads=H, num_kv_heads=Hkv, head_dim=D, block_size=B, dtype=dtype,
+                       seed=sum(lens) + sinks, window=window, sinks=sinks, spare_blocks=1)
+    poison_freed_middle(w)
+    d = run(session, w, num_workers=workers)
+    kp, vp = ref.build_pools(w)
+    out, lse = ref.decode(w.q, kp, vp, w.block_tables, w.context_lens, block_size=B, num_kv_heads=Hkv,
+                          window=window, scale=w.scale, dtype=dtype, sinks=sinks)
+    assert_close(d.out.cpu().numpy(), out, dtype, str(case))
+    check_lse(d, lse)
+
+
+@pytest.mark.parametrize("fmt", ["i8", "fp8"])
+def test_decode_sinks_8bit(lib, fmt):
+    pkv, session = lib
+    import oracle.quant as oq
+    note(f"decode sinks 8-bit {fmt}")
+    w = wl.make_decode(lens=[40, 600, 1500, 3], num_heads=16, num_kv_heads=4, head_dim=128, block_size=16,
+                       dtype="bf16", seed=77, window=100, sinks=4, spare_blocks=1)
+    poison_freed_middle(w)
+    d = session.DeviceWorkload(w, kv_format=fmt)
+    d.step()
+    torch.cuda.synchronize()
+    kp, vp = ref.build_pools(w)
+    kc, vc, ks, vs = oq.quantize_pools(kp, vp, "bf16", fmt)
+    kd, vd = oq.dequantize_pool(kc, ks, fmt), oq.dequantize_pool(vc, vs, fmt)
+    out, _ = ref.decode(w.q, kd, vd, w.block_tables, w.context_lens, block_size=16, num_kv_heads=4, window=100,
+                        scale=w.scale, dtype="bf16", kv_dtype="f64", sinks=4)
+    assert_close(d.out.cpu().numpy(), out, "bf16", f"sinks {fmt}")
+
+
+def test_decode_sinks_long_window(lib):
+    """Sliding-window sizes (contexts 16K-32K, window 4096) with 4 sinks,
+    against the contiguous oracle over the sink and window positions."""
+    pkv, session = lib
+    note("decode sinks long window")
+    w = wl.make_decode(lens=[16384, 20001, 32768, 24577], num_heads=32, num_kv_heads=8, head_dim=128,
+                       block_size=16, dtype="bf16", seed=78, window=4096, sinks=4, spare_blocks=1)
+    poison_freed_middle(w)
+    d = run(session, w)
+    got = d.out.cpu().numpy()
+    for s in range(w.num_seqs):
+        first, k, v = w.logical_kv(s)
+        o, _ = ref.contiguous_decode(w.q[s], k, v, first, int(w.context_lens[s]), num_kv_heads=8, window=4096,
+                                     scale=w.scale, dtype="bf16", sinks=4)
+        assert_close(got[s], o, "bf16", f"sinks long seq {s}")
+
+
+PREFILL_SINK_CASES = [
+    # (dtype, H, Hkv, D, B, prefix, chunks, window, sinks)
+    ("bf16", 8, 2, 128, 16, 160, [90, 31], 50, 4),
+    ("f16", 16, 2, 128, 32, 96, [200, 5], 64, 70),
+    ("bf16", 4, 4, 64, 16, 64, [130, 64], 17, 1),
+]
+
+
+@pytest.mark.parametrize("case", PREFILL_SINK_CASES,
+                         ids=[f"{c[0]}-g{c[1] // c[2]}-d{c[3]}-w{c[7]}-s{c[8]}" for c in PREFILL_SINK_CASES])
+def test_prefill_sinks(lib, case):
+    pkv, session = lib
+    dtype, H, Hkv, D, B, prefix, chunks, window, sinks = case
+    note(f"prefill sinks {case}")
+    w = wl.make_prefill(prefix_len=prefix, chunk_lens=chunks, num_heads=H, num_kv_heads=Hkv, head_dim=D,
+                        block_size=B, dtype=dtype, seed=prefix + sinks, window=window, sinks=sinks)
+    d = run(session, w)
+    kp, vp = ref.build_pools(w)
+    out, lse = ref.prefill(w.q, w.q_start, kp, vp, w.block_tables, w.context_lens, block_size=B,
+                           num_kv_heads=Hkv, window=window, scale=w.scale, dtype=dtype, sinks=sinks)
+    assert_close(d.out.cpu().numpy(), out, dtype, str(case))
+    check_lse(d, lse)
