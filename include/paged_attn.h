@@ -259,6 +259,43 @@ int paged_attn_decode_quant(const pkv_geometry_t* geom, float* out, float* lse, 
                             int32_t max_context_len, int32_t window, int32_t num_sinks, float scale,
                             int32_t num_workers, void* workspace, size_t workspace_bytes, void* stream);
 
+/* paged_kv_copy_blocks - copy whole blocks: pair i copies block src[i] to
+ * block dst[i] in both pools (every slot and kv head; with 8-bit pools the
+ * rows' scales too). This is the copy of copy-on-write: a sequence about to
+ * append into a block it shares with others first gets a private copy
+ * ("Build a Minimal LLM Inference Engine with Paged Attention and Adaptive
+ * KV Cache", Step 1: a page is shared while its refcount is above one;
+ * "Building a Streaming Sliding-Window Attention Engine in Pure Python",
+ * Step 4: prefixes are reused across requests).
+ *
+ *   k_pool, v_pool    [NB, B, Hkv, D] kv_dtype, written in place
+ *   k_scale, v_scale  [NB, Hkv, B] float32 for 8-bit pools (required), NULL
+ *                     otherwise (both or neither)
+ *   src, dst          int32 [num_pairs] block ids
+ * Pairs with an id outside [0, NB) or src == dst are skipped. A block that
+ * is a destination must not also be a source or another pair's
+ * destination in the same call (the copies run in parallel). */
+int paged_kv_copy_blocks(const pkv_geometry_t* geom, void* k_pool, void* v_pool, float* k_scale,
+                         float* v_scale, const int32_t* src, const int32_t* dst, int32_t num_pairs,
+                         void* stream);
+
+/* paged_attn_mixed - one call for a batch that mixes prefill chunks and
+ * decode rows ("Building a Streaming Sliding-Window Attention Engine in Pure
+ * Python", roadmap item 2, continuous batching: slots of finished requests
+ * are refilled mid-stream, so one step holds new prompts' chunks next to
+ * running sequences' decode tokens): the arguments and the result are those of
+ * paged_attn_prefill (sequence s owns rows [q_start[s], q_start[s+1]), its
+ * last positions); sequences with exactly one row are computed by the
+ * split decode kernel (workspace, num_workers as paged_attn_decode; size it
+ * with paged_attn_decode_workspace_bytes for num_seqs sequences), the others
+ * by the prefill kernel, both enqueued on `stream`. PKV_F16 / PKV_BF16. */
+int paged_attn_mixed(const pkv_geometry_t* geom, float* out, float* lse, const void* q,
+                     const int32_t* q_start, const void* k_pool, const void* v_pool,
+                     const int32_t* block_tables, int32_t max_blocks_per_seq,
+                     const int32_t* context_lens, int32_t num_seqs, int32_t max_q_len,
+                     int32_t max_context_len, int32_t window, int32_t num_sinks, float scale,
+                     int32_t num_workers, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Name of a status code (static string). */
 const char* pkv_status_string(int status);
 

@@ -59,6 +59,25 @@ def kv_write(k_pool, v_pool, k_new, v_new, seq_idx, pos, block_tables, block_siz
     return k_pool, v_pool
 
 
+def copy_blocks(k_pool, v_pool, src, dst, k_scale=None, v_scale=None):
+    """Copy block src[i] to block dst[i] in both pools (every slot and kv
+    head), and the rows' scales of 8-bit pools ([NB, Hkv, B]).  The copy of
+    copy-on-write: a page shared by several sequences ("Build a Minimal LLM
+    Inference Engine ...", Step 1: refcount above one) is duplicated before
+    one of them writes into it.  Pairs with an id outside [0, NB) or
+    src == dst are skipped.  Returns new arrays (inputs untouched)."""
+    out = [np.array(a, copy=True) if a is not None else None for a in (k_pool, v_pool, k_scale, v_scale)]
+    nb = out[0].shape[0]
+    for a, b in zip(np.asarray(src), np.asarray(dst)):
+        a, b = int(a), int(b)
+        if not (0 <= a < nb and 0 <= b < nb) or a == b:
+            continue
+        for arr, orig in zip(out, (k_pool, v_pool, k_scale, v_scale)):
+            if arr is not None:
+                arr[b] = np.asarray(orig)[a]
+    return tuple(out)
+
+
 # ------------------------------------------------------------------ gather
 
 def gather(pool, table_row, positions, g, block_size, dtype):

@@ -31,7 +31,8 @@ _QUANT = (torch.int8, torch.float8_e4m3fn)
 # Every symbol declared in include/paged_attn.h.
 EXPORTS = ("paged_kv_write", "paged_attn_decode_workspace_bytes", "paged_attn_decode_workers",
            "paged_attn_decode", "paged_attn_prefill", "paged_kv_write_quant", "paged_attn_decode_quant",
-           "pkv_status_string", "pkv_last_hip_error", "pkv_version")
+           "paged_kv_copy_blocks", "paged_attn_mixed", "pkv_status_string", "pkv_last_hip_error",
+           "pkv_version")
 
 
 class Geometry(ctypes.Structure):
@@ -69,6 +70,10 @@ def _load() -> ctypes.CDLL:
     lib.paged_attn_decode_quant.argtypes = [G, P, P, P, I32, P, P, P, P, P, I32, P, I32, I32, I32, I32, F, I32, P,
                                             SZ, P]
     lib.paged_attn_decode_quant.restype = ctypes.c_int
+    lib.paged_kv_copy_blocks.argtypes = [G, P, P, P, P, P, P, I32, P]
+    lib.paged_kv_copy_blocks.restype = ctypes.c_int
+    lib.paged_attn_mixed.argtypes = [G, P, P, P, P, P, P, P, I32, P, I32, I32, I32, I32, I32, F, I32, P, SZ, P]
+    lib.paged_attn_mixed.restype = ctypes.c_int
     lib.pkv_status_string.argtypes = [ctypes.c_int]
     lib.pkv_status_string.restype = ctypes.c_char_p
     lib.pkv_last_hip_error.argtypes = []
@@ -343,3 +348,68 @@ def paged_attn_decode_quant(out, q, k_pool, v_pool, k_scale, v_scale, block_tabl
     bind_decode_quant(out, q, k_pool, v_pool, k_scale, v_scale, block_tables, context_lens, max_context_len,
                       window=window, scale=scale, num_workers=num_workers, workspace=workspace, lse=lse,
                       sinks=sinks)(stream)
+
+
+# ------------------------------------------------- block copies, mixed batches
+
+def paged_kv_copy_blocks(k_pool, v_pool, src, dst, k_scale=None, v_scale=None, stream=None) -> None:
+    """C ``paged_kv_copy_blocks``: copy block src[i] to dst[i] in both pools
+    (and the row scales of 8-bit pools)."""
+    _dev(k_pool, "k_pool", ndim=4)
+    _dev(v_pool, "v_pool", dtype=k_pool.dtype)
+    if v_pool.shape != k_pool.shape:
+        raise ValueError("k_pool and v_pool differ in shape")
+    if k_pool.dtype in _QUANT:
+        _check_quant_pools(k_pool, v_pool, k_scale, v_scale)
+    elif k_scale is not None or v_scale is not None:
+        raise ValueError("row scales belong to 8-bit pools only")
+    _dev(src, "src", dtype=torch.int32, ndim=1)
+    _dev(dst, "dst", dtype=torch.int32, ndim=1)
+    if src.shape != dst.shape:
+        raise ValueError("src and dst need one entry per pair")
+    g = geometry(k_pool, k_pool.shape[2])
+    _check(LIB.paged_kv_copy_blocks(ctypes.byref(g), _ptr(k_pool), _ptr(v_pool), _ptr(k_scale), _ptr(v_scale),
+                                    _ptr(src), _ptr(dst), src.shape[0], _stream(stream)), "paged_kv_copy_blocks")
+
+
+def bind_mixed(out, q, q_start, k_pool, v_pool, block_tables, context_lens, max_q_len, max_context_len, *,
+               window=0, scale, num_workers=0, workspace=None, lse=None, sinks=0):
+    """Check and marshal the arguments of ``paged_attn_mixed`` once; returns
+    a callable ``f(stream=None)``."""
+    _dev(q, "q", dtype=k_pool.dtype, ndim=3)
+    _dev(out, "out", dtype=torch.float32, ndim=3)
+    _dev(q_start, "q_start", dtype=torch.int32, ndim=1)
+    _dev(k_pool, "k_pool", ndim=4)
+    _dev(v_pool, "v_pool", dtype=k_pool.dtype)
+    _dev(block_tables, "block_tables", dtype=torch.int32, ndim=2)
+    _dev(context_lens, "context_lens", dtype=torch.int32, ndim=1)
+    T, H, D = q.shape
+    S = context_lens.shape[0]
+    if out.shape != q.shape or q_start.shape[0] != S + 1 or block_tables.shape[0] != S:
+        raise ValueError("shape mismatch between q, out, q_start, context_lens and block_tables")
+    if lse is not None:
+        _dev(lse, "lse", dtype=torch.float32, ndim=2)
+        if lse.shape != (T, H):
+            raise ValueError("lse must be [T, H]")
+    ws_bytes = 0
+    if workspace is not None:
+        _dev(workspace, "workspace")
+        ws_bytes = workspace.numel() * workspace.element_size()
+    g = geometry(k_pool, H)
+    args = (ctypes.byref(g), _ptr(out), _ptr(lse), _ptr(q), _ptr(q_start), _ptr(k_pool), _ptr(v_pool),
+            _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), S, int(max_q_len), int(max_context_len),
+            int(window), int(sinks), float(scale), int(num_workers), _ptr(workspace), ws_bytes)
+    keep = (g, out, q, q_start, k_pool, v_pool, block_tables, context_lens, workspace, lse)
+
+    def call(stream=None):
+        _check(LIB.paged_attn_mixed(*args, _stream(stream)), "paged_attn_mixed")
+    call.keep = keep
+    return call
+
+
+def paged_attn_mixed(out, q, q_start, k_pool, v_pool, block_tables, context_lens, max_q_len, max_context_len, *,
+                     window=0, scale, num_workers=0, workspace=None, lse=None, stream=None, sinks=0) -> None:
+    """C ``paged_attn_mixed``: prefill chunks and single decode rows in one call."""
+    bind_mixed(out, q, q_start, k_pool, v_pool, block_tables, context_lens, max_q_len, max_context_len,
+               window=window, scale=scale, num_workers=num_workers, workspace=workspace, lse=lse,
+               sinks=sinks)(stream)

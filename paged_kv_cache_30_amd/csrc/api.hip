@@ -234,6 +234,59 @@ int paged_attn_prefill(const pkv_geometry_t* geom, float* out, float* lse, const
   return hip_status(pkv::launch_prefill(a, (hipStream_t)stream));
 }
 
+int paged_kv_copy_blocks(const pkv_geometry_t* geom, void* k_pool, void* v_pool, float* k_scale, float* v_scale,
+                        const int32_t* src, const int32_t* dst, int32_t num_pairs, void* stream) {
+  int st = check_geometry(geom);
+  if (st) return st;
+  if (num_pairs < 0) return PKV_EINVAL;
+  if (num_pairs == 0) return PKV_OK;
+  if (!k_pool || !v_pool || !src || !dst) return PKV_EINVAL;
+  if ((k_scale == nullptr) != (v_scale == nullptr)) return PKV_EINVAL;
+  if (is_quant(geom->kv_dtype) && !k_scale) return PKV_EINVAL;
+  pkv::CopyBlocksArgs a{k_pool, v_pool, k_scale, v_scale, src, dst, num_pairs, geom->num_blocks,
+                        geom->block_size, geom->num_kv_heads, geom->head_dim, elem_bytes(geom->kv_dtype)};
+  return hip_status(pkv::launch_kv_copy_blocks(a, (hipStream_t)stream));
+}
+
+int paged_attn_mixed(const pkv_geometry_t* geom, float* out, float* lse, const void* q, const int32_t* q_start,
+                     const void* k_pool, const void* v_pool, const int32_t* block_tables,
+                     int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs, int32_t max_q_len,
+                     int32_t max_context_len, int32_t window, int32_t num_sinks, float scale, int32_t num_workers,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_geometry(geom);
+  if (st) return st;
+  if (num_seqs < 0 || max_blocks_per_seq <= 0 || max_q_len < 0 || max_context_len < 0 || window < 0 ||
+      num_sinks < 0 || num_workers < 0 || !isfinite(scale))
+    return PKV_EINVAL;
+  if (window == 0) num_sinks = 0;
+  if ((long long)max_context_len > (long long)max_blocks_per_seq * geom->block_size) return PKV_EINVAL;
+  if (max_q_len > max_context_len) return PKV_EINVAL;
+  if (num_seqs == 0 || max_q_len == 0) return PKV_OK;
+  if (!out || !q || !q_start || !k_pool || !v_pool || !block_tables || !context_lens) return PKV_EINVAL;
+  const int G = geom->num_heads / geom->num_kv_heads;
+  if (is_quant(geom->kv_dtype) ||
+      !pkv::prefill_supported(geom->kv_dtype, geom->head_dim, geom->block_size, G) ||
+      !pkv::decode_supported(geom->kv_dtype, geom->kv_dtype, geom->head_dim, geom->block_size, G))
+    return PKV_EUNSUPPORTED;
+  DecodeSplit sp;
+  st = decode_split(geom, num_seqs, max_context_len, window, num_sinks, num_workers, &sp);
+  if (st) return st;
+  if (!workspace || workspace_bytes < sp.total() || ((uintptr_t)workspace & 15)) return PKV_EWORKSPACE;
+  char* ws = (char*)workspace;
+  pkv::DecodeArgs da{out, lse, q, k_pool, v_pool, block_tables, context_lens, nullptr, nullptr, geom->kv_dtype,
+                     (int32_t*)ws, (float*)(ws + sp.cum_bytes), (float*)(ws + sp.cum_bytes + sp.ml_bytes),
+                     num_seqs, geom->num_heads, geom->num_kv_heads, geom->head_dim, geom->block_size,
+                     max_blocks_per_seq, geom->num_blocks, window, geom->kv_dtype, max_context_len,
+                     sp.workers, scale, num_sinks, q_start};
+  st = hip_status(pkv::launch_decode(da, (hipStream_t)stream));
+  if (st || max_q_len < 2) return st;
+  pkv::PrefillArgs pa{out, lse, q, q_start, k_pool, v_pool, block_tables, context_lens, num_seqs,
+                      geom->num_heads, geom->num_kv_heads, geom->head_dim, geom->block_size,
+                      max_blocks_per_seq, geom->num_blocks, window, geom->kv_dtype, max_q_len,
+                      max_context_len, scale, num_sinks, 1};
+  return hip_status(pkv::launch_prefill(pa, (hipStream_t)stream));
+}
+
 const char* pkv_status_string(int status) {
   switch (status) {
     case PKV_OK: return "PKV_OK";
@@ -247,6 +300,6 @@ const char* pkv_status_string(int status) {
 
 int pkv_last_hip_error(void) { return g_last_hip_error; }
 
-int pkv_version(void) { return 300; }
+int pkv_version(void) { return 310; }
 
 }  // extern "C"

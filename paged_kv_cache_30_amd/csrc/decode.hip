@@ -121,6 +121,15 @@ __device__ __forceinline__ Attended attended(int L, int max_ctx, int window, int
   return r;
 }
 
+// Context length decode uses for sequence s: in a mixed batch (q_start set)
+// only sequences with exactly one query row are decoded here; the others
+// count as empty (the prefill kernel computes them). q/out/lse row of s.
+__device__ __forceinline__ int decode_len(const DecodeArgs& a, int s) {
+  if (a.q_start && a.q_start[s + 1] - a.q_start[s] != 1) return 0;
+  return a.lens[s];
+}
+__device__ __forceinline__ int q_row(const DecodeArgs& a, int s) { return a.q_start ? a.q_start[s] : s; }
+
 // cum[s] = attended blocks of sequences 0 .. s-1 for s <= S, computed by all
 // NT threads of the workgroup (a block-wide scan, NT/64 wavefronts).
 template <int NT>
@@ -133,7 +142,7 @@ __device__ void prefix_blocks(const DecodeArgs& a, int32_t* cum) {
   for (int base = 0; base < a.S; base += NT) {
     const int s = base + tid;
     int v = 0;
-    if (s < a.S) v = attended(a.lens[s], a.max_context_len, a.window, a.sinks, a.B).nblk;
+    if (s < a.S) v = attended(decode_len(a, s), a.max_context_len, a.window, a.sinks, a.B).nblk;
     int x = v;  // inclusive scan inside the wavefront
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -187,7 +196,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, fl
   if (in_reg) {
     int v = 0;
     if (lane < a.S) {
-      len_reg = a.lens[lane];
+      len_reg = decode_len(a, lane);
       v = attended(len_reg, a.max_context_len, a.window, a.sinks, B).nblk;
     }
     int x = v;
@@ -206,7 +215,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, fl
   }
   // cum[i] and lens[i] for a wavefront-uniform i.
   auto cum = [&](int i) -> int { return in_reg ? __builtin_amdgcn_readlane(cum_reg, i) : cum_mem[i]; };
-  auto len_of = [&](int i) -> int { return in_reg ? __builtin_amdgcn_readlane(len_reg, i) : a.lens[i]; };
+  auto len_of = [&](int i) -> int { return in_reg ? __builtin_amdgcn_readlane(len_reg, i) : decode_len(a, i); };
 
   const int w = blockIdx.x * kWaves + uniform(threadIdx.x >> 6);  // worker index
   const int c = lane % LPR;
@@ -260,7 +269,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, fl
     // table entries of attended blocks b_first .. b_first + 63 of the segment
     int tv = lane < n ? trow[at.block(b_first + lane)] : -1;
 
-    const char* qb = (const char*)a.q + ((size_t)(s * H + g * G) * D + c * E) * QB;
+    const char* qb = (const char*)a.q + ((size_t)(q_row(a, s) * H + g * G) * D + c * E) * QB;
     u32x4 qv[G][PC][QW];
 #pragma unroll
     for (int h = 0; h < G; ++h)
@@ -503,7 +512,8 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(DecodeArgs a) {
   const int hq = blockIdx.x, s = blockIdx.y, d = threadIdx.x;
   const int g = hq / G, hh = hq - g * G;
   const int Hkv = a.Hkv;
-  const size_t row = (size_t)s * a.H + hq;
+  if (a.q_start && a.q_start[s + 1] - a.q_start[s] != 1) return;  // a prefill chunk of a mixed batch
+  const size_t row = (size_t)q_row(a, s) * a.H + hq;
   const int c0 = a.ws_cum[s];
   const int nblk = a.ws_cum[s + 1] - c0;
   float M = -INFINITY, sl = 0.f, so = 0.f;

@@ -130,6 +130,41 @@ __global__ __launch_bounds__(256) void kv_write_quant_kernel(WriteQuantArgs a, l
   }
 }
 
+// Whole-block copies (copy-on-write of shared blocks): pair i copies block
+// src[i] to block dst[i] in both pools, 16-byte pieces, and the B row scales
+// of each kv head when scale pools are given. Pairs with an id outside
+// [0, NB) or src == dst are skipped.
+__global__ __launch_bounds__(256) void kv_copy_blocks_kernel(CopyBlocksArgs a, int pieces_per_block,
+                                                             long long total) {
+  const long long stride = (long long)gridDim.x * blockDim.x;
+  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
+    const int pair = (int)(i / (2 * pieces_per_block));
+    const int rem = (int)(i - (long long)pair * 2 * pieces_per_block);
+    const int which = rem >= pieces_per_block;  // 0 = K, 1 = V
+    const int piece = rem - which * pieces_per_block;
+    const int src = a.src[pair], dst = a.dst[pair];
+    if (src < 0 || src >= a.nb || dst < 0 || dst >= a.nb || src == dst) continue;
+    const long long bytes = (long long)pieces_per_block * 16;
+    const char* from = (const char*)(which ? a.v_pool : a.k_pool) + (long long)src * bytes + (long long)piece * 16;
+    char* to = (char*)(which ? a.v_pool : a.k_pool) + (long long)dst * bytes + (long long)piece * 16;
+    *reinterpret_cast<u32x4*>(to) = load16(from);
+    if (a.k_scale && piece < a.Hkv * a.B) {  // one fp32 scale per row: [NB, Hkv, B]
+      float* sp = which ? a.v_scale : a.k_scale;
+      sp[(long long)dst * a.Hkv * a.B + piece] = sp[(long long)src * a.Hkv * a.B + piece];
+    }
+  }
+}
+
+hipError_t launch_kv_copy_blocks(const CopyBlocksArgs& a, hipStream_t st) {
+  if (a.n == 0) return hipSuccess;
+  const int pieces = a.B * a.Hkv * a.D * a.elem_bytes / 16;
+  const long long total = (long long)a.n * 2 * pieces;
+  long long blocks = (total + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(kv_copy_blocks_kernel, dim3((unsigned)blocks), dim3(256), 0, st, a, pieces, total);
+  return hipGetLastError();
+}
+
 bool kv_write_quant_supported(int kv_dtype, int in_dtype, int D) {
   return (kv_dtype == 3 || kv_dtype == 4) && (in_dtype == 0 || in_dtype == 1 || in_dtype == 2) &&
          (D == 64 || D == 128);

@@ -33,6 +33,16 @@ struct WriteQuantArgs {
   int32_t num_tokens, num_seqs, mb, nb, B, Hkv, D, kv_dtype, in_dtype;
 };
 
+struct CopyBlocksArgs {
+  void* k_pool;
+  void* v_pool;
+  float* k_scale;  // 8-bit pools: [NB, Hkv, B] row scales, copied along; else null
+  float* v_scale;
+  const int32_t* src;
+  const int32_t* dst;
+  int32_t n, nb, B, Hkv, D, elem_bytes;
+};
+
 struct DecodeArgs {
   float* out;
   float* lse;
@@ -51,6 +61,10 @@ struct DecodeArgs {
   int32_t n_workers;  // wavefronts the attended blocks are divided among
   float scale;
   int32_t sinks;      // with a window: positions below this are attended too
+  // Mixed batches: null for plain decode. Otherwise [S + 1] row offsets of a
+  // prefill-style batch; sequence s is a decode row iff it has exactly one
+  // row, which is q/out/lse row q_start[s]; other sequences are left alone.
+  const int32_t* q_start;
 };
 
 struct PrefillArgs {
@@ -65,11 +79,13 @@ struct PrefillArgs {
   int32_t S, H, Hkv, D, B, mb, nb, window, dtype, max_q_len, max_context_len;
   float scale;
   int32_t sinks;      // with a window: positions below this are attended too
+  int32_t skip_single;  // mixed batches: sequences with one row are left to decode
 };
 
 hipError_t launch_kv_write(const WriteArgs& a, hipStream_t st);
 bool kv_write_quant_supported(int kv_dtype, int in_dtype, int D);
 hipError_t launch_kv_write_quant(const WriteQuantArgs& a, hipStream_t st);
+hipError_t launch_kv_copy_blocks(const CopyBlocksArgs& a, hipStream_t st);
 
 
 

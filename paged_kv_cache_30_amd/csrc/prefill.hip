@@ -195,6 +195,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a, float sc
   int L = a.lens[s];
   L = L < 0 ? 0 : (L > a.max_context_len ? a.max_context_len : L);
   if (qt * QT >= C || C > L) return;
+  if (a.skip_single && C == 1) return;  // a decode row of a mixed batch
   const int row0 = qt * QT + (wave / HPW) * 32;   // first chunk row of this wavefront
   const int wg_last = min(C, (qt + 1) * QT) - 1;  // last chunk row of the workgroup
   const int base = L - C;                         // position of chunk row 0

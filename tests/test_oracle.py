@@ -513,3 +513,17 @@ def test_planted_mistake_is_caught(name, monkeypatch):
         except Exception:
             failed.append(pin.__name__)
     assert failed, f"no pin catches the planted mistake {name}"
+
+
+def test_copy_blocks_definition():
+    """Copied blocks equal their sources byte for byte; every other block is
+    untouched; invalid pairs are skipped."""
+    rng = np.random.default_rng(3)
+    k = rng.standard_normal((6, 4, 2, 8)).astype(np.float32)
+    v = rng.standard_normal((6, 4, 2, 8)).astype(np.float32)
+    ks = rng.standard_normal((6, 2, 4)).astype(np.float32)
+    nk, nv, nks, _ = ref.copy_blocks(k, v, [1, 4, 9, 2], [3, 0, 2, 2], ks, ks.copy())
+    assert nk[3].tobytes() == k[1].tobytes() and nv[0].tobytes() == v[4].tobytes()
+    assert nks[3].tobytes() == ks[1].tobytes()
+    for b in (1, 2, 4, 5):
+        assert nk[b].tobytes() == k[b].tobytes() and nv[b].tobytes() == v[b].tobytes()
