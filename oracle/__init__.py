@@ -17,6 +17,10 @@ Two independent implementations:
   inputs, used to cross-check ``oracle.ref``.
 * ``oracle.quant`` - the 8-bit (INT8 / FP8 E4M3) row encoding of KV pages and
   decode over the decoded pools (float32 encoding steps, float64 attention).
+* ``oracle.compressed`` - the compressed-slot tier: mean-pooled slots of
+  evicted positions ("Build a Memory-Compressed Attention Engine with KV
+  Caching from Scratch", Steps 2-4), the paged compression step, decode over
+  slots plus the full tier, and the page's unpaged cache to compare against.
 
 Sources (the pages these follow, by title and section):
 
@@ -39,5 +43,8 @@ Parity-unpinned: none of the oracle's functions.  Every function is pinned by
 ``tests/test_oracle.py`` against closed forms, invariants, a library routine
 (``torch.nn.functional.scaled_dot_product_attention`` in float64) and the
 scalar brute force; the 8-bit encoding by ``tests/test_oracle_quant.py``
-(torch's float8_e4m3fn conversion, round-trip bounds, exact cases).
+(torch's float8_e4m3fn conversion, round-trip bounds, exact cases); the
+compressed tier by ``tests/test_oracle_compressed.py`` (numpy's casts, a
+hand-traced golden of the page's append procedure, closed forms, the plain
+decode it reduces to, the scalar brute force).
 """

@@ -109,3 +109,37 @@ def prefill(q, q_start, k_pool, v_pool, tables, lens, B, Hkv, window, scale, dty
                 rows.append(softmax_weighted(qv, keys, vals, scale)[0])
             out[r0 + i] = rows
     return out
+
+
+def decode_compressed(q, k_pool, v_pool, tables, lens, full_start, slot_tables, num_slots, B, Hkv, window,
+                      scale, dtype):
+    """Decode over a compressed-slot tier and a full tier: the positions t
+    with full_start <= t < L (and inside the window, if any) through the
+    block table, plus rows 0 .. num_slots-1 of the slot table (row r at
+    offset r % B of its block r // B).  Nested lists out[s][h][d], lse[s][h]."""
+    S, H, D = len(q), len(q[0]), len(q[0][0])
+    out, lse = [], []
+    for s in range(S):
+        L = int(lens[s])
+        fs = int(full_start[s])
+        rows, lrow = [], []
+        for h in range(H):
+            g = head_group(h, H, Hkv)
+            keys, vals = [], []
+            for t in range(L):
+                if t < fs or (window > 0 and L - t > window):
+                    continue
+                pb, off = slot(tables[s], t, B)
+                keys.append([value(k_pool[pb][off][g][d], dtype) for d in range(D)])
+                vals.append([value(v_pool[pb][off][g][d], dtype) for d in range(D)])
+            for r in range(int(num_slots[s])):
+                pb, off = slot(slot_tables[s], r, B)
+                keys.append([value(k_pool[pb][off][g][d], dtype) for d in range(D)])
+                vals.append([value(v_pool[pb][off][g][d], dtype) for d in range(D)])
+            qv = [value(q[s][h][d], dtype) for d in range(D)]
+            o, l = softmax_weighted(qv, keys, vals, scale)
+            rows.append(o)
+            lrow.append(l)
+        out.append(rows)
+        lse.append(lrow)
+    return out, lse
