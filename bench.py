@@ -5,7 +5,9 @@ One step = one pass of the whole hot path over one batch of synthetic,
 seeded input already resident in HBM: write the step's new tokens' K/V into
 their pool slots through the block table (``paged_kv_write``), then attend
 (``paged_attn_decode`` for the decode workloads, ``paged_attn_prefill`` for
-the chunked-prefill one).  W untimed warm-up steps, then exactly K timed
+the chunked-prefill one, ``paged_attn_decode_compressed`` for the
+compressed-slot tier, whose step first compresses as many groups as a steady
+state averages per step with ``paged_kv_compress``).  W untimed warm-up steps, then exactly K timed
 steps between two device synchronisations; HIP events on the launch stream
 also time the write and the attention call of every step (called eagerly:
 the host enqueues ahead of the GPU; ``--graph`` replays them as HIP graphs).
@@ -46,11 +48,16 @@ def decode_bytes(w, kv: str = "native") -> dict:
     S, H, D, B = w.num_seqs, w.num_heads, w.head_dim, w.block_size
     L = w.context_lens.astype(np.int64)
     lo = np.maximum(0, L - w.window) if w.window > 0 else np.zeros_like(L)
+    slot_blocks = 0
+    if w.full_start is not None:
+        lo = np.maximum(lo, np.minimum(w.full_start.astype(np.int64), L))
+        slot_blocks = int(((w.num_slots.astype(np.int64) + B - 1) // B).sum())
     blocks = np.where(L > 0, (L + B - 1) // B - lo // B, 0)
     kv_bytes = w.kv_bytes_attended()
     if kv != "native":
         kv_bytes = kv_bytes // (D * eb) * (D + 4)
-    attend = (kv_bytes + S * H * D * eb + S * H * D * 4 + S * H * 4 + int(blocks.sum()) * 4 + S * 4)
+    attend = (kv_bytes + S * H * D * eb + S * H * D * 4 + S * H * 4 + (int(blocks.sum()) + slot_blocks) * 4 +
+              S * 4 * (1 if w.full_start is None else 3))
     T = int((L > 0).sum())
     stored = D * eb if kv == "native" else D + 4
     write = T * w.num_kv_heads * 2 * (D * eb + stored) + T * 8 + T * 4
@@ -68,6 +75,20 @@ def prefill_flop(w) -> int:
             n = p + 1 if w.window <= 0 else min(p + 1, w.window)
             total += n
     return 4 * w.head_dim * w.num_heads * total
+
+
+def steady_compressions(w):
+    """Compressions of a step of the tier workload in its steady state: a
+    sequence compresses once every window/2 = 128 appended positions, so a
+    step of S sequences averages S / 128 of them. Op i averages the group
+    [full_start, full_start + 128) of sequence i (8 blocks, always inside its
+    full tier) into ring row 0 of its slot table: the same bytes as a real
+    compression, and idempotent, so repeated steps see the same state."""
+    import numpy as np
+    B, half = w.block_size, 128
+    n = max(1, round(w.num_seqs / half))
+    src = np.stack([w.block_tables[i, w.full_start[i] // B:w.full_start[i] // B + half // B] for i in range(n)])
+    return src.astype(np.int32), w.slot_tables[:n, 0].astype(np.int32), np.zeros(n, np.int32)
 
 
 def pkv_workers(d) -> int:
@@ -101,6 +122,7 @@ def cpu_baseline(w, target_s: float):
     """fp64 oracle on the host, one thread, on the first sequences of the
     workload until about target_s seconds of work (whole workload if less)."""
     import numpy as np
+    import oracle.compressed as oc
     import oracle.ref as ref
     try:
         from threadpoolctl import threadpool_limits
@@ -114,7 +136,15 @@ def cpu_baseline(w, target_s: float):
     with ctx:
         while done < w.num_seqs and elapsed < target_s:
             t = time.perf_counter()
-            if w.kind == "decode":
+            if w.kind == "decode" and w.full_start is not None:
+                s = [done]
+                oc.decode_compressed(w.q[s], kp, vp, w.block_tables[s], w.context_lens[s], w.full_start[s],
+                                     w.slot_tables[s], w.num_slots[s], block_size=w.block_size,
+                                     num_kv_heads=w.num_kv_heads, window=w.window, scale=w.scale, dtype=w.dtype)
+                L = int(w.context_lens[done])
+                n = L - max(int(w.full_start[done]), L - w.window if w.window > 0 else 0) + int(w.num_slots[done])
+                units += n * w.num_kv_heads * w.head_dim * 2 * eb
+            elif w.kind == "decode":
                 ref.decode(w.q, kp, vp, w.block_tables, w.context_lens, block_size=w.block_size,
                            num_kv_heads=w.num_kv_heads, window=w.window, scale=w.scale, dtype=w.dtype,
                            seqs=[done])
@@ -213,9 +243,10 @@ def main(argv=None) -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5],
+    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5, 6],
                     help="workload: 1 tiny fp32 decode, 2 batched MHA decode (default), 3 long GQA decode, "
-                         "4 sliding-window decode, 5 chunked prefill over a shared prefix")
+                         "4 sliding-window decode, 5 chunked prefill over a shared prefix, 6 decode over a "
+                         "compressed-slot tier (window 256, 16 slots)")
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--workers", type=int, default=0, help="decode wavefront workers (0 = automatic)")
     ap.add_argument("--kv", choices=["native", "i8", "fp8"], default="native",
@@ -256,6 +287,12 @@ def main(argv=None) -> int:
         print("8-bit pools (--kv) are decode only", file=sys.stderr)
         return 2
     d = session.DeviceWorkload(w, num_workers=args.workers, kv_format=args.kv)
+    comp_bytes = 0
+    if w.full_start is not None:
+        src_b, dst_b, dst_s = steady_compressions(w)
+        d.set_compress_ops(src_b, dst_b, dst_s)
+        row = w.num_kv_heads * w.head_dim * {"f32": 4, "f16": 2, "bf16": 2}[w.dtype]
+        comp_bytes = src_b.size * w.block_size * row * 2 + len(dst_b) * row * 2 + src_b.size * 4 + len(dst_b) * 8
     torch.cuda.synchronize()
     if args.calibration_copy_mib:
         # A plain device copy of known size, for scaling HBM byte counters.
@@ -272,12 +309,16 @@ def main(argv=None) -> int:
 
     # The step's two calls, replayed as HIP graphs (no host launch gaps) or
     # called eagerly.
+    def prep():  # compressions (tier workload only), then the write
+        d.compress_step()
+        d.write_step()
+
     if not args.graph:
-        do_write, do_attend = d.write_step, d.attend
+        do_write, do_attend = prep, d.attend
     else:
         g_write, g_attend = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
         with torch.cuda.graph(g_write):
-            d.write_step()
+            prep()
         with torch.cuda.graph(g_attend):
             d.attend()
         torch.cuda.synchronize()
@@ -318,7 +359,7 @@ def main(argv=None) -> int:
 
     if w.kind == "decode":
         by = decode_bytes(w, args.kv)
-        step_units = by["attend"] + by["write"]
+        step_units = by["attend"] + by["write"] + comp_bytes
         value = step_units / (ms_step * 1e-3) / 1e9
         unit = "GB/s"
         achieved = by["attend"] / (att_mean * 1e-3) / 1e9
@@ -327,6 +368,8 @@ def main(argv=None) -> int:
         roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_for(key, src)}
         n_part_info = {"decode_workers": d.num_workers or pkv_workers(d), "kv_pool": args.kv}
+        if w.full_start is not None:
+            n_part_info.update(compressions_per_step=int(len(d.compress_ops[1])), tier_window=256, max_slots=16)
     else:
         flop = prefill_flop(w)
         value = flop / (ms_step * 1e-3) / 1e12
@@ -359,7 +402,7 @@ def main(argv=None) -> int:
                    "total_context": int(w.context_lens.sum()), "seed": w.seed, **n_part_info},
         "roofline": roof,
         "timing": {"attend_ms_mean": round(att_mean, 5), "attend_ms_median": round(att_med, 5),
-                   "attend_ms_min": round(attend_ms[0], 5), "write_ms_mean": round(sum(write_ms) / K, 5),
+                   "attend_ms_min": round(attend_ms[0], 5), "write_ms_mean": round(sum(write_ms) / K, 5),  # with the compressions of the tier workload
                    "wall_s_timed": round(wall, 4), "mode": timing_mode, "flush_mib": args.flush_mib,
                    "source_hash": src},
     }

@@ -296,6 +296,53 @@ int paged_attn_mixed(const pkv_geometry_t* geom, float* out, float* lse, const v
                      int32_t max_context_len, int32_t window, int32_t num_sinks, float scale,
                      int32_t num_workers, void* workspace, size_t workspace_bytes, void* stream);
 
+/* paged_kv_compress - compress groups of whole blocks into slots ("Build a
+ * Memory-Compressed Attention Engine with KV Caching from Scratch", Step 2:
+ * a group of positions is summarised by the mean of its keys and the mean
+ * of its values, per head; Step 3: the oldest half of a full window becomes
+ * one slot). Op i replaces row dst_slot[i] of block dst_block[i] (every kv
+ * head, K and V) with the mean of all B rows of each block
+ * src_blocks[i * blocks_per_slot .. (i + 1) * blocks_per_slot).
+ *
+ *   k_pool, v_pool    [NB, B, Hkv, D] PKV_F32 / PKV_F16 / PKV_BF16, in place
+ *   src_blocks        int32 [num_ops, blocks_per_slot] block ids
+ *   dst_block         int32 [num_ops] block id of the slot row
+ *   dst_slot          int32 [num_ops] row inside it, 0 .. B-1
+ * The mean is computed in float64 (the sum is exact for rows whose
+ * magnitudes span fewer than about 53 - 24 - log2(rows) binades), divided
+ * by the number of rows and rounded once to the pool type (nearest, ties to
+ * even). Source ids outside [0, NB) are left out of the mean; an op with no
+ * valid source, or a destination outside the pool, writes nothing. A row a
+ * call writes must not lie in a block any op of the same call reads. Run it
+ * before reusing the source blocks (stream order). 8-bit pools:
+ * PKV_EUNSUPPORTED. blocks_per_slot * B at most 2^24. */
+int paged_kv_compress(const pkv_geometry_t* geom, void* k_pool, void* v_pool, const int32_t* src_blocks,
+                      int32_t blocks_per_slot, const int32_t* dst_block, const int32_t* dst_slot, int32_t num_ops,
+                      void* stream);
+
+/* paged_attn_decode_compressed - single-query decode over two tiers ("Build
+ * a Memory-Compressed Attention Engine with KV Caching from Scratch",
+ * Component Breakdown and Step 4: the query attends the full-resolution
+ * window and the compressed slots together, one softmax over both).
+ *
+ * Arguments as paged_attn_decode (no sinks), plus per sequence s:
+ *   full_start   int32 [num_seqs]  first position still held at full
+ *                resolution; positions [max(full_start, L - window), L) are
+ *                attended through block_tables (clamped to [0, L])
+ *   slot_tables  int32 [num_seqs, max_slot_blocks]  blocks holding slot rows;
+ *                slot row r of s is row r % B of block slot_tables[s][r / B]
+ *   num_slots    int32 [num_seqs]  slot rows [0, num_slots) are attended
+ *                (clamped to [0, max_slot_blocks * B])
+ * Size the workspace with paged_attn_decode_workspace_bytes(num_seqs,
+ * max_context_len, window, 0, num_workers). Table entries outside [0, NB)
+ * of attended blocks are skipped. PKV_F32 / PKV_F16 / PKV_BF16 pools. */
+int paged_attn_decode_compressed(const pkv_geometry_t* geom, float* out, float* lse, const void* q,
+                                 const void* k_pool, const void* v_pool, const int32_t* block_tables,
+                                 int32_t max_blocks_per_seq, const int32_t* context_lens, const int32_t* full_start,
+                                 const int32_t* slot_tables, int32_t max_slot_blocks, const int32_t* num_slots,
+                                 int32_t num_seqs, int32_t max_context_len, int32_t window, float scale,
+                                 int32_t num_workers, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Name of a status code (static string). */
 const char* pkv_status_string(int status);
 

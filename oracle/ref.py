@@ -315,6 +315,12 @@ def build_pools(w, *, poison=True, include_step=True):
     if include_step:
         si, pos, k, v = w.step_tokens()
         k_pool, v_pool = kv_write(k_pool, v_pool, k, v, si, pos, w.block_tables, w.block_size)
+    if getattr(w, "slot_kv", None) is not None:
+        # compressed slots: slot row r of s sits where position r would
+        # through the slot table (row r % B of block slot_tables[s, r // B])
+        for s, e in enumerate(w.slot_kv):
+            if e.k.shape[0]:
+                k_pool, v_pool = kv_write_run(k_pool, v_pool, e.k, e.v, s, 0, w.slot_tables, w.block_size)
     return k_pool, v_pool
 
 

@@ -31,8 +31,8 @@ _QUANT = (torch.int8, torch.float8_e4m3fn)
 # Every symbol declared in include/paged_attn.h.
 EXPORTS = ("paged_kv_write", "paged_attn_decode_workspace_bytes", "paged_attn_decode_workers",
            "paged_attn_decode", "paged_attn_prefill", "paged_kv_write_quant", "paged_attn_decode_quant",
-           "paged_kv_copy_blocks", "paged_attn_mixed", "pkv_status_string", "pkv_last_hip_error",
-           "pkv_version")
+           "paged_kv_copy_blocks", "paged_attn_mixed", "paged_kv_compress", "paged_attn_decode_compressed",
+           "pkv_status_string", "pkv_last_hip_error", "pkv_version")
 
 
 class Geometry(ctypes.Structure):
@@ -74,6 +74,11 @@ def _load() -> ctypes.CDLL:
     lib.paged_kv_copy_blocks.restype = ctypes.c_int
     lib.paged_attn_mixed.argtypes = [G, P, P, P, P, P, P, P, I32, P, I32, I32, I32, I32, I32, F, I32, P, SZ, P]
     lib.paged_attn_mixed.restype = ctypes.c_int
+    lib.paged_kv_compress.argtypes = [G, P, P, P, I32, P, P, I32, P]
+    lib.paged_kv_compress.restype = ctypes.c_int
+    lib.paged_attn_decode_compressed.argtypes = [G, P, P, P, P, P, P, I32, P, P, P, I32, P, I32, I32, I32, F, I32,
+                                                 P, SZ, P]
+    lib.paged_attn_decode_compressed.restype = ctypes.c_int
     lib.pkv_status_string.argtypes = [ctypes.c_int]
     lib.pkv_status_string.restype = ctypes.c_char_p
     lib.pkv_last_hip_error.argtypes = []
@@ -413,3 +418,84 @@ def paged_attn_mixed(out, q, q_start, k_pool, v_pool, block_tables, context_lens
     bind_mixed(out, q, q_start, k_pool, v_pool, block_tables, context_lens, max_q_len, max_context_len,
                window=window, scale=scale, num_workers=num_workers, workspace=workspace, lse=lse,
                sinks=sinks)(stream)
+
+
+# ------------------------------------------------------- compressed slots
+
+def bind_kv_compress(k_pool, v_pool, src_blocks, dst_block, dst_slot):
+    """Check and marshal the arguments of ``paged_kv_compress`` once; returns
+    a callable ``f(stream=None)``."""
+    _dev(k_pool, "k_pool", ndim=4)
+    _dev(v_pool, "v_pool", dtype=k_pool.dtype)
+    if v_pool.shape != k_pool.shape:
+        raise ValueError("k_pool and v_pool differ in shape")
+    _dev(src_blocks, "src_blocks", dtype=torch.int32, ndim=2)
+    _dev(dst_block, "dst_block", dtype=torch.int32, ndim=1)
+    _dev(dst_slot, "dst_slot", dtype=torch.int32, ndim=1)
+    n = dst_block.shape[0]
+    if dst_slot.shape[0] != n or src_blocks.shape[0] != n:
+        raise ValueError("src_blocks, dst_block and dst_slot need one entry (row) per op")
+    g = geometry(k_pool, k_pool.shape[2])
+    args = (ctypes.byref(g), _ptr(k_pool), _ptr(v_pool), _ptr(src_blocks), max(int(src_blocks.shape[1]), 1),
+            _ptr(dst_block), _ptr(dst_slot), n)
+    keep = (g, k_pool, v_pool, src_blocks, dst_block, dst_slot)
+
+    def call(stream=None):
+        _check(LIB.paged_kv_compress(*args, _stream(stream)), "paged_kv_compress")
+    call.keep = keep
+    return call
+
+
+def paged_kv_compress(k_pool, v_pool, src_blocks, dst_block, dst_slot, stream=None) -> None:
+    """C ``paged_kv_compress``: op i writes the mean of every row of blocks
+    src_blocks[i, :] into row dst_slot[i] of block dst_block[i]."""
+    bind_kv_compress(k_pool, v_pool, src_blocks, dst_block, dst_slot)(stream)
+
+
+def bind_decode_compressed(out, q, k_pool, v_pool, block_tables, context_lens, full_start, slot_tables, num_slots,
+                           max_context_len, *, window=0, scale, num_workers=0, workspace=None, lse=None):
+    """Check and marshal the arguments of ``paged_attn_decode_compressed``
+    once; returns a callable ``f(stream=None)``."""
+    _dev(q, "q", dtype=k_pool.dtype, ndim=3)
+    _dev(out, "out", dtype=torch.float32, ndim=3)
+    _dev(k_pool, "k_pool", ndim=4)
+    _dev(v_pool, "v_pool", dtype=k_pool.dtype)
+    _dev(block_tables, "block_tables", dtype=torch.int32, ndim=2)
+    _dev(context_lens, "context_lens", dtype=torch.int32, ndim=1)
+    _dev(full_start, "full_start", dtype=torch.int32, ndim=1)
+    _dev(slot_tables, "slot_tables", dtype=torch.int32, ndim=2)
+    _dev(num_slots, "num_slots", dtype=torch.int32, ndim=1)
+    S, H, D = q.shape
+    if (out.shape != q.shape or context_lens.shape[0] != S or block_tables.shape[0] != S
+            or full_start.shape[0] != S or slot_tables.shape[0] != S or num_slots.shape[0] != S):
+        raise ValueError("shape mismatch between q, out and the per-sequence arrays")
+    if lse is not None:
+        _dev(lse, "lse", dtype=torch.float32, ndim=2)
+        if lse.shape != (S, H):
+            raise ValueError("lse must be [S, H]")
+    ws_bytes = 0
+    if workspace is not None:
+        _dev(workspace, "workspace")
+        ws_bytes = workspace.numel() * workspace.element_size()
+    g = geometry(k_pool, H)
+    args = (ctypes.byref(g), _ptr(out), _ptr(lse), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables),
+            block_tables.shape[1], _ptr(context_lens), _ptr(full_start), _ptr(slot_tables), slot_tables.shape[1],
+            _ptr(num_slots), S, int(max_context_len), int(window), float(scale), int(num_workers),
+            _ptr(workspace), ws_bytes)
+    keep = (g, out, q, k_pool, v_pool, block_tables, context_lens, full_start, slot_tables, num_slots, workspace,
+            lse)
+
+    def call(stream=None):
+        _check(LIB.paged_attn_decode_compressed(*args, _stream(stream)), "paged_attn_decode_compressed")
+    call.keep = keep
+    return call
+
+
+def paged_attn_decode_compressed(out, q, k_pool, v_pool, block_tables, context_lens, full_start, slot_tables,
+                                 num_slots, max_context_len, *, window=0, scale, num_workers=0, workspace=None,
+                                 lse=None, stream=None) -> None:
+    """C ``paged_attn_decode_compressed``: decode over compressed slots and
+    the full-resolution positions [full_start, L)."""
+    bind_decode_compressed(out, q, k_pool, v_pool, block_tables, context_lens, full_start, slot_tables, num_slots,
+                           max_context_len, window=window, scale=scale, num_workers=num_workers,
+                           workspace=workspace, lse=lse)(stream)

@@ -127,11 +127,20 @@ size_t paged_attn_decode_workspace_bytes(const pkv_geometry_t* geom, int32_t num
 
 namespace {
 
+// Compressed slots of a decode call (all null for plain decode).
+struct SlotArgs {
+  const int32_t* full_start = nullptr;
+  const int32_t* slot_tables = nullptr;
+  const int32_t* num_slots = nullptr;
+  int32_t max_slot_blocks = 0;
+};
+
 int decode_common(const pkv_geometry_t* geom, float* out, float* lse, const void* q, int q_dtype,
                   const void* k_pool, const void* v_pool, const float* k_scale, const float* v_scale,
                   const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
                   int32_t num_seqs, int32_t max_context_len, int32_t window, int32_t num_sinks, float scale,
-                  int32_t num_workers, void* workspace, size_t workspace_bytes, void* stream) {
+                  int32_t num_workers, void* workspace, size_t workspace_bytes, void* stream,
+                  const SlotArgs& slots = SlotArgs()) {
   if (num_seqs < 0 || max_blocks_per_seq <= 0 || max_context_len < 0 || window < 0 || num_sinks < 0 ||
       num_workers < 0 || !isfinite(scale))
     return PKV_EINVAL;
@@ -152,7 +161,8 @@ int decode_common(const pkv_geometry_t* geom, float* out, float* lse, const void
                     (int32_t*)ws, (float*)(ws + sp.cum_bytes), (float*)(ws + sp.cum_bytes + sp.ml_bytes),
                     num_seqs, geom->num_heads, geom->num_kv_heads, geom->head_dim, geom->block_size,
                     max_blocks_per_seq, geom->num_blocks, window, geom->kv_dtype, max_context_len,
-                    sp.workers, scale, num_sinks};
+                    sp.workers, scale, num_sinks, nullptr, slots.full_start, slots.slot_tables,
+                    slots.num_slots, slots.max_slot_blocks};
   return hip_status(pkv::launch_decode(a, (hipStream_t)stream));
 }
 
@@ -287,6 +297,42 @@ int paged_attn_mixed(const pkv_geometry_t* geom, float* out, float* lse, const v
   return hip_status(pkv::launch_prefill(pa, (hipStream_t)stream));
 }
 
+int paged_kv_compress(const pkv_geometry_t* geom, void* k_pool, void* v_pool, const int32_t* src_blocks,
+                      int32_t blocks_per_slot, const int32_t* dst_block, const int32_t* dst_slot, int32_t num_ops,
+                      void* stream) {
+  int st = check_geometry(geom);
+  if (st) return st;
+  if (is_quant(geom->kv_dtype)) return PKV_EUNSUPPORTED;
+  if (num_ops < 0 || blocks_per_slot <= 0 || (long long)blocks_per_slot * geom->block_size > (1 << 24))
+    return PKV_EINVAL;
+  if (num_ops == 0) return PKV_OK;
+  if (!k_pool || !v_pool || !src_blocks || !dst_block || !dst_slot) return PKV_EINVAL;
+  pkv::CompressArgs a{k_pool, v_pool, src_blocks, dst_block, dst_slot, num_ops, blocks_per_slot,
+                      geom->num_blocks, geom->block_size, geom->num_kv_heads, geom->head_dim, geom->kv_dtype};
+  return hip_status(pkv::launch_kv_compress(a, (hipStream_t)stream));
+}
+
+int paged_attn_decode_compressed(const pkv_geometry_t* geom, float* out, float* lse, const void* q,
+                                 const void* k_pool, const void* v_pool, const int32_t* block_tables,
+                                 int32_t max_blocks_per_seq, const int32_t* context_lens, const int32_t* full_start,
+                                 const int32_t* slot_tables, int32_t max_slot_blocks, const int32_t* num_slots,
+                                 int32_t num_seqs, int32_t max_context_len, int32_t window, float scale,
+                                 int32_t num_workers, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_geometry(geom);
+  if (st) return st;
+  if (is_quant(geom->kv_dtype)) return PKV_EUNSUPPORTED;
+  if (max_slot_blocks <= 0) return PKV_EINVAL;
+  if (num_seqs > 0 && (!full_start || !slot_tables || !num_slots)) return PKV_EINVAL;
+  SlotArgs slots;
+  slots.full_start = full_start;
+  slots.slot_tables = slot_tables;
+  slots.num_slots = num_slots;
+  slots.max_slot_blocks = max_slot_blocks;
+  return decode_common(geom, out, lse, q, geom->kv_dtype, k_pool, v_pool, nullptr, nullptr, block_tables,
+                       max_blocks_per_seq, context_lens, num_seqs, max_context_len, window, 0, scale, num_workers,
+                       workspace, workspace_bytes, stream, slots);
+}
+
 const char* pkv_status_string(int status) {
   switch (status) {
     case PKV_OK: return "PKV_OK";
@@ -300,6 +346,6 @@ const char* pkv_status_string(int status) {
 
 int pkv_last_hip_error(void) { return g_last_hip_error; }
 
-int pkv_version(void) { return 310; }
+int pkv_version(void) { return 400; }
 
 }  // extern "C"

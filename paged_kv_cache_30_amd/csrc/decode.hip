@@ -101,23 +101,56 @@ struct DecodeShape {
   static_assert(LPR >= 4 && LPR <= 32 && B % CHUNK == 0, "shape");
 };
 
-// Attended blocks of a sequence, L clamped to [0, max_ctx] and
-// lo = max(0, L - window) with a window: sb sink blocks [0, sb) (those
-// holding positions below min(sinks, lo) that lie before the window's first
-// block), then the window's blocks [wb0, ceil(L / B)), wb0 = lo / B.
-// Entry i of this list is logical block i < sb ? i : wb0 + (i - sb).
+// Attended blocks of sequence s, L clamped to [0, max_ctx]. The full-
+// resolution positions are [lo, L): lo = max(0, L - window) with a window,
+// raised to full_start[s] with compressed slots. The list of attended blocks
+// starts with sb prefix entries read from ptab, then the blocks [wb0,
+// ceil(L / B)) of the sequence's table, wb0 = lo / B. Prefix entry i holds
+// rows [i*B, (i+1)*B) of which those below plim are attended:
+//  - sinks: ptab is the sequence's own table and the prefix is the blocks
+//    holding positions below min(sinks, lo) before the window's first block;
+//  - compressed slots: ptab is the sequence's slot table and the prefix the
+//    ceil(num_slots / B) blocks holding ring rows [0, num_slots).
+// Entry i of the list is block(i) of its table.
 struct Attended {
-  int L, lo, sb, wb0, nblk;
+  int L, lo, sb, wb0, nblk, plim;
+  const int32_t* ptab;
   __device__ __forceinline__ int block(int i) const { return i < sb ? i : wb0 + (i - sb); }
+  __device__ __forceinline__ int32_t entry(const int32_t* trow, int i) const {
+    return i < sb ? ptab[i] : trow[wb0 + (i - sb)];
+  }
+  // Keep the fields in scalar registers where the sequence is the same for
+  // the whole wavefront.
+  __device__ __forceinline__ void uniformize() {
+    L = uniform(L);
+    lo = uniform(lo);
+    sb = uniform(sb);
+    wb0 = uniform(wb0);
+    nblk = uniform(nblk);
+    plim = uniform(plim);
+    const uint64_t p = (uint64_t)(uintptr_t)ptab;
+    ptab = (const int32_t*)(uintptr_t)(((uint64_t)(uint32_t)uniform((int)(p >> 32)) << 32) |
+                                       (uint32_t)uniform((int)(uint32_t)p));
+  }
 };
-__device__ __forceinline__ Attended attended(int L, int max_ctx, int window, int sinks, int B) {
+__device__ __forceinline__ Attended attended(const DecodeArgs& a, int s, int L, int B) {
   Attended r;
-  L = L < 0 ? 0 : (L > max_ctx ? max_ctx : L);
+  L = L < 0 ? 0 : (L > a.max_context_len ? a.max_context_len : L);
   r.L = L;
-  r.lo = window > 0 ? max(0, L - window) : 0;
-  r.wb0 = r.lo / B;
-  r.sb = (window > 0 && sinks > 0 && L > 0) ? min((min(sinks, r.lo) + B - 1) / B, r.wb0) : 0;
-  r.nblk = L > 0 ? (L + B - 1) / B - r.wb0 + r.sb : 0;
+  r.lo = a.window > 0 ? max(0, L - a.window) : 0;
+  if (a.num_slots) {
+    r.lo = max(r.lo, min(max(a.full_start[s], 0), L));
+    r.wb0 = r.lo / B;
+    r.plim = min(max(a.num_slots[s], 0), a.msb * B);
+    r.sb = (r.plim + B - 1) / B;
+    r.ptab = a.slot_tables + (size_t)s * a.msb;
+  } else {
+    r.wb0 = r.lo / B;
+    r.plim = a.sinks;
+    r.sb = (a.window > 0 && a.sinks > 0 && L > 0) ? min((min(a.sinks, r.lo) + B - 1) / B, r.wb0) : 0;
+    r.ptab = a.tables + (size_t)s * a.mb;
+  }
+  r.nblk = (L > 0 ? (L + B - 1) / B - r.wb0 : 0) + r.sb;
   return r;
 }
 
@@ -142,7 +175,7 @@ __device__ void prefix_blocks(const DecodeArgs& a, int32_t* cum) {
   for (int base = 0; base < a.S; base += NT) {
     const int s = base + tid;
     int v = 0;
-    if (s < a.S) v = attended(decode_len(a, s), a.max_context_len, a.window, a.sinks, a.B).nblk;
+    if (s < a.S) v = attended(a, s, decode_len(a, s), a.B).nblk;
     int x = v;  // inclusive scan inside the wavefront
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -197,7 +230,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, fl
     int v = 0;
     if (lane < a.S) {
       len_reg = decode_len(a, lane);
-      v = attended(len_reg, a.max_context_len, a.window, a.sinks, B).nblk;
+      v = attended(a, lane, len_reg, B).nblk;
     }
     int x = v;
 #pragma unroll
@@ -263,11 +296,12 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, fl
     const long long seg_end = min(end, (long long)Hkv * c0 + (long long)(g + 1) * nblk);
     const int n = (int)(seg_end - pos);
 
-    const Attended at = attended(len_of(s), a.max_context_len, a.window, a.sinks, B);
+    Attended at = attended(a, s, len_of(s), B);
+    at.uniformize();
     const int L = at.L, lo = at.lo;
     const int32_t* trow = a.tables + (size_t)s * a.mb;
     // table entries of attended blocks b_first .. b_first + 63 of the segment
-    int tv = lane < n ? trow[at.block(b_first + lane)] : -1;
+    int tv = lane < n ? at.entry(trow, b_first + lane) : -1;
 
     const char* qb = (const char*)a.q + ((size_t)(q_row(a, s) * H + g * G) * D + c * E) * QB;
     u32x4 qv[G][PC][QW];
@@ -310,7 +344,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, fl
     auto issue = [&](int k, u32x4 (*kr)[PC], u32x4 (*vr)[PC], float* ks, float* vs) -> bool {
       const int bi = k / CPB;
       const int sub = k - bi * CPB;
-      if ((bi & 63) == 0 && bi > 0 && sub == 0) tv = bi + lane < n ? trow[at.block(b_first + bi + lane)] : -1;
+      if ((bi & 63) == 0 && bi > 0 && sub == 0) tv = bi + lane < n ? at.entry(trow, b_first + bi + lane) : -1;
       const int pb = __builtin_amdgcn_readlane(tv, bi & 63);
       if (pb < 0 || pb >= a.nb) return false;
       const size_t off = (size_t)pb * blk_stride + (size_t)sub * CHUNK * row_stride;
@@ -340,8 +374,10 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, fl
       const int bi = k / CPB;
       const int sub = k - bi * CPB;
       const int t0 = at.block(b_first + bi) * B + sub * CHUNK;
-      // attended: t in [lo, L), or t < sinks (below lo only with a window)
-      const bool full = (t0 >= lo || t0 + CHUNK <= a.sinks) && t0 + CHUNK <= L;
+      // attended: a prefix row below plim; otherwise t in [lo, L), or
+      // t < sinks (below lo only with a window)
+      const bool pre = b_first + bi < at.sb;
+      const bool full = pre ? t0 + CHUNK <= at.plim : (t0 >= lo || t0 + CHUNK <= a.sinks) && t0 + CHUNK <= L;
       float sc[CSTEPS][G];
 #pragma unroll
       for (int j = 0; j < CSTEPS; ++j) {
@@ -364,7 +400,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, fl
 #pragma unroll
         for (int j = 0; j < CSTEPS; ++j) {
           const int t = t0 + j * RPL + r;
-          const bool ok = (t >= lo || t < a.sinks) && t < L;
+          const bool ok = pre ? t < at.plim : (t >= lo || t < a.sinks) && t < L;
 #pragma unroll
           for (int h = 0; h < G; ++h) sc[j][h] = ok ? sc[j][h] : -INFINITY;
         }
@@ -395,7 +431,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, fl
 #pragma unroll
       for (int j = 0; j < CSTEPS; ++j) {
         const int t = t0 + j * RPL + r;
-        const bool ok = full || ((t >= lo || t < a.sinks) && t < L);
+        const bool ok = full || (pre ? t < at.plim : (t >= lo || t < a.sinks) && t < L);
         if constexpr (QU) {
           // Weight of the row times its V scale (0 for a masked row, whose
           // scale may be unset); codes widened to code + BIAS.
@@ -480,9 +516,34 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, fl
         m[h] = M;
       }
     }
-    // One partial per head, slot w + s*Hkv + g (unique: see the merge).
-    const size_t slot = (size_t)w + (size_t)s * Hkv + g;
-    if (r == 0) {
+    if (b_first == 0 && n == nblk) {
+      // This wavefront holds the whole segment of (s, g): its state is final,
+      // so it writes the normalised output and log-sum-exp itself (the same
+      // arithmetic as the merge of a single partial) and the merge skips it.
+      if (r == 0) {
+        const size_t orow = (size_t)q_row(a, s) * H + (size_t)g * G;
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const float lh = l[h];
+#pragma unroll
+          for (int pc = 0; pc < PC; ++pc) {
+            float* dst = a.out + (orow + h) * D + pc * LPR * E + c * E;
+#pragma unroll
+            for (int e = 0; e < E; e += 4) {
+              float4 v;
+              v.x = lh > 0.f ? o[h][pc * E + e] / lh : 0.f;
+              v.y = lh > 0.f ? o[h][pc * E + e + 1] / lh : 0.f;
+              v.z = lh > 0.f ? o[h][pc * E + e + 2] / lh : 0.f;
+              v.w = lh > 0.f ? o[h][pc * E + e + 3] / lh : 0.f;
+              *reinterpret_cast<float4*>(dst + e) = v;
+            }
+          }
+          if (a.lse && c == 0) a.lse[orow + h] = lh > 0.f ? (m[h] + __log2f(lh)) * kLn2 : -INFINITY;
+        }
+      }
+    } else if (r == 0) {
+      // One partial per head, slot w + s*Hkv + g (unique: see the merge).
+      const size_t slot = (size_t)w + (size_t)s * Hkv + g;
 #pragma unroll
       for (int h = 0; h < G; ++h) {
 #pragma unroll
@@ -500,49 +561,97 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, fl
   }
 }
 
-// Merge of the partials of one (sequence, query head): one thread per output
-// element. With NW = min(workers, T) active wavefronts, wavefront w holds
-// [w*T/NW, (w+1)*T/NW) (never empty), so flattened index i lies in wavefront
-// ((i + 1) * NW - 1) / T and the range [x, y) of (s, g) is covered by
-// wavefronts w_lo .. w_hi, each of which wrote its partial of (s, g) in slot
-// w + s*Hkv + g. Within a wavefront those slots are distinct, and a later
-// wavefront's (s, g) is never earlier, so no two writers share a slot.
-template <int D, int G>
-__global__ __launch_bounds__(D) void decode_merge_kernel(DecodeArgs a) {
-  const int hq = blockIdx.x, s = blockIdx.y, d = threadIdx.x;
-  const int g = hq / G, hh = hq - g * G;
+// Merge of the partials of one (sequence, kv head) by gridDim.z wavefronts,
+// each holding every gridDim.z-th group of 64 of the G x D outputs of its
+// query heads (one wavefront when there are many pairs, so that pairs with
+// nothing to merge cost one short wavefront each). With NW = min(workers, T) active
+// wavefronts, wavefront w holds [w*T/NW, (w+1)*T/NW) (never empty), so
+// flattened index i lies in wavefront ((i + 1) * NW - 1) / T and the range
+// [x, y) of (s, g) is covered by wavefronts w_lo .. w_hi, each of which wrote
+// its partial of (s, g) in slot w + s*Hkv + g. Within a wavefront those slots
+// are distinct, and a later wavefront's (s, g) is never earlier, so no two
+// writers share a slot. When w_lo == w_hi that one wavefront wrote the
+// output itself and there is nothing to merge.
+template <int D, int G, int PER>
+__global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
+  // gridDim.z = G * D / (64 * PER) wavefronts per pair; lane t of wavefront
+  // z holds outputs t + 64 * (z + gridDim.z * k), k < PER.
+  const int g = blockIdx.x, s = blockIdx.y;
   const int Hkv = a.Hkv;
   if (a.q_start && a.q_start[s + 1] - a.q_start[s] != 1) return;  // a prefill chunk of a mixed batch
-  const size_t row = (size_t)q_row(a, s) * a.H + hq;
+  const size_t row0 = (size_t)q_row(a, s) * a.H + (size_t)g * G;
+  auto elem = [&](int k) { return 64 * (blockIdx.z + gridDim.z * k) + threadIdx.x; };
   const int c0 = a.ws_cum[s];
   const int nblk = a.ws_cum[s + 1] - c0;
-  float M = -INFINITY, sl = 0.f, so = 0.f;
-  if (nblk > 0) {
-    const long long total = (long long)Hkv * a.ws_cum[a.S];
-    const long long NW = total < a.n_workers ? total : a.n_workers;
-    const long long x = (long long)Hkv * c0 + (long long)g * nblk;
-    const long long y = x + nblk;
-    const int w_lo = (int)(((x + 1) * NW - 1) / total);
-    const int w_hi = (int)((y * NW - 1) / total);
-    const size_t base = ((size_t)s * Hkv + g) * G + hh;  // slot of worker 0, head hh
-    // Eight partials at a time, their loads issued together.
-    constexpr int U = 8;
-    for (int w0 = w_lo; w0 <= w_hi; w0 += U) {
+  if (nblk == 0) {  // nothing attended: zeros and log-sum-exp -inf
+#pragma unroll
+    for (int k = 0; k < PER; ++k) a.out[row0 * D + elem(k)] = 0.f;
+    if (a.lse && blockIdx.z == 0 && threadIdx.x < G) a.lse[row0 + threadIdx.x] = -INFINITY;
+    return;
+  }
+  const long long total = (long long)Hkv * a.ws_cum[a.S];
+  const long long NW = total < a.n_workers ? total : a.n_workers;
+  const long long x = (long long)Hkv * c0 + (long long)g * nblk;
+  const long long y = x + nblk;
+  const int w_lo = (int)(((x + 1) * NW - 1) / total);
+  const int w_hi = (int)((y * NW - 1) / total);
+  if (w_lo == w_hi) return;  // written by the split kernel
+  const int np = w_hi - w_lo + 1;
+  const size_t base0 = ((size_t)s * Hkv + g) * G + (size_t)w_lo * G;  // slot of worker w_lo, head 0
+  if (np <= 4) {
+    // Every load of the lane's outputs issued before any is used.
+    float2 ml[PER][4];
+    float ov[PER][4];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int i = elem(k), hh = i / D, d = i - hh * D;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const size_t slot = base0 + hh + (size_t)j * G;
+        const bool ok = j < np;
+        ml[k][j] = ok ? *reinterpret_cast<const float2*>(a.ws_ml + slot * 2) : make_float2(-INFINITY, 0.f);
+        ov[k][j] = ok ? a.ws_o[slot * D + d] : 0.f;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int i = elem(k), hh = i / D, d = i - hh * D;
+      float M = ml[k][0].x;
+#pragma unroll
+      for (int j = 1; j < 4; ++j) M = fmaxf(M, ml[k][j].x);
+      const float Ms = M == -INFINITY ? 0.f : M;
+      float sl = 0.f, so = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float f = __builtin_amdgcn_exp2f(ml[k][j].x - Ms);
+        sl = __builtin_fmaf(f, ml[k][j].y, sl);
+        so = __builtin_fmaf(f, ov[k][j], so);
+      }
+      a.out[(row0 + hh) * D + d] = sl > 0.f ? so / sl : 0.f;
+      if (a.lse && d == 0) a.lse[row0 + hh] = sl > 0.f ? (M + __log2f(sl)) * kLn2 : -INFINITY;
+    }
+    return;
+  }
+  constexpr int U = 8;  // partials whose loads are issued together
+  for (int k = 0; k < PER; ++k) {
+    const int i = elem(k), hh = i / D, d = i - hh * D;
+    const size_t base = base0 + hh;
+    float M = -INFINITY, sl = 0.f, so = 0.f;
+    for (int w0 = 0; w0 < np; w0 += U) {
       float mv[U];
 #pragma unroll
-      for (int j = 0; j < U; ++j)
-        mv[j] = w0 + j <= w_hi ? a.ws_ml[(base + (size_t)(w0 + j) * G) * 2] : -INFINITY;
+      for (int j = 0; j < U; ++j) mv[j] = w0 + j < np ? a.ws_ml[(base + (size_t)(w0 + j) * G) * 2] : -INFINITY;
 #pragma unroll
       for (int j = 0; j < U; ++j) M = fmaxf(M, mv[j]);
     }
     const float Ms = M == -INFINITY ? 0.f : M;
-    for (int w0 = w_lo; w0 <= w_hi; w0 += U) {
+    for (int w0 = 0; w0 < np; w0 += U) {
       float2 ml[U];
       float ov[U];
 #pragma unroll
       for (int j = 0; j < U; ++j) {
         const size_t slot = base + (size_t)(w0 + j) * G;
-        const bool ok = w0 + j <= w_hi;
+        const bool ok = w0 + j < np;
         ml[j] = ok ? *reinterpret_cast<const float2*>(a.ws_ml + slot * 2) : make_float2(-INFINITY, 0.f);
         ov[j] = ok ? a.ws_o[slot * D + d] : 0.f;
       }
@@ -553,9 +662,9 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(DecodeArgs a) {
         so = __builtin_fmaf(f, ov[j], so);
       }
     }
+    a.out[(row0 + hh) * D + d] = sl > 0.f ? so / sl : 0.f;
+    if (a.lse && d == 0) a.lse[row0 + hh] = sl > 0.f ? (M + __log2f(sl)) * kLn2 : -INFINITY;
   }
-  a.out[row * D + d] = sl > 0.f ? so / sl : 0.f;
-  if (a.lse && d == 0) a.lse[row] = sl > 0.f ? (M + __log2f(sl)) * kLn2 : -INFINITY;
 }
 
 template <class T, class Q, int D, int B, int G>
@@ -572,7 +681,14 @@ struct DecodeKernels {
                        a.scale * kLog2e);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((decode_merge_kernel<D, G>), dim3(a.H, a.S), dim3(D), 0, st, a);
+    // Many (sequence, kv head) pairs: one wavefront each; few: one per 64
+    // outputs, to spread the merge over more of the chip.
+    constexpr int PAIR = G * D / 64;
+    constexpr int PER = PAIR < 8 ? PAIR : 8;
+    if (a.Hkv * a.S >= 2048)
+      hipLaunchKernelGGL((decode_merge_kernel<D, G, PER>), dim3(a.Hkv, a.S, PAIR / PER), dim3(64), 0, st, a);
+    else
+      hipLaunchKernelGGL((decode_merge_kernel<D, G, 1>), dim3(a.Hkv, a.S, PAIR), dim3(64), 0, st, a);
     return hipGetLastError();
   }
   // Workgroups of the split kernel resident per compute unit.

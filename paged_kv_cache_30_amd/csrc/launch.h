@@ -43,6 +43,18 @@ struct CopyBlocksArgs {
   int32_t n, nb, B, Hkv, D, elem_bytes;
 };
 
+// Compression of groups of blocks into slot rows: op i averages every row of
+// blocks src[i * bps .. i * bps + bps) into row dst_slot[i] of block
+// dst_block[i], for K and V.
+struct CompressArgs {
+  void* k_pool;
+  void* v_pool;
+  const int32_t* src;
+  const int32_t* dst_block;
+  const int32_t* dst_slot;
+  int32_t n, bps, nb, B, Hkv, D, dtype;
+};
+
 struct DecodeArgs {
   float* out;
   float* lse;
@@ -65,6 +77,14 @@ struct DecodeArgs {
   // prefill-style batch; sequence s is a decode row iff it has exactly one
   // row, which is q/out/lse row q_start[s]; other sequences are left alone.
   const int32_t* q_start;
+  // Compressed slots: null for plain decode. Otherwise per sequence the
+  // first full-resolution position [S], the slot table [S, msb] and the
+  // number of valid ring rows [S]; decode attends those rows, then the
+  // positions [max(full_start, L - window), L).
+  const int32_t* full_start;
+  const int32_t* slot_tables;
+  const int32_t* num_slots;
+  int32_t msb;
 };
 
 struct PrefillArgs {
@@ -86,6 +106,7 @@ hipError_t launch_kv_write(const WriteArgs& a, hipStream_t st);
 bool kv_write_quant_supported(int kv_dtype, int in_dtype, int D);
 hipError_t launch_kv_write_quant(const WriteQuantArgs& a, hipStream_t st);
 hipError_t launch_kv_copy_blocks(const CopyBlocksArgs& a, hipStream_t st);
+hipError_t launch_kv_compress(const CompressArgs& a, hipStream_t st);
 
 
 

@@ -82,8 +82,15 @@ class DeviceWorkload:
         self.step_pos = int_tensor(pos, device)
         self.step_k = to_device(k, w.dtype, device)
         self.step_v = to_device(v, w.dtype, device)
+        self.compressed = getattr(w, "full_start", None) is not None
+        if self.compressed:
+            if kv_format != "native":
+                raise ValueError("compressed slots need 16-bit or fp32 pools")
+            self.full_start = int_tensor(w.full_start, device)
+            self.slot_tables = int_tensor(w.slot_tables, device)
+            self.num_slots = int_tensor(w.num_slots, device)
         self.workspace: Optional[torch.Tensor] = None
-        self._bound_write = self._bound_attend = None
+        self._bound_write = self._bound_attend = self._bound_compress = None
         self.set_workers(num_workers)
         if write_history:
             self.write_history()
@@ -110,6 +117,15 @@ class DeviceWorkload:
             self._write(to_device(k, w.dtype, self.device), to_device(v, w.dtype, self.device),
                         torch.full((n,), s, dtype=torch.int32, device=self.device),
                         torch.arange(p0, p0 + n, dtype=torch.int32, device=self.device))()
+        if self.compressed:
+            # slot row r of s is written like position r through the slot table
+            for s, e in enumerate(w.slot_kv):
+                n = e.k.shape[0]
+                if n:
+                    _lib.bind_kv_write(self.k_pool, self.v_pool, to_device(e.k, w.dtype, self.device),
+                                       to_device(e.v, w.dtype, self.device),
+                                       torch.full((n,), s, dtype=torch.int32, device=self.device),
+                                       torch.arange(n, dtype=torch.int32, device=self.device), self.slot_tables)()
 
     def write_step(self, stream=None) -> None:
         if self._bound_write is None:
@@ -119,7 +135,12 @@ class DeviceWorkload:
     def attend(self, stream=None) -> None:
         w = self.w
         if self._bound_attend is None:
-            if w.kind == "decode" and self.kv_format != "native":
+            if self.compressed:
+                self._bound_attend = _lib.bind_decode_compressed(
+                    self.out, self.q, self.k_pool, self.v_pool, self.tables, self.lens, self.full_start,
+                    self.slot_tables, self.num_slots, w.max_context_len, window=w.window, scale=w.scale,
+                    num_workers=self.num_workers, workspace=self.workspace, lse=self.lse)
+            elif w.kind == "decode" and self.kv_format != "native":
                 self._bound_attend = _lib.bind_decode_quant(
                     self.out, self.q, self.k_pool, self.v_pool, self.k_scale, self.v_scale, self.tables, self.lens,
                     w.max_context_len, window=w.window, scale=w.scale, num_workers=self.num_workers,
@@ -135,7 +156,21 @@ class DeviceWorkload:
                     w.max_q_len, w.max_context_len, window=w.window, scale=w.scale, lse=self.lse, sinks=w.sinks)
         self._bound_attend(stream)
 
+    def set_compress_ops(self, src_blocks, dst_block, dst_slot) -> None:
+        """Compressions (``paged_kv_compress``) that every step runs before
+        its write: op i averages blocks src_blocks[i] into row dst_slot[i] of
+        block dst_block[i] (host int32 arrays)."""
+        self.compress_ops = (int_tensor(np.asarray(src_blocks).reshape(len(dst_block), -1), self.device),
+                             int_tensor(dst_block, self.device), int_tensor(dst_slot, self.device))
+        self._bound_compress = _lib.bind_kv_compress(self.k_pool, self.v_pool, *self.compress_ops)
+
+    def compress_step(self, stream=None) -> None:
+        if self._bound_compress is not None:
+            self._bound_compress(stream)
+
     def step(self, stream=None) -> None:
-        """One pass of the hot path: write the new tokens, then attend."""
+        """One pass of the hot path: compress (if set), write the new tokens,
+        then attend."""
+        self.compress_step(stream)
         self.write_step(stream)
         self.attend(stream)

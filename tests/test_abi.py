@@ -149,3 +149,33 @@ def test_quant_argument_errors_before_any_launch():
     # the workspace size of an 8-bit pool is that of any pool
     assert (pkv.LIB.paged_attn_decode_workspace_bytes(ctypes.byref(gi8), 2, 100, 0, 0, 4) ==
             pkv.LIB.paged_attn_decode_workspace_bytes(ctypes.byref(g16), 2, 100, 0, 0, 4))
+
+
+def test_compressed_argument_errors_before_any_launch():
+    """Compressed slots: 8-bit pools refused, missing per-sequence arrays,
+    bad slot-table width, bad group sizes -- before anything is enqueued."""
+    P = ctypes.c_void_p
+    g = geo()
+    gi8 = geo(dt=pkv.PKV_I8)
+
+    def comp(g, bps=2, n=3, src=P(1), dst=P(1)):
+        return pkv.LIB.paged_kv_compress(ctypes.byref(g), P(1), P(1), src, bps, dst, P(1), n, None)
+    assert comp(gi8) == pkv.PKV_EUNSUPPORTED
+    assert comp(g, bps=0) == pkv.PKV_EINVAL
+    assert comp(g, bps=(1 << 20) + 1) == pkv.PKV_EINVAL     # more than 2^24 rows per slot
+    assert comp(g, n=-1) == pkv.PKV_EINVAL
+    assert comp(g, n=0) == pkv.PKV_OK
+    assert comp(g, src=None) == pkv.PKV_EINVAL
+    assert comp(g, dst=None) == pkv.PKV_EINVAL
+
+    def dc(g, fs=P(1), st=P(1), msb=1, ns=P(1), S=2, ws=P(4096), wsb=1 << 30, window=0):
+        return pkv.LIB.paged_attn_decode_compressed(ctypes.byref(g), P(1), None, P(1), P(1), P(1), P(1), 8, P(1),
+                                                    fs, st, msb, ns, S, 100, window, 0.1, 0, ws, wsb, None)
+    assert dc(gi8) == pkv.PKV_EUNSUPPORTED
+    assert dc(g, fs=None) == pkv.PKV_EINVAL
+    assert dc(g, st=None) == pkv.PKV_EINVAL
+    assert dc(g, ns=None) == pkv.PKV_EINVAL
+    assert dc(g, msb=0) == pkv.PKV_EINVAL
+    assert dc(g, window=-1) == pkv.PKV_EINVAL
+    assert dc(g, ws=None) == pkv.PKV_EWORKSPACE
+    assert dc(g, S=0) == pkv.PKV_OK

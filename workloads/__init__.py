@@ -44,6 +44,7 @@ TAG_SEQ_KV = 1
 TAG_QUERY = 2
 TAG_PERM = 3
 TAG_PREFIX_KV = 4
+TAG_SLOTS = 5
 
 STORAGE = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16}
 ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2}
@@ -133,6 +134,13 @@ class Workload:
     prefix_len: int = 0
     shared_prefix_blocks: int = 0
     sinks: int = 0  # with a window: the first `sinks` positions are attended too
+    # Compressed slots (decode only): per sequence the first full-resolution
+    # position, the slot table [S, MSB] (slot row r at row r % B of block
+    # slot_tables[s, r // B]), the number of slot rows and their K/V rows.
+    full_start: Optional[np.ndarray] = None
+    slot_tables: Optional[np.ndarray] = None
+    num_slots: Optional[np.ndarray] = None
+    slot_kv: Optional[List[SeqKV]] = None
 
     @property
     def max_context_len(self) -> int:
@@ -208,8 +216,11 @@ class Workload:
         (token, kv-head) row once, for K and for V."""
         eb = ELEM_BYTES[self.dtype]
         L = self.context_lens.astype(np.int64)
-        if self.window > 0:
-            lo = np.maximum(0, L - self.window)
+        lo = np.maximum(0, L - self.window) if self.window > 0 else np.zeros_like(L)
+        if self.full_start is not None:
+            lo = np.maximum(lo, np.minimum(self.full_start.astype(np.int64), L))
+            n = (L - lo) + self.num_slots.astype(np.int64)
+        elif self.window > 0:
             n = (L - lo) + np.minimum(self.sinks, lo)
         else:
             n = L
@@ -247,7 +258,7 @@ def _deal_tables(rng_perm, blocks_per_seq: List[int], first_block: List[int], mb
 
 def make_decode(*, lens, num_heads, num_kv_heads, head_dim, block_size, dtype, seed,
                 window=0, scale=None, k_scale=1.0, max_blocks_per_seq=None,
-                spare_blocks=0, sinks=0, name="decode") -> Workload:
+                spare_blocks=0, sinks=0, full_start=None, name="decode") -> Workload:
     """A batched single-query decode workload.
 
     ``lens[s]`` is the context length of sequence s including the query token.
@@ -255,7 +266,8 @@ def make_decode(*, lens, num_heads, num_kv_heads, head_dim, block_size, dtype, s
     are mapped; table entries of blocks that end at or before ``L-window``
     are -1 (freed).  With ``sinks > 0`` as well, the blocks holding the first
     ``sinks`` positions stay mapped too (attention sinks); the blocks between
-    them and the window are freed.
+    them and the window are freed.  ``full_start[s]`` (optional) raises the
+    first held position the same way (positions below it were compressed).
     """
     lens = np.asarray(lens, dtype=np.int64)
     S = len(lens)
@@ -271,6 +283,8 @@ def make_decode(*, lens, num_heads, num_kv_heads, head_dim, block_size, dtype, s
             runs.append(None)
             continue
         lo = max(0, L - window) if window > 0 else 0
+        if full_start is not None:
+            lo = max(lo, min(int(full_start[len(first_block)]), L))
         b0 = lo // B
         b1 = (L + B - 1) // B
         sb = min((min(sinks, lo) + B - 1) // B, b0) if window > 0 else 0
@@ -302,6 +316,51 @@ def make_decode(*, lens, num_heads, num_kv_heads, head_dim, block_size, dtype, s
                     num_blocks=nb, max_blocks_per_seq=mb, window=window, scale=float(scale),
                     context_lens=lens.astype(np.int32), block_tables=tables, q=q, seq_kv=seq_kv,
                     sinks=int(sinks) if window > 0 else 0)
+
+
+def make_compressed(*, lens, full_start, num_slots, max_slots, num_heads, num_kv_heads, head_dim, block_size,
+                    dtype, seed, window=0, scale=None, max_blocks_per_seq=None, spare_blocks=0,
+                    name="compressed") -> Workload:
+    """A decode workload over two tiers: sequence s holds positions
+    [full_start[s], L) at full resolution (blocks below are unmapped) and
+    ``num_slots[s]`` slot rows, at most ``max_slots``, in slot blocks of its
+    own (ceil(max_slots / B) table entries, mapped as far as the rows
+    reach).  Slot rows are drawn like keys and values, scaled by
+    1/sqrt(B) (a mean of independent rows is that much narrower).  Slot blocks
+    get the pool ids after the full tier's, shuffled."""
+    w = make_decode(lens=lens, num_heads=num_heads, num_kv_heads=num_kv_heads, head_dim=head_dim,
+                    block_size=block_size, dtype=dtype, seed=seed, window=window, scale=scale,
+                    max_blocks_per_seq=max_blocks_per_seq, spare_blocks=spare_blocks, full_start=full_start,
+                    name=name)
+    B = block_size
+    S = w.num_seqs
+    if any(int(f) > max(int(L) - 1, 0) for f, L in zip(full_start, lens)):
+        raise ValueError("full_start must leave the step's own position at full resolution (<= L - 1)")
+    num_slots = np.asarray(num_slots, np.int64)
+    if (num_slots < 0).any() or (num_slots > max_slots).any():
+        raise ValueError("num_slots outside [0, max_slots]")
+    msb = max(1, -(-int(max_slots) // B))
+    used = [-(-int(n) // B) for n in num_slots]
+    ids = w.num_blocks + stream(seed, TAG_SLOTS).permutation(max(1, sum(used))).astype(np.int32)
+    st = np.full((S, msb), -1, np.int32)
+    at = 0
+    for s in range(S):
+        st[s, :used[s]] = ids[at:at + used[s]]
+        at += used[s]
+
+    def one(s):
+        rng = stream(seed, TAG_SLOTS, s + 1)
+        n = int(num_slots[s])
+        k = draw(rng, (n, num_kv_heads, head_dim), dtype, 1.0 / math.sqrt(B))
+        v = draw(rng, (n, num_kv_heads, head_dim), dtype, 1.0 / math.sqrt(B))
+        return SeqKV(0, k, v)
+
+    w.slot_kv = _parallel_map(one, range(S))
+    w.num_blocks += max(1, sum(used))
+    w.full_start = np.minimum(np.asarray(full_start, np.int64), w.context_lens).astype(np.int32)
+    w.slot_tables = st
+    w.num_slots = num_slots.astype(np.int32)
+    return w
 
 
 def make_prefill(*, prefix_len, chunk_lens, num_heads, num_kv_heads, head_dim, block_size,
@@ -393,6 +452,7 @@ CONFIG_NAMES = {
     3: "gqa_long_decode_s64_h32kv8_d128_b32_bf16",
     4: "sliding_window_decode_s16_h32kv8_d128_b16_w4096_bf16",
     5: "chunked_prefill_shared_prefix_s8_h32kv8_d128_b16_bf16",
+    6: "compressed_tier_decode_s512_h32kv8_d128_b16_w256_m16_bf16",
 }
 
 
@@ -423,4 +483,16 @@ def config(idx: int, seed: Optional[int] = None) -> Workload:
         return make_prefill(prefix_len=2048, chunk_lens=[512] * 8, num_heads=32, num_kv_heads=8,
                             head_dim=128, block_size=16, dtype="bf16", seed=seed,
                             max_blocks_per_seq=160, name=name)
+    if idx == 6:
+        # Compressed-slot tier with the page's defaults (full window 256,
+        # 16 slots, groups of 128 positions): each sequence is in a state the
+        # tier reaches, c >= 16 compressions behind it (full tier from
+        # c * 128) and 129 .. 256 positions held at full resolution.
+        rng = stream(seed, TAG_LENGTHS)
+        c = rng.integers(30, 255, size=512)
+        held = rng.integers(129, 257, size=512)
+        fs = c * 128
+        return make_compressed(lens=fs + held, full_start=fs, num_slots=np.full(512, 16), max_slots=16,
+                               num_heads=32, num_kv_heads=8, head_dim=128, block_size=16, dtype="bf16", seed=seed,
+                               max_blocks_per_seq=2048, name=name)
     raise KeyError(idx)
