@@ -22,10 +22,13 @@
 //    The V^T operand is read from row-major V with the LDS transpose read
 //    (ds_read_b64_tr_b16): within 16 lanes, lane j reads 4 consecutive dims
 //    of key j/4 and lane i receives dim i of those 4 keys.
-//  * Weights for P.V: fp16 inputs use the weights rounded to fp16; bf16
-//    inputs split each weight into bf16 high and low parts (p = hi + lo to
-//    about 2^-17 relative) and multiply both, so the 8-bit bf16 mantissa
-//    does not limit the result. The normaliser sums the weights as used.
+//  * P.V runs on the fp16 matrix cores for both input types, with the
+//    weights rounded to fp16 (11-bit mantissa) and the normaliser summing
+//    the weights as used. A bf16 V tile is converted to fp16 in LDS once it
+//    has arrived: each thread rewrites the 16-byte units its own direct
+//    loads wrote, before the tile's barrier. The conversion is exact for
+//    |v| in [2^-17, 65504] (bf16 has 8 significant bits); smaller values are
+//    truncated by less than 2^-24 and larger ones saturate at 65504.
 //  * The weights are taken relative to a reference maximum that moves only
 //    when some row's maximum grows by more than a factor 2^8 (weights then
 //    stay <= 256, well inside fp32 and the 16-bit formats); the output is
@@ -47,32 +50,23 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
-// pack(a, b): a and b rounded to nearest (even) in the 16-bit type, a in the
-// low half; lo(u), hi(u): the halves of a packed pair back in fp32 (exact).
+// mma: one 32x32x16 MFMA of the 16-bit type; pack(a, b): a and b rounded to
+// nearest (even) in that type, a in the low half.
 template <class T> struct Mma;
 template <> struct Mma<BF16T> {
   using V8 = bf16x8;
-  static constexpr bool kSplit = true;
   static __device__ __forceinline__ f32x16 mma(V8 a, V8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
   }
-  static __device__ __forceinline__ uint32_t pack(float a, float b) {
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{a, b}), bf16x2));
-  }
-  static __device__ __forceinline__ float lo(uint32_t u) { return __builtin_bit_cast(float, u << 16); }
-  static __device__ __forceinline__ float hi(uint32_t u) { return __builtin_bit_cast(float, u & 0xffff0000u); }
 };
 template <> struct Mma<F16T> {
   using V8 = f16x8;
-  static constexpr bool kSplit = false;
   static __device__ __forceinline__ f32x16 mma(V8 a, V8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
   }
   static __device__ __forceinline__ uint32_t pack(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{a, b}), f16x2));
   }
-  static __device__ __forceinline__ float lo(uint32_t u) { return (float)as_h2(u).x; }
-  static __device__ __forceinline__ float hi(uint32_t u) { return (float)as_h2(u).y; }
 };
 
 constexpr int kKT = 64;   // key positions per tile
@@ -159,10 +153,27 @@ __device__ __forceinline__ void settle(u32x4& x) { asm volatile("" : "+v"(x)); }
 
 template <int N> struct IntC { static constexpr int value = N; };
 
+// In-place bf16 -> fp16 conversion of one 16-byte unit of a V tile (exact
+// for |v| in [2^-17, 65504], see above); fp16 tiles are left alone.
+template <class T> __device__ __forceinline__ void v_to_f16(uint16_t* unit);
+template <> __device__ __forceinline__ void v_to_f16<F16T>(uint16_t*) {}
+template <> __device__ __forceinline__ void v_to_f16<BF16T>(uint16_t* unit) {
+  u32x4 x = *reinterpret_cast<const u32x4*>(unit);
+  uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float lo = __builtin_bit_cast(float, w[i] << 16), hi = __builtin_bit_cast(float, w[i] & 0xffff0000u);
+    w[i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+  }
+  *reinterpret_cast<u32x4*>(unit) = u32x4{w[0], w[1], w[2], w[3]};
+}
+
 template <class T, int D, int B, int G>
 __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a, float scale_log2) {
-  using M = Mma<T>;
+  using M = Mma<T>;      // S = K.Q^T in the input type
+  using MP = Mma<F16T>;  // O += V^T.P^T in fp16 (V converted in LDS when bf16)
   using V8 = typename M::V8;
+  using P8 = typename MP::V8;
   constexpr int KC = D / 16;            // MFMA k-chunks over the head dim
   constexpr int DT = D / 32;            // 32-wide output tiles over the head dim
   constexpr int HPW = G < 4 ? G : 4;    // query heads per workgroup
@@ -274,6 +285,11 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a, float sc
       dma16(ok ? vpool + boff + roff + 16 * (cs ^ Swz<D>::v(r)) : zero, vd + (4 * j + wave) * 512);
     }
   };
+  // Convert the V units this thread's direct loads wrote (after dma_wait).
+  auto convert_v = [&](uint16_t* vd) {
+#pragma unroll
+    for (int j = 0; j < NLD; ++j) v_to_f16<T>(vd + (4 * j + wave) * 512 + 8 * lane);
+  };
   // Key validity bitmask of a tile (64 lanes = 64 keys), by wavefront 0.
   auto put_valid = [&](int t0, int slot) {
     if (wave == 0) {
@@ -372,7 +388,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a, float sc
         const float mn = fmaxf(m_run, mt);
         const float alpha = __builtin_amdgcn_exp2f(m_run - (mn == -INFINITY ? 0.f : mn));
         l_run *= alpha;
-        if constexpr (!M::kSplit) l_lse *= alpha;
+        l_lse *= alpha;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
         m_run = mn;
@@ -394,24 +410,17 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a, float sc
           e03[dt] = lds_read_tr<16 * c * D * 2>(vbase + tr_addr[dt]);
           e47[dt] = lds_read_tr<(16 * c + 8) * D * 2>(vbase + tr_addr[dt]);
         }
-        uint32_t hi[4], lo[4];
+        uint32_t hi[4];
 #pragma unroll
         for (int e2 = 0; e2 < 4; ++e2) {
           const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kh][8 * sub + 2 * e2], scale_log2, -ms));
           const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kh][8 * sub + 2 * e2 + 1], scale_log2, -ms));
-          const uint32_t h = M::pack(p0, p1);
+          const uint32_t h = MP::pack(p0, p1);
           hi[e2] = h;
-          if constexpr (M::kSplit) {
-            lo[e2] = M::pack(p0 - M::lo(h), p1 - M::hi(h));
-            l_run += p0 + p1;
-          } else {
-            lo[e2] = 0;
-            l_run += M::lo(h) + M::hi(h);
-            l_lse += p0 + p1;
-          }
+          l_run = __builtin_amdgcn_fdot2(as_h2(h), f16x2{(_Float16)1.f, (_Float16)1.f}, l_run, false);
+          l_lse += p0 + p1;
         }
-        const V8 bhi = __builtin_bit_cast(V8, u32x4{hi[0], hi[1], hi[2], hi[3]});
-        const V8 blo = __builtin_bit_cast(V8, u32x4{lo[0], lo[1], lo[2], lo[3]});
+        const P8 bhi = __builtin_bit_cast(P8, u32x4{hi[0], hi[1], hi[2], hi[3]});
         lds_wait();
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
@@ -420,9 +429,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a, float sc
         }
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-          const V8 av = __builtin_bit_cast(V8, u32x4{e03[dt].x, e03[dt].y, e47[dt].x, e47[dt].y});
-          o[dt] = M::mma(av, bhi, o[dt]);
-          if constexpr (M::kSplit) o[dt] = M::mma(av, blo, o[dt]);
+          const P8 av = __builtin_bit_cast(P8, u32x4{e03[dt].x, e03[dt].y, e47[dt].x, e47[dt].y});
+          o[dt] = MP::mma(av, bhi, o[dt]);
         }
       };
       chunk(IntC<0>{});
@@ -431,6 +439,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a, float sc
       chunk(IntC<3>{});
     }
     dma_wait();
+    if (has_next) convert_v(Vn);  // the next tile's V units this thread loaded
     __syncthreads();
     return has_next;
   };
@@ -441,6 +450,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a, float sc
   put_valid(tile_t0(0), 0);
   if (ntiles > 1) fetch_table(tile_t0(1));
   dma_wait();
+  convert_v(v_lds0);
   __syncthreads();
   for (int i = 0;; i += 2) {
     if (!step(i, k_lds0, v_lds0, k_lds1, v_lds1, 0)) break;
@@ -462,7 +472,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a, float sc
     }
   }
   if (a.lse) {
-    const float l_exact = M::kSplit ? l_tot : l_lse + __shfl_xor(l_lse, 32, 64);
+    const float l_exact = l_lse + __shfl_xor(l_lse, 32, 64);
     if (hf == 0)
       a.lse[(size_t)(r0 + my_row) * a.H + hq] = l_exact > 0.f ? (m_run + __log2f(l_exact)) * kLn2 : -INFINITY;
   }
