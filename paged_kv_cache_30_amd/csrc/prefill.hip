@@ -271,18 +271,24 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a, float sc
       pb_ins[j] = trow[min((t0 + (4 * j + wave) * RPI) / B, a.mb - 1)];
     if (wave == 0) pb_key = trow[min((t0 + lane) / B, a.mb - 1)];
   };
+  // Per-lane byte offsets inside a block of load j (tiles start at multiples
+  // of kKT, a multiple of B, so row r of a tile is row r % B of its block).
+  auto unit_off = [&](int j, bool v) -> uint32_t {
+    const int r = (4 * j + wave) * RPI + lane / U, cs = lane % U;
+    return (uint32_t)((r % B) * row_stride) + 16 * (cs ^ (v ? Swz<D>::v(r) : Swz<D>::k(r)));
+  };
   auto gather = [&](int t0, uint16_t* kd, uint16_t* vd) {
+    // Whole tile inside the attended range: only the block entries decide.
+    const bool whole = t0 >= kv_lo && t0 + kKT <= kv_hi;
 #pragma unroll
     for (int j = 0; j < NLD; ++j) {
       const int pb = pb_ins[j];
       const bool blk_ok = pb >= 0 && pb < a.nb;
       const size_t boff = (size_t)(uint32_t)(blk_ok ? pb : 0) * block_stride;
-      const int r = (4 * j + wave) * RPI + lane / U, cs = lane % U;
-      const int t = t0 + r;
-      const bool ok = blk_ok && in_range(t);
-      const uint32_t roff = (uint32_t)((t % B) * row_stride);
-      dma16(ok ? kpool + boff + roff + 16 * (cs ^ Swz<D>::k(r)) : zero, kd + (4 * j + wave) * 512);
-      dma16(ok ? vpool + boff + roff + 16 * (cs ^ Swz<D>::v(r)) : zero, vd + (4 * j + wave) * 512);
+      bool ok = blk_ok;
+      if (!whole) ok = ok && in_range(t0 + (4 * j + wave) * RPI + lane / U);
+      dma16(ok ? kpool + boff + unit_off(j, false) : zero, kd + (4 * j + wave) * 512);
+      dma16(ok ? vpool + boff + unit_off(j, true) : zero, vd + (4 * j + wave) * 512);
     }
   };
   // Convert the V units this thread's direct loads wrote (after dma_wait).
@@ -374,13 +380,21 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a, float sc
           }
         }
       }
-      float mt = -INFINITY;
+      // Tile maximum as a tree, then across the two lane halves that hold
+      // the same query (v_permlane32_swap exchanges the halves).
+      float m8[8];
 #pragma unroll
-      for (int kh = 0; kh < 2; ++kh) {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) mt = fmaxf(mt, sacc[kh][v]);
+      for (int k = 0; k < 8; ++k)
+        m8[k] = fmaxf(fmaxf(sacc[k >> 2][4 * (k & 3)], sacc[k >> 2][4 * (k & 3) + 1]),
+                      fmaxf(sacc[k >> 2][4 * (k & 3) + 2], sacc[k >> 2][4 * (k & 3) + 3]));
+      float mt = fmaxf(fmaxf(fmaxf(m8[0], m8[1]), fmaxf(m8[2], m8[3])),
+                       fmaxf(fmaxf(m8[4], m8[5]), fmaxf(m8[6], m8[7])));
+      {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, mt),
+                                                         __builtin_bit_cast(uint32_t, mt), false, false);
+        mt = fmaxf(__builtin_bit_cast(float, (uint32_t)sw[0]), __builtin_bit_cast(float, (uint32_t)sw[1]));
       }
-      mt = fmaxf(mt, __shfl_xor(mt, 32, 64)) * scale_log2;
+      mt *= scale_log2;
       // The reference maximum m_run moves only when some row's tile maximum
       // exceeds it by more than kSlackLog2, so weights are at most
       // 2^kSlackLog2 and the output rescale (exact either way) is rare.
