@@ -598,15 +598,16 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
   if (w_lo == w_hi) return;  // written by the split kernel
   const int np = w_hi - w_lo + 1;
   const size_t base0 = ((size_t)s * Hkv + g) * G + (size_t)w_lo * G;  // slot of worker w_lo, head 0
-  if (np <= 4) {
+  constexpr int NP = PER == 1 ? 16 : 4;  // partials the all-at-once path takes
+  if (np <= NP) {
     // Every load of the lane's outputs issued before any is used.
-    float2 ml[PER][4];
-    float ov[PER][4];
+    float2 ml[PER][NP];
+    float ov[PER][NP];
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
       const int i = elem(k), hh = i / D, d = i - hh * D;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < NP; ++j) {
         const size_t slot = base0 + hh + (size_t)j * G;
         const bool ok = j < np;
         ml[k][j] = ok ? *reinterpret_cast<const float2*>(a.ws_ml + slot * 2) : make_float2(-INFINITY, 0.f);
@@ -618,11 +619,11 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
       const int i = elem(k), hh = i / D, d = i - hh * D;
       float M = ml[k][0].x;
 #pragma unroll
-      for (int j = 1; j < 4; ++j) M = fmaxf(M, ml[k][j].x);
+      for (int j = 1; j < NP; ++j) M = fmaxf(M, ml[k][j].x);
       const float Ms = M == -INFINITY ? 0.f : M;
       float sl = 0.f, so = 0.f;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < NP; ++j) {
         const float f = __builtin_amdgcn_exp2f(ml[k][j].x - Ms);
         sl = __builtin_fmaf(f, ml[k][j].y, sl);
         so = __builtin_fmaf(f, ov[k][j], so);
