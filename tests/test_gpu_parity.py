@@ -501,3 +501,51 @@ def test_prefill_sinks(lib, case):
                            num_kv_heads=Hkv, window=window, scale=w.scale, dtype=dtype, sinks=sinks)
     assert_close(d.out.cpu().numpy(), out, dtype, str(case))
     check_lse(d, lse)
+
+
+# ----------------------------------------------------- batch and length limits
+
+def test_decode_many_sequences_plan_launch(lib):
+    """More than 4096 sequences: the prefix of attended blocks comes from the
+    separate one-workgroup launch. Ragged short contexts (0..40, some empty);
+    the first, the last, the empty and 60 random sequences against the oracle."""
+    pkv, session = lib
+    note("decode 5000 sequences")
+    rng = np.random.default_rng(50)
+    lens = rng.integers(0, 41, 5000)
+    lens[::97] = 0
+    w = wl.make_decode(lens=lens, num_heads=8, num_kv_heads=2, head_dim=64, block_size=16, dtype="bf16", seed=50)
+    d = run(session, w)
+    kp, vp = ref.build_pools(w)
+    empty = [int(i) for i in np.where(lens == 0)[0][:3]]
+    pick = sorted(set([0, 1, 4998, 4999] + empty + [int(i) for i in rng.choice(5000, 60, replace=False)]))
+    out, lse = ref.decode(w.q, kp, vp, w.block_tables, w.context_lens, block_size=16, num_kv_heads=2, window=0,
+                          scale=w.scale, dtype="bf16", seqs=pick)
+    assert_close(d.out.cpu().numpy()[pick], out[pick], "bf16", "5000 sequences")
+    got_lse = d.lse.cpu().numpy()[pick]
+    fin = np.isfinite(lse[pick])
+    assert np.array_equal(fin, np.isfinite(got_lse))
+    assert np.abs(got_lse[fin] - lse[pick][fin]).max() <= 1e-4
+
+
+def test_decode_128k_context(lib):
+    """One 131072-token context next to a 5-token one (GQA, logits std ~3):
+    the long sequence is split over every wavefront; against attention over
+    its logical rows."""
+    pkv, session = lib
+    note("decode 128K context")
+    w = wl.make_decode(lens=[131072, 5], num_heads=8, num_kv_heads=2, head_dim=128, block_size=32, dtype="bf16",
+                       seed=51, k_scale=3.0)
+    d = run(session, w)
+    got = d.out.cpu().numpy()
+    for s in range(2):
+        first, k, v = w.logical_kv(s)
+        L = int(w.context_lens[s])
+        qf = ref.to_f64(w.q[s], "bf16")
+        want = np.zeros((8, 128))
+        for g in range(2):
+            K = ref.to_f64(k[:L - first, g], "bf16")
+            V = ref.to_f64(v[:L - first, g], "bf16")
+            o, _ = ref.attend(qf[4 * g:4 * g + 4], K, V, w.scale)
+            want[4 * g:4 * g + 4] = o
+        assert_close(got[s], want, "bf16", f"128K context seq {s} (L={L})")
