@@ -12,10 +12,13 @@ tier: mean-pooled slots of evicted blocks attended next to the recent window).
 ``PrefixCache`` shares cached prompt blocks between sequences;
 ``CompressedTier`` keeps the host bookkeeping of the compressed tier.
 ``BlockAllocator`` is the host-side block allocator that builds the tables.
+Every entry point takes ``debug=True`` to check its device-resident indices
+on the host first (``validate``; raises ``InvalidContent``).
 """
 from .allocator import BlockAllocator, UNMAPPED  # noqa: F401
 from .prefix_cache import PrefixCache  # noqa: F401
 from .compressed_tier import CompressedTier, CompressOps  # noqa: F401
+from .validate import InvalidContent  # noqa: F401
 from ._lib import (  # noqa: F401
     LIB, LIB_PATH, EXPORTS, PagedAttnError, Geometry, geometry,
     PKV_F32, PKV_F16, PKV_BF16, PKV_I8, PKV_FP8, PKV_OK, PKV_EINVAL, PKV_EUNSUPPORTED, PKV_EWORKSPACE, PKV_EHIP,

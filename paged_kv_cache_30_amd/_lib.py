@@ -5,6 +5,11 @@ pointers, shapes and the current HIP stream, and calls the C entry point of
 the same name; the computation is entirely in the library's kernels.  A
 missing library raises at import time: there is no fallback.
 
+``debug=True`` on a call (or PKV_DEBUG=1 in the environment) adds a host-side
+check of its device-resident indices before the C call (``validate``): it
+synchronises the device and copies tables and lengths back, so it is for
+finding a caller's bug, not for the hot path.
+
 The library is loaded after torch so that the HIP runtime torch already
 mapped serves both (same soname).
 """
@@ -15,6 +20,8 @@ import os
 from typing import Optional
 
 import torch
+
+from . import validate as _val
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("PKV_LIBRARY", os.path.join(_HERE, "libpagedattn.so"))
@@ -91,6 +98,21 @@ def _load() -> ctypes.CDLL:
 LIB = _load()
 
 
+def _debug(flag) -> bool:
+    """Debug mode of one call: the flag if given, else PKV_DEBUG=1 in the
+    environment."""
+    if flag is None:
+        return os.environ.get("PKV_DEBUG", "0") not in ("", "0")
+    return bool(flag)
+
+
+def _host(*ts):
+    """Host copies of device tensors, after every queued kernel has run
+    (debug mode only: it synchronises the device)."""
+    torch.cuda.synchronize()
+    return [t.cpu().numpy() for t in ts]
+
+
 def _check(status: int, what: str) -> None:
     if status != PKV_OK:
         msg = LIB.pkv_status_string(status).decode()
@@ -131,9 +153,11 @@ def geometry(k_pool: torch.Tensor, num_heads: int) -> Geometry:
     return Geometry(nb, b, num_heads, hkv, d, _DTYPES[k_pool.dtype])
 
 
-def bind_kv_write(k_pool, v_pool, k_new, v_new, seq_idx, pos, block_tables):
+def bind_kv_write(k_pool, v_pool, k_new, v_new, seq_idx, pos, block_tables, debug=None):
     """Check and marshal the arguments of ``paged_kv_write`` once; returns a
-    callable ``f(stream=None)`` that makes the C call with them."""
+    callable ``f(stream=None)`` that makes the C call with them.  With
+    ``debug`` (default: PKV_DEBUG=1) every call first checks the device-resident
+    indices on the host (``validate.check_write``)."""
     _dev(k_pool, "k_pool", ndim=4)
     _dev(v_pool, "v_pool", dtype=k_pool.dtype)
     if v_pool.shape != k_pool.shape:
@@ -152,16 +176,20 @@ def bind_kv_write(k_pool, v_pool, k_new, v_new, seq_idx, pos, block_tables):
     args = (ctypes.byref(g), _ptr(k_pool), _ptr(v_pool), _ptr(k_new), _ptr(v_new), _ptr(seq_idx), _ptr(pos), T,
             _ptr(block_tables), block_tables.shape[0], block_tables.shape[1])
     keep = (g, k_pool, v_pool, k_new, v_new, seq_idx, pos, block_tables)
+    dbg = _debug(debug)
 
     def call(stream=None):
+        if dbg:
+            _val.check_write(*_host(seq_idx, pos, block_tables), num_blocks=g.num_blocks,
+                             block_size=g.block_size)
         _check(LIB.paged_kv_write(*args, _stream(stream)), "paged_kv_write")
     call.keep = keep
     return call
 
 
-def paged_kv_write(k_pool, v_pool, k_new, v_new, seq_idx, pos, block_tables, stream=None) -> None:
+def paged_kv_write(k_pool, v_pool, k_new, v_new, seq_idx, pos, block_tables, stream=None, debug=None) -> None:
     """C ``paged_kv_write``: store k_new/v_new [T, Hkv, D] at (seq_idx, pos)."""
-    bind_kv_write(k_pool, v_pool, k_new, v_new, seq_idx, pos, block_tables)(stream)
+    bind_kv_write(k_pool, v_pool, k_new, v_new, seq_idx, pos, block_tables, debug)(stream)
 
 
 def paged_attn_decode_workspace_bytes(k_pool, num_heads, num_seqs, max_context_len, window=0,
@@ -184,9 +212,11 @@ def decode_workspace(k_pool, num_heads, num_seqs, max_context_len, window=0, num
 
 
 def bind_decode(out, q, k_pool, v_pool, block_tables, context_lens, max_context_len, *,
-                window=0, scale, num_workers=0, workspace=None, lse=None, sinks=0):
+                window=0, scale, num_workers=0, workspace=None, lse=None, sinks=0, debug=None):
     """Check and marshal the arguments of ``paged_attn_decode`` once; returns
-    a callable ``f(stream=None)`` that makes the C call with them."""
+    a callable ``f(stream=None)`` that makes the C call with them.  With
+    ``debug`` every call first checks the tables and lengths on the host
+    (``validate.check_decode``)."""
     _dev(q, "q", dtype=k_pool.dtype, ndim=3)
     _dev(out, "out", dtype=torch.float32, ndim=3)
     _dev(k_pool, "k_pool", ndim=4)
@@ -209,24 +239,33 @@ def bind_decode(out, q, k_pool, v_pool, block_tables, context_lens, max_context_
             block_tables.shape[1], _ptr(context_lens), S, int(max_context_len), int(window), int(sinks),
             float(scale), int(num_workers), _ptr(workspace), ws_bytes)
     keep = (g, out, q, k_pool, v_pool, block_tables, context_lens, workspace, lse)
+    dbg = _debug(debug)
 
     def call(stream=None):
+        if dbg:
+            _val.check_decode(*_host(block_tables, context_lens), max_context_len=int(max_context_len),
+                              num_blocks=g.num_blocks, block_size=g.block_size, window=int(window),
+                              sinks=int(sinks))
         _check(LIB.paged_attn_decode(*args, _stream(stream)), "paged_attn_decode")
     call.keep = keep
     return call
 
 
 def paged_attn_decode(out, q, k_pool, v_pool, block_tables, context_lens, max_context_len, *,
-                      window=0, scale, num_workers=0, workspace=None, lse=None, stream=None, sinks=0) -> None:
+                      window=0, scale, num_workers=0, workspace=None, lse=None, stream=None, sinks=0,
+                      debug=None) -> None:
     """C ``paged_attn_decode``: out[S, H, D] (fp32) for q[S, H, D]."""
     bind_decode(out, q, k_pool, v_pool, block_tables, context_lens, max_context_len, window=window,
-                scale=scale, num_workers=num_workers, workspace=workspace, lse=lse, sinks=sinks)(stream)
+                scale=scale, num_workers=num_workers, workspace=workspace, lse=lse, sinks=sinks,
+                debug=debug)(stream)
 
 
 def bind_prefill(out, q, q_start, k_pool, v_pool, block_tables, context_lens, max_q_len, max_context_len, *,
-                 window=0, scale, lse=None, sinks=0):
+                 window=0, scale, lse=None, sinks=0, debug=None):
     """Check and marshal the arguments of ``paged_attn_prefill`` once; returns
-    a callable ``f(stream=None)`` that makes the C call with them."""
+    a callable ``f(stream=None)`` that makes the C call with them.  With
+    ``debug`` every call first checks q_start, the tables and lengths on the
+    host (``validate.check_prefill``)."""
     _dev(q, "q", dtype=k_pool.dtype, ndim=3)
     _dev(out, "out", dtype=torch.float32, ndim=3)
     _dev(q_start, "q_start", dtype=torch.int32, ndim=1)
@@ -247,18 +286,23 @@ def bind_prefill(out, q, q_start, k_pool, v_pool, block_tables, context_lens, ma
             _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), S, int(max_q_len), int(max_context_len),
             int(window), int(sinks), float(scale))
     keep = (g, out, q, q_start, k_pool, v_pool, block_tables, context_lens, lse)
+    dbg = _debug(debug)
 
     def call(stream=None):
+        if dbg:
+            _val.check_prefill(*_host(q_start, block_tables, context_lens), num_rows=T, max_q_len=int(max_q_len),
+                               max_context_len=int(max_context_len), num_blocks=g.num_blocks,
+                               block_size=g.block_size, window=int(window), sinks=int(sinks))
         _check(LIB.paged_attn_prefill(*args, _stream(stream)), "paged_attn_prefill")
     call.keep = keep
     return call
 
 
 def paged_attn_prefill(out, q, q_start, k_pool, v_pool, block_tables, context_lens, max_q_len,
-                       max_context_len, *, window=0, scale, lse=None, stream=None, sinks=0) -> None:
+                       max_context_len, *, window=0, scale, lse=None, stream=None, sinks=0, debug=None) -> None:
     """C ``paged_attn_prefill``: out[T, H, D] (fp32) for chunk queries q[T, H, D]."""
     bind_prefill(out, q, q_start, k_pool, v_pool, block_tables, context_lens, max_q_len, max_context_len,
-                 window=window, scale=scale, lse=lse, sinks=sinks)(stream)
+                 window=window, scale=scale, lse=lse, sinks=sinks, debug=debug)(stream)
 
 
 # ------------------------------------------------------------- 8-bit pools
@@ -277,7 +321,7 @@ def _check_quant_pools(k_pool, v_pool, k_scale, v_scale):
             raise ValueError(f"{name} must be [num_blocks, num_kv_heads, block_size]")
 
 
-def bind_kv_write_quant(k_pool, v_pool, k_scale, v_scale, k_new, v_new, seq_idx, pos, block_tables):
+def bind_kv_write_quant(k_pool, v_pool, k_scale, v_scale, k_new, v_new, seq_idx, pos, block_tables, debug=None):
     """Check and marshal the arguments of ``paged_kv_write_quant`` once;
     returns a callable ``f(stream=None)``."""
     _check_quant_pools(k_pool, v_pool, k_scale, v_scale)
@@ -298,21 +342,26 @@ def bind_kv_write_quant(k_pool, v_pool, k_scale, v_scale, k_new, v_new, seq_idx,
             _DTYPES[k_new.dtype], _ptr(seq_idx), _ptr(pos), T, _ptr(block_tables), block_tables.shape[0],
             block_tables.shape[1])
     keep = (g, k_pool, v_pool, k_scale, v_scale, k_new, v_new, seq_idx, pos, block_tables)
+    dbg = _debug(debug)
 
     def call(stream=None):
+        if dbg:
+            _val.check_write(*_host(seq_idx, pos, block_tables), num_blocks=g.num_blocks,
+                             block_size=g.block_size, what="paged_kv_write_quant")
         _check(LIB.paged_kv_write_quant(*args, _stream(stream)), "paged_kv_write_quant")
     call.keep = keep
     return call
 
 
 def paged_kv_write_quant(k_pool, v_pool, k_scale, v_scale, k_new, v_new, seq_idx, pos, block_tables,
-                         stream=None) -> None:
+                         stream=None, debug=None) -> None:
     """C ``paged_kv_write_quant``: encode k_new/v_new [T, Hkv, D] into 8-bit pools."""
-    bind_kv_write_quant(k_pool, v_pool, k_scale, v_scale, k_new, v_new, seq_idx, pos, block_tables)(stream)
+    bind_kv_write_quant(k_pool, v_pool, k_scale, v_scale, k_new, v_new, seq_idx, pos, block_tables,
+                        debug)(stream)
 
 
 def bind_decode_quant(out, q, k_pool, v_pool, k_scale, v_scale, block_tables, context_lens, max_context_len, *,
-                      window=0, scale, num_workers=0, workspace=None, lse=None, sinks=0):
+                      window=0, scale, num_workers=0, workspace=None, lse=None, sinks=0, debug=None):
     """Check and marshal the arguments of ``paged_attn_decode_quant`` once;
     returns a callable ``f(stream=None)``."""
     _check_quant_pools(k_pool, v_pool, k_scale, v_scale)
@@ -339,8 +388,13 @@ def bind_decode_quant(out, q, k_pool, v_pool, k_scale, v_scale, block_tables, co
             int(max_context_len), int(window), int(sinks), float(scale), int(num_workers), _ptr(workspace),
             ws_bytes)
     keep = (g, out, q, k_pool, v_pool, k_scale, v_scale, block_tables, context_lens, workspace, lse)
+    dbg = _debug(debug)
 
     def call(stream=None):
+        if dbg:
+            _val.check_decode(*_host(block_tables, context_lens), max_context_len=int(max_context_len),
+                              num_blocks=g.num_blocks, block_size=g.block_size, window=int(window),
+                              sinks=int(sinks), what="paged_attn_decode_quant")
         _check(LIB.paged_attn_decode_quant(*args, _stream(stream)), "paged_attn_decode_quant")
     call.keep = keep
     return call
@@ -348,16 +402,16 @@ def bind_decode_quant(out, q, k_pool, v_pool, k_scale, v_scale, block_tables, co
 
 def paged_attn_decode_quant(out, q, k_pool, v_pool, k_scale, v_scale, block_tables, context_lens,
                             max_context_len, *, window=0, scale, num_workers=0, workspace=None, lse=None,
-                            stream=None, sinks=0) -> None:
+                            stream=None, sinks=0, debug=None) -> None:
     """C ``paged_attn_decode_quant``: decode over 8-bit pools with row scales."""
     bind_decode_quant(out, q, k_pool, v_pool, k_scale, v_scale, block_tables, context_lens, max_context_len,
                       window=window, scale=scale, num_workers=num_workers, workspace=workspace, lse=lse,
-                      sinks=sinks)(stream)
+                      sinks=sinks, debug=debug)(stream)
 
 
 # ------------------------------------------------- block copies, mixed batches
 
-def paged_kv_copy_blocks(k_pool, v_pool, src, dst, k_scale=None, v_scale=None, stream=None) -> None:
+def paged_kv_copy_blocks(k_pool, v_pool, src, dst, k_scale=None, v_scale=None, stream=None, debug=None) -> None:
     """C ``paged_kv_copy_blocks``: copy block src[i] to dst[i] in both pools
     (and the row scales of 8-bit pools)."""
     _dev(k_pool, "k_pool", ndim=4)
@@ -373,12 +427,14 @@ def paged_kv_copy_blocks(k_pool, v_pool, src, dst, k_scale=None, v_scale=None, s
     if src.shape != dst.shape:
         raise ValueError("src and dst need one entry per pair")
     g = geometry(k_pool, k_pool.shape[2])
+    if _debug(debug):
+        _val.check_copy_blocks(*_host(src, dst), num_blocks=g.num_blocks)
     _check(LIB.paged_kv_copy_blocks(ctypes.byref(g), _ptr(k_pool), _ptr(v_pool), _ptr(k_scale), _ptr(v_scale),
                                     _ptr(src), _ptr(dst), src.shape[0], _stream(stream)), "paged_kv_copy_blocks")
 
 
 def bind_mixed(out, q, q_start, k_pool, v_pool, block_tables, context_lens, max_q_len, max_context_len, *,
-               window=0, scale, num_workers=0, workspace=None, lse=None, sinks=0):
+               window=0, scale, num_workers=0, workspace=None, lse=None, sinks=0, debug=None):
     """Check and marshal the arguments of ``paged_attn_mixed`` once; returns
     a callable ``f(stream=None)``."""
     _dev(q, "q", dtype=k_pool.dtype, ndim=3)
@@ -405,24 +461,31 @@ def bind_mixed(out, q, q_start, k_pool, v_pool, block_tables, context_lens, max_
             _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), S, int(max_q_len), int(max_context_len),
             int(window), int(sinks), float(scale), int(num_workers), _ptr(workspace), ws_bytes)
     keep = (g, out, q, q_start, k_pool, v_pool, block_tables, context_lens, workspace, lse)
+    dbg = _debug(debug)
 
     def call(stream=None):
+        if dbg:
+            _val.check_prefill(*_host(q_start, block_tables, context_lens), num_rows=T, max_q_len=int(max_q_len),
+                               max_context_len=int(max_context_len), num_blocks=g.num_blocks,
+                               block_size=g.block_size, window=int(window), sinks=int(sinks),
+                               what="paged_attn_mixed")
         _check(LIB.paged_attn_mixed(*args, _stream(stream)), "paged_attn_mixed")
     call.keep = keep
     return call
 
 
 def paged_attn_mixed(out, q, q_start, k_pool, v_pool, block_tables, context_lens, max_q_len, max_context_len, *,
-                     window=0, scale, num_workers=0, workspace=None, lse=None, stream=None, sinks=0) -> None:
+                     window=0, scale, num_workers=0, workspace=None, lse=None, stream=None, sinks=0,
+                     debug=None) -> None:
     """C ``paged_attn_mixed``: prefill chunks and single decode rows in one call."""
     bind_mixed(out, q, q_start, k_pool, v_pool, block_tables, context_lens, max_q_len, max_context_len,
                window=window, scale=scale, num_workers=num_workers, workspace=workspace, lse=lse,
-               sinks=sinks)(stream)
+               sinks=sinks, debug=debug)(stream)
 
 
 # ------------------------------------------------------- compressed slots
 
-def bind_kv_compress(k_pool, v_pool, src_blocks, dst_block, dst_slot):
+def bind_kv_compress(k_pool, v_pool, src_blocks, dst_block, dst_slot, debug=None):
     """Check and marshal the arguments of ``paged_kv_compress`` once; returns
     a callable ``f(stream=None)``."""
     _dev(k_pool, "k_pool", ndim=4)
@@ -439,21 +502,26 @@ def bind_kv_compress(k_pool, v_pool, src_blocks, dst_block, dst_slot):
     args = (ctypes.byref(g), _ptr(k_pool), _ptr(v_pool), _ptr(src_blocks), max(int(src_blocks.shape[1]), 1),
             _ptr(dst_block), _ptr(dst_slot), n)
     keep = (g, k_pool, v_pool, src_blocks, dst_block, dst_slot)
+    dbg = _debug(debug)
 
     def call(stream=None):
+        if dbg:
+            _val.check_compress(*_host(src_blocks, dst_block, dst_slot), num_blocks=g.num_blocks,
+                                block_size=g.block_size)
         _check(LIB.paged_kv_compress(*args, _stream(stream)), "paged_kv_compress")
     call.keep = keep
     return call
 
 
-def paged_kv_compress(k_pool, v_pool, src_blocks, dst_block, dst_slot, stream=None) -> None:
+def paged_kv_compress(k_pool, v_pool, src_blocks, dst_block, dst_slot, stream=None, debug=None) -> None:
     """C ``paged_kv_compress``: op i writes the mean of every row of blocks
     src_blocks[i, :] into row dst_slot[i] of block dst_block[i]."""
-    bind_kv_compress(k_pool, v_pool, src_blocks, dst_block, dst_slot)(stream)
+    bind_kv_compress(k_pool, v_pool, src_blocks, dst_block, dst_slot, debug)(stream)
 
 
 def bind_decode_compressed(out, q, k_pool, v_pool, block_tables, context_lens, full_start, slot_tables, num_slots,
-                           max_context_len, *, window=0, scale, num_workers=0, workspace=None, lse=None):
+                           max_context_len, *, window=0, scale, num_workers=0, workspace=None, lse=None,
+                           debug=None):
     """Check and marshal the arguments of ``paged_attn_decode_compressed``
     once; returns a callable ``f(stream=None)``."""
     _dev(q, "q", dtype=k_pool.dtype, ndim=3)
@@ -484,8 +552,13 @@ def bind_decode_compressed(out, q, k_pool, v_pool, block_tables, context_lens, f
             _ptr(workspace), ws_bytes)
     keep = (g, out, q, k_pool, v_pool, block_tables, context_lens, full_start, slot_tables, num_slots, workspace,
             lse)
+    dbg = _debug(debug)
 
     def call(stream=None):
+        if dbg:
+            _val.check_decode_compressed(*_host(block_tables, context_lens, full_start, slot_tables, num_slots),
+                                         max_context_len=int(max_context_len), num_blocks=g.num_blocks,
+                                         block_size=g.block_size, window=int(window))
         _check(LIB.paged_attn_decode_compressed(*args, _stream(stream)), "paged_attn_decode_compressed")
     call.keep = keep
     return call
@@ -493,9 +566,9 @@ def bind_decode_compressed(out, q, k_pool, v_pool, block_tables, context_lens, f
 
 def paged_attn_decode_compressed(out, q, k_pool, v_pool, block_tables, context_lens, full_start, slot_tables,
                                  num_slots, max_context_len, *, window=0, scale, num_workers=0, workspace=None,
-                                 lse=None, stream=None) -> None:
+                                 lse=None, stream=None, debug=None) -> None:
     """C ``paged_attn_decode_compressed``: decode over compressed slots and
     the full-resolution positions [full_start, L)."""
     bind_decode_compressed(out, q, k_pool, v_pool, block_tables, context_lens, full_start, slot_tables, num_slots,
                            max_context_len, window=window, scale=scale, num_workers=num_workers,
-                           workspace=workspace, lse=lse)(stream)
+                           workspace=workspace, lse=lse, debug=debug)(stream)

@@ -365,6 +365,59 @@ def test_abi_errors_on_device(lib):
         pkv.paged_attn_decode(d.out, d.q.float(), d.k_pool, d.v_pool, d.tables, d.lens, 100, scale=0.1)
 
 
+def test_debug_mode_checks_device_content(lib):
+    """debug=True gives the same result as a plain call on valid input, and
+    rejects bad device-resident indices before anything is launched (the
+    output and the pools keep their bytes)."""
+    pkv, session = lib
+    note("debug mode")
+    w = wl.make_decode(lens=[700, 33, 1], num_heads=8, num_kv_heads=2, head_dim=128, block_size=16,
+                       dtype="bf16", seed=21, window=100, sinks=4)
+    d = run(session, w, num_workers=24)
+    kw = dict(window=w.window, sinks=w.sinks, scale=w.scale, num_workers=24, workspace=d.workspace)
+    out = torch.full_like(d.out, 7.0)
+    pkv.paged_attn_decode(out, d.q, d.k_pool, d.v_pool, d.tables, d.lens, w.max_context_len, debug=True, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(out, d.out)
+    bad = d.lens.clone()
+    bad[1] = w.max_context_len + 1
+    out.fill_(7.0)
+    with pytest.raises(pkv.InvalidContent, match=r"context_lens\[1\]"):
+        pkv.paged_attn_decode(out, d.q, d.k_pool, d.v_pool, d.tables, bad, w.max_context_len, debug=True, **kw)
+    tab = d.tables.clone()
+    tab[0, 0] = -1  # a sink block
+    with pytest.raises(pkv.InvalidContent, match="logical block 0"):
+        pkv.paged_attn_decode(out, d.q, d.k_pool, d.v_pool, tab, d.lens, w.max_context_len, debug=True, **kw)
+    torch.cuda.synchronize()
+    assert bool((out == 7.0).all())
+
+    kp = d.k_pool.clone()
+    seq = torch.tensor([0, 0], dtype=torch.int32, device="cuda")
+    pos = torch.tensor([699, 699], dtype=torch.int32, device="cuda")
+    kn = torch.zeros((2, 2, 128), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(pkv.InvalidContent, match="same slot"):
+        pkv.paged_kv_write(kp, kp, kn, kn, seq, pos, d.tables, debug=True)
+    torch.cuda.synchronize()
+    assert torch.equal(kp.view(torch.int16), d.k_pool.view(torch.int16))
+
+    wp = wl.make_prefill(prefix_len=64, chunk_lens=[40, 7], num_heads=8, num_kv_heads=2, head_dim=128,
+                         block_size=16, dtype="bf16", seed=22)
+    dp = run(session, wp)
+    outp = torch.full_like(dp.out, 7.0)
+    pkv.paged_attn_prefill(outp, dp.q, dp.q_start, dp.k_pool, dp.v_pool, dp.tables, dp.lens, wp.max_q_len,
+                           wp.max_context_len, scale=wp.scale, debug=True)
+    torch.cuda.synchronize()
+    assert torch.equal(outp, dp.out)
+    qs = dp.q_start.clone()
+    qs[2] += 1  # one row past the output
+    outp.fill_(7.0)
+    with pytest.raises(pkv.InvalidContent, match="q_start"):
+        pkv.paged_attn_prefill(outp, dp.q, qs, dp.k_pool, dp.v_pool, dp.tables, dp.lens, wp.max_q_len + 1,
+                               wp.max_context_len, scale=wp.scale, debug=True)
+    torch.cuda.synchronize()
+    assert bool((outp == 7.0).all())
+
+
 # ------------------------------------------------------------ HIP graphs
 
 @pytest.mark.parametrize("kind", ["decode", "prefill"])
@@ -549,3 +602,47 @@ def test_decode_128k_context(lib):
             o, _ = ref.attend(qf[4 * g:4 * g + 4], K, V, w.scale)
             want[4 * g:4 * g + 4] = o
         assert_close(got[s], want, "bf16", f"128K context seq {s} (L={L})")
+
+
+# ------------------------------------------------- robustness re-run seeds
+
+@pytest.mark.parametrize("seed", [101, 102, 103, 104, 105])
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_configs_robustness_seeds(lib, cfg, seed):
+    """The five workloads redrawn with seeds 101..105 (lengths, K/V, Q and
+    the physical-id permutation all change).  The write bit-exact for the
+    two MHA decode workloads; attention on every head of the tiny workload,
+    on the shortest, the longest and a third sequence of the batched ones
+    (against the contiguous cache), and on two sequences plus three heads
+    of all rows for the prefill."""
+    pkv, session = lib
+    note(f"cfg{cfg} seed {seed}")
+    w = wl.config(cfg, seed=seed)
+    d = run(session, w)
+    got = d.out.cpu().numpy()
+    if cfg in (1, 2):
+        kp, vp = ref.build_pools(w, poison=True)
+        assert session.from_device(d.k_pool).tobytes() == kp.tobytes()
+        assert session.from_device(d.v_pool).tobytes() == vp.tobytes()
+    if cfg == 1:
+        out, lse = oracle_decode(w, kp, vp)
+        assert_close(got, out, w.dtype, f"cfg{cfg} seed {seed}")
+        check_lse(d, lse)
+    elif cfg in (2, 3, 4):
+        order = np.argsort(w.context_lens)
+        third = int(np.random.default_rng(seed).integers(w.num_seqs))
+        for s in sorted({int(order[0]), int(order[-1]), third}):
+            first, k, v = w.logical_kv(s)
+            o, _ = ref.contiguous_decode(w.q[s], k, v, first, int(w.context_lens[s]), num_kv_heads=w.num_kv_heads,
+                                         window=w.window, scale=w.scale, dtype=w.dtype)
+            assert_close(got[s], o, w.dtype, f"cfg{cfg} seed {seed} seq {s}")
+    else:
+        kp, vp = ref.build_pools(w)
+        kw = dict(block_size=w.block_size, num_kv_heads=w.num_kv_heads, window=w.window, scale=w.scale,
+                  dtype=w.dtype)
+        out, _ = ref.prefill(w.q, w.q_start, kp, vp, w.block_tables, w.context_lens, seqs=[0, 5], **kw)
+        rows = np.r_[w.q_start[0]:w.q_start[1], w.q_start[5]:w.q_start[6]]
+        assert_close(got[rows], out[rows], w.dtype, f"cfg5 seed {seed} seqs 0,5")
+        heads = [1, 16, 30]
+        outh, _ = ref.prefill(w.q, w.q_start, kp, vp, w.block_tables, w.context_lens, heads=heads, **kw)
+        assert_close(got[:, heads], outh[:, heads], w.dtype, f"cfg5 seed {seed} heads")

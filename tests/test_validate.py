@@ -1,0 +1,252 @@
+"""Host checks of device-resident arguments (the binding's debug mode).
+
+Every seeded workload passes its own checks; each rule is then broken once,
+on a copy, and must raise ``InvalidContent``.  The attended-block sets are
+compared with the blocks of the positions each definition attends, listed
+one by one.
+"""
+import numpy as np
+import pytest
+
+import workloads as wl
+from paged_kv_cache_30_amd import validate as V
+from paged_kv_cache_30_amd.compressed_tier import CompressedTier
+from paged_kv_cache_30_amd.allocator import BlockAllocator
+
+Bad = V.InvalidContent
+
+
+def dec(w, tables=None, lens=None, mcl=None, window=None, sinks=None):
+    V.check_decode(w.block_tables if tables is None else tables, w.context_lens if lens is None else lens,
+                   max_context_len=w.max_context_len if mcl is None else mcl, num_blocks=w.num_blocks,
+                   block_size=w.block_size, window=w.window if window is None else window,
+                   sinks=w.sinks if sinks is None else sinks)
+
+
+def pre(w, q_start=None, tables=None, lens=None, max_q=None, rows=None):
+    qs = w.q_start if q_start is None else q_start
+    V.check_prefill(qs, w.block_tables if tables is None else tables, w.context_lens if lens is None else lens,
+                    num_rows=int(w.q_start[-1]) if rows is None else rows,
+                    max_q_len=w.max_q_len if max_q is None else max_q, max_context_len=w.max_context_len,
+                    num_blocks=w.num_blocks, block_size=w.block_size, window=w.window, sinks=w.sinks)
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4])
+def test_decode_configs_pass(cfg):
+    dec(wl.config(cfg))
+
+
+def test_decode_rules():
+    w = wl.make_decode(lens=[100, 1, 0, 700], num_heads=8, num_kv_heads=2, head_dim=64, block_size=16,
+                       dtype="f16", seed=1)
+    dec(w)
+    lens = w.context_lens.copy()
+    lens[3] = w.max_context_len + 1
+    with pytest.raises(Bad, match=r"context_lens\[3\]"):
+        dec(w, lens=lens, mcl=w.max_context_len)
+    lens[3] = -1
+    with pytest.raises(Bad, match=r"context_lens\[3\]"):
+        dec(w, lens=lens)
+    for entry in (-1, w.num_blocks):
+        t = w.block_tables.copy()
+        t[0, 6] = entry  # holds positions 96..99 of sequence 0
+        with pytest.raises(Bad, match="sequence 0, logical block 6"):
+            dec(w, tables=t)
+    t = w.block_tables.copy()
+    t[0, 7:] = -7  # past L: never read
+    dec(w, tables=t)
+    with pytest.raises(Bad, match="columns"):
+        dec(w, tables=w.block_tables[:, :10])
+
+
+def test_decode_window_and_sinks():
+    w = wl.make_decode(lens=[1000, 333], num_heads=4, num_kv_heads=4, head_dim=64, block_size=16, dtype="f16",
+                       seed=2, window=100, sinks=4)
+    dec(w)
+    # blocks between the sinks and the window are unmapped and allowed
+    assert (w.block_tables[0, 1:(1000 - 100) // 16] == -1).all()
+    t = w.block_tables.copy()
+    t[0, (1000 - 100) // 16] = -1  # partially covered first window block
+    with pytest.raises(Bad):
+        dec(w, tables=t)
+    t = w.block_tables.copy()
+    t[0, 0] = -1  # sink block
+    with pytest.raises(Bad, match="logical block 0"):
+        dec(w, tables=t)
+    dec(w, tables=t, sinks=0)
+
+
+def test_attended_blocks_match_positions():
+    """The block set equals the blocks of every attended position, listed
+    one by one from the window and sink definitions."""
+    rng = np.random.default_rng(0)
+    for _ in range(400):
+        B = int(rng.choice([16, 32]))
+        L = int(rng.integers(0, 300))
+        window = int(rng.choice([0, 1, 5, 16, 40, 500]))
+        sinks = int(rng.choice([0, 1, 4, 20]))
+        lo = max(0, L - window) if window > 0 else 0
+        pos = [t for t in range(L) if t >= lo or (window > 0 and t < sinks)]
+        want = sorted({t // B for t in pos})
+        got = V._blocks_needed(lo, L, sinks, window, B).tolist()
+        assert got == want, (B, L, window, sinks)
+
+
+@pytest.mark.parametrize("cfg", [5])
+def test_prefill_config_passes(cfg):
+    pre(wl.config(cfg))
+
+
+def test_prefill_rules():
+    w = wl.make_prefill(prefix_len=64, chunk_lens=[40, 1, 0, 100], num_heads=8, num_kv_heads=2, head_dim=128,
+                        block_size=16, dtype="bf16", seed=3)
+    pre(w)
+    qs = w.q_start.copy()
+    qs[0] = 1
+    with pytest.raises(Bad, match=r"q_start\[0\]"):
+        pre(w, q_start=qs)
+    qs = w.q_start.copy()
+    qs[2] = qs[1] - 1
+    with pytest.raises(Bad, match="decreases"):
+        pre(w, q_start=qs)
+    with pytest.raises(Bad, match="rows"):
+        pre(w, rows=int(w.q_start[-1]) - 1)
+    with pytest.raises(Bad, match="max_q_len"):
+        pre(w, max_q=99)
+    lens = w.context_lens.copy()
+    lens[0] = 39  # fewer positions than chunk rows
+    with pytest.raises(Bad, match="query rows but context length"):
+        pre(w, lens=lens)
+    t = w.block_tables.copy()
+    t[3, 0] = -1  # shared prefix block of sequence 3
+    with pytest.raises(Bad, match="sequence 3, logical block 0"):
+        pre(w, tables=t)
+    t = w.block_tables.copy()
+    t[2, :] = -1  # sequence 2 has no rows: nothing is attended
+    pre(w, tables=t)
+
+
+def test_prefill_window_first_row():
+    w = wl.make_prefill(prefix_len=160, chunk_lens=[20], num_heads=4, num_kv_heads=4, head_dim=64,
+                        block_size=16, dtype="bf16", seed=4, window=50)
+    pre(w)
+    # the first row sits at 160 and attends (110, 160]: block 6 is the lowest
+    t = w.block_tables.copy()
+    t[0, :6] = -1
+    pre(w, tables=t)
+    t[0, 6] = -1
+    with pytest.raises(Bad, match="logical block 6"):
+        pre(w, tables=t)
+
+
+def test_write_rules():
+    w = wl.make_decode(lens=[40, 70], num_heads=4, num_kv_heads=4, head_dim=64, block_size=16, dtype="f16",
+                       seed=5)
+    seq = np.array([0, 0, 1, 1], np.int32)
+    pos = np.array([0, 39, 16, 69], np.int32)
+    V.check_write(seq, pos, w.block_tables, num_blocks=w.num_blocks, block_size=16)
+    V.check_write(seq[:0], pos[:0], w.block_tables, num_blocks=w.num_blocks, block_size=16)
+    for s2, p2, msg in ((2, 0, "sequence index"), (-1, 0, "sequence index"), (0, -1, "position"),
+                        (0, w.max_blocks_per_seq * 16, "position")):
+        s_, p_ = seq.copy(), pos.copy()
+        s_[1], p_[1] = s2, p2
+        with pytest.raises(Bad, match=msg):
+            V.check_write(s_, p_, w.block_tables, num_blocks=w.num_blocks, block_size=16)
+    t = w.block_tables.copy()
+    t[1, 4] = -1
+    with pytest.raises(Bad, match="table entry -1"):
+        V.check_write(seq, pos, t, num_blocks=w.num_blocks, block_size=16)
+    p_ = pos.copy()
+    p_[1] = 0
+    with pytest.raises(Bad, match="tokens 0 and 1 write the same slot"):
+        V.check_write(seq, p_, w.block_tables, num_blocks=w.num_blocks, block_size=16)
+    # two sequences whose tables share a block collide in it too
+    t = w.block_tables.copy()
+    t[1, 1] = t[0, 1]
+    s_ = np.array([0, 1], np.int32)
+    p_ = np.array([20, 20], np.int32)
+    with pytest.raises(Bad, match="same slot"):
+        V.check_write(s_, p_, t, num_blocks=w.num_blocks, block_size=16)
+
+
+def test_copy_rules():
+    V.check_copy_blocks(np.array([1, 2]), np.array([3, 4]), num_blocks=5)
+    V.check_copy_blocks(np.array([1, 1]), np.array([3, 4]), num_blocks=5)  # one source, two copies
+    for src, dst, msg in (([5], [1], "src"), ([1], [-1], "dst"), ([2], [2], "onto itself"),
+                          ([1, 2], [3, 3], "two pairs"), ([1, 3], [3, 4], "source and a destination")):
+        with pytest.raises(Bad, match=msg):
+            V.check_copy_blocks(np.array(src), np.array(dst), num_blocks=5)
+
+
+def test_compress_rules():
+    B = 16
+    src = np.array([[0, 1], [2, 3]])
+    V.check_compress(src, np.array([4, 4]), np.array([0, 1]), num_blocks=6, block_size=B)
+    cases = (
+        (np.array([[0, 6], [2, 3]]), [4, 4], [0, 1], "source"),
+        (src, [6, 4], [0, 1], "dst_block"),
+        (src, [4, 4], [0, B], "dst_slot"),
+        (src, [4, 4], [1, 1], "two ops write row 1 of block 4"),
+        (src, [4, 3], [0, 1], "read and written"),
+    )
+    for s, db, ds, msg in cases:
+        with pytest.raises(Bad, match=msg):
+            V.check_compress(s, np.array(db), np.array(ds), num_blocks=6, block_size=B)
+
+
+def comp(w, **over):
+    a = dict(tables=w.block_tables, lens=w.context_lens, full_start=w.full_start, slot_tables=w.slot_tables,
+             num_slots=w.num_slots)
+    a.update(over)
+    V.check_decode_compressed(a["tables"], a["lens"], a["full_start"], a["slot_tables"], a["num_slots"],
+                              max_context_len=w.max_context_len, num_blocks=w.num_blocks,
+                              block_size=w.block_size, window=w.window)
+
+
+def test_compressed_config_passes():
+    comp(wl.config(6))
+
+
+def test_compressed_rules():
+    w = wl.make_compressed(lens=[300, 90], full_start=[128, 0], num_slots=[20, 0], max_slots=32, num_heads=4,
+                           num_kv_heads=2, head_dim=64, block_size=16, dtype="bf16", seed=6)
+    comp(w)
+    fs = w.full_start.copy()
+    fs[1] = 91
+    with pytest.raises(Bad, match=r"full_start\[1\]"):
+        comp(w, full_start=fs)
+    ns = w.num_slots.copy()
+    ns[0] = 33
+    with pytest.raises(Bad, match=r"num_slots\[0\]"):
+        comp(w, num_slots=ns)
+    st = w.slot_tables.copy()
+    st[0, 1] = -1  # holds slot rows 16..19
+    with pytest.raises(Bad, match="slot rows"):
+        comp(w, slot_tables=st)
+    st = w.slot_tables.copy()
+    st[1, :] = -1  # sequence 1 has no slots
+    comp(w, slot_tables=st)
+    t = w.block_tables.copy()
+    t[0, 8] = -1  # position 128, the first held one
+    with pytest.raises(Bad, match="logical block 8"):
+        comp(w, tables=t)
+
+
+def test_compressed_tier_arrays_pass():
+    """What the host tier hands the kernels satisfies the checks at every
+    step of a long append."""
+    B, window, M = 16, 64, 3
+    alloc = BlockAllocator(200, B)
+    tier = CompressedTier(alloc, window=window, max_slots=M)
+    lens = {0: 0, 1: 0}
+    for step in range(60):
+        for s, n in ((0, 7), (1, 3)):
+            _, ops = tier.reserve(s, n)
+            lens[s] += n
+            if ops.dst_block.size:
+                V.check_compress(ops.src_blocks, ops.dst_block, ops.dst_slot, num_blocks=200, block_size=B)
+        tables, L, fs, st, ns = tier.arrays([0, 1])
+        assert L.tolist() == [lens[0], lens[1]]
+        V.check_decode_compressed(tables, L, fs, st, ns, max_context_len=int(max(L)), num_blocks=200,
+                                  block_size=B, window=0)
+    assert tier.num_slots(0) == M and tier.num_slots(1) == M
