@@ -20,7 +20,7 @@ second.  ``roofline`` relates the attention call alone to MI355X's peak (HBM
 8 TB/s; dense bf16/fp16 MFMA 2.5 PFLOP/s).  ``cpu_baseline`` times the fp64
 oracle on the host on a bounded sample of the same workload.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--config 2]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 100] [--config 2]
 """
 from __future__ import annotations
 
@@ -242,7 +242,9 @@ def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=100,
+                    help="untimed steps before the timed ones; 100 lets the clocks settle (the MFMA-bound prefill "
+                         "call is ~20 %% slower in its first milliseconds of load)")
     ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5, 6],
                     help="workload: 1 tiny fp32 decode, 2 batched MHA decode (default), 3 long GQA decode, "
                          "4 sliding-window decode, 5 chunked prefill over a shared prefix, 6 decode over a "
