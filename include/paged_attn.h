@@ -194,10 +194,13 @@ int paged_attn_decode(const pkv_geometry_t* geom, float* out, float* lse, const 
  *   max_q_len        host bound on the chunk lengths
  *   max_context_len  host bound on context_lens (<= max_blocks_per_seq * B)
  * Requires C <= L for every sequence. Scores and outputs accumulate in
- * float32. The softmax weights multiply V on the matrix cores: rounded to
- * fp16 for PKV_F16; for PKV_BF16 each weight is split into two bf16 parts
- * (high part and rounded remainder) that are both multiplied, which keeps
- * about 16 significant bits. */
+ * float32. The softmax weights multiply V on the fp16 matrix cores for both
+ * input types: each weight is rounded to fp16 (11 significant bits), and a
+ * bf16 V is converted to fp16 (exact for |v| in [2^-17, 65504]; smaller
+ * magnitudes keep their bits down to 2^-24, larger ones saturate). The
+ * output divides by the sum of the weights as rounded, and lse uses the
+ * same sum: within 2^-11 relative of the exact sum, plus 2^-25 per
+ * subnormal weight against a sum of at least 1, so lse is within 6e-4. */
 int paged_attn_prefill(const pkv_geometry_t* geom, float* out, float* lse, const void* q,
                        const int32_t* q_start, const void* k_pool, const void* v_pool,
                        const int32_t* block_tables, int32_t max_blocks_per_seq,

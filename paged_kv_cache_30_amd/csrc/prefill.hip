@@ -24,7 +24,9 @@
 //    of key j/4 and lane i receives dim i of those 4 keys.
 //  * P.V runs on the fp16 matrix cores for both input types, with the
 //    weights rounded to fp16 (11-bit mantissa) and the normaliser summing
-//    the weights as used. A bf16 V tile is converted to fp16 in LDS once it
+//    the weights as used; lse takes the same sum, which is within 2^-11
+//    relative of the sum of the unrounded weights (plus at most 2^-25 per
+//    subnormal weight, against a sum of at least 1). A bf16 V tile is converted to fp16 in LDS once it
 //    has arrived: each thread rewrites the 16-byte units its own direct
 //    loads wrote, before the tile's barrier. The conversion is exact for
 //    |v| in [2^-17, 65504] (bf16 has 8 significant bits); smaller values are
@@ -36,7 +38,10 @@
 //    on the reference, so this is exact up to rounding.
 //  * Masked keys (causal, window, unmapped blocks) are removed by selection
 //    (score -inf); V rows outside the loaded range are zero-filled so a
-//    zero weight never meets a NaN.
+//    zero weight never meets a NaN. Every K and V row multiplied is thus a
+//    written row or zeros, and every score finite or -inf: this file is
+//    compiled with -fno-honor-nans, which lets the maximum skip quieting its
+//    operands.
 #include "common.h"
 #include "launch.h"
 
@@ -243,7 +248,6 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a, float sc
   for (int dt = 0; dt < DT; ++dt) o[dt] = f32x16{};
   float m_run = -INFINITY;  // running max of the scaled scores (base 2)
   float l_run = 0.f;        // sum of the weights as multiplied (normaliser)
-  float l_lse = 0.f;        // exact fp32 sum, for lse (differs when weights are rounded)
 
   const int wave_pmin = base + row0;
   const int wave_pmax = base + min(row0 + 31, C - 1);
@@ -402,7 +406,6 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a, float sc
         const float mn = fmaxf(m_run, mt);
         const float alpha = __builtin_amdgcn_exp2f(m_run - (mn == -INFINITY ? 0.f : mn));
         l_run *= alpha;
-        l_lse *= alpha;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
         m_run = mn;
@@ -432,7 +435,6 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a, float sc
           const uint32_t h = MP::pack(p0, p1);
           hi[e2] = h;
           l_run = __builtin_amdgcn_fdot2(as_h2(h), f16x2{(_Float16)1.f, (_Float16)1.f}, l_run, false);
-          l_lse += p0 + p1;
         }
         const P8 bhi = __builtin_bit_cast(P8, u32x4{hi[0], hi[1], hi[2], hi[3]});
         lds_wait();
@@ -486,9 +488,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a, float sc
     }
   }
   if (a.lse) {
-    const float l_exact = l_lse + __shfl_xor(l_lse, 32, 64);
     if (hf == 0)
-      a.lse[(size_t)(r0 + my_row) * a.H + hq] = l_exact > 0.f ? (m_run + __log2f(l_exact)) * kLn2 : -INFINITY;
+      a.lse[(size_t)(r0 + my_row) * a.H + hq] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
   }
 }
 

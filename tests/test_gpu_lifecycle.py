@@ -110,7 +110,10 @@ def test_mixed_batch(lib, case):
     out, lse = ref.prefill(w.q, w.q_start, kp, vp, w.block_tables, w.context_lens, block_size=B,
                            num_kv_heads=Hkv, window=window, scale=w.scale, dtype=dtype, sinks=sinks)
     max_err(got, out, str(case))
-    assert np.abs(got_lse - lse).max() <= 1e-4
+    # decode rows sum fp32 weights; prefill rows sum the fp16-rounded weights
+    # the matrix cores multiply (within 2^-11 relative, plus 2^-25 per
+    # subnormal weight against a sum of at least 1: below 6e-4 in lse)
+    assert np.abs(got_lse - lse).max() <= 6e-4
 
 
 # -------------------------------------------------- serving flow, end to end

@@ -18,6 +18,12 @@ pytestmark = pytest.mark.gpu
 
 TOL_ABS_16 = 2e-3
 TOL_REL_32 = 1e-5
+# lse: decode sums the fp32 weights (1e-4 covers fp32 accumulation); prefill
+# sums its weights as rounded to fp16 for the matrix cores, within 2^-11
+# relative of the exact sum plus 2^-25 per subnormal weight against a sum of
+# at least 1 (a few thousand keys): |error| <= 4.9e-4 + 0.8e-4 < 6e-4.
+TOL_LSE = 1e-4
+TOL_LSE_PREFILL = 6e-4
 
 
 def note(msg):
@@ -72,12 +78,14 @@ def run(session, w, **kw):
     return d
 
 
-def check_lse(d, want_lse):
+def check_lse(d, want_lse, tol=TOL_LSE):
     got = d.lse.cpu().numpy().astype(np.float64)
     fin = np.isfinite(want_lse)
     assert np.array_equal(fin, np.isfinite(got))
     assert np.all(np.isneginf(got[~fin]))
-    assert np.abs(got[fin] - want_lse[fin]).max(initial=0) <= 1e-4
+    err = np.abs(got[fin] - want_lse[fin]).max(initial=0)
+    note(f"lse max abs err {err:.3g}")
+    assert err <= tol
 
 
 # ------------------------------------------------------------------ write
@@ -291,7 +299,7 @@ def test_prefill_small(lib, case):
     kp, vp = ref.build_pools(w)
     out, lse = oracle_prefill(w, kp, vp)
     assert_close(d.out.cpu().numpy(), out, dtype, str(case))
-    check_lse(d, lse)
+    check_lse(d, lse, TOL_LSE_PREFILL)
 
 
 def test_prefill_config5(lib):
@@ -553,7 +561,7 @@ def test_prefill_sinks(lib, case):
     out, lse = ref.prefill(w.q, w.q_start, kp, vp, w.block_tables, w.context_lens, block_size=B,
                            num_kv_heads=Hkv, window=window, scale=w.scale, dtype=dtype, sinks=sinks)
     assert_close(d.out.cpu().numpy(), out, dtype, str(case))
-    check_lse(d, lse)
+    check_lse(d, lse, TOL_LSE_PREFILL)
 
 
 # ----------------------------------------------------- batch and length limits
