@@ -245,10 +245,11 @@ def main(argv=None) -> int:
     ap.add_argument("--warmup", type=int, default=100,
                     help="untimed steps before the timed ones; 100 lets the clocks settle (the MFMA-bound prefill "
                          "call is ~20 %% slower in its first milliseconds of load)")
-    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5, 6],
+    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5, 6, 7],
                     help="workload: 1 tiny fp32 decode, 2 batched MHA decode (default), 3 long GQA decode, "
                          "4 sliding-window decode, 5 chunked prefill over a shared prefix, 6 decode over a "
-                         "compressed-slot tier (window 256, 16 slots)")
+                         "compressed-slot tier (window 256, 16 slots), 7 long decode with 8 query heads per "
+                         "kv head")
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--workers", type=int, default=0, help="decode wavefront workers (0 = automatic)")
     ap.add_argument("--kv", choices=["native", "i8", "fp8"], default="native",

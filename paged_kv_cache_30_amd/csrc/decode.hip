@@ -86,7 +86,11 @@ struct DecodeShape {
   // Pieces of a K/V row per lane: with 4 or more query heads per kv head the
   // per-position softmax work, done redundantly by every lane of a row, is
   // halved by giving each lane two pieces (fewer lanes per row).
-  static constexpr int PIECES = (G >= 4 && D * EB / 16 >= 16) ? 2 : 1;
+  // (Not with scores on the matrix cores, see MQK: the exchange that hands
+  // each lane its row's scores makes the softmax cheap, and one piece per
+  // lane halves the output registers.)
+  static constexpr bool MQK8 = !T::QUANT && EB == 2 && G >= 8 && D == 128;
+  static constexpr int PIECES = (G >= 4 && D * EB / 16 >= 16 && !MQK8) ? 2 : 1;
   static constexpr int LPR = D * EB / 16 / PIECES;     // lanes per K/V row
   static constexpr int RPL = 64 / LPR;                 // rows per step
   static constexpr int STEPS = B / RPL;                // steps per block
@@ -99,7 +103,33 @@ struct DecodeShape {
   static constexpr int CHUNK = RPL * CSTEPS;           // slots per chunk
   static constexpr int CPB = B / CHUNK;                // chunks per block
   static_assert(LPR >= 4 && LPR <= 32 && B % CHUNK == 0, "shape");
+  // Scores on the matrix cores: 16-bit pools with 8 query heads per kv
+  // head, in chunks of 16 positions. The chunk's K registers (CSTEPS *
+  // PIECES = D / 32 per lane) then hold exactly the D / 32 B operands of a
+  // 16x16x32 MFMA chain. With 4 heads the dot products on the vector ALU
+  // are cheaper than the chain's latency and the exchange (measured).
+  static constexpr bool MQK = MQK8 && CHUNK == 16;
+  // Workgroups per CU the register budget is set for: two for the matrix-
+  // core instances (two wavefronts per SIMD, at the cost of a few spilled
+  // registers), else whatever the compiler needs.
+  static constexpr int MIN_WG = MQK ? 2 : 1;
 };
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// One v_mfma_f32_16x16x32 of the 16-bit type: lane l supplies A[l % 16][8 (l / 16) + e]
+// and B[8 (l / 16) + e][l % 16] (e = 0..7) and receives C[4 (l / 16) + i][l % 16] (i = 0..3).
+template <class T> __device__ __forceinline__ f32x4_t mma16(const u32x4& a, const u32x4& b, f32x4_t c);
+template <> __device__ __forceinline__ f32x4_t mma16<BF16T>(const u32x4& a, const u32x4& b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
+                                                 0, 0, 0);
+}
+template <> __device__ __forceinline__ f32x4_t mma16<F16T>(const u32x4& a, const u32x4& b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c, 0,
+                                                0, 0);
+}
 
 // Attended blocks of sequence s, L clamped to [0, max_ctx]. The full-
 // resolution positions are [lo, L): lo = max(0, L - window) with a window,
@@ -206,7 +236,8 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(DecodeArgs a)
 // T: storage type of the pools; Q: type of q (T itself, or fp16/bf16 for the
 // 8-bit pools, whose rows also carry a scale each).
 template <class T, class Q, int D, int B, int G>
-__global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, float scale_log2) {
+__global__ __launch_bounds__(kThreads, (DecodeShape<T, D, B, G>::MIN_WG)) void decode_split_kernel(DecodeArgs a,
+                                                                                                float scale_log2) {
   using Sh = DecodeShape<T, D, B, G>;
   constexpr int E = Sh::E, LPR = Sh::LPR, RPL = Sh::RPL, CSTEPS = Sh::CSTEPS, CHUNK = Sh::CHUNK,
                 CPB = Sh::CPB, EB = Sh::EB, PC = Sh::PIECES;
@@ -216,6 +247,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, fl
   constexpr int QW = E * QB / 16;    // 16-byte words of q per piece
   constexpr float BIAS = T::BIAS;
   static_assert(QU || (QB == EB && QW == 1), "q has the pools' type unless the pools are 8-bit");
+  constexpr bool MQK = Sh::MQK;
+  constexpr int KS = D / 32;  // MFMA k-steps over the head dim (matrix-core scores)
 
   const int lane = threadIdx.x & 63;
   // Prefix of attended blocks, in one of three places: batches of fewer than
@@ -305,13 +338,27 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, fl
 
     const char* qb = (const char*)a.q + ((size_t)(q_row(a, s) * H + g * G) * D + c * E) * QB;
     u32x4 qv[G][PC][QW];
+    // Matrix-core scores: A operand = q of the group (row l % 16 = head,
+    // zero beyond G), dims 8 (l / 16) + 32 ks.
+    u32x4 qm[KS];
+    if constexpr (MQK) {
+      const int hh = lane & 15;  // rows past the group read head G - 1 and are zeroed
+      const char* qa =
+          (const char*)a.q + ((size_t)(q_row(a, s) * H + g * G + min(hh, G - 1)) * D + 8 * (lane >> 4)) * QB;
 #pragma unroll
-    for (int h = 0; h < G; ++h)
+      for (int ks = 0; ks < KS; ++ks) {
+        const u32x4 v = load16(qa + (size_t)ks * 32 * QB);
+        qm[ks] = hh < G ? v : u32x4{0, 0, 0, 0};
+      }
+    } else {
 #pragma unroll
-      for (int pc = 0; pc < PC; ++pc)
+      for (int h = 0; h < G; ++h)
 #pragma unroll
-        for (int qw = 0; qw < QW; ++qw)
-          qv[h][pc][qw] = load16(qb + (size_t)h * D * QB + (size_t)pc * LPR * E * QB + qw * 16);
+        for (int pc = 0; pc < PC; ++pc)
+#pragma unroll
+          for (int qw = 0; qw < QW; ++qw)
+            qv[h][pc][qw] = load16(qb + (size_t)h * D * QB + (size_t)pc * LPR * E * QB + qw * 16);
+    }
     // INT8: the sum of this lane's q values, for the BIAS correction of its
     // partial dot products; lvb: the running sum of the V weights (same role).
     float qsum[G], lvb[G];
@@ -336,7 +383,11 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, fl
       }
     }
     const size_t lane_off = (size_t)g * D * EB + (size_t)c * 16 + (size_t)r * row_stride;
-    const char* kbase = (const char*)a.k_pool + lane_off;
+    // K lanes for matrix-core scores: position l % 16 of the chunk, dims
+    // 8 (l / 16) + 32 ks (16 bytes at 64 ks bytes further per k-step).
+    const char* kbase = (const char*)a.k_pool +
+                        (MQK ? (size_t)g * D * EB + (size_t)(lane & 15) * row_stride + (size_t)(lane >> 4) * 16
+                             : lane_off);
     const char* vbase = (const char*)a.v_pool + lane_off;
 
     // Loads of chunk k of the segment; false when its table entry is out of
@@ -356,11 +407,18 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, fl
           vs[j] = a.v_scale[sidx + j * RPL];
         }
       }
+      if constexpr (MQK) {  // k-step ks = j * PC + pc
 #pragma unroll
-      for (int j = 0; j < CSTEPS; ++j)
+        for (int j = 0; j < CSTEPS; ++j)
 #pragma unroll
-        for (int pc = 0; pc < PC; ++pc)
-          kr[j][pc] = load_stream(kbase + off + (size_t)j * RPL * row_stride + pc * PSTRIDE);
+          for (int pc = 0; pc < PC; ++pc) kr[j][pc] = load_stream(kbase + off + (size_t)(j * PC + pc) * 32 * EB);
+      } else {
+#pragma unroll
+        for (int j = 0; j < CSTEPS; ++j)
+#pragma unroll
+          for (int pc = 0; pc < PC; ++pc)
+            kr[j][pc] = load_stream(kbase + off + (size_t)j * RPL * row_stride + pc * PSTRIDE);
+      }
 #pragma unroll
       for (int j = 0; j < CSTEPS; ++j)
 #pragma unroll
@@ -379,6 +437,26 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, fl
       const bool pre = b_first + bi < at.sb;
       const bool full = pre ? t0 + CHUNK <= at.plim : (t0 >= lo || t0 + CHUNK <= a.sinks) && t0 + CHUNK <= L;
       float sc[CSTEPS][G];
+      if constexpr (MQK) {
+        // C[head][position] of the chunk: lane l holds heads 4 (l / 16) + i
+        // of position l % 16. Each lane then takes the scores of its row
+        // (position j * RPL + r) from lane position + 16 (h / 4).
+        f32x4_t cm = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) cm = mma16<T>(qm[ks], kr[ks / PC][ks % PC], cm);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) cm[i] *= scale_log2;
+        // (The element is copied to a scalar first: a bit cast of a vector
+        // element in place reads element 0 whatever the index.)
+        int cv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) cv[i] = __float_as_int((float)cm[i]);
+#pragma unroll
+        for (int j = 0; j < CSTEPS; ++j)
+#pragma unroll
+          for (int h = 0; h < G; ++h)
+            sc[j][h] = __int_as_float(__builtin_amdgcn_ds_bpermute(4 * (j * RPL + r + 16 * (h >> 2)), cv[h & 3]));
+      } else {
 #pragma unroll
       for (int j = 0; j < CSTEPS; ++j) {
 #pragma unroll
@@ -395,6 +473,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, fl
             sc[j][h] = group_sum<LPR>(x) * scale_log2;
           }
         }
+      }
       }
       if (!full) {
 #pragma unroll

@@ -138,6 +138,11 @@ DECODE_CASES = [
     ("f32", 4, 2, 64, 16, [10, 70], 16, 3),
     ("bf16", 32, 8, 128, 16, [0, 0, 2000, 0, 4100, 1], 0, 0),
     ("f16", 64, 8, 128, 16, [300, 20000, 7], 0, 0),
+    # 8 query heads per kv head: scores on the matrix cores (16-bit, D = 128)
+    ("bf16", 64, 8, 128, 32, [1, 15, 16, 17, 33, 1000, 5000], 0, 0),
+    ("bf16", 64, 8, 128, 32, [1, 15, 16, 17, 33, 1000, 5000], 0, 9),
+    ("f16", 32, 4, 128, 16, [20, 700, 2100], 300, 0),
+    ("bf16", 16, 2, 64, 32, [40, 600, 1500], 0, 0),
 ]
 
 
@@ -186,6 +191,26 @@ def test_decode_config3_sampled(lib):
                                      scale=w.scale, dtype="bf16")
         assert_close(got[s], o, "bf16", f"cfg3 seq {s}")
         assert np.abs(got_lse[s] - l).max() <= 1e-4
+
+
+def test_decode_config7_sampled(lib):
+    """Long decode with 8 query heads per kv head (scores on the matrix cores)
+    at full size: the longest, the shortest and four more sequences, every
+    head, against the contiguous (never paged) oracle."""
+    pkv, session = lib
+    note("decode cfg7 sampled")
+    w = wl.config(7)
+    d = run(session, w)
+    got = d.out.cpu().numpy()
+    got_lse = d.lse.cpu().numpy()
+    order = np.argsort(w.context_lens)
+    pick = sorted(set([int(order[0]), int(order[-1])] + list(np.random.default_rng(7).choice(32, 4, replace=False))))
+    for s in pick:
+        first, k, v = w.logical_kv(s)
+        o, l = ref.contiguous_decode(w.q[s], k, v, first, int(w.context_lens[s]), num_kv_heads=8, window=0,
+                                     scale=w.scale, dtype="bf16")
+        assert_close(got[s], o, "bf16", f"cfg7 seq {s}")
+        assert np.abs(got_lse[s] - l).max() <= TOL_LSE
 
 
 def test_decode_config4_contiguous(lib):
@@ -470,6 +495,7 @@ SINK_CASES = [
     ("bf16", 8, 1, 64, 16, [5, 64, 700], 30, 20, 3),
     ("f32", 4, 2, 64, 16, [10, 170, 90], 16, 40, 0),
     ("bf16", 32, 8, 128, 16, [2000, 4100, 1], 256, 1, 48),
+    ("bf16", 64, 8, 128, 32, [2000, 4100, 1], 256, 4, 0),
 ]
 
 

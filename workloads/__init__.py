@@ -444,8 +444,9 @@ def repermute(w: Workload, seed_perm: int) -> Workload:
     return dataclasses.replace(w, block_tables=tables)
 
 
-# The five workloads: a tiny fp32 decode, batched MHA decode, long-context GQA
-# decode, sliding-window decode and chunked prefill over a shared prefix.
+# The workloads: a tiny fp32 decode, batched MHA decode, long-context GQA
+# decode, sliding-window decode, chunked prefill over a shared prefix, decode
+# over a compressed-slot tier and long decode with 8 query heads per kv head.
 CONFIG_NAMES = {
     1: "tiny_decode_mha4_d64_b16_L100_f32",
     2: "batched_mha_decode_s32_h32_d128_b16_f16",
@@ -453,11 +454,12 @@ CONFIG_NAMES = {
     4: "sliding_window_decode_s16_h32kv8_d128_b16_w4096_bf16",
     5: "chunked_prefill_shared_prefix_s8_h32kv8_d128_b16_bf16",
     6: "compressed_tier_decode_s512_h32kv8_d128_b16_w256_m16_bf16",
+    7: "gqa8_long_decode_s32_h64kv8_d128_b32_bf16",
 }
 
 
 def config(idx: int, seed: Optional[int] = None) -> Workload:
-    """Build one of the five workloads.  ``seed`` defaults to the index."""
+    """Build one of the workloads by index.  ``seed`` defaults to the index."""
     seed = idx if seed is None else seed
     name = CONFIG_NAMES[idx]
     if idx == 1:
@@ -495,4 +497,11 @@ def config(idx: int, seed: Optional[int] = None) -> Workload:
         return make_compressed(lens=fs + held, full_start=fs, num_slots=np.full(512, 16), max_slots=16,
                                num_heads=32, num_kv_heads=8, head_dim=128, block_size=16, dtype="bf16", seed=seed,
                                max_blocks_per_seq=2048, name=name)
+    if idx == 7:
+        # Long-context decode with 8 query heads per kv head (64 query heads
+        # over 8 kv heads), otherwise drawn like workload 3.
+        u = stream(seed, TAG_LENGTHS).uniform(math.log(1024), math.log(32768), size=32)
+        lens = np.clip(np.floor(np.exp(u)), 1024, 32768).astype(np.int64)
+        return make_decode(lens=lens, num_heads=64, num_kv_heads=8, head_dim=128, block_size=32,
+                           dtype="bf16", seed=seed, k_scale=3.0, max_blocks_per_seq=1024, name=name)
     raise KeyError(idx)
