@@ -99,6 +99,7 @@ DECODE_CASES = [
     ("f16", 16, 4, 128, 16, [33, 48, 1200, 0], [32, 16, 1100, 0], [4, 4, 4, 0], 4, 0, 3),
     ("bf16", 8, 1, 128, 32, [4000, 17], [3800, 0], [64, 64], 64, 0, 0),
     ("bf16", 32, 8, 128, 16, [700, 800], [512, 640], [20, 99], 16, 50, 1000),
+    ("f16", 64, 8, 128, 16, [500, 900, 77], [256, 512, 0], [8, 16, 0], 16, 100, 0),
 ]
 
 

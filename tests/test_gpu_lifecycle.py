@@ -86,6 +86,7 @@ MIXED_CASES = [
     ("f16", 8, 2, 64, 32, 100, [64, 1, 1, 7], 0, 0, 5),
     ("bf16", 16, 4, 128, 16, 500, [1, 1, 1], 0, 0, 0),
     ("bf16", 8, 8, 128, 16, 160, [90, 1, 31, 1], 50, 4, 0),
+    ("bf16", 64, 8, 128, 32, 256, [1, 100, 1, 1], 0, 0, 0),
 ]
 
 
