@@ -119,55 +119,59 @@ def traffic_for(kernel_key: str, src: str):
 
 
 def cpu_baseline(w, target_s: float):
-    """fp64 oracle on the host, one thread, on the first sequences of the
-    workload until about target_s seconds of work (whole workload if less)."""
+    """fp64 oracle on the host cores (NumPy, its BLAS free to use every
+    visible core), on the first sequences of the workload until about
+    target_s seconds of work (whole workload if less)."""
+    import os
     import numpy as np
     import oracle.compressed as oc
     import oracle.ref as ref
+    cores = len(os.sched_getaffinity(0))
+    threads = cores
     try:
-        from threadpoolctl import threadpool_limits
+        from threadpoolctl import threadpool_info
+        blas = [d.get("num_threads", 0) for d in threadpool_info() if d.get("user_api") == "blas"]
+        if blas:
+            threads = max(blas)
     except ImportError:  # pragma: no cover
-        threadpool_limits = None
+        pass
     kp, vp = ref.build_pools(w)
-    import contextlib
-    ctx = threadpool_limits(limits=1) if threadpool_limits else contextlib.nullcontext()
     eb = {"f32": 4, "f16": 2, "bf16": 2}[w.dtype]
     done, elapsed, units = 0, 0.0, 0.0
-    with ctx:
-        while done < w.num_seqs and elapsed < target_s:
-            t = time.perf_counter()
-            if w.kind == "decode" and w.full_start is not None:
-                s = [done]
-                oc.decode_compressed(w.q[s], kp, vp, w.block_tables[s], w.context_lens[s], w.full_start[s],
-                                     w.slot_tables[s], w.num_slots[s], block_size=w.block_size,
-                                     num_kv_heads=w.num_kv_heads, window=w.window, scale=w.scale, dtype=w.dtype)
-                L = int(w.context_lens[done])
-                n = L - max(int(w.full_start[done]), L - w.window if w.window > 0 else 0) + int(w.num_slots[done])
-                units += n * w.num_kv_heads * w.head_dim * 2 * eb
-            elif w.kind == "decode":
-                ref.decode(w.q, kp, vp, w.block_tables, w.context_lens, block_size=w.block_size,
-                           num_kv_heads=w.num_kv_heads, window=w.window, scale=w.scale, dtype=w.dtype,
-                           seqs=[done])
-                L = int(w.context_lens[done])
-                n = min(L, w.window) if w.window > 0 else L
-                units += n * w.num_kv_heads * w.head_dim * 2 * eb
-            else:
-                ref.prefill(w.q, w.q_start, kp, vp, w.block_tables, w.context_lens, block_size=w.block_size,
-                            num_kv_heads=w.num_kv_heads, window=w.window, scale=w.scale, dtype=w.dtype,
-                            seqs=[done])
-                C = int(w.q_start[done + 1] - w.q_start[done])
-                L = int(w.context_lens[done])
-                pairs = sum((L - C + i + 1) if w.window <= 0 else min(L - C + i + 1, w.window) for i in range(C))
-                units += 4 * w.head_dim * w.num_heads * pairs
-            elapsed += time.perf_counter() - t
-            done += 1
+    while done < w.num_seqs and elapsed < target_s:
+        t = time.perf_counter()
+        if w.kind == "decode" and w.full_start is not None:
+            s = [done]
+            oc.decode_compressed(w.q[s], kp, vp, w.block_tables[s], w.context_lens[s], w.full_start[s],
+                                 w.slot_tables[s], w.num_slots[s], block_size=w.block_size,
+                                 num_kv_heads=w.num_kv_heads, window=w.window, scale=w.scale, dtype=w.dtype)
+            L = int(w.context_lens[done])
+            n = L - max(int(w.full_start[done]), L - w.window if w.window > 0 else 0) + int(w.num_slots[done])
+            units += n * w.num_kv_heads * w.head_dim * 2 * eb
+        elif w.kind == "decode":
+            ref.decode(w.q, kp, vp, w.block_tables, w.context_lens, block_size=w.block_size,
+                       num_kv_heads=w.num_kv_heads, window=w.window, scale=w.scale, dtype=w.dtype,
+                       seqs=[done])
+            L = int(w.context_lens[done])
+            n = min(L, w.window) if w.window > 0 else L
+            units += n * w.num_kv_heads * w.head_dim * 2 * eb
+        else:
+            ref.prefill(w.q, w.q_start, kp, vp, w.block_tables, w.context_lens, block_size=w.block_size,
+                        num_kv_heads=w.num_kv_heads, window=w.window, scale=w.scale, dtype=w.dtype,
+                        seqs=[done])
+            C = int(w.q_start[done + 1] - w.q_start[done])
+            L = int(w.context_lens[done])
+            pairs = sum((L - C + i + 1) if w.window <= 0 else min(L - C + i + 1, w.window) for i in range(C))
+            units += 4 * w.head_dim * w.num_heads * pairs
+        elapsed += time.perf_counter() - t
+        done += 1
     if w.kind == "decode":
         value, unit = units / elapsed / 1e9, "GB/s"
     else:
         value, unit = units / elapsed / 1e12, "TFLOP/s"
-    return {"value": round(value, 4), "unit": unit, "cores": 1, "kind": "oracle",
+    return {"value": round(value, 4), "unit": unit, "cores": threads, "kind": "oracle",
             "sample": f"first {done} of {w.num_seqs} sequences (all heads), fp64 NumPy oracle, "
-                      f"{elapsed:.2f} s, one BLAS thread"}
+                      f"{elapsed:.2f} s, BLAS threads {threads} of {cores} visible cores"}
 
 
 KERNELS = {"decode": ("decode_split_kernel", "decode_merge_kernel", "decode_plan_kernel"),
