@@ -680,3 +680,66 @@ def test_configs_robustness_seeds(lib, cfg, seed):
         heads = [1, 16, 30]
         outh, _ = ref.prefill(w.q, w.q_start, kp, vp, w.block_tables, w.context_lens, heads=heads, **kw)
         assert_close(got[:, heads], outh[:, heads], w.dtype, f"cfg5 seed {seed} heads")
+
+
+# ------------------------------------------------------ pools beyond 4 GiB
+
+def test_decode_pool_beyond_4gib(lib):
+    """Pools of 12.2 GiB each (400k blocks of 32 KB): the sequences' blocks
+    are scattered over the whole pool, most of them at byte offsets above
+    2^32, so every address computation of the write and of decode needs 64
+    bits. Checked against attention over each sequence's logical rows (no
+    host copy of the pool)."""
+    pkv, session = lib
+    note("decode, pools beyond 4 GiB")
+    w = wl.make_decode(lens=[5000, 333, 17, 2048], num_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
+                       dtype="bf16", seed=61, k_scale=3.0, spare_blocks=400000)
+    blk_bytes = 16 * 8 * 128 * 2
+    assert w.num_blocks * blk_bytes > 12 * 2 ** 30
+    mapped = w.block_tables[w.block_tables >= 0]
+    assert (mapped.astype(np.int64) * blk_bytes >= 2 ** 32).mean() > 0.5
+    d = run(session, w)
+    got = d.out.cpu().numpy()
+    got_lse = d.lse.cpu().numpy()
+    for s in range(w.num_seqs):
+        first, k, v = w.logical_kv(s)
+        o, l = ref.contiguous_decode(w.q[s], k, v, first, int(w.context_lens[s]), num_kv_heads=8, window=0,
+                                     scale=w.scale, dtype="bf16")
+        assert_close(got[s], o, "bf16", f"4GiB+ pool seq {s}")
+        assert np.abs(got_lse[s] - l).max() <= TOL_LSE
+    del d
+    torch.cuda.empty_cache()
+
+
+def test_prefill_pool_beyond_4gib(lib):
+    """Chunked prefill over pools of 12.2 GiB each (400k blocks), the prefix
+    and chunk blocks spread over the whole pool: sampled rows of every
+    sequence against attention over its logical rows up to the row's
+    position."""
+    pkv, session = lib
+    note("prefill, pools beyond 4 GiB")
+    w = wl.make_prefill(prefix_len=512, chunk_lens=[300, 64, 1], num_heads=16, num_kv_heads=8, head_dim=128,
+                        block_size=16, dtype="bf16", seed=62, spare_blocks=400000)
+    blk_bytes = 16 * 8 * 128 * 2
+    mapped = w.block_tables[w.block_tables >= 0]
+    assert (mapped.astype(np.int64) * blk_bytes >= 2 ** 32).mean() > 0.5
+    d = run(session, w)
+    got = d.out.cpu().numpy()
+    for s in range(w.num_seqs):
+        first, k, v = w.logical_kv(s)
+        assert first == 0
+        L = int(w.context_lens[s])
+        C = int(w.q_start[s + 1] - w.q_start[s])
+        for i in sorted({0, C // 2, C - 1}):
+            p = L - C + i
+            row = int(w.q_start[s]) + i
+            qf = ref.to_f64(w.q[row], "bf16")
+            want = np.zeros((16, 128))
+            for g in range(8):
+                K = ref.to_f64(k[:p + 1, g], "bf16")
+                V = ref.to_f64(v[:p + 1, g], "bf16")
+                o, _ = ref.attend(qf[2 * g:2 * g + 2], K, V, w.scale)
+                want[2 * g:2 * g + 2] = o
+            assert_close(got[row], want, "bf16", f"4GiB+ prefill seq {s} row {i}")
+    del d
+    torch.cuda.empty_cache()

@@ -365,12 +365,14 @@ def make_compressed(*, lens, full_start, num_slots, max_slots, num_heads, num_kv
 
 def make_prefill(*, prefix_len, chunk_lens, num_heads, num_kv_heads, head_dim, block_size,
                  dtype, seed, window=0, scale=None, share_prefix=True, max_blocks_per_seq=None,
-                 sinks=0, name="prefill") -> Workload:
+                 sinks=0, spare_blocks=0, name="prefill") -> Workload:
     """Chunked prefill: every sequence has a common prefix of ``prefix_len``
     tokens (already cached) followed by its own chunk of ``chunk_lens[s]``
     query tokens.  With ``share_prefix`` the prefix blocks are one set of
     physical blocks mapped by every table (``prefix_len`` must then be a
     multiple of the block size); otherwise each sequence gets private copies.
+    ``spare_blocks`` unused blocks widen the pool (the used ids are spread over
+    all of it).
     """
     chunk_lens = [int(c) for c in chunk_lens]
     S = len(chunk_lens)
@@ -382,7 +384,7 @@ def make_prefill(*, prefix_len, chunk_lens, num_heads, num_kv_heads, head_dim, b
     priv = [((int(L) + B - 1) // B) - pb for L in lens]
     need_mb = max([pb + p for p in priv] + [1])
     mb = max_blocks_per_seq if max_blocks_per_seq is not None else need_mb
-    nb = max(pb + sum(priv), 1)
+    nb = max(pb + sum(priv) + int(spare_blocks), 1)
     perm = stream(seed, TAG_PERM).permutation(nb).astype(np.int32)
     tables = np.full((S, mb), -1, dtype=np.int32)
     at = pb
