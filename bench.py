@@ -175,7 +175,14 @@ def cpu_baseline(w, target_s: float):
 
 
 KERNELS = {"decode": ("decode_split_kernel", "decode_merge_kernel", "decode_plan_kernel"),
-           "prefill": ("prefill_kernel",)}
+           "prefill": ("prefill_kernel", "widen_kernel")}
+
+
+def attend_sources(kind: str, kv: str):
+    """Source files of the kernels one attention call launches."""
+    if kind == "decode":
+        return ("decode.hip", "common.h")
+    return ("prefill.hip", "common.h") + (("widen.hip",) if kv != "native" else ())
 
 
 def summarize_pmc(args, fetch_dir, write_dir, copy_mib) -> int:
@@ -215,10 +222,12 @@ def summarize_pmc(args, fetch_dir, write_dir, copy_mib) -> int:
         copy_val = max(copies)[1] if copies else None
         scale = copy_bytes / (copy_val * 1024.0) if copy_val else 1.0
         ours = sorted((i, k, v) for (i, k), v in vals.items() if any(n in k for n in KERNELS[kind]))
-        # group consecutive dispatches of one call: the split/prefill kernel starts a call
+        # group consecutive dispatches of one call: the split/prefill kernel
+        # starts a call, the widening kernel over 8-bit pools
+        first = "widen_kernel" if (kind == "prefill" and args.kv != "native") else KERNELS[kind][0]
         calls, cur = [], None
         for i, k, v in ours:
-            if KERNELS[kind][0] in k:
+            if first in k:
                 cur = [v]
                 calls.append(cur)
             elif cur is not None:
@@ -227,7 +236,7 @@ def summarize_pmc(args, fetch_dir, write_dir, copy_mib) -> int:
         out[counter] = {"kib_per_call_raw": round(sum(sum(c) for c in calls) / max(len(calls), 1), 1),
                         "calls": len(calls), "copy_kib_raw": copy_val, "scale": round(scale, 4),
                         "bytes_per_call": round(sum(per_call) / max(len(per_call), 1))}
-    src = source_hash("decode.hip", "common.h") if kind == "decode" else source_hash("prefill.hip", "common.h")
+    src = source_hash(*attend_sources(kind, args.kv))
     key = f"paged_attn_{kind}|{w.name}" + ("" if args.kv == "native" else f"|{args.kv}")
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
@@ -257,8 +266,8 @@ def main(argv=None) -> int:
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--workers", type=int, default=0, help="decode wavefront workers (0 = automatic)")
     ap.add_argument("--kv", choices=["native", "i8", "fp8"], default="native",
-                    help="decode pools: the workload's dtype (default) or 8-bit INT8 / FP8 E4M3 codes with row "
-                         "scales, encoded from the workload's rows on write")
+                    help="pools: the workload's dtype (default) or 8-bit INT8 / FP8 E4M3 codes with row "
+                         "scales, encoded from the workload's rows on write (decode and prefill workloads)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true",
@@ -290,8 +299,8 @@ def main(argv=None) -> int:
         return 1
     torch.cuda.set_device(0)
     w = wl.config(args.config, args.seed)
-    if args.kv != "native" and w.kind != "decode":
-        print("8-bit pools (--kv) are decode only", file=sys.stderr)
+    if args.kv != "native" and w.kind not in ("decode", "prefill"):
+        print("8-bit pools (--kv) serve decode and prefill workloads", file=sys.stderr)
         return 2
     d = session.DeviceWorkload(w, num_workers=args.workers, kv_format=args.kv)
     comp_bytes = 0
@@ -370,7 +379,7 @@ def main(argv=None) -> int:
         value = step_units / (ms_step * 1e-3) / 1e9
         unit = "GB/s"
         achieved = by["attend"] / (att_mean * 1e-3) / 1e9
-        src = source_hash("decode.hip", "common.h")
+        src = source_hash(*attend_sources("decode", args.kv))
         key = f"paged_attn_decode|{w.name}" + ("" if args.kv == "native" else f"|{args.kv}")
         roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_for(key, src)}
@@ -382,12 +391,12 @@ def main(argv=None) -> int:
         value = flop / (ms_step * 1e-3) / 1e12
         unit = "TFLOP/s"
         achieved = flop / (att_mean * 1e-3) / 1e12
-        src = source_hash("prefill.hip", "common.h")
-        key = f"paged_attn_prefill|{w.name}"
+        src = source_hash(*attend_sources("prefill", args.kv))
+        key = f"paged_attn_prefill|{w.name}" + ("" if args.kv == "native" else f"|{args.kv}")
         peak = MFMA_PEAK_TFLOPS[w.dtype]
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4), "traffic": traffic_for(key, src)}
-        n_part_info = {}
+        n_part_info = {"kv_pool": args.kv} if args.kv != "native" else {}
 
     timing_mode = "hip_graph" if args.graph else "eager"
     rec = {

@@ -262,6 +262,50 @@ int paged_attn_decode_quant(const pkv_geometry_t* geom, float* out, float* lse, 
                             int32_t max_context_len, int32_t window, int32_t num_sinks, float scale,
                             int32_t num_workers, void* workspace, size_t workspace_bytes, void* stream);
 
+/* paged_attn_prefill_quant_workspace_bytes - bytes of device workspace
+ * paged_attn_prefill_quant needs for num_seqs sequences of context at most
+ * max_context_len with this (8-bit) geometry: two staging pools of
+ * num_seqs * ceil(max_context_len / B) blocks in 16-bit, their row scales and
+ * a staging table. 0 if the geometry is invalid or not 8-bit. */
+size_t paged_attn_prefill_quant_workspace_bytes(const pkv_geometry_t* geom, int32_t num_seqs,
+                                                int32_t max_context_len);
+
+/* paged_attn_prefill_quant - paged_attn_prefill over 8-bit pools ("Build a
+ * Memory-Compressed Attention Engine with KV Caching from Scratch",
+ * "Extending It" item 2, with the prefill of "Building a Streaming
+ * Sliding-Window Attention Engine in Pure Python", Step 3): the same
+ * attention with every key and value replaced by its decoded value
+ * code * scale.
+ *
+ * Two kernels on `stream`: the blocks holding positions [0, L) of each
+ * sequence are widened into the workspace, codes unchanged as q_dtype values
+ * (exact), then the prefill kernel reads them through a staging table. A
+ * key's score is the dot product with its codes times its K scale (float32);
+ * a weight is multiplied by its key's V scale times 2^4 (PKV_I8) or 2^6
+ * (PKV_FP8) and rounded to fp16 for the matrix cores, and the output is
+ * divided by the same power of two. Rounding as paged_attn_prefill (lse
+ * within 6e-4). A row whose largest |value| exceeds 2031 (PKV_I8) or 1791
+ * (PKV_FP8) is attended with its V scale capped there.
+ *
+ *   geom->kv_dtype    PKV_I8 or PKV_FP8; head_dim, block_size and
+ *                     num_heads / num_kv_heads as paged_attn_prefill
+ *   q                 q_dtype [q_start[num_seqs], H, D], q_dtype PKV_F16 or
+ *                     PKV_BF16
+ *   k_pool, v_pool    codes [NB, B, Hkv, D]
+ *   k_scale, v_scale  float32 [NB, Hkv, B]
+ *   workspace         device, 16-byte aligned, at least
+ *                     paged_attn_prefill_quant_workspace_bytes(geom, num_seqs,
+ *                     max_context_len) bytes (else PKV_EWORKSPACE); owned by
+ *                     the caller and overwritten; calls that share it on
+ *                     different streams race
+ *   all other arguments as paged_attn_prefill. */
+int paged_attn_prefill_quant(const pkv_geometry_t* geom, float* out, float* lse, const void* q,
+                             int32_t q_dtype, const int32_t* q_start, const void* k_pool, const void* v_pool,
+                             const float* k_scale, const float* v_scale, const int32_t* block_tables,
+                             int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
+                             int32_t max_q_len, int32_t max_context_len, int32_t window, int32_t num_sinks,
+                             float scale, void* workspace, size_t workspace_bytes, void* stream);
+
 /* paged_kv_copy_blocks - copy whole blocks: pair i copies block src[i] to
  * block dst[i] in both pools (every slot and kv head; with 8-bit pools the
  * rows' scales too). This is the copy of copy-on-write: a sequence about to

@@ -25,7 +25,10 @@ scales together); code pools are uint8 ``[NB, B, Hkv, D]`` like the 16-bit
 pools.
 
 Pinned by ``tests/test_oracle_quant.py`` (the FP8 codec against torch's
-float8_e4m3fn conversion, round-trip bounds, exact cases).
+float8_e4m3fn conversion, round-trip bounds, exact cases; decode and prefill
+over the decoded pools equal the plain attention on values that are on the
+code grid, and a prefill chunk's last row equals the decode of its
+sequence).
 """
 from __future__ import annotations
 
@@ -132,11 +135,24 @@ def dequantize_pool(codes, scale_nhb, fmt: str) -> np.ndarray:
 
 
 def decode(q, k_codes, v_codes, k_scale, v_scale, block_tables, context_lens, *, fmt, q_dtype,
-           block_size, num_kv_heads, window, scale, seqs=None, heads=None):
+           block_size, num_kv_heads, window, scale, seqs=None, heads=None, sinks=0):
     """Single-query decode over the decoded 8-bit pools: the attention of
     ``ref.decode`` with keys and values replaced by code * scale."""
     kp = dequantize_pool(k_codes, k_scale, fmt)
     vp = dequantize_pool(v_codes, v_scale, fmt)
     return ref.decode(q, kp, vp, block_tables, context_lens, block_size=block_size,
                       num_kv_heads=num_kv_heads, window=window, scale=scale, dtype=q_dtype,
-                      kv_dtype="f64", seqs=seqs, heads=heads)
+                      kv_dtype="f64", seqs=seqs, heads=heads, sinks=sinks)
+
+
+def prefill(q, q_start, k_codes, v_codes, k_scale, v_scale, block_tables, context_lens, *, fmt, q_dtype,
+            block_size, num_kv_heads, window, scale, sinks=0, seqs=None, heads=None):
+    """Causal chunked prefill over the decoded 8-bit pools: the attention of
+    ``ref.prefill`` (the prefill of "Building a Streaming Sliding-Window
+    Attention Engine in Pure Python", Step 3) with keys and values replaced
+    by code * scale."""
+    kp = dequantize_pool(k_codes, k_scale, fmt)
+    vp = dequantize_pool(v_codes, v_scale, fmt)
+    return ref.prefill(q, q_start, kp, vp, block_tables, context_lens, block_size=block_size,
+                       num_kv_heads=num_kv_heads, window=window, scale=scale, dtype=q_dtype, kv_dtype="f64",
+                       sinks=sinks, seqs=seqs, heads=heads)

@@ -233,14 +233,17 @@ def prefill_keys(L: int, C: int, window: int, sinks: int = 0):
 
 
 def prefill(q, q_start, k_pool, v_pool, block_tables, context_lens, *, block_size,
-            num_kv_heads, window, scale, dtype, seqs=None, heads=None, sinks=0):
+            num_kv_heads, window, scale, dtype, seqs=None, heads=None, sinks=0, kv_dtype=None):
     """Causal chunked prefill through the block table.
 
     q [sum C, H, D] with sequence s owning rows q_start[s]:q_start[s+1] (its
     chunk = its last C_s positions).  Dense masked attention per (seq, head),
     with the mask of ``prefill_keys``; masked keys are excluded (weight 0).
+    ``kv_dtype`` (default ``dtype``) is the pools' storage type when it
+    differs from the queries' ("f64": already decoded values).
     Returns (out [sum C, H, D], lse [sum C, H]) float64.
     """
+    kv_dtype = dtype if kv_dtype is None else kv_dtype
     T, H, D = q.shape
     out = np.full((T, H, D), np.nan)
     lse = np.full((T, H), np.nan)
@@ -259,8 +262,8 @@ def prefill(q, q_start, k_pool, v_pool, block_tables, context_lens, *, block_siz
         mask = mask[:, lo:]
         for h in heads:
             g = kv_head_of(h, H, num_kv_heads)
-            K = gather(k_pool, block_tables[s], pos, g, block_size, dtype)
-            V = gather(v_pool, block_tables[s], pos, g, block_size, dtype)
+            K = gather(k_pool, block_tables[s], pos, g, block_size, kv_dtype)
+            V = gather(v_pool, block_tables[s], pos, g, block_size, kv_dtype)
             scores = (qf[r0:r1, h] @ K.T) * scale
             scores = np.where(mask, scores, -np.inf)
             m = scores.max(axis=1, keepdims=True)

@@ -173,7 +173,9 @@ template <> __device__ __forceinline__ void v_to_f16<BF16T>(uint16_t* unit) {
   *reinterpret_cast<u32x4*>(unit) = u32x4{w[0], w[1], w[2], w[3]};
 }
 
-template <class T, int D, int B, int G>
+// QS: the pools hold widened 8-bit codes whose row scales multiply each
+// key's score (K scale) and weight (V scale).
+template <class T, int D, int B, int G, bool QS>
 __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a, float scale_log2) {
   using M = Mma<T>;      // S = K.Q^T in the input type
   using MP = Mma<F16T>;  // O += V^T.P^T in fp16 (V converted in LDS when bf16)
@@ -195,6 +197,9 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a, float sc
   __shared__ __attribute__((aligned(16))) uint16_t v_lds0[kKT * D];
   __shared__ __attribute__((aligned(16))) uint16_t v_lds1[kKT * D];
   __shared__ unsigned long long kvalid[2];  // bit t: key t0 + t of the tile is mapped
+  // QS: the K and V scales of the tile's keys (zero for keys outside the
+  // range, which are masked), [slot][K or V][key].
+  __shared__ __attribute__((aligned(16))) float scl[QS ? 2 : 1][2][kKT];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -300,12 +305,29 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a, float sc
 #pragma unroll
     for (int j = 0; j < NLD; ++j) v_to_f16<T>(vd + (4 * j + wave) * 512 + 8 * lane);
   };
-  // Key validity bitmask of a tile (64 lanes = 64 keys), by wavefront 0.
+  // Key validity bitmask of a tile (64 lanes = 64 keys), by wavefront 0;
+  // with QS also the keys' scales, into registers (stored to LDS by
+  // store_scales once the tile's loads are waited for).
+  float sk_reg = 0.f, sv_reg = 0.f;
   auto put_valid = [&](int t0, int slot) {
     if (wave == 0) {
       const int t = t0 + lane;
-      const unsigned long long vm = __ballot(in_range(t) && pb_key >= 0 && pb_key < a.nb);
+      const bool ok = in_range(t) && pb_key >= 0 && pb_key < a.nb;
+      const unsigned long long vm = __ballot(ok);
       if (lane == 0) kvalid[slot] = vm;
+      if constexpr (QS) {
+        const size_t si = ((size_t)(uint32_t)(ok ? pb_key : 0) * a.Hkv + g) * B + (t & (B - 1));
+        sk_reg = ok ? a.k_scale[si] : 0.f;
+        sv_reg = ok ? a.v_scale[si] : 0.f;
+      }
+    }
+  };
+  auto store_scales = [&](int slot) {
+    if constexpr (QS) {
+      if (wave == 0) {
+        scl[slot][0][lane] = sk_reg;
+        scl[slot][1][lane] = sv_reg;
+      }
     }
   };
 
@@ -368,6 +390,18 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a, float sc
         sacc[0] = M::mma(__builtin_bit_cast(V8, ka[cur][0]), qf[kc], sacc[0]);
         sacc[1] = M::mma(__builtin_bit_cast(V8, ka[cur][1]), qf[kc], sacc[1]);
       }
+      if constexpr (QS) {  // key t's score times its K scale (keys 8*(v/4) + 4*hf + v%4 of each half)
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const float4 k4 = *reinterpret_cast<const float4*>(&scl[QS ? slot : 0][0][kh * 32 + 8 * q4 + 4 * hf]);
+            sacc[kh][4 * q4] *= k4.x;
+            sacc[kh][4 * q4 + 1] *= k4.y;
+            sacc[kh][4 * q4 + 2] *= k4.z;
+            sacc[kh][4 * q4 + 3] *= k4.w;
+          }
+      }
       // Mask (selection, branch-free), running maximum of the raw scores.
       const bool need_mask = vmask != ~0ull || wave_pmin < t0 + kKT - 1 || row0 + 31 >= C ||
                              (a.window > 0 && t0 <= wave_pmax - a.window);
@@ -428,12 +462,22 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a, float sc
           e47[dt] = lds_read_tr<(16 * c + 8) * D * 2>(vbase + tr_addr[dt]);
         }
         uint32_t hi[4];
+        float vs[8];  // QS: V scales of this lane's 8 keys of the chunk
+        if constexpr (QS) {
+          const float4 va = *reinterpret_cast<const float4*>(&scl[QS ? slot : 0][1][16 * c + 4 * hf]);
+          const float4 vb = *reinterpret_cast<const float4*>(&scl[QS ? slot : 0][1][16 * c + 8 + 4 * hf]);
+          vs[0] = va.x; vs[1] = va.y; vs[2] = va.z; vs[3] = va.w;
+          vs[4] = vb.x; vs[5] = vb.y; vs[6] = vb.z; vs[7] = vb.w;
+        }
 #pragma unroll
         for (int e2 = 0; e2 < 4; ++e2) {
           const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kh][8 * sub + 2 * e2], scale_log2, -ms));
           const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kh][8 * sub + 2 * e2 + 1], scale_log2, -ms));
           const uint32_t h = MP::pack(p0, p1);
-          hi[e2] = h;
+          // The normaliser sums the weights; V is multiplied by weight x V scale.
+          uint32_t hv = h;
+          if constexpr (QS) hv = MP::pack(p0 * vs[2 * e2], p1 * vs[2 * e2 + 1]);
+          hi[e2] = hv;
           l_run = __builtin_amdgcn_fdot2(as_h2(h), f16x2{(_Float16)1.f, (_Float16)1.f}, l_run, false);
         }
         const P8 bhi = __builtin_bit_cast(P8, u32x4{hi[0], hi[1], hi[2], hi[3]});
@@ -455,7 +499,10 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a, float sc
       chunk(IntC<3>{});
     }
     dma_wait();
-    if (has_next) convert_v(Vn);  // the next tile's V units this thread loaded
+    if (has_next) {
+      convert_v(Vn);  // the next tile's V units this thread loaded
+      store_scales(slot ^ 1);
+    }
     __syncthreads();
     return has_next;
   };
@@ -467,6 +514,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a, float sc
   if (ntiles > 1) fetch_table(tile_t0(1));
   dma_wait();
   convert_v(v_lds0);
+  store_scales(0);
   __syncthreads();
   for (int i = 0;; i += 2) {
     if (!step(i, k_lds0, v_lds0, k_lds1, v_lds1, 0)) break;
@@ -475,7 +523,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a, float sc
 
   if (!row_ok) return;
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  const float inv = l_tot > 0.f ? (QS ? a.o_mul : 1.f) / l_tot : 0.f;
   float* op = a.out + ((size_t)(r0 + my_row) * a.H + hq) * D;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) {
@@ -498,7 +546,10 @@ static hipError_t launch_typed(const PrefillArgs& a, hipStream_t st) {
   constexpr int HPW = G < 4 ? G : 4;
   constexpr int QT = 32 * (4 / HPW);
   dim3 grid((a.max_q_len + QT - 1) / QT, a.Hkv * (G / HPW), a.S);
-  hipLaunchKernelGGL((prefill_kernel<T, D, B, G>), grid, dim3(256), 0, st, a, a.scale * kLog2e);
+  if (a.k_scale)
+    hipLaunchKernelGGL((prefill_kernel<T, D, B, G, true>), grid, dim3(256), 0, st, a, a.scale * kLog2e);
+  else
+    hipLaunchKernelGGL((prefill_kernel<T, D, B, G, false>), grid, dim3(256), 0, st, a, a.scale * kLog2e);
   return hipGetLastError();
 }
 

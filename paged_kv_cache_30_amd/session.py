@@ -47,7 +47,7 @@ def int_tensor(a, device="cuda") -> torch.Tensor:
 class DeviceWorkload:
     """``kv_format``: "native" (pools in the workload's dtype) or "i8" / "fp8"
     (8-bit pools with row scales; keys and values are encoded on write from
-    the workload's 16-bit or fp32 rows; decode only)."""
+    the workload's 16-bit or fp32 rows; decode and prefill)."""
 
     def __init__(self, w, device: str = "cuda", poison: bool = True, num_workers: int = 0,
                  with_lse: bool = True, write_history: bool = True, kv_format: str = "native"):
@@ -62,8 +62,8 @@ class DeviceWorkload:
             self.k_pool = torch.full(shape, fill, dtype=dt, device=device)
             self.v_pool = torch.full(shape, fill, dtype=dt, device=device)
         else:
-            if w.kind != "decode":
-                raise ValueError("8-bit pools are decode only")
+            if w.kind not in ("decode", "prefill"):
+                raise ValueError("8-bit pools serve decode and prefill workloads")
             # unwritten rows: code 0xFF (NaN for FP8) and scale NaN (or zeros)
             code = 0xFF if poison else 0
             self.k_pool = torch.full(shape, code, dtype=torch.uint8, device=device).view(QUANT_DTYPE[kv_format])
@@ -103,6 +103,9 @@ class DeviceWorkload:
         if w.kind == "decode":
             self.workspace = _lib.decode_workspace(self.k_pool, w.num_heads, w.num_seqs, w.max_context_len,
                                                    w.window, num_workers, sinks=w.sinks)
+        elif self.kv_format != "native":
+            self.workspace = _lib.prefill_quant_workspace(self.k_pool, w.num_heads, w.num_seqs,
+                                                          w.max_context_len)
 
     def _write(self, k, v, seq, pos):
         if self.kv_format == "native":
@@ -150,6 +153,11 @@ class DeviceWorkload:
                     self.out, self.q, self.k_pool, self.v_pool, self.tables, self.lens, w.max_context_len,
                     window=w.window, scale=w.scale, num_workers=self.num_workers, workspace=self.workspace,
                     lse=self.lse, sinks=w.sinks)
+            elif self.kv_format != "native":
+                self._bound_attend = _lib.bind_prefill_quant(
+                    self.out, self.q, self.q_start, self.k_pool, self.v_pool, self.k_scale, self.v_scale,
+                    self.tables, self.lens, w.max_q_len, w.max_context_len, window=w.window, scale=w.scale,
+                    workspace=self.workspace, lse=self.lse, sinks=w.sinks)
             else:
                 self._bound_attend = _lib.bind_prefill(
                     self.out, self.q, self.q_start, self.k_pool, self.v_pool, self.tables, self.lens,

@@ -1,9 +1,10 @@
 """GPU parity of the 8-bit KV pages (INT8 / FP8 E4M3) through the C ABI.
 
 Bars: the encoded pools (codes and row scales) bit-exact against the oracle's
-encoding of the same rows, unwritten rows untouched; decode over 8-bit pools
-within max-abs 2e-3 of the fp64 oracle's attention over the decoded values
-(code * scale), 16-bit queries.
+encoding of the same rows, unwritten rows untouched; decode and chunked
+prefill over 8-bit pools within max-abs 2e-3 of the fp64 oracle's attention
+over the decoded values (code * scale), 16-bit queries; prefill lse within
+6e-4.
 """
 import sys
 
@@ -222,3 +223,103 @@ def test_quant_group_of_eight_unsupported(lib):
     with pytest.raises(pkv.PagedAttnError) as e:
         run(session, w, "i8")
     assert e.value.status == pkv.PKV_EUNSUPPORTED
+
+
+# ---------------------------------------------------------------- prefill
+
+TOL_LSE_PREFILL = 6e-4  # the normaliser sums the fp16-rounded weights
+
+PREFILL_CASES = [
+    # (fmt, dtype, H, Hkv, D, B, prefix, chunks, window, sinks)
+    ("i8", "bf16", 8, 2, 128, 16, 64, [40, 1, 0, 130], 0, 0),
+    ("fp8", "bf16", 8, 2, 128, 16, 64, [40, 1, 0, 130], 0, 0),
+    ("i8", "f16", 8, 8, 64, 32, 96, [100, 33], 0, 0),
+    ("fp8", "f16", 8, 8, 64, 32, 96, [100, 33], 0, 0),
+    ("fp8", "f16", 16, 4, 128, 32, 0, [200, 65], 50, 4),
+    ("i8", "bf16", 16, 4, 128, 16, 32, [150, 70, 3], 37, 0),
+    ("i8", "bf16", 32, 4, 128, 16, 128, [300, 7], 0, 0),
+    ("fp8", "bf16", 8, 1, 128, 16, 48, [129, 64], 0, 0),
+    ("fp8", "f16", 4, 2, 64, 16, 16, [1, 2, 3], 0, 0),
+]
+
+
+@pytest.mark.parametrize("case", PREFILL_CASES,
+                         ids=[f"{c[0]}-{c[1]}-g{c[2] // c[3]}-d{c[4]}-b{c[5]}-w{c[8]}-s{c[9]}" for c in PREFILL_CASES])
+def test_quant_prefill_small(lib, case):
+    """Chunked prefill over 8-bit pools written by the 8-bit write, against
+    the oracle's prefill over the decoded pools: every row and head."""
+    pkv, session = lib
+    fmt, dtype, H, Hkv, D, B, prefix, chunks, window, sinks = case
+    note(f"quant prefill {case}")
+    w = wl.make_prefill(prefix_len=prefix, chunk_lens=chunks, num_heads=H, num_kv_heads=Hkv, head_dim=D,
+                        block_size=B, dtype=dtype, seed=sum(chunks) + H + D, window=window, sinks=sinks,
+                        spare_blocks=3)
+    d = run(session, w, fmt)
+    kp, vp = ref.build_pools(w)
+    kc, vc, ks, vs = oq.quantize_pools(kp, vp, dtype, fmt)
+    assert d.k_scale.cpu().numpy().tobytes() == ks.tobytes()  # the write encoded the same rows
+    out, lse = oq.prefill(w.q, w.q_start, kc, vc, ks, vs, w.block_tables, w.context_lens, fmt=fmt,
+                          q_dtype=dtype, block_size=B, num_kv_heads=Hkv, window=window, scale=w.scale, sinks=sinks)
+    max_err(d.out.cpu().numpy(), out, str(case))
+    got_lse = d.lse.cpu().numpy()
+    assert np.abs(got_lse - lse).max(initial=0) <= TOL_LSE_PREFILL
+
+
+def test_quant_prefill_scaled_values(lib):
+    """Rows with very different magnitudes (1e-3 to 300 times unit normal
+    values): the staged V scales span five decades and many weight x scale
+    products are small.  The bar is 2e-3 for outputs up to 4 in magnitude
+    and scales with the largest output above that (the weights carry 11
+    significant bits)."""
+    pkv, session = lib
+    note("quant prefill scaled values")
+    w = wl.make_prefill(prefix_len=64, chunk_lens=[90, 40], num_heads=8, num_kv_heads=2, head_dim=128,
+                        block_size=16, dtype="bf16", seed=31)
+    rng = np.random.default_rng(31)
+    for arr in [w.prefix.k, w.prefix.v] + [e.k for e in w.seq_kv] + [e.v for e in w.seq_kv]:
+        f = ref.to_f64(arr, "bf16")
+        mag = 10.0 ** rng.uniform(-3, 2.5, size=f.shape[:2] + (1,))
+        arr[...] = wl.to_storage((f * mag).astype(np.float32), "bf16")
+    for fmt in ("i8", "fp8"):
+        d = run(session, w, fmt)
+        kp, vp = ref.build_pools(w)
+        kc, vc, ks, vs = oq.quantize_pools(kp, vp, "bf16", fmt)
+        out, lse = oq.prefill(w.q, w.q_start, kc, vc, ks, vs, w.block_tables, w.context_lens, fmt=fmt,
+                              q_dtype="bf16", block_size=16, num_kv_heads=2, window=0, scale=w.scale)
+        got = d.out.cpu().numpy()
+        # absolute bar relative to the largest value a row attends
+        err = float(np.abs(got - out).max())
+        big = float(np.abs(out).max())
+        note(f"scaled {fmt}: max abs err {err:.3g} (largest output {big:.3g})")
+        assert np.isfinite(got).all()
+        assert err <= TOL * max(1.0, big / 4)
+        assert np.abs(d.lse.cpu().numpy() - lse).max() <= TOL_LSE_PREFILL
+
+
+@pytest.mark.parametrize("fmt", ["i8", "fp8"])
+def test_quant_prefill_config5_sampled(lib, fmt):
+    """The chunked-prefill workload (8 sequences, 2048 shared prefix
+    positions and a 512-row chunk each, 32 heads over 8 kv heads, D 128,
+    B 16, bf16 queries) with 8-bit pools: three sequences x four heads
+    against the oracle; the encoding error against the 16-bit result is
+    reported."""
+    pkv, session = lib
+    note(f"quant prefill cfg5 {fmt}")
+    w = wl.config(5)
+    d = run(session, w, fmt)
+    kc, vc, ks, vs = (t.cpu().numpy() for t in (d.k_pool.view(torch.uint8), d.v_pool.view(torch.uint8),
+                                                d.k_scale, d.v_scale))
+    seqs, heads = [0, 3, 7], [0, 5, 17, 31]
+    out, lse = oq.prefill(w.q, w.q_start, kc, vc, ks, vs, w.block_tables, w.context_lens, fmt=fmt,
+                          q_dtype="bf16", block_size=16, num_kv_heads=8, window=0, scale=w.scale,
+                          seqs=seqs, heads=heads)
+    got = d.out.cpu().numpy()
+    got_lse = d.lse.cpu().numpy()
+    for s in seqs:
+        r0, r1 = int(w.q_start[s]), int(w.q_start[s + 1])
+        max_err(got[r0:r1, heads], out[r0:r1, heads], f"cfg5 {fmt} seq {s}")
+        assert np.abs(got_lse[r0:r1, heads] - lse[r0:r1, heads]).max() <= TOL_LSE_PREFILL
+    d16 = run(session, w, "native")
+    q_err = float(np.abs(got - d16.out.cpu().numpy()).max())
+    note(f"cfg5 {fmt}: encoding error vs 16-bit K/V {q_err:.3g}")
+    assert q_err < 0.25

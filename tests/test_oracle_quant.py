@@ -123,6 +123,67 @@ def test_quantized_decode_equals_plain_decode_on_exact_data(fmt):
     assert np.abs(got - want).max() <= 1e-12 and np.abs(glse - wlse).max() <= 1e-12
 
 
+def _on_grid(pool, fmt, rng):
+    """Replace every written row of ``pool`` by values on the code grid whose
+    largest magnitude is QMAX, so that each row encodes exactly, scale 1."""
+    live = np.isfinite(pool).all(axis=-1)
+    if fmt == "i8":
+        vals = rng.integers(-127, 128, size=pool.shape).astype(np.float32)
+        vals[..., 0] = 127
+    else:
+        vals = oq._POS_VALUES[rng.integers(0, 127, size=pool.shape)].astype(np.float32)
+        vals *= np.where(rng.random(pool.shape) < 0.5, -1, 1).astype(np.float32)
+        vals[..., 0] = 448
+    pool[live] = vals[live]
+
+
+@pytest.mark.parametrize("fmt", ["i8", "fp8"])
+def test_quantized_prefill_equals_plain_prefill_on_exact_data(fmt):
+    """Chunked prefill over 8-bit pools whose rows encode exactly (scale 1)
+    equals the plain prefill of the same values."""
+    w = wl.make_prefill(prefix_len=32, chunk_lens=[20, 1, 0, 45], num_heads=8, num_kv_heads=2, head_dim=64,
+                        block_size=16, dtype="f32", seed=13)
+    kp, vp = ref.build_pools(w)
+    rng = np.random.default_rng(6)
+    _on_grid(kp, fmt, rng)
+    _on_grid(vp, fmt, rng)
+    kc, vc, ks, vs = oq.quantize_pools(kp, vp, "f32", fmt)
+    assert np.all(ks[np.isfinite(ks)] == 1.0)
+    got, glse = oq.prefill(w.q, w.q_start, kc, vc, ks, vs, w.block_tables, w.context_lens, fmt=fmt,
+                           q_dtype="f32", block_size=16, num_kv_heads=2, window=0, scale=w.scale / 64)
+    want, wlse = ref.prefill(w.q, w.q_start, kp, vp, w.block_tables, w.context_lens, block_size=16,
+                             num_kv_heads=2, window=0, scale=w.scale / 64, dtype="f32")
+    fin = np.isfinite(want)
+    assert np.array_equal(fin, np.isfinite(got)) and fin.any()
+    assert np.abs(got[fin] - want[fin]).max() <= 1e-9
+    assert np.abs(glse[np.isfinite(wlse)] - wlse[np.isfinite(wlse)]).max() <= 1e-9
+
+
+@pytest.mark.parametrize("fmt,window,sinks", [("i8", 0, 0), ("fp8", 0, 0), ("i8", 24, 0), ("fp8", 24, 3)])
+def test_quantized_prefill_last_row_is_decode(fmt, window, sinks):
+    """The last row of a chunk sits at position L - 1 and attends what a
+    decode step of the same sequence attends: quantized prefill and
+    quantized decode agree there (real-valued rows, row scales not 1)."""
+    w = wl.make_prefill(prefix_len=48, chunk_lens=[30, 1, 17], num_heads=8, num_kv_heads=4, head_dim=64,
+                        block_size=16, dtype="bf16", seed=14, window=window, sinks=sinks)
+    kp, vp = ref.build_pools(w)
+    kc, vc, ks, vs = oq.quantize_pools(kp, vp, "bf16", fmt)
+    assert not np.all(ks[np.isfinite(ks)] == 1.0)
+    out, lse = oq.prefill(w.q, w.q_start, kc, vc, ks, vs, w.block_tables, w.context_lens, fmt=fmt,
+                          q_dtype="bf16", block_size=16, num_kv_heads=4, window=window, scale=w.scale, sinks=sinks)
+    last = w.q_start[1:] - 1
+    dout, dlse = oq.decode(w.q[last], kc, vc, ks, vs, w.block_tables, w.context_lens, fmt=fmt, q_dtype="bf16",
+                           block_size=16, num_kv_heads=4, window=window, scale=w.scale, sinks=sinks)
+    assert np.abs(out[last] - dout).max() <= 1e-12
+    assert np.abs(lse[last] - dlse).max() <= 1e-12
+    # and the encoding moves the result away from the 16-bit prefill (the
+    # scales are applied, not dropped)
+    o16, _ = ref.prefill(w.q, w.q_start, kp, vp, w.block_tables, w.context_lens, block_size=16, num_kv_heads=4,
+                         window=window, scale=w.scale, dtype="bf16", sinks=sinks)
+    d = np.abs(out - o16).max()
+    assert 1e-6 < d < 0.2, d
+
+
 def test_unwritten_rows_stay_nan():
     w = wl.make_decode(seed=12, num_heads=4, num_kv_heads=4, head_dim=64, block_size=16,
                        dtype="bf16", lens=[20, 3], window=0)
