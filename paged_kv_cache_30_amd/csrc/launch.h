@@ -111,8 +111,9 @@ struct PrefillArgs {
 // Widening of the 8-bit blocks a batch attends into 16-bit staging pools
 // (exact: every INT8 code and E4M3 value is a bf16 and an fp16 value), with
 // their row scales: staged block s * msb + j holds logical block j of
-// sequence s, and stage_tables [S, msb] maps it (-1 where nothing is staged).
-// K scales are copied; V scales are multiplied by v_mul (a power of two) and
+// sequence s, and stage_tables [S, msb] maps each entry to the copy of its
+// physical block (-1 where nothing is staged; a block that several entries
+// map is copied once). K scales are copied; V scales are multiplied by v_mul (a power of two) and
 // capped at 65504 / 256, so that a weight (at most 256) times a V scale is a
 // finite fp16 value.
 struct WidenArgs {
@@ -127,6 +128,7 @@ struct WidenArgs {
   float* ks_out;
   float* vs_out;
   int32_t* stage_tables;
+  int32_t* owner;  // [nb]: entry s * msb + j that owns the copy of a physical block
   int32_t S, mb, msb, nb, B, Hkv, D, code_dtype, out_dtype, max_context_len;
   float v_mul;
 };

@@ -14,7 +14,12 @@
 // divided by it) so that this product sits in fp16's normal range for the
 // weights that matter, capped at 65504 / 256 so that it stays finite.
 // Blocks past the context, and entries outside the pool, are not staged
-// (table entry -1).
+// (table entry -1). A physical block that several sequences map (a shared
+// prefix) is staged once: the first (sequence, logical block) entry that
+// maps it, in row-major order, owns the copy, and every entry that maps the
+// block points the staging table at that copy. Ownership takes two small
+// launches before the widening: reset the owner slot of every mapped
+// physical block, then an atomic minimum over the entries that map it.
 #include "common.h"
 #include "launch.h"
 
@@ -59,19 +64,41 @@ template <> __device__ __forceinline__ u32x4 pack8<F16T>(const float* f) {
 // 65504, the largest finite fp16 value.
 constexpr float kVScaleCap = 65504.f / 256.f;
 
-// One workgroup per staged block (logical block j = blockIdx.x of sequence
-// s = blockIdx.y); each thread widens 16-code pieces of the block.
-template <class C, class O>
-__global__ __launch_bounds__(256) void widen_kernel(WidenArgs a) {
-  const int j = blockIdx.x, s = blockIdx.y;
+// Physical block of entry (s, j) when it holds positions below the
+// (clamped) context length and lies in the pool, else -1.
+__device__ __forceinline__ int staged_source(const WidenArgs& a, int s, int j) {
   int L = a.lens[s];
   L = L < 0 ? 0 : (L > a.max_context_len ? a.max_context_len : L);
   const int nblk = (L + a.B - 1) / a.B;
   const int pb = (j < nblk && j < a.mb) ? a.tables[(size_t)s * a.mb + j] : -1;
-  const bool ok = pb >= 0 && pb < a.nb;
+  return (pb >= 0 && pb < a.nb) ? pb : -1;
+}
+
+// One thread per entry (s, j) of the [S, msb] grid of logical blocks.
+__global__ __launch_bounds__(256) void widen_reset_kernel(WidenArgs a) {
+  const long long e = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (e >= (long long)a.S * a.msb) return;
+  const int pb = staged_source(a, (int)(e / a.msb), (int)(e % a.msb));
+  if (pb >= 0) a.owner[pb] = INT32_MAX;
+}
+__global__ __launch_bounds__(256) void widen_claim_kernel(WidenArgs a) {
+  const long long e = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (e >= (long long)a.S * a.msb) return;
+  const int pb = staged_source(a, (int)(e / a.msb), (int)(e % a.msb));
+  if (pb >= 0) atomicMin(&a.owner[pb], (int32_t)e);
+}
+
+// One workgroup per entry (logical block j = blockIdx.x of sequence
+// s = blockIdx.y): it maps the entry to its block's copy and, if it owns
+// the copy, widens 16-code pieces of the block into it.
+template <class C, class O>
+__global__ __launch_bounds__(256) void widen_kernel(WidenArgs a) {
+  const int j = blockIdx.x, s = blockIdx.y;
+  const int pb = staged_source(a, s, j);
   const size_t stg = (size_t)s * a.msb + j;
-  if (threadIdx.x == 0) a.stage_tables[stg] = ok ? (int32_t)stg : -1;
-  if (!ok) return;  // the same for the whole workgroup
+  const int32_t own = pb >= 0 ? a.owner[pb] : -1;
+  if (threadIdx.x == 0) a.stage_tables[stg] = own;
+  if (pb < 0 || (size_t)own != stg) return;  // the same for the whole workgroup
   const size_t blk_codes = (size_t)a.B * a.Hkv * a.D;  // bytes of codes per block
   const int pieces = (int)(blk_codes / 16);
   const char* kc = (const char*)a.k_codes + (size_t)pb * blk_codes;
@@ -99,6 +126,10 @@ __global__ __launch_bounds__(256) void widen_kernel(WidenArgs a) {
 hipError_t launch_widen(const WidenArgs& a, hipStream_t st) {
   if (a.S == 0 || a.msb == 0) return hipSuccess;
   if (((size_t)a.B * a.Hkv * a.D) % 16) return hipErrorInvalidValue;
+  const long long entries = (long long)a.S * a.msb;
+  const unsigned eb = (unsigned)((entries + 255) / 256);
+  hipLaunchKernelGGL(widen_reset_kernel, dim3(eb), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(widen_claim_kernel, dim3(eb), dim3(256), 0, st, a);
   const dim3 grid(a.msb, a.S), block(256);
   if (a.code_dtype == 3 && a.out_dtype == 2) hipLaunchKernelGGL((widen_kernel<I8T, BF16T>), grid, block, 0, st, a);
   else if (a.code_dtype == 3 && a.out_dtype == 1) hipLaunchKernelGGL((widen_kernel<I8T, F16T>), grid, block, 0, st, a);

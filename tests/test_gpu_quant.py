@@ -323,3 +323,37 @@ def test_quant_prefill_config5_sampled(lib, fmt):
     q_err = float(np.abs(got - d16.out.cpu().numpy()).max())
     note(f"cfg5 {fmt}: encoding error vs 16-bit K/V {q_err:.3g}")
     assert q_err < 0.25
+
+
+@pytest.mark.parametrize("fmt", ["i8", "fp8"])
+def test_quant_prefill_workspace_reuse(lib, fmt):
+    """The workspace needs no initialisation: a call over a workspace full of
+    random bytes, then a call over a sub-batch (the prefix's owner changes
+    from sequence 0 to sequence 1) in the same workspace, give the rows of
+    the full batch bit for bit."""
+    pkv, session = lib
+    note(f"quant prefill workspace reuse {fmt}")
+    w = wl.make_prefill(prefix_len=64, chunk_lens=[50, 20, 33], num_heads=8, num_kv_heads=2, head_dim=128,
+                        block_size=16, dtype="bf16", seed=41, spare_blocks=4)
+    d = session.DeviceWorkload(w, kv_format=fmt)
+    d.write_step()
+    torch.cuda.synchronize()
+    H = w.num_heads
+    ws = pkv.prefill_quant_workspace(d.k_pool, H, w.num_seqs, w.max_context_len)
+    ws.copy_(torch.randint(0, 256, ws.shape, dtype=torch.uint8, device="cuda"))
+    out = torch.empty_like(d.out)
+    pkv.paged_attn_prefill_quant(out, d.q, d.q_start, d.k_pool, d.v_pool, d.k_scale, d.v_scale, d.tables, d.lens,
+                                 w.max_q_len, w.max_context_len, scale=w.scale, workspace=ws)
+    r1 = int(w.q_start[1])
+    qs2 = (d.q_start[1:] - r1).contiguous()
+    out2 = torch.empty_like(d.out[r1:])
+    pkv.paged_attn_prefill_quant(out2, d.q[r1:].contiguous(), qs2, d.k_pool, d.v_pool, d.k_scale, d.v_scale,
+                                 d.tables[1:].contiguous(), d.lens[1:].contiguous(), w.max_q_len, w.max_context_len,
+                                 scale=w.scale, workspace=ws)
+    torch.cuda.synchronize()
+    kp, vp = ref.build_pools(w)
+    kc, vc, ks, vs = oq.quantize_pools(kp, vp, "bf16", fmt)
+    want, _ = oq.prefill(w.q, w.q_start, kc, vc, ks, vs, w.block_tables, w.context_lens, fmt=fmt, q_dtype="bf16",
+                         block_size=16, num_kv_heads=2, window=0, scale=w.scale)
+    max_err(out.cpu().numpy(), want, f"reuse {fmt} first call")
+    assert torch.equal(out2, out[r1:]), "sub-batch rows differ from the full batch"
