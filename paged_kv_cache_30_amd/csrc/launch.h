@@ -106,6 +106,7 @@ struct PrefillArgs {
   const float* k_scale;
   const float* v_scale;
   float o_mul = 1.f;  // factor on the output rows (undoes a power of two folded into the V scales)
+  int32_t grid_q = 0, grid_y = 0;  // set by the launcher: query tiles and kv-head groups per sequence
 };
 
 // Widening of the 8-bit blocks a batch attends into 16-bit staging pools

@@ -206,10 +206,22 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a, float sc
   const int wave = uniform(tid >> 6);
   const int hf = lane >> 5;
   const int ql = lane & 31;
-  const int s = blockIdx.z;
-  const int g = blockIdx.y / (G / HPW);
-  const int hq = g * G + (blockIdx.y % (G / HPW)) * HPW + wave % HPW;
-  const int qt = gridDim.x - 1 - blockIdx.x;  // heaviest (latest) tiles first
+  // Workgroups are dispatched to the 8 XCDs round-robin by index; the index
+  // is renumbered so that each XCD runs a contiguous range of work items,
+  // ordered (kv-head group, sequence, query tile): the workgroups sharing a
+  // kv head's keys and values then share one XCD's L2.
+  int s, yg, qt;
+  {
+    const int N = a.grid_q * a.grid_y * a.S;
+    const int b = blockIdx.x, per = N / 8, rem = N % 8, x = b % 8;
+    const int w = x * per + min(x, rem) + b / 8;
+    yg = w / (a.grid_q * a.S);
+    const int r = w % (a.grid_q * a.S);
+    s = r / a.grid_q;
+    qt = a.grid_q - 1 - r % a.grid_q;  // heaviest (latest) tiles first
+  }
+  const int g = yg / (G / HPW);
+  const int hq = g * G + (yg % (G / HPW)) * HPW + wave % HPW;
 
   const int r0 = a.q_start[s];
   const int C = a.q_start[s + 1] - r0;
@@ -545,11 +557,16 @@ template <class T, int D, int B, int G>
 static hipError_t launch_typed(const PrefillArgs& a, hipStream_t st) {
   constexpr int HPW = G < 4 ? G : 4;
   constexpr int QT = 32 * (4 / HPW);
-  dim3 grid((a.max_q_len + QT - 1) / QT, a.Hkv * (G / HPW), a.S);
+  PrefillArgs b = a;
+  b.grid_q = (a.max_q_len + QT - 1) / QT;
+  b.grid_y = a.Hkv * (G / HPW);
+  const long long n = (long long)b.grid_q * b.grid_y * a.S;
+  if (n > INT32_MAX) return hipErrorInvalidValue;
+  dim3 grid((unsigned)n);
   if (a.k_scale)
-    hipLaunchKernelGGL((prefill_kernel<T, D, B, G, true>), grid, dim3(256), 0, st, a, a.scale * kLog2e);
+    hipLaunchKernelGGL((prefill_kernel<T, D, B, G, true>), grid, dim3(256), 0, st, b, a.scale * kLog2e);
   else
-    hipLaunchKernelGGL((prefill_kernel<T, D, B, G, false>), grid, dim3(256), 0, st, a, a.scale * kLog2e);
+    hipLaunchKernelGGL((prefill_kernel<T, D, B, G, false>), grid, dim3(256), 0, st, b, a.scale * kLog2e);
   return hipGetLastError();
 }
 
