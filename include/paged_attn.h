@@ -249,7 +249,11 @@ int paged_kv_write_quant(const pkv_geometry_t* geom, void* k_pool, void* v_pool,
  * code * scale. Scores and outputs accumulate in float32 (the row scales
  * factor out of each dot product).
  *
- *   geom->kv_dtype    PKV_I8 or PKV_FP8; num_heads / num_kv_heads in {1, 2, 4}
+ *   geom->kv_dtype    PKV_I8 or PKV_FP8; num_heads / num_kv_heads in {1, 2, 4, 8}
+ *                     (with 8, each kv head is read by two groups of 4 query
+ *                     heads: twice its bytes, and the workspace of
+ *                     paged_attn_decode_workspace_bytes for this geometry is
+ *                     sized for that)
  *   q                 q_dtype [num_seqs, H, D], q_dtype PKV_F16 or PKV_BF16
  *   k_pool, v_pool    codes [NB, B, Hkv, D]
  *   k_scale, v_scale  float32 [NB, Hkv, B]

@@ -315,7 +315,8 @@ __global__ __launch_bounds__(kThreads, (DecodeShape<T, D, B, G>::MIN_WG)) void d
     s = s_lo;
   }
 
-  const size_t row_stride = (size_t)Hkv * D * EB;  // bytes between slots
+  const int Hkv_pool = Hkv >> a.kv_shift;  // kv heads the pools hold
+  const size_t row_stride = (size_t)Hkv_pool * D * EB;  // bytes between slots
   const size_t blk_stride = row_stride * B;
   float m[G], l[G], o[G][PC * E];
 
@@ -382,11 +383,12 @@ __global__ __launch_bounds__(kThreads, (DecodeShape<T, D, B, G>::MIN_WG)) void d
           }
       }
     }
-    const size_t lane_off = (size_t)g * D * EB + (size_t)c * 16 + (size_t)r * row_stride;
+    const int gp = g >> a.kv_shift;  // pool kv head
+    const size_t lane_off = (size_t)gp * D * EB + (size_t)c * 16 + (size_t)r * row_stride;
     // K lanes for matrix-core scores: position l % 16 of the chunk, dims
     // 8 (l / 16) + 32 ks (16 bytes at 64 ks bytes further per k-step).
     const char* kbase = (const char*)a.k_pool +
-                        (MQK ? (size_t)g * D * EB + (size_t)(lane & 15) * row_stride + (size_t)(lane >> 4) * 16
+                        (MQK ? (size_t)gp * D * EB + (size_t)(lane & 15) * row_stride + (size_t)(lane >> 4) * 16
                              : lane_off);
     const char* vbase = (const char*)a.v_pool + lane_off;
 
@@ -400,7 +402,7 @@ __global__ __launch_bounds__(kThreads, (DecodeShape<T, D, B, G>::MIN_WG)) void d
       if (pb < 0 || pb >= a.nb) return false;
       const size_t off = (size_t)pb * blk_stride + (size_t)sub * CHUNK * row_stride;
       if constexpr (QU) {  // this lane's row scales, [NB, Hkv, B]
-        const size_t sidx = ((size_t)pb * Hkv + g) * B + sub * CHUNK + r;
+        const size_t sidx = ((size_t)pb * Hkv_pool + gp) * B + sub * CHUNK + r;
 #pragma unroll
         for (int j = 0; j < CSTEPS; ++j) {
           ks[j] = a.k_scale[sidx + j * RPL];

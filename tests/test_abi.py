@@ -135,7 +135,7 @@ def test_quant_argument_errors_before_any_launch():
     assert dq(g16) == pkv.PKV_EINVAL                               # not an 8-bit pool
     assert dq(gi8, q_dtype=pkv.PKV_F32) == pkv.PKV_EUNSUPPORTED    # query type
     assert dq(gi8, ks=None) == pkv.PKV_EINVAL                      # missing scales
-    assert dq(gi8, H=64) == pkv.PKV_EUNSUPPORTED                   # 8 query heads per kv head
+    assert dq(gi8, H=24) == pkv.PKV_EUNSUPPORTED                   # 3 query heads per kv head
     assert dq(gfp8, ws=None) == pkv.PKV_EWORKSPACE
 
     def wq(g, new_dtype=pkv.PKV_BF16, n=3, ks=P(1)):
@@ -149,6 +149,14 @@ def test_quant_argument_errors_before_any_launch():
     # the workspace size of an 8-bit pool is that of any pool
     assert (pkv.LIB.paged_attn_decode_workspace_bytes(ctypes.byref(gi8), 2, 100, 0, 0, 4) ==
             pkv.LIB.paged_attn_decode_workspace_bytes(ctypes.byref(g16), 2, 100, 0, 0, 4))
+    # ... except with 8 query heads per kv head: two groups of 4 over each
+    # kv head, so partial slots for 16 kv heads of 4 query heads each
+    g8q = geo(H=64, Hkv=8, dt=pkv.PKV_I8)
+    slots = 4 + 2 * 16
+    want8 = -(-3 * 4 // 256) * 256 + -(-slots * 4 * 2 * 4 // 256) * 256 + slots * 4 * 128 * 4
+    assert pkv.LIB.paged_attn_decode_workspace_bytes(ctypes.byref(g8q), 2, 100, 0, 0, 4) == want8
+    assert pkv.LIB.paged_attn_decode_workspace_bytes(ctypes.byref(geo(H=64, Hkv=8)), 2, 100, 0, 0, 4) == (
+        -(-3 * 4 // 256) * 256 + -(-(4 + 16) * 8 * 2 * 4 // 256) * 256 + (4 + 16) * 8 * 128 * 4)
 
 
 def test_prefill_quant_workspace_and_errors():

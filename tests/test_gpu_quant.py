@@ -136,6 +136,10 @@ DECODE_CASES = [
     ("fp8", "f16", 16, 4, 128, 32, [40, 600, 1500], 100, 1),
     ("i8", "f16", 4, 2, 64, 32, [3, 90, 129], 1, 0),
     ("fp8", "bf16", 32, 8, 128, 32, [0, 0, 2000, 0, 4100, 1], 0, 0),
+    # 8 query heads per kv head: two groups of 4 over each kv head
+    ("i8", "bf16", 64, 8, 128, 32, [1, 33, 700, 3000], 0, 0),
+    ("fp8", "f16", 16, 2, 64, 16, [5, 200, 1500], 100, 0),
+    ("fp8", "bf16", 8, 1, 128, 16, [17, 2048], 0, 5),
 ]
 
 
@@ -177,10 +181,10 @@ def oracle_seq_decode(w, s, fmt):
 
 
 @pytest.mark.parametrize("fmt", ["i8", "fp8"])
-@pytest.mark.parametrize("cfg", [2, 3, 4])
+@pytest.mark.parametrize("cfg", [2, 3, 4, 7])
 def test_quant_decode_configs_sampled(lib, cfg, fmt):
-    """The batched MHA, long-context GQA and sliding-window workloads with
-    8-bit pools: the shortest, the longest and four more sequences against
+    """The batched MHA, long-context GQA (4 and 8 query heads per kv head)
+    and sliding-window workloads with 8-bit pools: the shortest, the longest and four more sequences against
     the oracle over their encoded logical rows; the encoding error against
     the 16-bit result is reported."""
     pkv, session = lib
@@ -216,13 +220,19 @@ def test_quant_decode_worker_independence(lib):
         assert np.abs(o - outs[0]).max() <= 1e-5
 
 
-def test_quant_group_of_eight_unsupported(lib):
+def test_quant_group_of_eight_worker_independence(lib):
+    """8 query heads per kv head run as two groups of 4: the result does not
+    depend on how the work is split."""
     pkv, session = lib
-    note("quant G=8 unsupported")
-    w = wl.make_decode(lens=[20], num_heads=8, num_kv_heads=1, head_dim=64, block_size=16, dtype="bf16", seed=2)
-    with pytest.raises(pkv.PagedAttnError) as e:
-        run(session, w, "i8")
-    assert e.value.status == pkv.PKV_EUNSUPPORTED
+    note("quant G=8 worker independence")
+    w = wl.make_decode(lens=[20, 999, 64], num_heads=16, num_kv_heads=2, head_dim=128, block_size=16,
+                       dtype="bf16", seed=2, spare_blocks=2)
+    outs = []
+    for workers in (1, 5, 300, 0):
+        d = run(session, w, "fp8", num_workers=workers)
+        outs.append(d.out.cpu().numpy())
+    for o in outs[1:]:
+        assert np.abs(o - outs[0]).max() <= 1e-5
 
 
 # ---------------------------------------------------------------- prefill
