@@ -88,12 +88,12 @@ __global__ __launch_bounds__(256) void widen_claim_kernel(WidenArgs a) {
   if (pb >= 0) atomicMin(&a.owner[pb], (int32_t)e);
 }
 
-// One workgroup per entry (logical block j = blockIdx.x of sequence
-// s = blockIdx.y): it maps the entry to its block's copy and, if it owns
-// the copy, widens 16-code pieces of the block into it.
+// One workgroup per entry s * msb + j (logical block j of sequence s): it
+// maps the entry to its block's copy and, if it owns the copy, widens
+// 16-code pieces of the block into it.
 template <class C, class O>
 __global__ __launch_bounds__(256) void widen_kernel(WidenArgs a) {
-  const int j = blockIdx.x, s = blockIdx.y;
+  const int j = (int)(blockIdx.x % (unsigned)a.msb), s = (int)(blockIdx.x / (unsigned)a.msb);
   const int pb = staged_source(a, s, j);
   const size_t stg = (size_t)s * a.msb + j;
   const int32_t own = pb >= 0 ? a.owner[pb] : -1;
@@ -130,7 +130,7 @@ hipError_t launch_widen(const WidenArgs& a, hipStream_t st) {
   const unsigned eb = (unsigned)((entries + 255) / 256);
   hipLaunchKernelGGL(widen_reset_kernel, dim3(eb), dim3(256), 0, st, a);
   hipLaunchKernelGGL(widen_claim_kernel, dim3(eb), dim3(256), 0, st, a);
-  const dim3 grid(a.msb, a.S), block(256);
+  const dim3 grid((unsigned)entries), block(256);
   if (a.code_dtype == 3 && a.out_dtype == 2) hipLaunchKernelGGL((widen_kernel<I8T, BF16T>), grid, block, 0, st, a);
   else if (a.code_dtype == 3 && a.out_dtype == 1) hipLaunchKernelGGL((widen_kernel<I8T, F16T>), grid, block, 0, st, a);
   else if (a.code_dtype == 4 && a.out_dtype == 2) hipLaunchKernelGGL((widen_kernel<FP8T, BF16T>), grid, block, 0, st, a);
