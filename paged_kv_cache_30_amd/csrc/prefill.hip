@@ -175,19 +175,19 @@ template <> __device__ __forceinline__ void v_to_f16<BF16T>(uint16_t* unit) {
 
 // QS: the pools hold widened 8-bit codes whose row scales multiply each
 // key's score (K scale) and weight (V scale).
-template <class T, int D, int B, int G, bool QS>
-__global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a, float scale_log2) {
+template <class T, int D, int B, int G, bool QS, int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_kernel(PrefillArgs a, float scale_log2) {
   using M = Mma<T>;      // S = K.Q^T in the input type
   using MP = Mma<F16T>;  // O += V^T.P^T in fp16 (V converted in LDS when bf16)
   using V8 = typename M::V8;
   using P8 = typename MP::V8;
   constexpr int KC = D / 16;            // MFMA k-chunks over the head dim
   constexpr int DT = D / 32;            // 32-wide output tiles over the head dim
-  constexpr int HPW = G < 4 ? G : 4;    // query heads per workgroup
-  constexpr int PSUB = 4 / HPW;         // 32-row query sub-tiles per workgroup
+  constexpr int HPW = G < NW ? G : NW;  // query heads per workgroup
+  constexpr int PSUB = NW / HPW;        // 32-row query sub-tiles per workgroup
   constexpr int QT = 32 * PSUB;         // query rows per workgroup
   constexpr int U = D / 8;              // 16-byte units per key row
-  constexpr int NLD = kKT * U / 256;    // direct loads per thread per tile (each of K and V)
+  constexpr int NLD = kKT * U / (64 * NW);  // direct loads per thread per tile (each of K and V)
 
   // Two buffers of each of K and V, as separate arrays: the compiler then
   // knows that reads of one buffer do not depend on direct loads in flight
@@ -289,13 +289,13 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a, float sc
   auto fetch_table = [&](int t0) {
 #pragma unroll
     for (int j = 0; j < NLD; ++j)  // in range of the table row even past the context
-      pb_ins[j] = trow[min((t0 + (4 * j + wave) * RPI) / B, a.mb - 1)];
+      pb_ins[j] = trow[min((t0 + (NW * j + wave) * RPI) / B, a.mb - 1)];
     if (wave == 0) pb_key = trow[min((t0 + lane) / B, a.mb - 1)];
   };
   // Per-lane byte offsets inside a block of load j (tiles start at multiples
   // of kKT, a multiple of B, so row r of a tile is row r % B of its block).
   auto unit_off = [&](int j, bool v) -> uint32_t {
-    const int r = (4 * j + wave) * RPI + lane / U, cs = lane % U;
+    const int r = (NW * j + wave) * RPI + lane / U, cs = lane % U;
     return (uint32_t)((r % B) * row_stride) + 16 * (cs ^ (v ? Swz<D>::v(r) : Swz<D>::k(r)));
   };
   auto gather = [&](int t0, uint16_t* kd, uint16_t* vd) {
@@ -307,15 +307,15 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a, float sc
       const bool blk_ok = pb >= 0 && pb < a.nb;
       const size_t boff = (size_t)(uint32_t)(blk_ok ? pb : 0) * block_stride;
       bool ok = blk_ok;
-      if (!whole) ok = ok && in_range(t0 + (4 * j + wave) * RPI + lane / U);
-      dma16(ok ? kpool + boff + unit_off(j, false) : zero, kd + (4 * j + wave) * 512);
-      dma16(ok ? vpool + boff + unit_off(j, true) : zero, vd + (4 * j + wave) * 512);
+      if (!whole) ok = ok && in_range(t0 + (NW * j + wave) * RPI + lane / U);
+      dma16(ok ? kpool + boff + unit_off(j, false) : zero, kd + (NW * j + wave) * 512);
+      dma16(ok ? vpool + boff + unit_off(j, true) : zero, vd + (NW * j + wave) * 512);
     }
   };
   // Convert the V units this thread's direct loads wrote (after dma_wait).
   auto convert_v = [&](uint16_t* vd) {
 #pragma unroll
-    for (int j = 0; j < NLD; ++j) v_to_f16<T>(vd + (4 * j + wave) * 512 + 8 * lane);
+    for (int j = 0; j < NLD; ++j) v_to_f16<T>(vd + (NW * j + wave) * 512 + 8 * lane);
   };
   // Key validity bitmask of a tile (64 lanes = 64 keys), by wavefront 0;
   // with QS also the keys' scales, into registers (stored to LDS by
@@ -555,8 +555,11 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a, float sc
 
 template <class T, int D, int B, int G>
 static hipError_t launch_typed(const PrefillArgs& a, hipStream_t st) {
-  constexpr int HPW = G < 4 ? G : 4;
-  constexpr int QT = 32 * (4 / HPW);
+  // Wavefronts per workgroup: 8 with 4 or more query heads per kv head (the
+  // tile gather and its table reads are then shared by 8 wavefronts), else 4.
+  constexpr int NW = G >= 4 ? 8 : 4;
+  constexpr int HPW = G < NW ? G : NW;
+  constexpr int QT = 32 * (NW / HPW);
   PrefillArgs b = a;
   b.grid_q = (a.max_q_len + QT - 1) / QT;
   b.grid_y = a.Hkv * (G / HPW);
@@ -564,9 +567,9 @@ static hipError_t launch_typed(const PrefillArgs& a, hipStream_t st) {
   if (n > INT32_MAX) return hipErrorInvalidValue;
   dim3 grid((unsigned)n);
   if (a.k_scale)
-    hipLaunchKernelGGL((prefill_kernel<T, D, B, G, true>), grid, dim3(256), 0, st, b, a.scale * kLog2e);
+    hipLaunchKernelGGL((prefill_kernel<T, D, B, G, true, NW>), grid, dim3(64 * NW), 0, st, b, a.scale * kLog2e);
   else
-    hipLaunchKernelGGL((prefill_kernel<T, D, B, G, false>), grid, dim3(256), 0, st, b, a.scale * kLog2e);
+    hipLaunchKernelGGL((prefill_kernel<T, D, B, G, false, NW>), grid, dim3(64 * NW), 0, st, b, a.scale * kLog2e);
   return hipGetLastError();
 }
 
