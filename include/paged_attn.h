@@ -282,11 +282,12 @@ size_t paged_attn_prefill_quant_workspace_bytes(const pkv_geometry_t* geom, int3
  * attention with every key and value replaced by its decoded value
  * code * scale.
  *
- * Four kernels on `stream`: the physical blocks holding positions [0, L) of
- * the sequences are widened into the workspace, codes unchanged as q_dtype
- * values (exact), once per physical block however many tables map it (two
- * small launches pick one owner per block first); then the prefill kernel
- * reads them through a staging table. A
+ * Four kernels on `stream`: the physical blocks the chunks read (below L,
+ * and with a window from the first row's window on, plus sink blocks) are
+ * widened into the workspace, codes unchanged as q_dtype values (exact),
+ * once per physical block however many tables map it (two small launches
+ * pick one owner per block first); then the prefill kernel reads them
+ * through a staging table. A
  * key's score is the dot product with its codes times its K scale (float32);
  * a weight is multiplied by its key's V scale times 2^4 (PKV_I8) or 2^6
  * (PKV_FP8) and rounded to fp16 for the matrix cores, and the output is
@@ -349,6 +350,35 @@ int paged_attn_mixed(const pkv_geometry_t* geom, float* out, float* lse, const v
                      const int32_t* context_lens, int32_t num_seqs, int32_t max_q_len,
                      int32_t max_context_len, int32_t window, int32_t num_sinks, float scale,
                      int32_t num_workers, void* workspace, size_t workspace_bytes, void* stream);
+
+/* paged_attn_mixed_quant_workspace_bytes - workspace of paged_attn_mixed_quant:
+ * the decode workspace (paged_attn_decode_workspace_bytes with the same
+ * arguments), rounded up to 256 bytes, plus the prefill staging
+ * (paged_attn_prefill_quant_workspace_bytes). 0 if either is 0. */
+size_t paged_attn_mixed_quant_workspace_bytes(const pkv_geometry_t* geom, int32_t num_seqs,
+                                              int32_t max_context_len, int32_t window, int32_t num_sinks,
+                                              int32_t num_workers);
+
+/* paged_attn_mixed_quant - paged_attn_mixed over 8-bit pools (the 8-bit
+ * pages of paged_attn_decode_quant with the continuous batching of
+ * paged_attn_mixed): sequences with one query row are computed as
+ * paged_attn_decode_quant computes them, the others as
+ * paged_attn_prefill_quant (only their blocks are widened), all enqueued on
+ * `stream`.
+ *
+ *   geom->kv_dtype, q / q_dtype, k_pool, v_pool, k_scale, v_scale: as
+ *                     paged_attn_prefill_quant (q has q_start[num_seqs] rows)
+ *   workspace         device, 16-byte aligned, at least
+ *                     paged_attn_mixed_quant_workspace_bytes(geom, num_seqs,
+ *                     max_context_len, window, num_sinks, num_workers) bytes
+ *                     (else PKV_EWORKSPACE, before anything is enqueued)
+ *   all other arguments as paged_attn_mixed. */
+int paged_attn_mixed_quant(const pkv_geometry_t* geom, float* out, float* lse, const void* q, int32_t q_dtype,
+                           const int32_t* q_start, const void* k_pool, const void* v_pool, const float* k_scale,
+                           const float* v_scale, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                           const int32_t* context_lens, int32_t num_seqs, int32_t max_q_len,
+                           int32_t max_context_len, int32_t window, int32_t num_sinks, float scale,
+                           int32_t num_workers, void* workspace, size_t workspace_bytes, void* stream);
 
 /* paged_kv_compress - compress groups of whole blocks into slots ("Build a
  * Memory-Compressed Attention Engine with KV Caching from Scratch", Step 2:

@@ -38,7 +38,8 @@ _QUANT = (torch.int8, torch.float8_e4m3fn)
 # Every symbol declared in include/paged_attn.h.
 EXPORTS = ("paged_kv_write", "paged_attn_decode_workspace_bytes", "paged_attn_decode_workers",
            "paged_attn_decode", "paged_attn_prefill", "paged_kv_write_quant", "paged_attn_decode_quant",
-           "paged_attn_prefill_quant_workspace_bytes", "paged_attn_prefill_quant", "paged_kv_copy_blocks", "paged_attn_mixed", "paged_kv_compress", "paged_attn_decode_compressed",
+           "paged_attn_prefill_quant_workspace_bytes", "paged_attn_prefill_quant", "paged_kv_copy_blocks",
+           "paged_attn_mixed_quant_workspace_bytes", "paged_attn_mixed_quant", "paged_attn_mixed", "paged_kv_compress", "paged_attn_decode_compressed",
            "pkv_status_string", "pkv_last_hip_error", "pkv_version")
 
 
@@ -82,6 +83,11 @@ def _load() -> ctypes.CDLL:
     lib.paged_attn_prefill_quant.argtypes = [G, P, P, P, I32, P, P, P, P, P, P, I32, P, I32, I32, I32, I32, I32, F,
                                              P, SZ, P]
     lib.paged_attn_prefill_quant.restype = ctypes.c_int
+    lib.paged_attn_mixed_quant_workspace_bytes.argtypes = [G, I32, I32, I32, I32, I32]
+    lib.paged_attn_mixed_quant_workspace_bytes.restype = SZ
+    lib.paged_attn_mixed_quant.argtypes = [G, P, P, P, I32, P, P, P, P, P, P, I32, P, I32, I32, I32, I32, I32, F,
+                                           I32, P, SZ, P]
+    lib.paged_attn_mixed_quant.restype = ctypes.c_int
     lib.paged_kv_copy_blocks.argtypes = [G, P, P, P, P, P, P, I32, P]
     lib.paged_kv_copy_blocks.restype = ctypes.c_int
     lib.paged_attn_mixed.argtypes = [G, P, P, P, P, P, P, P, I32, P, I32, I32, I32, I32, I32, F, I32, P, SZ, P]
@@ -643,3 +649,67 @@ def paged_attn_decode_compressed(out, q, k_pool, v_pool, block_tables, context_l
     bind_decode_compressed(out, q, k_pool, v_pool, block_tables, context_lens, full_start, slot_tables, num_slots,
                            max_context_len, window=window, scale=scale, num_workers=num_workers,
                            workspace=workspace, lse=lse, debug=debug)(stream)
+
+
+def paged_attn_mixed_quant_workspace_bytes(k_pool, num_heads, num_seqs, max_context_len, window=0, num_workers=0,
+                                           sinks=0) -> int:
+    """C ``paged_attn_mixed_quant_workspace_bytes`` for an 8-bit pool."""
+    return int(LIB.paged_attn_mixed_quant_workspace_bytes(ctypes.byref(geometry(k_pool, num_heads)), int(num_seqs),
+                                                          int(max_context_len), int(window), int(sinks),
+                                                          int(num_workers)))
+
+
+def bind_mixed_quant(out, q, q_start, k_pool, v_pool, k_scale, v_scale, block_tables, context_lens, max_q_len,
+                     max_context_len, *, window=0, scale, num_workers=0, workspace=None, lse=None, sinks=0,
+                     debug=None):
+    """Check and marshal the arguments of ``paged_attn_mixed_quant`` once;
+    returns a callable ``f(stream=None)``.  Without ``workspace`` one of the
+    size the call needs is allocated here, once."""
+    _check_quant_pools(k_pool, v_pool, k_scale, v_scale)
+    _dev(q, "q", ndim=3)
+    if q.dtype not in (torch.float16, torch.bfloat16):
+        raise ValueError("q must be float16 or bfloat16 for 8-bit pools")
+    _dev(out, "out", dtype=torch.float32, ndim=3)
+    _dev(q_start, "q_start", dtype=torch.int32, ndim=1)
+    _dev(block_tables, "block_tables", dtype=torch.int32, ndim=2)
+    _dev(context_lens, "context_lens", dtype=torch.int32, ndim=1)
+    T, H, D = q.shape
+    S = context_lens.shape[0]
+    if out.shape != q.shape or q_start.shape[0] != S + 1 or block_tables.shape[0] != S:
+        raise ValueError("shape mismatch between q, out, q_start, context_lens and block_tables")
+    if lse is not None:
+        _dev(lse, "lse", dtype=torch.float32, ndim=2)
+        if lse.shape != (T, H):
+            raise ValueError("lse must be [T, H]")
+    if workspace is None:
+        n = paged_attn_mixed_quant_workspace_bytes(k_pool, H, S, max_context_len, window, num_workers, sinks)
+        workspace = torch.empty(max(n, 16), dtype=torch.uint8, device=k_pool.device)
+    _dev(workspace, "workspace")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    g = geometry(k_pool, H)
+    args = (ctypes.byref(g), _ptr(out), _ptr(lse), _ptr(q), _DTYPES[q.dtype], _ptr(q_start), _ptr(k_pool),
+            _ptr(v_pool), _ptr(k_scale), _ptr(v_scale), _ptr(block_tables), block_tables.shape[1],
+            _ptr(context_lens), S, int(max_q_len), int(max_context_len), int(window), int(sinks), float(scale),
+            int(num_workers), _ptr(workspace), ws_bytes)
+    keep = (g, out, q, q_start, k_pool, v_pool, k_scale, v_scale, block_tables, context_lens, workspace, lse)
+    dbg = _debug(debug)
+
+    def call(stream=None):
+        if dbg:
+            _val.check_prefill(*_host(q_start, block_tables, context_lens), num_rows=T, max_q_len=int(max_q_len),
+                               max_context_len=int(max_context_len), num_blocks=g.num_blocks,
+                               block_size=g.block_size, window=int(window), sinks=int(sinks),
+                               what="paged_attn_mixed_quant")
+        _check(LIB.paged_attn_mixed_quant(*args, _stream(stream)), "paged_attn_mixed_quant")
+    call.keep = keep
+    return call
+
+
+def paged_attn_mixed_quant(out, q, q_start, k_pool, v_pool, k_scale, v_scale, block_tables, context_lens, max_q_len,
+                           max_context_len, *, window=0, scale, num_workers=0, workspace=None, lse=None,
+                           stream=None, sinks=0, debug=None) -> None:
+    """C ``paged_attn_mixed_quant``: prefill chunks and single decode rows in
+    one call over 8-bit pools."""
+    bind_mixed_quant(out, q, q_start, k_pool, v_pool, k_scale, v_scale, block_tables, context_lens, max_q_len,
+                     max_context_len, window=window, scale=scale, num_workers=num_workers, workspace=workspace,
+                     lse=lse, sinks=sinks, debug=debug)(stream)

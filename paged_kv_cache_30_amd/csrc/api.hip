@@ -301,12 +301,19 @@ size_t paged_attn_prefill_quant_workspace_bytes(const pkv_geometry_t* geom, int3
   return quant_prefill_stage(geom, num_seqs, max_context_len).total();
 }
 
-int paged_attn_prefill_quant(const pkv_geometry_t* geom, float* out, float* lse, const void* q, int32_t q_dtype,
-                             const int32_t* q_start, const void* k_pool, const void* v_pool, const float* k_scale,
-                             const float* v_scale, const int32_t* block_tables, int32_t max_blocks_per_seq,
-                             const int32_t* context_lens, int32_t num_seqs, int32_t max_q_len,
-                             int32_t max_context_len, int32_t window, int32_t num_sinks, float scale,
-                             void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Widening plus the prefill kernel over 8-bit pools, for the sequences with
+// at least min_rows query rows (1: every chunk; 2: the chunks of a mixed
+// batch, whose single rows decode computes).
+int prefill_quant_common(const pkv_geometry_t* geom, float* out, float* lse, const void* q, int32_t q_dtype,
+                         const int32_t* q_start, const void* k_pool, const void* v_pool, const float* k_scale,
+                         const float* v_scale, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                         const int32_t* context_lens, int32_t num_seqs, int32_t max_q_len,
+                         int32_t max_context_len, int32_t window, int32_t num_sinks, float scale,
+                         void* workspace, size_t workspace_bytes, void* stream, int min_rows) {
   int st = check_geometry(geom);
   if (st) return st;
   if (!is_quant(geom->kv_dtype) || (q_dtype != PKV_F16 && q_dtype != PKV_BF16)) return PKV_EUNSUPPORTED;
@@ -340,6 +347,10 @@ int paged_attn_prefill_quant(const pkv_geometry_t* geom, float* out, float* lse,
   // rounding error, back in output units, is below 2^-22 (8 ulps of the
   // smallest subnormal); the output is divided by the same power of two.
   w.v_mul = geom->kv_dtype == PKV_I8 ? 16.f : 64.f;
+  w.q_start = q_start;
+  w.min_rows = min_rows;
+  w.window = window;
+  w.sinks = num_sinks;
   st = hip_status(pkv::launch_widen(w, (hipStream_t)stream));
   if (st) return st;
   pkv::PrefillArgs a{out, lse, q, q_start, k_stage, v_stage, t_stage, context_lens, num_seqs,
@@ -349,7 +360,23 @@ int paged_attn_prefill_quant(const pkv_geometry_t* geom, float* out, float* lse,
   a.k_scale = ks_stage;
   a.v_scale = vs_stage;
   a.o_mul = 1.f / w.v_mul;
+  a.skip_single = min_rows > 1;
   return hip_status(pkv::launch_prefill(a, (hipStream_t)stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int paged_attn_prefill_quant(const pkv_geometry_t* geom, float* out, float* lse, const void* q, int32_t q_dtype,
+                             const int32_t* q_start, const void* k_pool, const void* v_pool, const float* k_scale,
+                             const float* v_scale, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                             const int32_t* context_lens, int32_t num_seqs, int32_t max_q_len,
+                             int32_t max_context_len, int32_t window, int32_t num_sinks, float scale,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  return prefill_quant_common(geom, out, lse, q, q_dtype, q_start, k_pool, v_pool, k_scale, v_scale, block_tables,
+                              max_blocks_per_seq, context_lens, num_seqs, max_q_len, max_context_len, window,
+                              num_sinks, scale, workspace, workspace_bytes, stream, 1);
 }
 
 int paged_kv_copy_blocks(const pkv_geometry_t* geom, void* k_pool, void* v_pool, float* k_scale, float* v_scale,
@@ -403,6 +430,64 @@ int paged_attn_mixed(const pkv_geometry_t* geom, float* out, float* lse, const v
                       max_blocks_per_seq, geom->num_blocks, window, geom->kv_dtype, max_q_len,
                       max_context_len, scale, num_sinks, 1};
   return hip_status(pkv::launch_prefill(pa, (hipStream_t)stream));
+}
+
+size_t paged_attn_mixed_quant_workspace_bytes(const pkv_geometry_t* geom, int32_t num_seqs,
+                                              int32_t max_context_len, int32_t window, int32_t num_sinks,
+                                              int32_t num_workers) {
+  const size_t d = paged_attn_decode_workspace_bytes(geom, num_seqs, max_context_len, window, num_sinks,
+                                                     num_workers);
+  const size_t p = paged_attn_prefill_quant_workspace_bytes(geom, num_seqs, max_context_len);
+  if (!d || !p) return 0;
+  return (d + 255) / 256 * 256 + p;
+}
+
+int paged_attn_mixed_quant(const pkv_geometry_t* geom, float* out, float* lse, const void* q, int32_t q_dtype,
+                           const int32_t* q_start, const void* k_pool, const void* v_pool, const float* k_scale,
+                           const float* v_scale, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                           const int32_t* context_lens, int32_t num_seqs, int32_t max_q_len,
+                           int32_t max_context_len, int32_t window, int32_t num_sinks, float scale,
+                           int32_t num_workers, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_geometry(geom);
+  if (st) return st;
+  if (!is_quant(geom->kv_dtype) || (q_dtype != PKV_F16 && q_dtype != PKV_BF16)) return PKV_EUNSUPPORTED;
+  if (num_seqs < 0 || max_blocks_per_seq <= 0 || max_q_len < 0 || max_context_len < 0 || window < 0 ||
+      num_sinks < 0 || num_workers < 0 || !isfinite(scale))
+    return PKV_EINVAL;
+  if (window == 0) num_sinks = 0;
+  if ((long long)max_context_len > (long long)max_blocks_per_seq * geom->block_size) return PKV_EINVAL;
+  if (max_q_len > max_context_len) return PKV_EINVAL;
+  if (num_seqs == 0 || max_q_len == 0) return PKV_OK;
+  if (!out || !q || !q_start || !k_pool || !v_pool || !k_scale || !v_scale || !block_tables || !context_lens)
+    return PKV_EINVAL;
+  const int G = geom->num_heads / geom->num_kv_heads;
+  int kv_shift;
+  const pkv_geometry_t view = decode_view(geom, &kv_shift);
+  if (!pkv::prefill_supported(q_dtype, geom->head_dim, geom->block_size, G) ||
+      !pkv::decode_supported(view.kv_dtype, q_dtype, view.head_dim, view.block_size,
+                             view.num_heads / view.num_kv_heads))
+    return PKV_EUNSUPPORTED;
+  DecodeSplit sp;
+  st = decode_split(&view, num_seqs, max_context_len, window, num_sinks, num_workers, &sp);
+  if (st) return st;
+  const size_t dec_bytes = (sp.total() + 255) / 256 * 256;
+  if (!workspace || workspace_bytes < dec_bytes || ((uintptr_t)workspace & 15)) return PKV_EWORKSPACE;
+  char* ws = (char*)workspace;
+  pkv::DecodeArgs da{out, lse, q, k_pool, v_pool, block_tables, context_lens, k_scale, v_scale, q_dtype,
+                     (int32_t*)ws, (float*)(ws + sp.cum_bytes), (float*)(ws + sp.cum_bytes + sp.ml_bytes),
+                     num_seqs, view.num_heads, view.num_kv_heads, view.head_dim, view.block_size,
+                     max_blocks_per_seq, view.num_blocks, window, view.kv_dtype, max_context_len,
+                     sp.workers, scale, num_sinks, q_start};
+  da.kv_shift = kv_shift;
+  if (max_q_len >= 2) {  // the chunks' staging must fit too: check before enqueueing anything
+    if (workspace_bytes - dec_bytes < quant_prefill_stage(geom, num_seqs, max_context_len).total())
+      return PKV_EWORKSPACE;
+  }
+  st = hip_status(pkv::launch_decode(da, (hipStream_t)stream));
+  if (st || max_q_len < 2) return st;
+  return prefill_quant_common(geom, out, lse, q, q_dtype, q_start, k_pool, v_pool, k_scale, v_scale, block_tables,
+                              max_blocks_per_seq, context_lens, num_seqs, max_q_len, max_context_len, window,
+                              num_sinks, scale, ws + dec_bytes, workspace_bytes - dec_bytes, stream, 2);
 }
 
 int paged_kv_compress(const pkv_geometry_t* geom, void* k_pool, void* v_pool, const int32_t* src_blocks,

@@ -136,6 +136,11 @@ struct WidenArgs {
   int32_t* owner;  // [nb]: entry s * msb + j that owns the copy of a physical block
   int32_t S, mb, msb, nb, B, Hkv, D, code_dtype, out_dtype, max_context_len;
   float v_mul;
+  // What the prefill will read: sequences with at least min_rows query rows
+  // (q_start [S + 1]), and with a window only blocks that hold a position
+  // its first row attends or a sink position.
+  const int32_t* q_start;
+  int32_t min_rows, window, sinks;
 };
 hipError_t launch_widen(const WidenArgs& a, hipStream_t st);
 

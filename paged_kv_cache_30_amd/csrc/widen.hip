@@ -64,13 +64,23 @@ template <> __device__ __forceinline__ u32x4 pack8<F16T>(const float* f) {
 // 65504, the largest finite fp16 value.
 constexpr float kVScaleCap = 65504.f / 256.f;
 
-// Physical block of entry (s, j) when it holds positions below the
-// (clamped) context length and lies in the pool, else -1.
+// Physical block of entry (s, j) when the prefill reads it and it lies in
+// the pool, else -1. The prefill reads, for a sequence with C >= min_rows
+// query rows, the blocks below the (clamped) context length L; with a
+// window only those holding a position at or after L - C - window + 1 (the
+// first row's window) or below the sink count.
 __device__ __forceinline__ int staged_source(const WidenArgs& a, int s, int j) {
+  const int C = a.q_start[s + 1] - a.q_start[s];
+  if (C < a.min_rows) return -1;
   int L = a.lens[s];
   L = L < 0 ? 0 : (L > a.max_context_len ? a.max_context_len : L);
   const int nblk = (L + a.B - 1) / a.B;
-  const int pb = (j < nblk && j < a.mb) ? a.tables[(size_t)s * a.mb + j] : -1;
+  if (j >= nblk || j >= a.mb) return -1;
+  if (a.window > 0) {
+    const int lo = L - C - a.window + 1;
+    if ((j + 1) * a.B <= lo && j * a.B >= a.sinks) return -1;
+  }
+  const int pb = a.tables[(size_t)s * a.mb + j];
   return (pb >= 0 && pb < a.nb) ? pb : -1;
 }
 

@@ -193,6 +193,24 @@ def test_prefill_quant_workspace_and_errors():
     assert pq(gi8, max_q=101) == pkv.PKV_EINVAL                    # chunk longer than any context
     assert pq(gi8, S=0) == pkv.PKV_OK
     assert pq(gi8, max_q=0) == pkv.PKV_OK
+    # mixed batches over 8-bit pools: decode workspace (256-aligned) + staging
+    for g, S, L in ((gi8, 8, 2560), (gfp8, 3, 1000), (geo(H=64, Hkv=8, dt=pkv.PKV_I8), 4, 300)):
+        d = pkv.LIB.paged_attn_decode_workspace_bytes(ctypes.byref(g), S, L, 0, 0, 0)
+        p = pkv.LIB.paged_attn_prefill_quant_workspace_bytes(ctypes.byref(g), S, L)
+        assert pkv.LIB.paged_attn_mixed_quant_workspace_bytes(ctypes.byref(g), S, L, 0, 0, 0) == up(d) + p
+    assert pkv.LIB.paged_attn_mixed_quant_workspace_bytes(ctypes.byref(geo()), 8, 2560, 0, 0, 0) == 0
+    mneed = pkv.LIB.paged_attn_mixed_quant_workspace_bytes(ctypes.byref(gi8), 2, 100, 0, 0, 0)
+
+    def mq(g, q_dtype=pkv.PKV_BF16, ks=P(1), ws=P(4096), wsb=mneed, S=2, max_q=4, mcl=100):
+        return pkv.LIB.paged_attn_mixed_quant(ctypes.byref(g), P(1), None, P(1), q_dtype, P(1), P(1), P(1), ks,
+                                              P(1), P(1), 8, P(1), S, max_q, mcl, 0, 0, 0.1, 0, ws, wsb, None)
+    assert mq(geo()) == pkv.PKV_EUNSUPPORTED                       # not an 8-bit pool
+    assert mq(gi8, q_dtype=pkv.PKV_F32) == pkv.PKV_EUNSUPPORTED
+    assert mq(gi8, ks=None) == pkv.PKV_EINVAL
+    assert mq(gi8, ws=None) == pkv.PKV_EWORKSPACE
+    assert mq(gi8, wsb=mneed - 1) == pkv.PKV_EWORKSPACE            # staging part short: refused before any launch
+    assert mq(gi8, mcl=129) == pkv.PKV_EINVAL
+    assert mq(gi8, S=0) == pkv.PKV_OK
 
 
 def test_compressed_argument_errors_before_any_launch():

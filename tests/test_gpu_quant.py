@@ -367,3 +367,44 @@ def test_quant_prefill_workspace_reuse(lib, fmt):
                          block_size=16, num_kv_heads=2, window=0, scale=w.scale)
     max_err(out.cpu().numpy(), want, f"reuse {fmt} first call")
     assert torch.equal(out2, out[r1:]), "sub-batch rows differ from the full batch"
+
+
+# ------------------------------------------------------------ mixed batches
+
+MIXED_CASES = [
+    # (fmt, dtype, H, Hkv, D, B, prefix, chunks, window, sinks, workers)
+    ("i8", "bf16", 32, 8, 128, 16, 256, [1, 300, 1, 40, 1, 1], 0, 0, 0),
+    ("fp8", "f16", 8, 2, 64, 32, 96, [64, 1, 1, 7, 0], 0, 0, 5),
+    ("fp8", "bf16", 8, 8, 128, 16, 160, [90, 1, 31, 1], 50, 4, 0),
+    ("i8", "bf16", 64, 8, 128, 32, 256, [1, 100, 1, 1], 0, 0, 0),
+    ("i8", "f16", 16, 4, 128, 16, 48, [1, 1, 1], 0, 0, 0),
+]
+
+
+@pytest.mark.parametrize("case", MIXED_CASES,
+                         ids=[f"{c[0]}-{c[1]}-g{c[2] // c[3]}-c{'.'.join(map(str, c[7]))}-w{c[8]}" for c in MIXED_CASES])
+def test_quant_mixed_batch(lib, case):
+    """Prefill chunks and single decode rows in one call over 8-bit pools,
+    against the oracle's prefill over the decoded pools (a single row is a
+    chunk of one)."""
+    pkv, session = lib
+    fmt, dtype, H, Hkv, D, B, prefix, chunks, window, sinks, workers = case
+    note(f"quant mixed batch {case}")
+    w = wl.make_prefill(prefix_len=prefix, chunk_lens=chunks, num_heads=H, num_kv_heads=Hkv, head_dim=D,
+                        block_size=B, dtype=dtype, seed=prefix + sum(chunks) + 7, window=window, sinks=sinks,
+                        spare_blocks=2)
+    d = session.DeviceWorkload(w, kv_format=fmt)
+    d.write_step()
+    n = pkv.paged_attn_mixed_quant_workspace_bytes(d.k_pool, H, w.num_seqs, w.max_context_len, window, workers,
+                                                   sinks=sinks)
+    ws = torch.randint(0, 256, (n,), dtype=torch.uint8, device="cuda")  # no initialisation needed
+    pkv.paged_attn_mixed_quant(d.out, d.q, d.q_start, d.k_pool, d.v_pool, d.k_scale, d.v_scale, d.tables, d.lens,
+                               w.max_q_len, w.max_context_len, window=window, scale=w.scale, num_workers=workers,
+                               workspace=ws, lse=d.lse, sinks=sinks)
+    torch.cuda.synchronize()
+    kp, vp = ref.build_pools(w)
+    kc, vc, ks, vs = oq.quantize_pools(kp, vp, dtype, fmt)
+    out, lse = oq.prefill(w.q, w.q_start, kc, vc, ks, vs, w.block_tables, w.context_lens, fmt=fmt, q_dtype=dtype,
+                          block_size=B, num_kv_heads=Hkv, window=window, scale=w.scale, sinks=sinks)
+    max_err(d.out.cpu().numpy(), out, str(case))
+    assert np.abs(d.lse.cpu().numpy() - lse).max() <= TOL_LSE_PREFILL
