@@ -264,7 +264,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_kernel(PrefillArgs a,
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) o[dt] = f32x16{};
   float m_run = -INFINITY;  // running max of the scaled scores (base 2)
-  float l_run = 0.f;        // sum of the weights as multiplied (normaliser)
+  float l_run = 0.f;        // normaliser: sum of the weights (fp16-rounded ones; fp32 with QS)
 
   const int wave_pmin = base + row0;
   const int wave_pmax = base + min(row0 + 31, C - 1);
@@ -485,12 +485,20 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_kernel(PrefillArgs a,
         for (int e2 = 0; e2 < 4; ++e2) {
           const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kh][8 * sub + 2 * e2], scale_log2, -ms));
           const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kh][8 * sub + 2 * e2 + 1], scale_log2, -ms));
-          const uint32_t h = MP::pack(p0, p1);
-          // The normaliser sums the weights; V is multiplied by weight x V scale.
-          uint32_t hv = h;
-          if constexpr (QS) hv = MP::pack(p0 * vs[2 * e2], p1 * vs[2 * e2 + 1]);
-          hi[e2] = hv;
-          l_run = __builtin_amdgcn_fdot2(as_h2(h), f16x2{(_Float16)1.f, (_Float16)1.f}, l_run, false);
+          if constexpr (QS) {
+            // V is multiplied by weight x V scale, rounded to fp16; the
+            // normaliser sums the weights in fp32 (the rounded products,
+            // divided by their scales, then err by 2^-12 relative each
+            // against it, independently).
+            hi[e2] = MP::pack(p0 * vs[2 * e2], p1 * vs[2 * e2 + 1]);
+            l_run += p0 + p1;
+          } else {
+            // The normaliser sums the weights as rounded for the matrix
+            // cores, so the output is their exact weighted average.
+            const uint32_t h = MP::pack(p0, p1);
+            hi[e2] = h;
+            l_run = __builtin_amdgcn_fdot2(as_h2(h), f16x2{(_Float16)1.f, (_Float16)1.f}, l_run, false);
+          }
         }
         const P8 bhi = __builtin_bit_cast(P8, u32x4{hi[0], hi[1], hi[2], hi[3]});
         lds_wait();
