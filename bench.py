@@ -175,7 +175,7 @@ def cpu_baseline(w, target_s: float):
 
 
 KERNELS = {"decode": ("decode_split_kernel", "decode_merge_kernel", "decode_plan_kernel"),
-           "prefill": ("prefill_kernel", "widen_")}
+           "prefill": ("prefill_kernel", "widen_kernel")}
 
 
 def attend_sources(kind: str, kv: str):
@@ -224,7 +224,7 @@ def summarize_pmc(args, fetch_dir, write_dir, copy_mib) -> int:
         ours = sorted((i, k, v) for (i, k), v in vals.items() if any(n in k for n in KERNELS[kind]))
         # group consecutive dispatches of one call: the split/prefill kernel
         # starts a call, the widening kernel over 8-bit pools
-        first = "widen_reset_kernel" if (kind == "prefill" and args.kv != "native") else KERNELS[kind][0]
+        first = "widen_kernel" if (kind == "prefill" and args.kv != "native") else KERNELS[kind][0]
         calls, cur = [], None
         for i, k, v in ours:
             if first in k:

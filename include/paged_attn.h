@@ -269,9 +269,8 @@ int paged_attn_decode_quant(const pkv_geometry_t* geom, float* out, float* lse, 
 /* paged_attn_prefill_quant_workspace_bytes - bytes of device workspace
  * paged_attn_prefill_quant needs for num_seqs sequences of context at most
  * max_context_len with this (8-bit) geometry: two staging pools of
- * num_seqs * ceil(max_context_len / B) blocks in 16-bit, their row scales, a
- * staging table and one int32 per pool block (geom->num_blocks). 0 if the
- * geometry is invalid or not 8-bit. */
+ * num_seqs * ceil(max_context_len / B) blocks in 16-bit, their row scales and
+ * a staging table. 0 if the geometry is invalid or not 8-bit. */
 size_t paged_attn_prefill_quant_workspace_bytes(const pkv_geometry_t* geom, int32_t num_seqs,
                                                 int32_t max_context_len);
 
@@ -282,12 +281,12 @@ size_t paged_attn_prefill_quant_workspace_bytes(const pkv_geometry_t* geom, int3
  * attention with every key and value replaced by its decoded value
  * code * scale.
  *
- * Four kernels on `stream`: the physical blocks the chunks read (below L,
+ * Two kernels on `stream`: the physical blocks the chunks read (below L,
  * and with a window from the first row's window on, plus sink blocks) are
  * widened into the workspace, codes unchanged as q_dtype values (exact),
- * once per physical block however many tables map it (two small launches
- * pick one owner per block first); then the prefill kernel reads them
- * through a staging table. A
+ * once per block for all the sequences that map it at the same logical
+ * index (a shared prefix); then the prefill kernel reads them through a
+ * staging table. A
  * key's score is the dot product with its codes times its K scale (float32);
  * a weight is multiplied by its key's V scale times 2^4 (PKV_I8) or 2^6
  * (PKV_FP8) and rounded to fp16 for the matrix cores, and the output is

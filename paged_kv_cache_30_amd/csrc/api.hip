@@ -275,8 +275,8 @@ namespace {
 // staging table, each 256-byte aligned.
 struct QuantPrefillStage {
   int msb;
-  size_t pool_bytes, scale_bytes, table_bytes, owner_bytes;
-  size_t total() const { return 2 * pool_bytes + 2 * scale_bytes + table_bytes + owner_bytes; }
+  size_t pool_bytes, scale_bytes, table_bytes;
+  size_t total() const { return 2 * pool_bytes + 2 * scale_bytes + table_bytes; }
 };
 
 QuantPrefillStage quant_prefill_stage(const pkv_geometry_t* g, int num_seqs, int max_context_len) {
@@ -287,7 +287,6 @@ QuantPrefillStage quant_prefill_stage(const pkv_geometry_t* g, int num_seqs, int
   q.pool_bytes = up(blocks * g->block_size * g->num_kv_heads * g->head_dim * 2);
   q.scale_bytes = up(blocks * g->num_kv_heads * g->block_size * sizeof(float));
   q.table_bytes = up(blocks * sizeof(int32_t));
-  q.owner_bytes = up((size_t)g->num_blocks * sizeof(int32_t));
   return q;
 }
 
@@ -338,9 +337,8 @@ int prefill_quant_common(const pkv_geometry_t* geom, float* out, float* lse, con
   float* ks_stage = (float*)(ws + 2 * sp.pool_bytes);
   float* vs_stage = (float*)(ws + 2 * sp.pool_bytes + sp.scale_bytes);
   int32_t* t_stage = (int32_t*)(ws + 2 * sp.pool_bytes + 2 * sp.scale_bytes);
-  int32_t* owner = (int32_t*)(ws + 2 * sp.pool_bytes + 2 * sp.scale_bytes + sp.table_bytes);
   pkv::WidenArgs w{k_pool, v_pool, k_scale, v_scale, block_tables, context_lens, k_stage, v_stage, ks_stage,
-                   vs_stage, t_stage, owner, num_seqs, max_blocks_per_seq, sp.msb, geom->num_blocks, geom->block_size,
+                   vs_stage, t_stage, num_seqs, max_blocks_per_seq, sp.msb, geom->num_blocks, geom->block_size,
                    geom->num_kv_heads, geom->head_dim, geom->kv_dtype, q_dtype, max_context_len};
   // V scales staged times 2^4 (INT8) or 2^6 (FP8), about QMAX / 8: a weight
   // times a staged scale is then below fp16's normal range only where its

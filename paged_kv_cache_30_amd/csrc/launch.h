@@ -117,8 +117,8 @@ struct PrefillArgs {
 // (exact: every INT8 code and E4M3 value is a bf16 and an fp16 value), with
 // their row scales: staged block s * msb + j holds logical block j of
 // sequence s, and stage_tables [S, msb] maps each entry to the copy of its
-// physical block (-1 where nothing is staged; a block that several entries
-// map is copied once). K scales are copied; V scales are multiplied by v_mul (a power of two) and
+// physical block (-1 where nothing is staged; a block that several
+// sequences map at the same logical index is copied once). K scales are copied; V scales are multiplied by v_mul (a power of two) and
 // capped at 65504 / 256, so that a weight (at most 256) times a V scale is a
 // finite fp16 value.
 struct WidenArgs {
@@ -133,7 +133,6 @@ struct WidenArgs {
   float* ks_out;
   float* vs_out;
   int32_t* stage_tables;
-  int32_t* owner;  // [nb]: entry s * msb + j that owns the copy of a physical block
   int32_t S, mb, msb, nb, B, Hkv, D, code_dtype, out_dtype, max_context_len;
   float v_mul;
   // What the prefill will read: sequences with at least min_rows query rows

@@ -14,12 +14,11 @@
 // divided by it) so that this product sits in fp16's normal range for the
 // weights that matter, capped at 65504 / 256 so that it stays finite.
 // Blocks past the context, and entries outside the pool, are not staged
-// (table entry -1). A physical block that several sequences map (a shared
-// prefix) is staged once: the first (sequence, logical block) entry that
-// maps it, in row-major order, owns the copy, and every entry that maps the
-// block points the staging table at that copy. Ownership takes two small
-// launches before the widening: reset the owner slot of every mapped
-// physical block, then an atomic minimum over the entries that map it.
+// (table entry -1). A physical block that several sequences map at the same
+// logical index (a shared prefix) is staged once: the entry of the first
+// such sequence owns the copy, and the others point the staging table at
+// it. (A block mapped at different logical indexes is staged once per
+// index.)
 #include "common.h"
 #include "launch.h"
 
@@ -84,31 +83,24 @@ __device__ __forceinline__ int staged_source(const WidenArgs& a, int s, int j) {
   return (pb >= 0 && pb < a.nb) ? pb : -1;
 }
 
-// One thread per entry (s, j) of the [S, msb] grid of logical blocks.
-__global__ __launch_bounds__(256) void widen_reset_kernel(WidenArgs a) {
-  const long long e = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (e >= (long long)a.S * a.msb) return;
-  const int pb = staged_source(a, (int)(e / a.msb), (int)(e % a.msb));
-  if (pb >= 0) a.owner[pb] = INT32_MAX;
-}
-__global__ __launch_bounds__(256) void widen_claim_kernel(WidenArgs a) {
-  const long long e = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (e >= (long long)a.S * a.msb) return;
-  const int pb = staged_source(a, (int)(e / a.msb), (int)(e % a.msb));
-  if (pb >= 0) atomicMin(&a.owner[pb], (int32_t)e);
-}
-
 // One workgroup per entry s * msb + j (logical block j of sequence s): it
 // maps the entry to its block's copy and, if it owns the copy, widens
 // 16-code pieces of the block into it.
 template <class C, class O>
 __global__ __launch_bounds__(256) void widen_kernel(WidenArgs a) {
   const int j = (int)(blockIdx.x % (unsigned)a.msb), s = (int)(blockIdx.x / (unsigned)a.msb);
-  const int pb = staged_source(a, s, j);
+  const int pb = staged_source(a, s, j);  // uniform over the workgroup
+  __shared__ int first;  // the first sequence whose entry j stages the same block
+  if (threadIdx.x == 0) first = s;
+  __syncthreads();
+  if (pb >= 0)
+    for (int t = threadIdx.x; t < s; t += 256)
+      if (staged_source(a, t, j) == pb) atomicMin(&first, t);
+  __syncthreads();
+  const int owner = first;
   const size_t stg = (size_t)s * a.msb + j;
-  const int32_t own = pb >= 0 ? a.owner[pb] : -1;
-  if (threadIdx.x == 0) a.stage_tables[stg] = own;
-  if (pb < 0 || (size_t)own != stg) return;  // the same for the whole workgroup
+  if (threadIdx.x == 0) a.stage_tables[stg] = pb >= 0 ? (int32_t)((size_t)owner * a.msb + j) : -1;
+  if (pb < 0 || owner != s) return;  // the same for the whole workgroup
   const size_t blk_codes = (size_t)a.B * a.Hkv * a.D;  // bytes of codes per block
   const int pieces = (int)(blk_codes / 16);
   const char* kc = (const char*)a.k_codes + (size_t)pb * blk_codes;
@@ -137,9 +129,6 @@ hipError_t launch_widen(const WidenArgs& a, hipStream_t st) {
   if (a.S == 0 || a.msb == 0) return hipSuccess;
   if (((size_t)a.B * a.Hkv * a.D) % 16) return hipErrorInvalidValue;
   const long long entries = (long long)a.S * a.msb;
-  const unsigned eb = (unsigned)((entries + 255) / 256);
-  hipLaunchKernelGGL(widen_reset_kernel, dim3(eb), dim3(256), 0, st, a);
-  hipLaunchKernelGGL(widen_claim_kernel, dim3(eb), dim3(256), 0, st, a);
   const dim3 grid((unsigned)entries), block(256);
   if (a.code_dtype == 3 && a.out_dtype == 2) hipLaunchKernelGGL((widen_kernel<I8T, BF16T>), grid, block, 0, st, a);
   else if (a.code_dtype == 3 && a.out_dtype == 1) hipLaunchKernelGGL((widen_kernel<I8T, F16T>), grid, block, 0, st, a);

@@ -161,9 +161,8 @@ def test_quant_argument_errors_before_any_launch():
 
 def test_prefill_quant_workspace_and_errors():
     """8-bit prefill: the workspace holds two 16-bit staging pools, their
-    scales, a staging table and one owner entry per pool block (each
-    256-byte aligned); argument errors return before anything is
-    enqueued."""
+    scales and a staging table (each 256-byte aligned); argument errors
+    return before anything is enqueued."""
     P = ctypes.c_void_p
     up = lambda x: -(-x // 256) * 256
     gi8 = geo(dt=pkv.PKV_I8)
@@ -171,7 +170,7 @@ def test_prefill_quant_workspace_and_errors():
     for g, S, L in ((gi8, 8, 2560), (gi8, 1, 1), (gfp8, 3, 1000)):
         blocks = S * -(-L // g.block_size)
         want = (2 * up(blocks * g.block_size * g.num_kv_heads * g.head_dim * 2) +
-                2 * up(blocks * g.num_kv_heads * g.block_size * 4) + up(blocks * 4) + up(g.num_blocks * 4))
+                2 * up(blocks * g.num_kv_heads * g.block_size * 4) + up(blocks * 4))
         assert pkv.LIB.paged_attn_prefill_quant_workspace_bytes(ctypes.byref(g), S, L) == want
     assert pkv.LIB.paged_attn_prefill_quant_workspace_bytes(ctypes.byref(geo()), 8, 2560) == 0  # 16-bit pool
     assert pkv.LIB.paged_attn_prefill_quant_workspace_bytes(ctypes.byref(gi8), 0, 100) == 0
