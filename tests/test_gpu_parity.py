@@ -453,19 +453,21 @@ def test_debug_mode_checks_device_content(lib):
 
 # ------------------------------------------------------------ HIP graphs
 
-@pytest.mark.parametrize("kind", ["decode", "prefill"])
+@pytest.mark.parametrize("kind", ["decode", "prefill", "decode-i8", "prefill-fp8"])
 def test_graph_replay_matches_eager(lib, kind):
     """The step's calls captured in a HIP graph: every replay, with eager work
-    and synchronisations between replays, gives the eager result bit for bit."""
+    and synchronisations between replays, gives the eager result bit for bit
+    (16-bit pages, and 8-bit pages with their write, widening and prefill)."""
     pkv, session = lib
     note(f"graph replay {kind}")
+    kind, _, fmt = kind.partition("-")
     if kind == "decode":
         w = wl.make_decode(lens=[33, 700, 1500, 4], num_heads=16, num_kv_heads=4, head_dim=128, block_size=16,
                            dtype="bf16", seed=23)
     else:
         w = wl.make_prefill(prefix_len=64, chunk_lens=[50, 20], num_heads=8, num_kv_heads=2, head_dim=128,
                             block_size=16, dtype="bf16", seed=24)
-    d = session.DeviceWorkload(w)
+    d = session.DeviceWorkload(w, kv_format=fmt or "native")
     d.step()
     torch.cuda.synchronize()
     eager = d.out.clone()
