@@ -286,8 +286,8 @@ size_t paged_attn_prefill_quant_workspace_bytes(const pkv_geometry_t* geom, int3
  * widened into the workspace, codes unchanged as q_dtype values (exact),
  * once per block for all the sequences that map it at the same logical
  * index (a shared prefix); then the prefill kernel reads them through a
- * staging table. A
- * key's score is the dot product with its codes times its K scale (float32);
+ * staging table. A key's score is the dot product with its codes times its
+ * K scale (float32);
  * a weight is multiplied by its key's V scale times 2^4 (PKV_I8) or 2^6
  * (PKV_FP8) and rounded to fp16 for the matrix cores, and the output is
  * divided by the same power of two; the normaliser (and lse) sums the
