@@ -240,3 +240,20 @@ def test_compressed_argument_errors_before_any_launch():
     assert dc(g, window=-1) == pkv.PKV_EINVAL
     assert dc(g, ws=None) == pkv.PKV_EWORKSPACE
     assert dc(g, S=0) == pkv.PKV_OK
+
+
+def test_plain_c_consumer(tmp_path):
+    """The header is valid C99 and the library links from C: a small C
+    program (tests/c_abi_consumer.c) calls the size queries, status strings
+    and argument checks, none of which touches a GPU."""
+    import shutil
+    if shutil.which("gcc") is None:
+        pytest.skip("no gcc")
+    exe = tmp_path / "c_abi"
+    libdir = os.path.dirname(pkv.LIB_PATH)
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror", "-I", os.path.join(ROOT, "include"),
+                    os.path.join(ROOT, "tests", "c_abi_consumer.c"), "-L", libdir, "-lpagedattn",
+                    f"-Wl,-rpath,{libdir}", "-o", str(exe)], check=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0, r.stderr
+    assert "c abi consumer ok" in r.stdout
