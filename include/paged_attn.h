@@ -290,9 +290,11 @@ size_t paged_attn_prefill_quant_workspace_bytes(const pkv_geometry_t* geom, int3
  * K scale (float32);
  * a weight is multiplied by its key's V scale times 2^4 (PKV_I8) or 2^6
  * (PKV_FP8) and rounded to fp16 for the matrix cores, and the output is
- * divided by the same power of two; the normaliser (and lse) sums the
- * weights in float32. A row whose largest |value| exceeds 2031 (PKV_I8) or
- * 1791 (PKV_FP8) is attended with its V scale capped there.
+ * divided by the same power of two; the normaliser (and lse) sums those
+ * rounded products divided by their V scales (float32), i.e. the weights the
+ * matrix cores actually apply, so the output is their exact weighted
+ * average. A row whose largest |value| exceeds 2031 (PKV_I8) or 1791
+ * (PKV_FP8) is attended with its V scale capped there.
  *
  *   geom->kv_dtype    PKV_I8 or PKV_FP8; head_dim, block_size and
  *                     num_heads / num_kv_heads as paged_attn_prefill

@@ -199,7 +199,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_kernel(PrefillArgs a,
   __shared__ unsigned long long kvalid[2];  // bit t: key t0 + t of the tile is mapped
   // QS: the K and V scales of the tile's keys (zero for keys outside the
   // range, which are masked), [slot][K or V][key].
-  __shared__ __attribute__((aligned(16))) float scl[QS ? 2 : 1][2][kKT];
+  __shared__ __attribute__((aligned(16))) float scl[QS ? 2 : 1][QS ? 3 : 1][kKT];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -264,7 +264,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_kernel(PrefillArgs a,
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) o[dt] = f32x16{};
   float m_run = -INFINITY;  // running max of the scaled scores (base 2)
-  float l_run = 0.f;        // normaliser: sum of the weights (fp16-rounded ones; fp32 with QS)
+  float l_run = 0.f;        // normaliser: sum of the fp16-rounded weights (with QS, weight x V scale / V scale)
 
   const int wave_pmin = base + row0;
   const int wave_pmax = base + min(row0 + 31, C - 1);
@@ -339,6 +339,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_kernel(PrefillArgs a,
       if (wave == 0) {
         scl[slot][0][lane] = sk_reg;
         scl[slot][1][lane] = sv_reg;
+        scl[slot][QS ? 2 : 0][lane] = sv_reg > 0.f ? 1.f / sv_reg : 0.f;
       }
     }
   };
@@ -474,12 +475,16 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_kernel(PrefillArgs a,
           e47[dt] = lds_read_tr<(16 * c + 8) * D * 2>(vbase + tr_addr[dt]);
         }
         uint32_t hi[4];
-        float vs[8];  // QS: V scales of this lane's 8 keys of the chunk
+        float vs[8], vi[8];  // QS: V scales of this lane's 8 keys of the chunk, and their inverses
         if constexpr (QS) {
           const float4 va = *reinterpret_cast<const float4*>(&scl[QS ? slot : 0][1][16 * c + 4 * hf]);
           const float4 vb = *reinterpret_cast<const float4*>(&scl[QS ? slot : 0][1][16 * c + 8 + 4 * hf]);
+          const float4 ia = *reinterpret_cast<const float4*>(&scl[QS ? slot : 0][QS ? 2 : 0][16 * c + 4 * hf]);
+          const float4 ib = *reinterpret_cast<const float4*>(&scl[QS ? slot : 0][QS ? 2 : 0][16 * c + 8 + 4 * hf]);
           vs[0] = va.x; vs[1] = va.y; vs[2] = va.z; vs[3] = va.w;
           vs[4] = vb.x; vs[5] = vb.y; vs[6] = vb.z; vs[7] = vb.w;
+          vi[0] = ia.x; vi[1] = ia.y; vi[2] = ia.z; vi[3] = ia.w;
+          vi[4] = ib.x; vi[5] = ib.y; vi[6] = ib.z; vi[7] = ib.w;
         }
 #pragma unroll
         for (int e2 = 0; e2 < 4; ++e2) {
@@ -487,11 +492,14 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_kernel(PrefillArgs a,
           const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kh][8 * sub + 2 * e2 + 1], scale_log2, -ms));
           if constexpr (QS) {
             // V is multiplied by weight x V scale, rounded to fp16; the
-            // normaliser sums the weights in fp32 (the rounded products,
-            // divided by their scales, then err by 2^-12 relative each
-            // against it, independently).
-            hi[e2] = MP::pack(p0 * vs[2 * e2], p1 * vs[2 * e2 + 1]);
-            l_run += p0 + p1;
+            // normaliser sums those rounded products divided by their
+            // scales, so that it holds exactly the weights the matrix cores
+            // multiply (a lone key's row then comes out exact).
+            const uint32_t hv = MP::pack(p0 * vs[2 * e2], p1 * vs[2 * e2 + 1]);
+            hi[e2] = hv;
+            const f16x2 w = as_h2(hv);
+            l_run = __builtin_fmaf((float)w[0], vi[2 * e2], l_run);
+            l_run = __builtin_fmaf((float)w[1], vi[2 * e2 + 1], l_run);
           } else {
             // The normaliser sums the weights as rounded for the matrix
             // cores, so the output is their exact weighted average.

@@ -121,7 +121,10 @@ __global__ __launch_bounds__(256) void widen_kernel(WidenArgs a) {
   const int nsc = a.Hkv * a.B;  // scales per block, [Hkv, B]
   for (int i = threadIdx.x; i < nsc; i += 256) {
     a.ks_out[stg * nsc + i] = a.k_scale[(size_t)pb * nsc + i];
-    a.vs_out[stg * nsc + i] = fminf(a.v_scale[(size_t)pb * nsc + i] * a.v_mul, kVScaleCap);
+    // A zero row (scale 0) adds nothing to the output whatever its scale:
+    // staged as 1 so that the weight it carries stays in the normaliser.
+    const float vsc = a.v_scale[(size_t)pb * nsc + i];
+    a.vs_out[stg * nsc + i] = vsc > 0.f ? fminf(vsc * a.v_mul, kVScaleCap) : 1.f;
   }
 }
 

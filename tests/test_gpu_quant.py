@@ -408,3 +408,67 @@ def test_quant_mixed_batch(lib, case):
                           block_size=B, num_kv_heads=Hkv, window=window, scale=w.scale, sinks=sinks)
     max_err(d.out.cpu().numpy(), out, str(case))
     assert np.abs(d.lse.cpu().numpy() - lse).max() <= TOL_LSE_PREFILL
+
+
+def test_quant_prefill_and_mixed_random_shapes(lib):
+    """Twelve seeded random shapes (format, query type, group size, head dim,
+    block size, prefix, chunk lengths incl. empty and single rows, window,
+    sinks), each through paged_attn_prefill_quant and paged_attn_mixed_quant,
+    against the oracle over the decoded pools."""
+    pkv, session = lib
+    rng = np.random.default_rng(2024)
+    for k in range(12):
+        fmt = str(rng.choice(["i8", "fp8"]))
+        dtype = str(rng.choice(["bf16", "f16"]))
+        G = int(rng.choice([1, 2, 4, 8]))
+        Hkv = int(rng.choice([1, 2, 4]))
+        D = int(rng.choice([64, 128]))
+        B = int(rng.choice([16, 32]))
+        prefix = B * int(rng.integers(0, 12))
+        chunks = [int(x) for x in rng.choice([0, 1, 1, 2, 17, 64, 150, 300], size=int(rng.integers(1, 6)))]
+        if sum(chunks) == 0:
+            chunks[0] = 5
+        window = int(rng.choice([0, 0, 1, 40, 200]))
+        sinks = int(rng.choice([0, 3])) if window else 0
+        case = (fmt, dtype, G * Hkv, Hkv, D, B, prefix, chunks, window, sinks)
+        note(f"random quant prefill/mixed {k}: {case}")
+        w = wl.make_prefill(prefix_len=prefix, chunk_lens=chunks, num_heads=G * Hkv, num_kv_heads=Hkv, head_dim=D,
+                            block_size=B, dtype=dtype, seed=300 + k, window=window, sinks=sinks, spare_blocks=2)
+        d = session.DeviceWorkload(w, kv_format=fmt)
+        d.write_step()
+        kp, vp = ref.build_pools(w)
+        kc, vc, ks, vs = oq.quantize_pools(kp, vp, dtype, fmt)
+        want, want_lse = oq.prefill(w.q, w.q_start, kc, vc, ks, vs, w.block_tables, w.context_lens, fmt=fmt,
+                                    q_dtype=dtype, block_size=B, num_kv_heads=Hkv, window=window, scale=w.scale,
+                                    sinks=sinks)
+        for name, fn in (("prefill", pkv.paged_attn_prefill_quant), ("mixed", pkv.paged_attn_mixed_quant)):
+            d.out.fill_(float("nan"))
+            d.lse.fill_(float("nan"))
+            fn(d.out, d.q, d.q_start, d.k_pool, d.v_pool, d.k_scale, d.v_scale, d.tables, d.lens, w.max_q_len,
+               w.max_context_len, window=window, scale=w.scale, lse=d.lse, sinks=sinks)
+            torch.cuda.synchronize()
+            max_err(d.out.cpu().numpy(), want, f"{name} {k}")
+            assert np.abs(d.lse.cpu().numpy() - want_lse).max() <= TOL_LSE_PREFILL
+
+
+@pytest.mark.parametrize("fmt", ["i8", "fp8"])
+def test_quant_prefill_single_key_rows_exact(lib, fmt):
+    """With a window of 1 each row attends only its own position, so its
+    output is that position's decoded V row. The normaliser sums exactly the
+    weights the matrix cores multiply, so the row comes out to fp32 rounding
+    (not the 2^-11 of an fp16-rounded weight x V scale), zero rows too."""
+    pkv, session = lib
+    note(f"quant prefill window 1 {fmt}")
+    w = wl.make_prefill(prefix_len=32, chunk_lens=[100, 37], num_heads=8, num_kv_heads=2, head_dim=128,
+                        block_size=16, dtype="bf16", seed=61, window=1)
+    w.seq_kv[0].v[5] = 0  # an all-zero V row (scale 0)
+    d = run(session, w, fmt)
+    kp, vp = ref.build_pools(w)
+    kc, vc, ks, vs = oq.quantize_pools(kp, vp, "bf16", fmt)
+    out, lse = oq.prefill(w.q, w.q_start, kc, vc, ks, vs, w.block_tables, w.context_lens, fmt=fmt,
+                          q_dtype="bf16", block_size=16, num_kv_heads=2, window=1, scale=w.scale)
+    got = d.out.cpu().numpy()
+    err = float(np.abs(got - out).max())
+    note(f"window 1 {fmt}: max abs err {err:.3g}")
+    assert err <= 1e-5 * max(1.0, float(np.abs(out).max()))
+    assert np.abs(d.lse.cpu().numpy() - lse).max() <= TOL_LSE_PREFILL
