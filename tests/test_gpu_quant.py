@@ -472,3 +472,32 @@ def test_quant_prefill_single_key_rows_exact(lib, fmt):
     note(f"window 1 {fmt}: max abs err {err:.3g}")
     assert err <= 1e-5 * max(1.0, float(np.abs(out).max()))
     assert np.abs(d.lse.cpu().numpy() - lse).max() <= TOL_LSE_PREFILL
+
+
+def test_quant_prefill_and_mixed_debug_mode(lib):
+    """debug=True checks the device-resident indices on the host first: a
+    valid call matches the same call without it bit for bit; an unmapped
+    attended block raises InvalidContent before anything is enqueued (output
+    untouched)."""
+    pkv, session = lib
+    note("quant prefill/mixed debug mode")
+    w = wl.make_prefill(prefix_len=32, chunk_lens=[40, 1, 9], num_heads=8, num_kv_heads=2, head_dim=64,
+                        block_size=16, dtype="bf16", seed=71)
+    d = run(session, w, "i8")
+    for name, fn in (("prefill", pkv.paged_attn_prefill_quant), ("mixed", pkv.paged_attn_mixed_quant)):
+        plain = torch.empty_like(d.out)
+        fn(plain, d.q, d.q_start, d.k_pool, d.v_pool, d.k_scale, d.v_scale, d.tables, d.lens, w.max_q_len,
+           w.max_context_len, scale=w.scale)
+        out = torch.empty_like(d.out)
+        fn(out, d.q, d.q_start, d.k_pool, d.v_pool, d.k_scale, d.v_scale, d.tables, d.lens, w.max_q_len,
+           w.max_context_len, scale=w.scale, debug=True)
+        torch.cuda.synchronize()
+        assert torch.equal(out, plain), name
+        bad = d.tables.clone()
+        bad[2, 0] = -1  # a prefix block sequence 2 attends
+        out.fill_(7.0)
+        with pytest.raises(pkv.InvalidContent, match="sequence 2, logical block 0"):
+            fn(out, d.q, d.q_start, d.k_pool, d.v_pool, d.k_scale, d.v_scale, bad, d.lens, w.max_q_len,
+               w.max_context_len, scale=w.scale, debug=True)
+        torch.cuda.synchronize()
+        assert bool((out == 7.0).all()), name
