@@ -208,26 +208,6 @@ int paged_attn_prefill(const pkv_geometry_t* geom, float* out, float* lse, const
                        int32_t max_context_len, int32_t window, int32_t num_sinks, float scale,
                        void* stream);
 
-/* paged_attn_decode_write - one decode step in one launch: writes each
- * sequence's newest token (position context_lens[s] - 1, "Build a Paged KV
- * Cache in Pure Python", Step 3 slot rule) and attends, exactly as
- * paged_kv_write of those tokens followed by paged_attn_decode. The
- * wavefront that reads the newest position takes its row from k_new /
- * v_new and stores it into the pools; no other wavefront reads that row.
- *
- *   k_new, v_new  [num_seqs, Hkv, D] kv_dtype: row s is written at
- *                 (block_tables[s][(L-1) / B], (L-1) % B) when L =
- *                 context_lens[s] >= 1 (rows of empty sequences are ignored)
- *   k_pool, v_pool written in place (only those rows)
- *   all other arguments as paged_attn_decode.
- * 16-bit and fp32 pools with num_heads / num_kv_heads <= 4 (else
- * PKV_EUNSUPPORTED: call paged_kv_write, then paged_attn_decode). */
-int paged_attn_decode_write(const pkv_geometry_t* geom, float* out, float* lse, const void* q, const void* k_new,
-                            const void* v_new, void* k_pool, void* v_pool, const int32_t* block_tables,
-                            int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
-                            int32_t max_context_len, int32_t window, int32_t num_sinks, float scale,
-                            int32_t num_workers, void* workspace, size_t workspace_bytes, void* stream);
-
 /* 8-bit key/value pages.
  *
  * "Build a Memory-Compressed Attention Engine with KV Caching from

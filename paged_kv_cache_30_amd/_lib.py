@@ -39,7 +39,7 @@ _QUANT = (torch.int8, torch.float8_e4m3fn)
 EXPORTS = ("paged_kv_write", "paged_attn_decode_workspace_bytes", "paged_attn_decode_workers",
            "paged_attn_decode", "paged_attn_prefill", "paged_kv_write_quant", "paged_attn_decode_quant",
            "paged_attn_prefill_quant_workspace_bytes", "paged_attn_prefill_quant", "paged_kv_copy_blocks",
-           "paged_attn_mixed_quant_workspace_bytes", "paged_attn_mixed_quant", "paged_attn_decode_write", "paged_attn_mixed", "paged_kv_compress", "paged_attn_decode_compressed",
+           "paged_attn_mixed_quant_workspace_bytes", "paged_attn_mixed_quant", "paged_attn_mixed", "paged_kv_compress", "paged_attn_decode_compressed",
            "pkv_status_string", "pkv_last_hip_error", "pkv_version")
 
 
@@ -88,8 +88,6 @@ def _load() -> ctypes.CDLL:
     lib.paged_attn_mixed_quant.argtypes = [G, P, P, P, I32, P, P, P, P, P, P, I32, P, I32, I32, I32, I32, I32, F,
                                            I32, P, SZ, P]
     lib.paged_attn_mixed_quant.restype = ctypes.c_int
-    lib.paged_attn_decode_write.argtypes = [G, P, P, P, P, P, P, P, P, I32, P, I32, I32, I32, I32, F, I32, P, SZ, P]
-    lib.paged_attn_decode_write.restype = ctypes.c_int
     lib.paged_kv_copy_blocks.argtypes = [G, P, P, P, P, P, P, I32, P]
     lib.paged_kv_copy_blocks.restype = ctypes.c_int
     lib.paged_attn_mixed.argtypes = [G, P, P, P, P, P, P, P, I32, P, I32, I32, I32, I32, I32, F, I32, P, SZ, P]
@@ -715,58 +713,3 @@ def paged_attn_mixed_quant(out, q, q_start, k_pool, v_pool, k_scale, v_scale, bl
     bind_mixed_quant(out, q, q_start, k_pool, v_pool, k_scale, v_scale, block_tables, context_lens, max_q_len,
                      max_context_len, window=window, scale=scale, num_workers=num_workers, workspace=workspace,
                      lse=lse, sinks=sinks, debug=debug)(stream)
-
-
-def bind_decode_write(out, q, k_new, v_new, k_pool, v_pool, block_tables, context_lens, max_context_len, *,
-                      window=0, scale, num_workers=0, workspace=None, lse=None, sinks=0, debug=None):
-    """Check and marshal the arguments of ``paged_attn_decode_write`` (write
-    each sequence's newest token, then decode, in one launch) once; returns a
-    callable ``f(stream=None)``."""
-    _dev(q, "q", dtype=k_pool.dtype, ndim=3)
-    _dev(out, "out", dtype=torch.float32, ndim=3)
-    _dev(k_pool, "k_pool", ndim=4)
-    _dev(v_pool, "v_pool", dtype=k_pool.dtype)
-    _dev(block_tables, "block_tables", dtype=torch.int32, ndim=2)
-    _dev(context_lens, "context_lens", dtype=torch.int32, ndim=1)
-    S, H, D = q.shape
-    _, _, Hkv, _ = k_pool.shape
-    for name, t in (("k_new", k_new), ("v_new", v_new)):
-        _dev(t, name, dtype=k_pool.dtype, ndim=3)
-        if tuple(t.shape) != (S, Hkv, D):
-            raise ValueError(f"{name} must be [num_seqs, num_kv_heads, head_dim]")
-    if out.shape != q.shape or context_lens.shape[0] != S or block_tables.shape[0] != S:
-        raise ValueError("shape mismatch between q, out, context_lens and block_tables")
-    if lse is not None:
-        _dev(lse, "lse", dtype=torch.float32, ndim=2)
-        if lse.shape != (S, H):
-            raise ValueError("lse must be [S, H]")
-    ws_bytes = 0
-    if workspace is not None:
-        _dev(workspace, "workspace")
-        ws_bytes = workspace.numel() * workspace.element_size()
-    g = geometry(k_pool, H)
-    args = (ctypes.byref(g), _ptr(out), _ptr(lse), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool),
-            _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), S, int(max_context_len), int(window),
-            int(sinks), float(scale), int(num_workers), _ptr(workspace), ws_bytes)
-    keep = (g, out, q, k_new, v_new, k_pool, v_pool, block_tables, context_lens, workspace, lse)
-    dbg = _debug(debug)
-
-    def call(stream=None):
-        if dbg:
-            tables_h, lens_h = _host(block_tables, context_lens)
-            _val.check_decode(tables_h, lens_h, max_context_len=int(max_context_len), num_blocks=g.num_blocks,
-                              block_size=g.block_size, window=int(window), sinks=int(sinks),
-                              what="paged_attn_decode_write")
-        _check(LIB.paged_attn_decode_write(*args, _stream(stream)), "paged_attn_decode_write")
-    call.keep = keep
-    return call
-
-
-def paged_attn_decode_write(out, q, k_new, v_new, k_pool, v_pool, block_tables, context_lens, max_context_len, *,
-                            window=0, scale, num_workers=0, workspace=None, lse=None, stream=None, sinks=0,
-                            debug=None) -> None:
-    """C ``paged_attn_decode_write``: write row s of k_new/v_new at position
-    context_lens[s] - 1 and decode, in one launch."""
-    bind_decode_write(out, q, k_new, v_new, k_pool, v_pool, block_tables, context_lens, max_context_len,
-                      window=window, scale=scale, num_workers=num_workers, workspace=workspace, lse=lse,
-                      sinks=sinks, debug=debug)(stream)

@@ -159,7 +159,7 @@ int decode_common(const pkv_geometry_t* geom, float* out, float* lse, const void
                   const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
                   int32_t num_seqs, int32_t max_context_len, int32_t window, int32_t num_sinks, float scale,
                   int32_t num_workers, void* workspace, size_t workspace_bytes, void* stream,
-                  const SlotArgs& slots = SlotArgs(), const void* k_new = nullptr, const void* v_new = nullptr) {
+                  const SlotArgs& slots = SlotArgs()) {
   if (num_seqs < 0 || max_blocks_per_seq <= 0 || max_context_len < 0 || window < 0 || num_sinks < 0 ||
       num_workers < 0 || !isfinite(scale))
     return PKV_EINVAL;
@@ -185,8 +185,6 @@ int decode_common(const pkv_geometry_t* geom, float* out, float* lse, const void
                     sp.workers, scale, num_sinks, nullptr, slots.full_start, slots.slot_tables,
                     slots.num_slots, slots.max_slot_blocks};
   a.kv_shift = kv_shift;
-  a.k_new = k_new;
-  a.v_new = v_new;
   return hip_status(pkv::launch_decode(a, (hipStream_t)stream));
 }
 
@@ -205,20 +203,6 @@ int paged_attn_decode(const pkv_geometry_t* geom, float* out, float* lse, const 
   return decode_common(geom, out, lse, q, geom->kv_dtype, k_pool, v_pool, nullptr, nullptr, block_tables,
                        max_blocks_per_seq, context_lens, num_seqs, max_context_len, window, num_sinks, scale,
                        num_workers, workspace, workspace_bytes, stream);
-}
-
-int paged_attn_decode_write(const pkv_geometry_t* geom, float* out, float* lse, const void* q, const void* k_new,
-                            const void* v_new, void* k_pool, void* v_pool, const int32_t* block_tables,
-                            int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
-                            int32_t max_context_len, int32_t window, int32_t num_sinks, float scale,
-                            int32_t num_workers, void* workspace, size_t workspace_bytes, void* stream) {
-  int st = check_geometry(geom);
-  if (st) return st;
-  if (is_quant(geom->kv_dtype) || geom->num_heads / geom->num_kv_heads > 4) return PKV_EUNSUPPORTED;
-  if (num_seqs > 0 && (!k_new || !v_new)) return PKV_EINVAL;
-  return decode_common(geom, out, lse, q, geom->kv_dtype, k_pool, v_pool, nullptr, nullptr, block_tables,
-                       max_blocks_per_seq, context_lens, num_seqs, max_context_len, window, num_sinks, scale,
-                       num_workers, workspace, workspace_bytes, stream, SlotArgs(), k_new, v_new);
 }
 
 int paged_attn_decode_quant(const pkv_geometry_t* geom, float* out, float* lse, const void* q, int32_t q_dtype,

@@ -409,35 +409,6 @@ __global__ __launch_bounds__(kThreads, (DecodeShape<T, D, B, G>::MIN_WG)) void d
           vs[j] = a.v_scale[sidx + j * RPL];
         }
       }
-      if constexpr (!MQK && !QU) {
-        // Fused write (k_new set): the chunk that holds the sequence's
-        // newest position L - 1 takes that row from k_new / v_new and stores
-        // it into the pool. This wavefront is the only reader of the row.
-        if (a.k_new) {
-          const int t0c = at.block(b_first + bi) * B + sub * CHUNK;
-          const int tn = at.L - 1;
-          if (b_first + bi >= at.sb && tn >= t0c && tn < t0c + CHUNK) {  // uniform
-            const size_t nrow = ((size_t)s * Hkv_pool + gp) * D * EB + (size_t)c * 16;
-            const char* kn = (const char*)a.k_new + nrow;
-            const char* vn = (const char*)a.v_new + nrow;
-#pragma unroll
-            for (int j = 0; j < CSTEPS; ++j) {
-              const bool mine = t0c + j * RPL + r == tn;
-#pragma unroll
-              for (int pc = 0; pc < PC; ++pc) {
-                const size_t po = off + (size_t)j * RPL * row_stride + pc * PSTRIDE;
-                kr[j][pc] = load_stream(mine ? kn + pc * PSTRIDE : kbase + po);
-                vr[j][pc] = load_stream(mine ? vn + pc * PSTRIDE : vbase + po);
-                if (mine) {
-                  *reinterpret_cast<u32x4*>(const_cast<char*>(kbase) + po) = load16(kn + pc * PSTRIDE);
-                  *reinterpret_cast<u32x4*>(const_cast<char*>(vbase) + po) = load16(vn + pc * PSTRIDE);
-                }
-              }
-            }
-            return true;
-          }
-        }
-      }
       if constexpr (MQK) {  // k-step ks = j * PC + pc
 #pragma unroll
         for (int j = 0; j < CSTEPS; ++j)

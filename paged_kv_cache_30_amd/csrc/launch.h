@@ -89,11 +89,6 @@ struct DecodeArgs {
   // pools hold Hkv >> kv_shift heads): 8-bit pools with 8 query heads per kv
   // head run as two groups of 4 over each pool kv head.
   int32_t kv_shift = 0;
-  // Fused write (16-bit pools, up to 4 query heads per kv head): row s of
-  // k_new / v_new [S, Hkv, D] is sequence s's newest position L - 1; the
-  // split kernel reads it from there and stores it into the pools.
-  const void* k_new = nullptr;
-  const void* v_new = nullptr;
 };
 
 struct PrefillArgs {
