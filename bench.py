@@ -20,7 +20,15 @@ second.  ``roofline`` relates the attention call alone to MI355X's peak (HBM
 8 TB/s; dense bf16/fp16 MFMA 2.5 PFLOP/s).  ``cpu_baseline`` times the fp64
 oracle on the host on a bounded sample of the same workload.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 100] [--config 2]
+By default the line is the long-context GQA decode workload (64 sequences,
+32 query / 8 kv heads, head_dim 128, block_size 32, bf16, contexts
+log-uniform in [1024, 32768]), the largest that fits one GPU, with the
+chunked prefill over a shared prefix (8 sequences x 512-row chunks after a
+2048-position prefix, 32 / 8 heads, bf16) timed on the same GPU in the same
+run and reported under "prefill" (its own steps, roofline and oracle
+baseline).
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 100] [--config 3] [--prefill-config 5]
 """
 from __future__ import annotations
 
@@ -251,57 +259,13 @@ def summarize_pmc(args, fetch_dir, write_dir, copy_mib) -> int:
     return 0
 
 
-def main(argv=None) -> int:
-    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=100,
-                    help="untimed steps before the timed ones; 100 lets the clocks settle (the MFMA-bound prefill "
-                         "call is ~20 %% slower in its first milliseconds of load)")
-    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5, 6, 7],
-                    help="workload: 1 tiny fp32 decode, 2 batched MHA decode (default), 3 long GQA decode, "
-                         "4 sliding-window decode, 5 chunked prefill over a shared prefix, 6 decode over a "
-                         "compressed-slot tier (window 256, 16 slots), 7 long decode with 8 query heads per "
-                         "kv head")
-    ap.add_argument("--seed", type=int, default=None)
-    ap.add_argument("--workers", type=int, default=0, help="decode wavefront workers (0 = automatic)")
-    ap.add_argument("--kv", choices=["native", "i8", "fp8"], default="native",
-                    help="pools: the workload's dtype (default) or 8-bit INT8 / FP8 E4M3 codes with row "
-                         "scales, encoded from the workload's rows on write (decode and prefill workloads)")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--graph", action="store_true",
-                    help="replay the step's two calls as HIP graphs instead of calling the library per step")
-    ap.add_argument("--flush-mib", type=int, default=0,
-                    help="before every step, overwrite a buffer of this many MiB (evicts L2 and the 256 MiB "
-                         "MALL); ms_per_step then sums the per-step events, which exclude the flush")
-    ap.add_argument("--calibration-copy-mib", type=int, default=0,
-                    help="copy this many MiB once before the timed steps (scale for HBM byte counters)")
-    ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_MIB"),
-                    help="turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this command into "
-                         "profiles/traffic.json entries and exit")
-    args = ap.parse_args(argv)
-    if args.summarize_pmc:
-        return summarize_pmc(args, *args.summarize_pmc)
-
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the decode and prefill paths "
-              "shard by sequence or kv head with no exchange, which this build does not launch.",
-              file=sys.stderr)
-        return 2
-
+def run_leg(w, args, warmup: int, steps: int, settle_s: float = 0.0) -> dict:
+    """Stage workload w on the GPU, run `warmup` untimed steps (then more
+    until `settle_s` seconds of steps have run, if asked), time exactly
+    `steps` steps and return the leg's figures."""
     import torch
-    import workloads as wl
     from paged_kv_cache_30_amd import session
 
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        return 1
-    torch.cuda.set_device(0)
-    w = wl.config(args.config, args.seed)
-    if args.kv != "native" and w.kind not in ("decode", "prefill"):
-        print("8-bit pools (--kv) serve decode and prefill workloads", file=sys.stderr)
-        return 2
     d = session.DeviceWorkload(w, num_workers=args.workers, kv_format=args.kv)
     comp_bytes = 0
     if w.full_start is not None:
@@ -319,9 +283,17 @@ def main(argv=None) -> int:
         torch.cuda.synchronize()
         del src_t, dst_t
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         d.step()
     torch.cuda.synchronize()
+    n_settle = 0
+    if settle_s > 0:
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < settle_s:
+            for _ in range(50):
+                d.step()
+            n_settle += 50
+            torch.cuda.synchronize()
 
     # The step's two calls, replayed as HIP graphs (no host launch gaps) or
     # called eagerly.
@@ -344,7 +316,7 @@ def main(argv=None) -> int:
         torch.cuda.synchronize()
         do_write, do_attend = g_write.replay, g_attend.replay
 
-    K = args.steps
+    K = steps
     flush_buf = (torch.empty(args.flush_mib << 20, dtype=torch.uint8, device="cuda")
                  if args.flush_mib > 0 else None)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
@@ -383,9 +355,9 @@ def main(argv=None) -> int:
         key = f"paged_attn_decode|{w.name}" + ("" if args.kv == "native" else f"|{args.kv}")
         roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_for(key, src)}
-        n_part_info = {"decode_workers": d.num_workers or pkv_workers(d), "kv_pool": args.kv}
+        extra = {"decode_workers": d.num_workers or pkv_workers(d), "kv_pool": args.kv}
         if w.full_start is not None:
-            n_part_info.update(compressions_per_step=int(len(d.compress_ops[1])), tier_window=256, max_slots=16)
+            extra.update(compressions_per_step=int(len(d.compress_ops[1])), tier_window=256, max_slots=16)
     else:
         flop = prefill_flop(w)
         value = flop / (ms_step * 1e-3) / 1e12
@@ -396,34 +368,122 @@ def main(argv=None) -> int:
         peak = MFMA_PEAK_TFLOPS[w.dtype]
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4), "traffic": traffic_for(key, src)}
-        n_part_info = {"kv_pool": args.kv} if args.kv != "native" else {}
-
-    timing_mode = "hip_graph" if args.graph else "eager"
-    rec = {
-        "metric": METRIC,
-        "value": round(value, 3),
-        "unit": unit,
-        "n_gpus": 1,
-        "steps": K,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
+        extra = {"kv_pool": args.kv} if args.kv != "native" else {}
+    del d
+    return {
+        "value": round(value, 3), "unit": unit, "ms_per_step": round(ms_step, 5), "steps": K,
+        "warmup": warmup + n_settle,
         "dtype": w.dtype if args.kv == "native" else f"{args.kv}+{w.dtype}",
-        "data": "synthetic (seeded, shapes and distributions of the workload)",
         "config": {"workload": w.name, "kind": w.kind, "num_seqs": w.num_seqs, "num_heads": w.num_heads,
                    "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "block_size": w.block_size,
                    "window": w.window, "max_context_len": w.max_context_len,
-                   "total_context": int(w.context_lens.sum()), "seed": w.seed, **n_part_info},
+                   "total_context": int(w.context_lens.sum()), "seed": w.seed, **extra},
         "roofline": roof,
         "timing": {"attend_ms_mean": round(att_mean, 5), "attend_ms_median": round(att_med, 5),
-                   "attend_ms_min": round(attend_ms[0], 5), "write_ms_mean": round(sum(write_ms) / K, 5),  # with the compressions of the tier workload
-                   "wall_s_timed": round(wall, 4), "mode": timing_mode, "flush_mib": args.flush_mib,
-                   "source_hash": src},
+                   "attend_ms_min": round(attend_ms[0], 5), "write_ms_mean": round(sum(write_ms) / K, 5),
+                   "wall_s_timed": round(wall, 4), "mode": "hip_graph" if args.graph else "eager",
+                   "flush_mib": args.flush_mib, "source_hash": src},
     }
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=100,
+                    help="untimed steps before the timed ones")
+    ap.add_argument("--config", type=int, default=3, choices=[1, 2, 3, 4, 5, 6, 7],
+                    help="workload: 1 tiny fp32 decode, 2 batched MHA decode, 3 long GQA decode (default: the "
+                         "largest), 4 sliding-window decode, 5 chunked prefill over a shared prefix, 6 decode over "
+                         "a compressed-slot tier (window 256, 16 slots), 7 long decode with 8 query heads per "
+                         "kv head")
+    ap.add_argument("--prefill-config", type=int, default=5, choices=[0, 5],
+                    help="with a decode --config, also time this chunked-prefill workload on the same GPU and "
+                         "report it under \"prefill\" (0 = skip)")
+    ap.add_argument("--settle-s", type=float, default=0.5,
+                    help="seconds of back-to-back prefill steps run before the prefill leg's timed steps, after "
+                         "its warm-up steps (the MFMA-bound call runs ~20 %% slower until the clocks settle "
+                         "under load)")
+    ap.add_argument("--seed", type=int, default=None)
+    ap.add_argument("--workers", type=int, default=0, help="decode wavefront workers (0 = automatic)")
+    ap.add_argument("--kv", choices=["native", "i8", "fp8"], default="native",
+                    help="pools: the workload's dtype (default) or 8-bit INT8 / FP8 E4M3 codes with row "
+                         "scales, encoded from the workload's rows on write (decode and prefill workloads)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay the step's two calls as HIP graphs instead of calling the library per step")
+    ap.add_argument("--flush-mib", type=int, default=0,
+                    help="before every step, overwrite a buffer of this many MiB (evicts L2 and the 256 MiB "
+                         "MALL); ms_per_step then sums the per-step events, which exclude the flush")
+    ap.add_argument("--calibration-copy-mib", type=int, default=0,
+                    help="copy this many MiB once before the timed steps (scale for HBM byte counters)")
+    ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_MIB"),
+                    help="turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this command into "
+                         "profiles/traffic.json entries and exit")
+    args = ap.parse_args(argv)
+    if args.summarize_pmc:
+        return summarize_pmc(args, *args.summarize_pmc)
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the decode and prefill paths "
+              "shard by sequence or kv head with no exchange, which this build does not launch.",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    import workloads as wl
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    torch.cuda.set_device(0)
+    w = wl.config(args.config, args.seed)
+    if args.kv != "native" and w.kind not in ("decode", "prefill"):
+        print("8-bit pools (--kv) serve decode and prefill workloads", file=sys.stderr)
+        return 2
+    settle = args.settle_s if w.kind == "prefill" else 0.0
+    leg = run_leg(w, args, args.warmup, args.steps, settle)
+    print(f"leg {w.name}: {leg['value']} {leg['unit']} per step, call frac {leg['roofline']['frac']}",
+          file=sys.stderr, flush=True)
+    pw = None
+    pleg = None
+    if w.kind == "decode" and args.prefill_config:
+        pw = wl.config(args.prefill_config, None)
+        pleg = run_leg(pw, args, args.warmup, args.steps, args.settle_s)
+        print(f"leg {pw.name}: {pleg['value']} {pleg['unit']} per step, call frac {pleg['roofline']['frac']}",
+              file=sys.stderr, flush=True)
+        torch.cuda.empty_cache()
+
+    rec = {
+        "metric": METRIC,
+        "value": leg["value"],
+        "unit": leg["unit"],
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": leg["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": leg["dtype"],
+        "data": "synthetic (seeded, shapes and distributions of the workload)",
+        "config": leg["config"],
+        "roofline": leg["roofline"],
+        "timing": leg["timing"],
+    }
+    if leg["warmup"] != args.warmup:
+        rec["timing"]["settle_steps"] = leg["warmup"] - args.warmup
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    if pleg is not None:
+        prec = {k: pleg[k] for k in ("value", "unit", "ms_per_step", "steps", "dtype", "config", "roofline",
+                                      "timing")}
+        prec["warmup"] = args.warmup
+        prec["timing"]["settle_steps"] = pleg["warmup"] - args.warmup
+        if not args.no_cpu_baseline:
+            prec["cpu_baseline"] = cpu_baseline(pw, args.cpu_seconds)
+        rec["prefill"] = prec
     print(json.dumps(rec), flush=True)
     return 0
 

@@ -286,10 +286,18 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_kernel(PrefillArgs a,
   static_assert(B % RPI == 0, "a wavefront instruction must not straddle blocks");
   int pb_ins[NLD];  // table entry of instruction j of this wavefront, next tile
   int pb_key = -1;  // wavefront 0: table entry of key t0 + lane, next tile
+  // The entries are loaded as lane values (through an index offset the
+  // compiler cannot see is zero): a uniform load would be moved to a scalar
+  // register right away, which waits for it, and vector memory operations
+  // complete in order, so that wait would also wait for every direct load
+  // issued before it. As lane values they are first used one step later,
+  // after the end-of-tile wait has completed them anyway.
+  int lane_zero;
+  asm volatile("v_mov_b32 %0, 0" : "=v"(lane_zero));
   auto fetch_table = [&](int t0) {
 #pragma unroll
     for (int j = 0; j < NLD; ++j)  // in range of the table row even past the context
-      pb_ins[j] = trow[min((t0 + (NW * j + wave) * RPI) / B, a.mb - 1)];
+      pb_ins[j] = trow[min((t0 + (NW * j + wave) * RPI) / B, a.mb - 1) + lane_zero];
     if (wave == 0) pb_key = trow[min((t0 + lane) / B, a.mb - 1)];
   };
   // Per-lane byte offsets inside a block of load j (tiles start at multiples
