@@ -304,9 +304,26 @@ def bind_prefill(out, q, q_start, k_pool, v_pool, block_tables, context_lens, ma
             _val.check_prefill(*_host(q_start, block_tables, context_lens), num_rows=T, max_q_len=int(max_q_len),
                                max_context_len=int(max_context_len), num_blocks=g.num_blocks,
                                block_size=g.block_size, window=int(window), sinks=int(sinks))
+            _debug_v_range(v_pool, q_start, block_tables, context_lens, window=window, sinks=sinks, min_rows=1,
+                           what="paged_attn_prefill")
         _check(LIB.paged_attn_prefill(*args, _stream(stream)), "paged_attn_prefill")
     call.keep = keep
     return call
+
+
+def _debug_v_range(v_pool, q_start, block_tables, context_lens, *, window, sinks, min_rows, what):
+    """Debug mode, bf16 pools: the attended V rows of the chunks the prefill
+    kernel computes lie within the range it converts to fp16 exactly."""
+    if v_pool.dtype != torch.bfloat16:
+        return
+    qs, tb, ln = _host(q_start, block_tables, context_lens)
+    blk, slot, seq = _val.prefill_v_rows(qs, tb, ln, block_size=v_pool.shape[1], window=int(window),
+                                         sinks=int(sinks), min_rows=min_rows)
+    if blk.size == 0:
+        return
+    rows = v_pool[torch.from_numpy(blk).to(v_pool.device), torch.from_numpy(slot).to(v_pool.device)]
+    amax = rows.float().abs().amax(dim=(1, 2)).cpu().numpy()
+    _val.check_prefill_v_range(amax, seq, _val.PREFILL_BF16_V_LIMIT, what)
 
 
 def paged_attn_prefill(out, q, q_start, k_pool, v_pool, block_tables, context_lens, max_q_len,
@@ -546,6 +563,8 @@ def bind_mixed(out, q, q_start, k_pool, v_pool, block_tables, context_lens, max_
                                max_context_len=int(max_context_len), num_blocks=g.num_blocks,
                                block_size=g.block_size, window=int(window), sinks=int(sinks),
                                what="paged_attn_mixed")
+            _debug_v_range(v_pool, q_start, block_tables, context_lens, window=window, sinks=sinks, min_rows=2,
+                           what="paged_attn_mixed")
         _check(LIB.paged_attn_mixed(*args, _stream(stream)), "paged_attn_mixed")
     call.keep = keep
     return call

@@ -113,15 +113,22 @@ class BlockAllocator:
                 self._release(b)
         self.lengths.pop(seq_id, None)
 
-    def trim_window(self, seq_id: int, context_len: int, window: int) -> int:
-        """Free the blocks that hold no position of [L - window, L): entry b
-        goes when (b + 1) * B <= L - window.  Returns how many were freed."""
+    def trim_window(self, seq_id: int, context_len: int, window: int, sinks: int = 0,
+                    chunk_len: int = 1) -> int:
+        """Free the blocks that hold no position the next attention call can
+        read: its query rows are the last ``chunk_len`` positions of
+        ``context_len`` (1 for decode), so the earliest attended position is
+        lo = L - chunk_len - window + 1, and with attention sinks positions
+        [0, sinks) stay attended too.  Entry b goes when (b + 1) * B <= lo and
+        b * B >= sinks.  Returns how many blocks were freed."""
         if window <= 0:
             return 0
-        cut = (int(context_len) - int(window)) // self.block_size
+        lo = int(context_len) - max(int(chunk_len), 1) - int(window) + 1
+        cut = lo // self.block_size
+        keep_below = -(-max(int(sinks), 0) // self.block_size)  # blocks holding sink positions
         row = self.tables.get(seq_id, [])
         freed = 0
-        for b in range(min(max(cut, 0), len(row))):
+        for b in range(keep_below, min(max(cut, 0), len(row))):
             if row[b] != UNMAPPED:
                 self._release(row[b])
                 row[b] = UNMAPPED

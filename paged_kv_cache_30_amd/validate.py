@@ -137,6 +137,51 @@ def check_prefill(q_start, tables, lens, *, num_rows: int, max_q_len: int, max_c
         _check_mapped(tables, s, _blocks_needed(lo, L, sinks, window, block_size), num_blocks, what)
 
 
+# Largest magnitude a bf16 value keeps when the prefill converts V to fp16
+# for the matrix cores: bf16 values at or below 65280 are fp16 values; the
+# next bf16 value, 65536, is beyond fp16's range (its largest value is 65504).
+PREFILL_BF16_V_LIMIT = 65280.0
+
+
+def prefill_v_rows(q_start, tables, lens, *, block_size: int, window: int = 0, sinks: int = 0,
+                   min_rows: int = 1):
+    """(physical block, slot) of every cached row a chunk of at least
+    ``min_rows`` query rows attends: positions [lo, L) with lo the first
+    row's window start (0 without a window), plus the sink positions.
+    Returns two int64 arrays and the sequence each row belongs to."""
+    q_start = np.asarray(q_start, np.int64)
+    tables = np.asarray(tables, np.int64)
+    lens = np.asarray(lens, np.int64)
+    blk, slot, seq = [], [], []
+    for s in range(lens.shape[0]):
+        c, L = int(q_start[s + 1] - q_start[s]), int(lens[s])
+        if c < min_rows or c == 0 or c > L:
+            continue
+        lo = max(0, L - c - window + 1) if window > 0 else 0
+        pos = np.arange(lo, L)
+        if window > 0 and sinks > 0:
+            pos = np.union1d(np.arange(0, min(sinks, L)), pos)
+        blk.append(tables[s, pos // block_size])
+        slot.append(pos % block_size)
+        seq.append(np.full(pos.shape, s))
+    if not blk:
+        z = np.zeros(0, np.int64)
+        return z, z, z
+    return np.concatenate(blk), np.concatenate(slot), np.concatenate(seq)
+
+
+def check_prefill_v_range(row_absmax, seq, limit: float, what="paged_attn_prefill") -> None:
+    """Every attended V row's largest magnitude within the prefill's limit
+    (``row_absmax`` and ``seq`` as given by ``prefill_v_rows``)."""
+    row_absmax = np.asarray(row_absmax, np.float64)
+    bad = ~(row_absmax <= limit)
+    if bad.any():
+        i = int(np.flatnonzero(bad)[0])
+        raise InvalidContent(f"{what}: sequence {int(seq[i])} attends a V row of largest magnitude "
+                             f"{row_absmax[i]:.7g}, beyond the {limit:.7g} that bf16 prefill converts to fp16 "
+                             "exactly")
+
+
 def check_copy_blocks(src, dst, *, num_blocks: int, what="paged_kv_copy_blocks") -> None:
     """Ids in the pool, src != dst, destinations distinct and never a source
     of the same call."""

@@ -250,3 +250,35 @@ def test_compressed_tier_arrays_pass():
         V.check_decode_compressed(tables, L, fs, st, ns, max_context_len=int(max(L)), num_blocks=200,
                                   block_size=B, window=0)
     assert tier.num_slots(0) == M and tier.num_slots(1) == M
+
+
+def test_prefill_v_rows_and_range():
+    """The rows a prefill chunk attends: [first row's window start, L) plus
+    sinks, through the table; single rows skipped when min_rows is 2. The
+    range check names the sequence of the first row beyond the limit."""
+    B = 4
+    tables = np.array([[7, 3, 9, -1], [5, 6, 1, 2]], np.int64)
+    lens = np.array([10, 13], np.int64)
+    q_start = np.array([0, 3, 4], np.int64)  # chunk of 3 rows, then a single row
+    blk, slot, seq = V.prefill_v_rows(q_start, tables, lens, block_size=B)
+    pos0 = np.arange(0, 10)
+    pos1 = np.arange(0, 13)
+    assert np.array_equal(blk, np.r_[tables[0, pos0 // B], tables[1, pos1 // B]])
+    assert np.array_equal(slot, np.r_[pos0 % B, pos1 % B])
+    assert np.array_equal(seq, np.r_[np.zeros(10), np.ones(13)])
+    blk, slot, seq = V.prefill_v_rows(q_start, tables, lens, block_size=B, min_rows=2)
+    assert set(seq.tolist()) == {0}
+    # window 4: the chunk's first row sits at 7 and sees [4, 8); sinks add [0, 2)
+    blk, slot, seq = V.prefill_v_rows(q_start, tables, lens, block_size=B, window=4, sinks=2, min_rows=2)
+    pos = np.r_[0, 1, 4:10]
+    assert np.array_equal(blk, tables[0, pos // B]) and np.array_equal(slot, pos % B)
+    V.check_prefill_v_range(np.array([1.0, 65280.0]), np.array([0, 1]), V.PREFILL_BF16_V_LIMIT)
+    with pytest.raises(V.InvalidContent, match="sequence 1"):
+        V.check_prefill_v_range(np.array([1.0, 65536.0]), np.array([0, 1]), V.PREFILL_BF16_V_LIMIT)
+    with pytest.raises(V.InvalidContent, match="sequence 0"):
+        V.check_prefill_v_range(np.array([np.inf]), np.array([0]), V.PREFILL_BF16_V_LIMIT)
+    # the limit is the largest bf16 value that fp16 represents: 65280 is both,
+    # the next bf16 value 65536 is not an fp16 value
+    assert np.float16(V.PREFILL_BF16_V_LIMIT) == V.PREFILL_BF16_V_LIMIT
+    assert wl.f32_to_bf16_bits(np.float32(V.PREFILL_BF16_V_LIMIT)) + 1 == wl.f32_to_bf16_bits(np.float32(65536.0))
+    assert not np.isfinite(np.float16(65536.0))
