@@ -27,8 +27,10 @@
  * Conventions shared by every entry point
  *  - Every pointer argument except `geom` and `stream` is DEVICE memory
  *    (allocated by the caller, e.g. through torch); `geom` is host memory.
- *    The library never allocates, frees or keeps device memory and keeps no
- *    state between calls.
+ *    The library never allocates or frees device memory and keeps no state
+ *    between calls; its one piece of device memory is the fixed 32 MiB
+ *    scratch array of paged_attn_decode_noalloc (one per GPU, part of the
+ *    loaded code object).
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream). All
  *    work is enqueued on it; nothing synchronises. Results are valid once
  *    the stream reaches them.
@@ -66,7 +68,8 @@ enum {
   PKV_EINVAL = -1,        /* bad argument (null pointer, negative size, ...) */
   PKV_EUNSUPPORTED = -2,  /* valid but not built: head_dim, block_size, dtype, group size */
   PKV_EWORKSPACE = -3,    /* workspace missing or smaller than the query says */
-  PKV_EHIP = -4           /* a HIP launch failed; pkv_last_hip_error() has the code */
+  PKV_EHIP = -4,          /* a HIP launch failed; pkv_last_hip_error() has the code */
+  PKV_ESCRATCH = -5       /* paged_attn_decode_noalloc: the call needs more than its fixed scratch */
 };
 
 /* Cache geometry (host struct).
@@ -172,6 +175,25 @@ int paged_attn_decode(const pkv_geometry_t* geom, float* out, float* lse, const 
                       const int32_t* context_lens, int32_t num_seqs, int32_t max_context_len,
                       int32_t window, int32_t num_sinks, float scale, int32_t num_workers,
                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* paged_attn_decode_noalloc - paged_attn_decode without a workspace
+ * argument, for callers that cannot allocate device memory around the call
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc). The call allocates nothing: its workspace is a fixed 32 MiB
+ * device array inside the library, one per GPU, held until the process ends.
+ *
+ * Arguments, results and the worker count as paged_attn_decode. A call
+ * whose workspace (paged_attn_decode_workspace_bytes with the same sizes)
+ * exceeds 32 MiB returns PKV_ESCRATCH before anything is enqueued. Every
+ * call on one GPU uses that GPU's single scratch array: two calls that can
+ * run at the same time on one GPU (different streams, or different host
+ * threads) race and give wrong results; calls in one stream's order are
+ * safe. Nothing in the scratch needs clearing between calls. */
+int paged_attn_decode_noalloc(const pkv_geometry_t* geom, float* out, float* lse, const void* q,
+                              const void* k_pool, const void* v_pool, const int32_t* block_tables,
+                              int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
+                              int32_t max_context_len, int32_t window, int32_t num_sinks, float scale,
+                              int32_t num_workers, void* stream);
 
 /* paged_attn_prefill - causal attention of a chunk of query tokens per
  * sequence over everything cached before them and the chunk itself.

@@ -24,7 +24,7 @@ from .validate import InvalidContent  # noqa: F401
 from ._lib import (  # noqa: F401
     LIB, LIB_PATH, EXPORTS, PagedAttnError, Geometry, geometry,
     PKV_F32, PKV_F16, PKV_BF16, PKV_I8, PKV_FP8, PKV_OK, PKV_EINVAL, PKV_EUNSUPPORTED, PKV_EWORKSPACE, PKV_EHIP,
-    paged_kv_write, paged_attn_decode, paged_attn_prefill,
+    PKV_ESCRATCH, paged_kv_write, paged_attn_decode, paged_attn_decode_noalloc, paged_attn_prefill,
     paged_attn_decode_workspace_bytes, paged_attn_decode_workers, decode_workspace,
     paged_kv_write_quant, paged_attn_decode_quant, bind_kv_write_quant, bind_decode_quant,
     paged_attn_prefill_quant, paged_attn_prefill_quant_workspace_bytes, prefill_quant_workspace,

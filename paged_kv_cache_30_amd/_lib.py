@@ -27,7 +27,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("PKV_LIBRARY", os.path.join(_HERE, "libpagedattn.so"))
 
 PKV_F32, PKV_F16, PKV_BF16, PKV_I8, PKV_FP8 = 0, 1, 2, 3, 4
-PKV_OK, PKV_EINVAL, PKV_EUNSUPPORTED, PKV_EWORKSPACE, PKV_EHIP = 0, -1, -2, -3, -4
+PKV_OK, PKV_EINVAL, PKV_EUNSUPPORTED, PKV_EWORKSPACE, PKV_EHIP, PKV_ESCRATCH = 0, -1, -2, -3, -4, -5
 
 # 8-bit pools are torch.int8 (INT8 codes) or torch.float8_e4m3fn (FP8 E4M3
 # codes); their row scales are separate float32 tensors.
@@ -39,7 +39,8 @@ _QUANT = (torch.int8, torch.float8_e4m3fn)
 EXPORTS = ("paged_kv_write", "paged_attn_decode_workspace_bytes", "paged_attn_decode_workers",
            "paged_attn_decode", "paged_attn_prefill", "paged_kv_write_quant", "paged_attn_decode_quant",
            "paged_attn_prefill_quant_workspace_bytes", "paged_attn_prefill_quant", "paged_kv_copy_blocks",
-           "paged_attn_mixed_quant_workspace_bytes", "paged_attn_mixed_quant", "paged_attn_mixed", "paged_kv_compress", "paged_attn_decode_compressed",
+           "paged_attn_mixed_quant_workspace_bytes", "paged_attn_mixed_quant", "paged_attn_mixed", "paged_kv_compress",
+           "paged_attn_decode_compressed", "paged_attn_decode_noalloc",
            "pkv_status_string", "pkv_last_hip_error", "pkv_version")
 
 
@@ -71,6 +72,8 @@ def _load() -> ctypes.CDLL:
     lib.paged_attn_decode_workers.restype = I32
     lib.paged_attn_decode.argtypes = [G, P, P, P, P, P, P, I32, P, I32, I32, I32, I32, F, I32, P, SZ, P]
     lib.paged_attn_decode.restype = ctypes.c_int
+    lib.paged_attn_decode_noalloc.argtypes = [G, P, P, P, P, P, P, I32, P, I32, I32, I32, I32, F, I32, P]
+    lib.paged_attn_decode_noalloc.restype = ctypes.c_int
     lib.paged_attn_prefill.argtypes = [G, P, P, P, P, P, P, P, I32, P, I32, I32, I32, I32, I32, F, P]
     lib.paged_attn_prefill.restype = ctypes.c_int
     lib.paged_kv_write_quant.argtypes = [G, P, P, P, P, P, P, I32, P, P, I32, P, I32, I32, P]
@@ -269,6 +272,36 @@ def paged_attn_decode(out, q, k_pool, v_pool, block_tables, context_lens, max_co
     bind_decode(out, q, k_pool, v_pool, block_tables, context_lens, max_context_len, window=window,
                 scale=scale, num_workers=num_workers, workspace=workspace, lse=lse, sinks=sinks,
                 debug=debug)(stream)
+
+
+def paged_attn_decode_noalloc(out, q, k_pool, v_pool, block_tables, context_lens, max_context_len, *,
+                              window=0, scale, lse=None, num_workers=0, stream=None, sinks=0, debug=None) -> None:
+    """C ``paged_attn_decode_noalloc``: ``paged_attn_decode`` with the library's
+    fixed per-GPU scratch as its workspace (no allocation in the call; calls
+    that can overlap on one GPU race)."""
+    _dev(q, "q", dtype=k_pool.dtype, ndim=3)
+    _dev(out, "out", dtype=torch.float32, ndim=3)
+    _dev(k_pool, "k_pool", ndim=4)
+    _dev(v_pool, "v_pool", dtype=k_pool.dtype)
+    _dev(block_tables, "block_tables", dtype=torch.int32, ndim=2)
+    _dev(context_lens, "context_lens", dtype=torch.int32, ndim=1)
+    S, H, D = q.shape
+    if out.shape != q.shape or context_lens.shape[0] != S or block_tables.shape[0] != S:
+        raise ValueError("shape mismatch between q, out, context_lens and block_tables")
+    if lse is not None:
+        _dev(lse, "lse", dtype=torch.float32, ndim=2)
+        if lse.shape != (S, H):
+            raise ValueError("lse must be [S, H]")
+    g = geometry(k_pool, H)
+    if _debug(debug):
+        _val.check_decode(*_host(block_tables, context_lens), max_context_len=int(max_context_len),
+                          num_blocks=g.num_blocks, block_size=g.block_size, window=int(window), sinks=int(sinks),
+                          what="paged_attn_decode_noalloc")
+    _check(LIB.paged_attn_decode_noalloc(ctypes.byref(g), _ptr(out), _ptr(lse), _ptr(q), _ptr(k_pool), _ptr(v_pool),
+                                         _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), S,
+                                         int(max_context_len), int(window), int(sinks), float(scale),
+                                         int(num_workers), _stream(stream)),
+           "paged_attn_decode_noalloc")
 
 
 def bind_prefill(out, q, q_start, k_pool, v_pool, block_tables, context_lens, max_q_len, max_context_len, *,

@@ -5,6 +5,9 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "launch.h"
 
 namespace {
@@ -203,6 +206,75 @@ int paged_attn_decode(const pkv_geometry_t* geom, float* out, float* lse, const 
   return decode_common(geom, out, lse, q, geom->kv_dtype, k_pool, v_pool, nullptr, nullptr, block_tables,
                        max_blocks_per_seq, context_lens, num_seqs, max_context_len, window, num_sinks, scale,
                        num_workers, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Scratch of paged_attn_decode_noalloc: the decode workspace (attended-block
+// prefix sums and the split's partial results) in a fixed device array, so
+// that the call allocates nothing. Every GPU the library runs on holds its
+// own copy for the life of the process. In host code the array's name is
+// not a device address: kernels get the address hipGetSymbolAddress gives
+// for the current device, looked up once per device.
+constexpr size_t kScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 256;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of this device's scratch (nullptr and the HIP error on failure).
+void* scratch_for_current_device(hipError_t* err) {
+  int dev = 0;
+  *err = hipGetDevice(&dev);
+  if (*err != hipSuccess) return nullptr;
+  if (dev < 0 || dev >= kMaxDevices) {
+    *err = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+  if (!p) {
+    *err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (*err != hipSuccess || !p) {
+      if (*err == hipSuccess) *err = hipErrorInvalidSymbol;
+      return nullptr;
+    }
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+int paged_attn_decode_noalloc(const pkv_geometry_t* geom, float* out, float* lse, const void* q,
+                              const void* k_pool, const void* v_pool, const int32_t* block_tables,
+                              int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
+                              int32_t max_context_len, int32_t window, int32_t num_sinks, float scale,
+                              int32_t num_workers, void* stream) {
+  int st = check_geometry(geom);
+  if (st) return st;
+  if (is_quant(geom->kv_dtype)) return PKV_EUNSUPPORTED;
+  if (num_seqs < 0 || max_context_len < 0 || window < 0 || num_sinks < 0 || num_workers < 0) return PKV_EINVAL;
+  if (num_seqs == 0) return PKV_OK;
+  const size_t need = paged_attn_decode_workspace_bytes(geom, num_seqs, max_context_len, window, num_sinks,
+                                                        num_workers);
+  if (need == 0) return PKV_EINVAL;
+  if (need > kScratchBytes) return PKV_ESCRATCH;
+  hipError_t err;
+  void* ws = scratch_for_current_device(&err);
+  if (!ws) return hip_status(err);
+  // Nothing in the workspace has to start at zero: every word the kernels
+  // read is written earlier in the same call.
+  return decode_common(geom, out, lse, q, geom->kv_dtype, k_pool, v_pool, nullptr, nullptr, block_tables,
+                       max_blocks_per_seq, context_lens, num_seqs, max_context_len, window, num_sinks, scale,
+                       num_workers, ws, kScratchBytes, stream);
 }
 
 int paged_attn_decode_quant(const pkv_geometry_t* geom, float* out, float* lse, const void* q, int32_t q_dtype,
@@ -531,6 +603,9 @@ const char* pkv_status_string(int status) {
     case PKV_EUNSUPPORTED: return "PKV_EUNSUPPORTED: unsupported head_dim, block_size, dtype or group size";
     case PKV_EWORKSPACE: return "PKV_EWORKSPACE: workspace missing or too small";
     case PKV_EHIP: return "PKV_EHIP: HIP launch failed";
+    case PKV_ESCRATCH:
+      return "PKV_ESCRATCH: the call needs more than the 32 MiB scratch of paged_attn_decode_noalloc "
+             "(paged_attn_decode_workspace_bytes gives the need; fewer sequences or workers fit)";
   }
   return "unknown status";
 }
