@@ -7,17 +7,15 @@
 // t < sinks for the attention sinks of the same page's Step 4 and roadmap).
 //
 // How, on gfx950 (v_mfma_f32_32x32x16 on 16-bit inputs, fp32 accumulate):
-//  * Workgroup = 4 wavefronts; each wavefront owns 32 query rows of one query
-//    head. The wavefronts of a workgroup share one kv head, so each K/V tile
-//    is gathered once into LDS for up to 4 query heads of the group.
-//  * Tiles of 64 key positions are gathered through the block table into LDS
-//    (K and V both row-major, two buffers): the next tile's global loads are
-//    in flight while the current tile is computed, one barrier per tile.
+//  * Each wavefront owns 32 query rows of one query head; the wavefronts of
+//    a workgroup share one kv head, so each K/V tile of 64 key positions is
+//    gathered once into LDS (direct global->LDS loads through the block
+//    table) for every query head of the group the workgroup covers.
 //  * Per tile and wavefront
 //      S^T (64 keys x 32 queries) = K_tile . Q^T        (16 MFMAs, D = 128)
 //    so each lane holds the scores of one query; the running maximum is
 //    exchanged between the two lane halves that hold the same query; then
-//      O^T (D x 32 queries) += V_tile^T . P^T
+//      O^T (D x 32 queries) += V_tile^T . P^T           (16 MFMAs)
 //    keeps one query's output per lane, so the rescale never leaves the lane.
 //    The V^T operand is read from row-major V with the LDS transpose read
 //    (ds_read_b64_tr_b16): within 16 lanes, lane j reads 4 consecutive dims
@@ -26,22 +24,29 @@
 //    weights rounded to fp16 (11-bit mantissa) and the normaliser summing
 //    the weights as used; lse takes the same sum, which is within 2^-11
 //    relative of the sum of the unrounded weights (plus at most 2^-25 per
-//    subnormal weight, against a sum of at least 1). A bf16 V tile is converted to fp16 in LDS once it
-//    has arrived: each thread rewrites the 16-byte units its own direct
-//    loads wrote, before the tile's barrier. The conversion is exact for
-//    |v| in [2^-17, 65504] (bf16 has 8 significant bits); smaller values are
-//    truncated by less than 2^-24 and larger ones saturate at 65504.
+//    subnormal weight, against a sum of at least 1). A bf16 V tile is
+//    converted to fp16 in LDS once it has arrived, each thread rewriting the
+//    16-byte units its own direct loads wrote. The conversion is exact for
+//    |v| in [2^-17, 65280] (bf16 has 8 significant bits, and 65280 is its
+//    largest value fp16 holds); smaller values are truncated by less than
+//    2^-24 and larger ones saturate at 65504.
 //  * The weights are taken relative to a reference maximum that moves only
 //    when some row's maximum grows by more than a factor 2^8 (weights then
 //    stay <= 256, well inside fp32 and the 16-bit formats); the output is
 //    rescaled only then. The result o / l and lse = m + log l do not depend
 //    on the reference, so this is exact up to rounding.
 //  * Masked keys (causal, window, unmapped blocks) are removed by selection
-//    (score -inf); V rows outside the loaded range are zero-filled so a
-//    zero weight never meets a NaN. Every K and V row multiplied is thus a
+//    (score -inf); K and V rows outside the loaded range are zero-filled so
+//    a zero weight never meets a NaN. Every K and V row multiplied is thus a
 //    written row or zeros, and every score finite or -inf: this file is
 //    compiled with -fno-honor-nans, which lets the maximum skip quieting its
 //    operands.
+//
+// Two kernels: prefill_kernel (16-bit pools; software-pipelined, described
+// at its definition) and prefill_kernel_staged (8-bit pools widened into
+// 16-bit staging blocks with row scales; one tile per step).
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -154,6 +159,11 @@ __device__ __forceinline__ u32x4 lds_read16(uint32_t addr) {
 }
 template <int N>
 __device__ __forceinline__ void lds_wait_n() { asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(N)); }
+// 16-byte LDS store at byte addr as inline asm (counted by lgkmcnt like the
+// reads above; waited for with lds_wait_n<0>() before a barrier).
+__device__ __forceinline__ void lds_write16(uint32_t addr, const u32x4& x) {
+  asm volatile("ds_write_b128 %0, %1" ::"v"(addr), "v"(x) : "memory");
+}
 __device__ __forceinline__ void settle(u32x4& x) { asm volatile("" : "+v"(x)); }
 
 template <int N> struct IntC { static constexpr int value = N; };
@@ -176,7 +186,7 @@ template <> __device__ __forceinline__ void v_to_f16<BF16T>(uint16_t* unit) {
 // QS: the pools hold widened 8-bit codes whose row scales multiply each
 // key's score (K scale) and weight (V scale).
 template <class T, int D, int B, int G, bool QS, int NW>
-__global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_kernel(PrefillArgs a, float scale_log2) {
+__global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_kernel_staged(PrefillArgs a, float scale_log2) {
   using M = Mma<T>;      // S = K.Q^T in the input type
   using MP = Mma<F16T>;  // O += V^T.P^T in fp16 (V converted in LDS when bf16)
   using V8 = typename M::V8;
@@ -577,23 +587,545 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_kernel(PrefillArgs a,
   }
 }
 
+// Wait until at most N of this wavefront's vector memory operations
+// (direct loads included) are outstanding; the compiler may not keep LDS
+// values across it.
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// A table row in the constant address space: uniform loads from it become
+// scalar loads, which are counted apart from vector memory operations, so
+// waiting for a table entry never waits for a tile's direct loads.
+typedef const __attribute__((address_space(4))) int32_t* ctab_t;
+
+// Bits [0, n) of a 64-bit mask, n clamped to [0, 64].
+__device__ __forceinline__ unsigned long long low_bits(int n) {
+  return n <= 0 ? 0ull : (n >= 64 ? ~0ull : ((1ull << n) - 1));
+}
+
+// Prefill over 16-bit pools, software-pipelined per wavefront.
+//
+// A workgroup of 8 wavefronts covers the query heads of one kv head (up to
+// 8) and as many 32-row sub-tiles as the rest allows; each wavefront owns 32
+// query rows of one head. Key tiles of 64 positions rotate through three LDS
+// stages. Iteration i of a wavefront overlaps two tiles:
+//   phase X: the 16 MFMAs of tile i+1's scores S^T = K.Q^T, interleaved with
+//            tile i's weights (exp2, fp16 rounding, row sum) on the vector ALU;
+//   phase Y: the 16 MFMAs of tile i's O^T += V^T.P^T, interleaved with tile
+//            i+1's mask and row maximum;
+// then the reference-maximum update of tile i+1 (rare output rescale).
+// K fragments are read from LDS two k-chunks ahead of their MFMAs, V
+// fragments one 16-key chunk ahead. Each iteration starts the direct loads
+// of tile i+2 into the stage tile i-1 held and ends with each thread waiting
+// for its own loads, converting its V units (bf16 -> fp16) and one barrier.
+// The table entries come from scalar loads one tile further ahead.
+template <class T, int D, int B, int G>
+__global__ __launch_bounds__(512, 1) void prefill_kernel(PrefillArgs a, float scale_log2) {
+  using M = Mma<T>;      // S = K.Q^T in the input type
+  using MP = Mma<F16T>;  // O += V^T.P^T in fp16 (V converted in LDS when bf16)
+  using V8 = typename M::V8;
+  using P8 = typename MP::V8;
+  constexpr int NW = 8;                 // wavefronts per workgroup
+  constexpr int KC = D / 16;            // MFMA k-chunks over the head dim
+  constexpr int DT = D / 32;            // 32-wide output tiles over the head dim
+  constexpr int HPW = G < NW ? G : NW;  // query heads per workgroup
+  constexpr int PSUB = NW / HPW;        // 32-row query sub-tiles per workgroup
+  constexpr int QT = 32 * PSUB;         // query rows per workgroup
+  constexpr int U = D / 8;              // 16-byte units per key row
+  constexpr int NLD = kKT * U / (64 * NW);  // direct loads per thread per tile (each of K and V)
+  constexpr int RPI = 64 / U;           // key rows per wavefront load instruction
+  constexpr int TB = kKT / B;           // table entries per tile
+  constexpr int NST = 4;                // LDS stages
+  constexpr int TILE = kKT * D;         // 16-bit elements of one K or V tile
+  static_assert(B % RPI == 0, "a wavefront instruction must not straddle blocks");
+  static_assert(KC >= 4, "the K read pipeline assumes at least 4 k-chunks");
+
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[NST * TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds[NST * TILE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = uniform(tid >> 6);
+  const int hf = lane >> 5;
+  const int ql = lane & 31;
+  // Workgroups are dispatched to the 8 XCDs round-robin by index; the index
+  // is renumbered so that each XCD runs a contiguous range of work items,
+  // ordered (kv-head group, sequence, query tile): the workgroups sharing a
+  // kv head's keys and values then share one XCD's L2.
+  int s, yg, qt;
+  {
+    const int N = a.grid_q * a.grid_y * a.S;
+    const int b = blockIdx.x, per = N / 8, rem = N % 8, x = b % 8;
+    const int w = x * per + min(x, rem) + b / 8;
+    yg = w / (a.grid_q * a.S);
+    const int r = w % (a.grid_q * a.S);
+    s = r / a.grid_q;
+    qt = a.grid_q - 1 - r % a.grid_q;  // heaviest (latest) tiles first
+  }
+  const int g = yg / (G / HPW);
+  const int hq = g * G + (yg % (G / HPW)) * HPW + wave % HPW;
+
+  const int r0 = a.q_start[s];
+  const int C = a.q_start[s + 1] - r0;
+  int L = a.lens[s];
+  L = L < 0 ? 0 : (L > a.max_context_len ? a.max_context_len : L);
+  if (qt * QT >= C || C > L) return;
+  if (a.skip_single && C == 1) return;  // a decode row of a mixed batch
+  const int row0 = qt * QT + (wave / HPW) * 32;   // first chunk row of this wavefront
+  const int wg_last = min(C, (qt + 1) * QT) - 1;  // last chunk row of the workgroup
+  const int base = L - C;                         // position of chunk row 0
+  const int kv_hi = base + wg_last + 1;
+  int kv_lo = 0;
+  if (a.window > 0) kv_lo = max(0, base + qt * QT - a.window + 1);
+  const int t_first = (kv_lo / kKT) * kKT;
+  // Key tiles in processing order: with attention sinks, first the tiles
+  // holding positions below min(sinks, kv_lo) that lie before the window's
+  // first tile (ns of them), then the window's tiles from t_first.
+  const int ns = min((min(a.sinks, kv_lo) + kKT - 1) / kKT, t_first / kKT);
+  const int ntiles = ns + (kv_hi - t_first + kKT - 1) / kKT;
+  auto tile_t0 = [&](int i) { return i < ns ? i * kKT : t_first + (i - ns) * kKT; };
+
+  // Query fragment of this lane: row ql of the wavefront, 8 elements per k-chunk.
+  const int my_row = row0 + ql;
+  const bool row_ok = my_row < C;
+  const int my_pos = base + my_row;
+  V8 qf[KC];
+  {
+    const char* qp = (const char*)a.q + ((size_t)(r0 + (row_ok ? my_row : 0)) * a.H + hq) * D * 2;
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+      u32x4 v = load16(qp + (size_t)(kc * 16 + 8 * hf) * 2);
+      if (!row_ok) v = u32x4{0, 0, 0, 0};
+      qf[kc] = __builtin_bit_cast(V8, v);
+    }
+  }
+
+  f32x16 o[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) o[dt] = f32x16{};
+  float m_run = -INFINITY;  // reference maximum of the scaled scores (base 2)
+  float l_run = 0.f;        // normaliser: sum of the fp16-rounded weights
+
+  const int wave_pmin = base + row0;
+  const int wave_pmax = base + min(row0 + 31, C - 1);
+  const uint32_t row_stride = (uint32_t)a.Hkv * D * 2;
+  const uint32_t block_stride = (uint32_t)B * row_stride;
+  const ctab_t trow = (ctab_t)(a.tables + (size_t)s * a.mb);
+  const char* zero = (const char*)g_zero16;
+
+  // Tile gather. Load j of thread (wave, lane) fills unit P = 64 (8 j + wave)
+  // + lane of the tile: row P / U, stored unit P % U, holding the logical
+  // unit that the swizzle puts there. The 64 / U rows of one wavefront
+  // instruction lie in one block (tile entry bj[j]), so a load's address is
+  // that block's base (scalar) plus a per-lane offset fixed for the kernel.
+  int bj[NLD];
+  uint32_t koff[NLD], voff[NLD];
+  int rj[NLD];
+#pragma unroll
+  for (int j = 0; j < NLD; ++j) {
+    const int r = (NW * j + wave) * RPI + lane / U, cs = lane % U;
+    rj[j] = r;
+    bj[j] = uniform((NW * j + wave) * RPI / B);
+    koff[j] = (uint32_t)((r % B) * row_stride) + 16 * (cs ^ Swz<D>::k(r)) + (uint32_t)g * D * 2;
+    voff[j] = (uint32_t)((r % B) * row_stride) + 16 * (cs ^ Swz<D>::v(r)) + (uint32_t)g * D * 2;
+  }
+  // Table entries of a tile (scalar loads; clamped inside the table row):
+  // all of them for the key mask, and this wavefront's own (pb_j[j] for its
+  // load j) loaded apart, so no register array is indexed at run time.
+  int ent[TB], pb_j[NLD];
+  auto fetch = [&](int t0) {
+    const int b0 = t0 / B;
+#pragma unroll
+    for (int k = 0; k < TB; ++k) ent[k] = trow[min(b0 + k, a.mb - 1)];
+#pragma unroll
+    for (int j = 0; j < NLD; ++j) pb_j[j] = trow[min(b0 + bj[j], a.mb - 1)];
+  };
+  // Bit k of a tile's key mask: key t0 + k is in the workgroup's range and
+  // its block is mapped.
+  auto key_mask = [&](int t0) -> unsigned long long {
+    unsigned long long blk = 0;
+#pragma unroll
+    for (int k = 0; k < TB; ++k)
+      if (ent[k] >= 0 && ent[k] < a.nb) blk |= low_bits(B) << (k * B);
+    const unsigned long long range =
+        low_bits(kv_hi - t0) & (~low_bits(kv_lo - t0) | low_bits(a.sinks - t0));
+    return blk & range;
+  };
+  const char* kpool = (const char*)a.k_pool;
+  const char* vpool = (const char*)a.v_pool;
+  auto gather = [&](int st, unsigned long long vmask) {
+    uint16_t* kd = k_lds + st * TILE;
+    uint16_t* vd = v_lds + st * TILE;
+    if (vmask == ~0ull) {
+#pragma unroll
+      for (int j = 0; j < NLD; ++j) {
+        const size_t boff = (size_t)(uint32_t)pb_j[j] * block_stride;
+        dma16(kpool + boff + koff[j], kd + (NW * j + wave) * 512);
+        dma16(vpool + boff + voff[j], vd + (NW * j + wave) * 512);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < NLD; ++j) {
+        const bool ok = (vmask >> rj[j]) & 1;
+        const size_t boff = (size_t)(uint32_t)(ok ? pb_j[j] : 0) * block_stride;
+        dma16(ok ? kpool + boff + koff[j] : zero, kd + (NW * j + wave) * 512);
+        dma16(ok ? vpool + boff + voff[j] : zero, vd + (NW * j + wave) * 512);
+      }
+    }
+  };
+  // Conversion of this thread's V units of a tile (bf16 -> fp16) once its
+  // loads have completed, in three parts so that it can sit between matrix
+  // instructions: cv_read issues the LDS reads (inline asm, like the operand
+  // reads, so that the compiler's own waits are not disturbed), cv_convert
+  // converts once they have arrived, cv_write stores the units back.
+  u32x4 cvu[NLD];
+  uint32_t cv_addr[NLD];
+  auto cv_read = [&](int st) {
+    if constexpr (!std::is_same<T, F16T>::value) {
+#pragma unroll
+      for (int j = 0; j < NLD; ++j) {
+        cv_addr[j] = lds_offset(v_lds + st * TILE + (NW * j + wave) * 512 + 8 * lane);
+        cvu[j] = lds_read16<0>(cv_addr[j]);
+      }
+    }
+  };
+  auto cv_convert = [&]() {
+    if constexpr (!std::is_same<T, F16T>::value) {
+#pragma unroll
+      for (int j = 0; j < NLD; ++j) {
+        settle(cvu[j]);
+        uint32_t w[4] = {cvu[j].x, cvu[j].y, cvu[j].z, cvu[j].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float lo = __builtin_bit_cast(float, w[e] << 16), hi = __builtin_bit_cast(float, w[e] & 0xffff0000u);
+          w[e] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+        }
+        cvu[j] = u32x4{w[0], w[1], w[2], w[3]};
+      }
+    }
+  };
+  auto cv_write = [&]() {
+    if constexpr (!std::is_same<T, F16T>::value) {
+#pragma unroll
+      for (int j = 0; j < NLD; ++j) lds_write16(cv_addr[j], cvu[j]);
+    }
+  };
+
+  // V^T operand addressing for the transpose read: 16-lane group gq = lane/16
+  // covers dims 16*(gq&1) .. +16 of a 32-dim tile and key half hf = gq>>1.
+  const int gq = lane >> 4, j16 = lane & 15;
+  const int tr_row = j16 >> 2;                          // key offset inside 4
+  const int tr_unit = 2 * (gq & 1) + ((j16 & 3) >> 1);  // 16-byte unit inside a 32-dim tile
+  const int tr_sw = Swz<D>::v(tr_row) >> 2;             // swizzle of rows 4i + tr_row, in 4-unit steps
+  const int tr_elem = 4 * (j16 & 1);                    // element inside the unit
+  uint32_t tr_addr[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+    tr_addr[dt] = 2 * ((4 * hf + tr_row) * D + tr_elem + 8 * (4 * (dt ^ tr_sw) + tr_unit));
+  // K operand: row kh*32 + ql, logical unit 2 kc + hf, stored at
+  // (2 kc) ^ (hf ^ swizzle(ql)) (the swizzle is the same for both halves).
+  const int k_sw = hf ^ Swz<D>::k(ql);
+  const uint32_t k_lane = 2 * ql * D;
+  auto kaddr = [&](uint32_t kb, int kc) { return kb + k_lane + 16 * ((2 * kc) ^ k_sw); };
+
+  unsigned long long vm0 = 0, vm1 = 0, vm2 = 0, vm3 = 0;  // key masks (see the prologue)
+  float ms = 0.f;  // reference maximum the current tile's weights are taken against
+  uint32_t pk[4][4];  // fp16 weights of the current tile: [key chunk][pair]
+
+  // Weights of pair j (0..15) of the current tile's scores sc: chunk c = j/4
+  // supplies keys 16c + 8*(e/4) + 4*hf + e%4 (accumulator registers
+  // 8*(c%2) .. +7 of half c/2); each pair is rounded to fp16 for the matrix
+  // cores and the normaliser sums the weights as rounded, so the output is
+  // their exact weighted average.
+  auto weights = [&](const f32x16* sc, int j) {
+    const int c = j >> 2, e2 = j & 3, kh = c >> 1, sub = c & 1;
+    const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kh][8 * sub + 2 * e2], scale_log2, -ms));
+    const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kh][8 * sub + 2 * e2 + 1], scale_log2, -ms));
+    const uint32_t h = MP::pack(p0, p1);
+    pk[c][e2] = h;
+    l_run = __builtin_amdgcn_fdot2(as_h2(h), f16x2{(_Float16)1.f, (_Float16)1.f}, l_run, false);
+  };
+
+  // Phase X: scores of the next tile (K in stage kst) into sn, with the
+  // current tile's weights (from sc) between the MFMAs. K fragments are read
+  // two k-chunks ahead: ring slot kc % 3.
+  auto phase_x = [&](const f32x16* sc, f32x16* sn, int kst, bool conv, int cst) {
+    const uint32_t kb = lds_offset(k_lds + kst * TILE);
+    sn[0] = f32x16{};
+    sn[1] = f32x16{};
+    if (conv) cv_read(cst);  // oldest reads: complete before the first K fragments
+    u32x4 ka[3][2];
+    ka[0][0] = lds_read16<0>(kaddr(kb, 0));
+    ka[0][1] = lds_read16<32 * D * 2>(kaddr(kb, 0));
+    ka[1][0] = lds_read16<0>(kaddr(kb, 1));
+    ka[1][1] = lds_read16<32 * D * 2>(kaddr(kb, 1));
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+      const int cur = kc % 3;
+      if (kc + 2 < KC) {
+        ka[(kc + 2) % 3][0] = lds_read16<0>(kaddr(kb, kc + 2));
+        ka[(kc + 2) % 3][1] = lds_read16<32 * D * 2>(kaddr(kb, kc + 2));
+        lds_wait_n<4>();
+      } else if (kc + 1 < KC) {
+        lds_wait_n<2>();
+      } else {
+        lds_wait_n<0>();
+      }
+      settle(ka[cur][0]);
+      settle(ka[cur][1]);
+      sn[0] = M::mma(__builtin_bit_cast(V8, ka[cur][0]), qf[kc], sn[0]);
+      if (kc < 8) weights(sc, 2 * kc);
+      sn[1] = M::mma(__builtin_bit_cast(V8, ka[cur][1]), qf[kc], sn[1]);
+      if (kc < 8) weights(sc, 2 * kc + 1);
+      if (conv && kc == 1) cv_convert();
+      if (conv && kc == 3) cv_write();
+    }
+#pragma unroll
+    for (int j = 2 * KC; j < 16; ++j) weights(sc, j);  // head dim 64: the rest of the weights
+  };
+  // The last tile's weights, with no next tile to overlap.
+  auto weights_only = [&](const f32x16* sc) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) weights(sc, j);
+  };
+
+  // Mask of the next tile's scores (branch-free selection) where the tile
+  // is not wholly attended by every row of the wavefront.
+  auto mask = [&](f32x16* sn, int t0, unsigned long long vmask) {
+    const bool need = vmask != ~0ull || wave_pmin < t0 + kKT - 1 || row0 + 31 >= C ||
+                      (a.window > 0 && t0 <= wave_pmax - a.window);
+    if (!need) return;
+    // Bit kl: key t0 + kl is attended by this lane's query row.
+    unsigned long long m = vmask & low_bits(row_ok ? my_pos - t0 + 1 : 0);
+    if (a.window > 0) m &= ~low_bits(my_pos - a.window + 1 - t0) | low_bits(a.sinks - t0);
+    m >>= 4 * hf;  // the lane's keys: kh*32 + 8*(v/4) + 4*hf + v%4
+    const uint32_t mh[2] = {(uint32_t)m, (uint32_t)(m >> 32)};
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        sn[kh][v] = (mh[kh] >> (8 * (v >> 2) + (v & 3))) & 1 ? sn[kh][v] : -INFINITY;
+  };
+
+  // Phase Y: O^T += V^T.P^T of the current tile (V in stage vst), with the
+  // next tile's row maximum (if any) between the MFMAs. V^T fragments of
+  // chunk c+1 are read while chunk c multiplies.
+  float m8[8];
+  auto max_part = [&](const f32x16* sn, int j) {
+    if (j < 8)
+      m8[j] = fmaxf(fmaxf(sn[j >> 2][4 * (j & 3)], sn[j >> 2][4 * (j & 3) + 1]),
+                    fmaxf(sn[j >> 2][4 * (j & 3) + 2], sn[j >> 2][4 * (j & 3) + 3]));
+    else if (j == 8)
+      m8[0] = fmaxf(fmaxf(m8[0], m8[1]), fmaxf(m8[2], m8[3]));
+    else if (j == 9)
+      m8[4] = fmaxf(fmaxf(m8[4], m8[5]), fmaxf(m8[6], m8[7]));
+  };
+  auto phase_y = [&](const f32x16* sn, bool with_next, int vst, int gi, int gst) {
+    const uint32_t vb = lds_offset(v_lds + vst * TILE);
+    u32x2 e03[2][DT], e47[2][DT];
+    auto rd = [&](auto cc, int slot) {
+      constexpr int c = decltype(cc)::value;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        e03[slot][dt] = lds_read_tr<16 * c * D * 2>(vb + tr_addr[dt]);
+        e47[slot][dt] = lds_read_tr<(16 * c + 8) * D * 2>(vb + tr_addr[dt]);
+      }
+    };
+    // The 10 parts of the maximum spread over the 4 * DT MFMAs.
+    constexpr int PPM = (10 + 4 * DT - 1) / (4 * DT);
+    auto mm = [&](auto cc, auto sl) {
+      constexpr int c = decltype(cc)::value, slot = decltype(sl)::value;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        settle(e03[slot][dt]);
+        settle(e47[slot][dt]);
+      }
+      const P8 bw = __builtin_bit_cast(P8, u32x4{pk[c][0], pk[c][1], pk[c][2], pk[c][3]});
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const P8 av = __builtin_bit_cast(P8, u32x4{e03[slot][dt].x, e03[slot][dt].y, e47[slot][dt].x,
+                                                     e47[slot][dt].y});
+        o[dt] = MP::mma(av, bw, o[dt]);
+        if (with_next) {
+#pragma unroll
+          for (int k = 0; k < PPM; ++k) max_part(sn, (4 * c + dt) * PPM + k);
+        }
+      }
+    };
+    rd(IntC<0>{}, 0);
+    rd(IntC<1>{}, 1);
+    lds_wait_n<2 * DT>();
+    mm(IntC<0>{}, IntC<0>{});
+    // The direct loads of tile gi (if any) into stage gst, and the table
+    // entries of the tile after it.
+    if (gi < ntiles) {
+      vm2 = key_mask(tile_t0(gi));
+      gather(gst, vm2);
+      if (gi + 1 < ntiles) fetch(tile_t0(gi + 1));
+    }
+    rd(IntC<2>{}, 0);
+    lds_wait_n<2 * DT>();
+    mm(IntC<1>{}, IntC<1>{});
+    rd(IntC<3>{}, 1);
+    lds_wait_n<2 * DT>();
+    mm(IntC<2>{}, IntC<0>{});
+    lds_wait_n<0>();
+    mm(IntC<3>{}, IntC<1>{});
+  };
+  // Reference maximum after the next tile's maximum: moves only when some
+  // row's maximum exceeds it by more than kSlackLog2 (weights then stay at
+  // most 2^kSlackLog2); the output rescale, exact either way, is rare.
+  auto update_max = [&]() {
+    float mt = fmaxf(m8[0], m8[4]);
+    const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, mt),
+                                                     __builtin_bit_cast(uint32_t, mt), false, false);
+    mt = fmaxf(__builtin_bit_cast(float, (uint32_t)sw[0]), __builtin_bit_cast(float, (uint32_t)sw[1]));
+    mt *= scale_log2;
+    if (__any(mt > m_run + kSlackLog2)) {
+      const float mn = fmaxf(m_run, mt);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - (mn == -INFINITY ? 0.f : mn));
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+      m_run = mn;
+    }
+    ms = m_run == -INFINITY ? 0.f : m_run;
+  };
+
+  // Prologue: tiles 0, 1 and 2 requested, tiles 0 and 1 waited for, tile 0's
+  // V converted, tile 3's table entries requested. Key masks rotate with the
+  // iterations: on entry to iteration i, vm0, vm1 and vm3 hold those of
+  // tiles i, i+1 and i+2; phase Y puts tile i+3's in vm2.
+  fetch(tile_t0(0));
+  vm0 = key_mask(tile_t0(0));
+  gather(0, vm0);
+  if (ntiles > 1) {
+    fetch(tile_t0(1));
+    vm1 = key_mask(tile_t0(1));
+    gather(1, vm1);
+  }
+  if (ntiles > 2) {
+    fetch(tile_t0(2));
+    vm3 = key_mask(tile_t0(2));
+    gather(2, vm3);
+  }
+  if (ntiles > 3) fetch(tile_t0(3));
+  if (ntiles > 2)
+    vm_wait<2 * NLD>();
+  else
+    vm_wait<0>();
+  cv_read(0);
+  lds_wait_n<0>();
+  cv_convert();
+  cv_write();
+  lds_wait_n<0>();
+  __syncthreads();
+
+  f32x16 sA[2], sB[2];
+  {
+    const uint32_t kb = lds_offset(k_lds);
+    sA[0] = f32x16{};
+    sA[1] = f32x16{};
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+      const u32x4 k0 = lds_read16<0>(kaddr(kb, kc));
+      const u32x4 k1 = lds_read16<32 * D * 2>(kaddr(kb, kc));
+      u32x4 x0 = k0, x1 = k1;
+      lds_wait_n<0>();
+      settle(x0);
+      settle(x1);
+      sA[0] = M::mma(__builtin_bit_cast(V8, x0), qf[kc], sA[0]);
+      sA[1] = M::mma(__builtin_bit_cast(V8, x1), qf[kc], sA[1]);
+    }
+    mask(sA, tile_t0(0), vm0);
+#pragma unroll
+    for (int j = 0; j < 10; ++j) max_part(sA, j);
+    update_max();
+  }
+
+  // Iteration i with the current tile's scores in sc and the next tile's
+  // going to sn; stage of tile i is st. Tile i+1's V is converted in phase
+  // X; tile i+3's loads are issued in phase Y (into the stage tile i-1
+  // held); at the end every thread waits for its loads of tile i+2 (issued
+  // one iteration earlier), and one barrier publishes both.
+  auto iteration = [&](int i, int st, const f32x16* sc, f32x16* sn) {
+    const int st1 = (st + 1) & (NST - 1);
+    const int st3 = (st + 3) & (NST - 1);
+    const bool has_next = i + 1 < ntiles;
+    vm2 = 0;
+    if (has_next)
+      phase_x(sc, sn, st1, true, st1);
+    else
+      weights_only(sc);
+    if (has_next) mask(sn, tile_t0(i + 1), vm1);
+    // phase_y sets vm2 to the key mask of tile i+3 when it gathers it
+    phase_y(sn, has_next, st, i + 3, st3);
+    if (has_next) update_max();
+    if (i + 3 < ntiles)
+      vm_wait<2 * NLD>();
+    else
+      vm_wait<0>();
+    lds_wait_n<0>();
+    __syncthreads();
+    vm0 = vm1;
+    vm1 = vm3;  // tile i+2
+    vm3 = vm2;  // tile i+3
+    return st1;
+  };
+  int st = 0;
+  for (int i = 0;;) {
+    st = iteration(i, st, sA, sB);
+    if (++i == ntiles) break;
+    st = iteration(i, st, sB, sA);
+    if (++i == ntiles) break;
+  }
+
+  if (!row_ok) return;
+  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  float* op = a.out + ((size_t)(r0 + my_row) * a.H + hq) * D;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+    for (int v4 = 0; v4 < 4; ++v4) {
+      const int d = dt * 32 + 8 * v4 + 4 * hf;
+      float4 w = make_float4(o[dt][4 * v4] * inv, o[dt][4 * v4 + 1] * inv, o[dt][4 * v4 + 2] * inv,
+                             o[dt][4 * v4 + 3] * inv);
+      *reinterpret_cast<float4*>(op + d) = w;
+    }
+  }
+  if (a.lse) {
+    if (hf == 0)
+      a.lse[(size_t)(r0 + my_row) * a.H + hq] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+  }
+}
+
 template <class T, int D, int B, int G>
 static hipError_t launch_typed(const PrefillArgs& a, hipStream_t st) {
-  // Wavefronts per workgroup: 8 with 4 or more query heads per kv head (the
-  // tile gather and its table reads are then shared by 8 wavefronts), else 4.
-  constexpr int NW = G >= 4 ? 8 : 4;
+  PrefillArgs b = a;
+  if (a.k_scale) {
+    // Widened 8-bit codes with row scales.
+    constexpr int NW = G >= 4 ? 8 : 4;
+    constexpr int HPW = G < NW ? G : NW;
+    constexpr int QT = 32 * (NW / HPW);
+    b.grid_q = (a.max_q_len + QT - 1) / QT;
+    b.grid_y = a.Hkv * (G / HPW);
+    const long long n = (long long)b.grid_q * b.grid_y * a.S;
+    if (n > INT32_MAX) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((prefill_kernel_staged<T, D, B, G, true, NW>), dim3((unsigned)n), dim3(64 * NW), 0, st, b,
+                       a.scale * kLog2e);
+    return hipGetLastError();
+  }
+  constexpr int NW = 8;
   constexpr int HPW = G < NW ? G : NW;
   constexpr int QT = 32 * (NW / HPW);
-  PrefillArgs b = a;
   b.grid_q = (a.max_q_len + QT - 1) / QT;
   b.grid_y = a.Hkv * (G / HPW);
   const long long n = (long long)b.grid_q * b.grid_y * a.S;
   if (n > INT32_MAX) return hipErrorInvalidValue;
-  dim3 grid((unsigned)n);
-  if (a.k_scale)
-    hipLaunchKernelGGL((prefill_kernel<T, D, B, G, true, NW>), grid, dim3(64 * NW), 0, st, b, a.scale * kLog2e);
-  else
-    hipLaunchKernelGGL((prefill_kernel<T, D, B, G, false, NW>), grid, dim3(64 * NW), 0, st, b, a.scale * kLog2e);
+  hipLaunchKernelGGL((prefill_kernel<T, D, B, G>), dim3((unsigned)n), dim3(64 * NW), 0, st, b, a.scale * kLog2e);
   return hipGetLastError();
 }
 
