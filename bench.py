@@ -183,14 +183,14 @@ def cpu_baseline(w, target_s: float):
 
 
 KERNELS = {"decode": ("decode_split_kernel", "decode_merge_kernel", "decode_plan_kernel"),
-           "prefill": ("prefill_kernel", "widen_kernel")}
+           "prefill": ("prefill_kernel",)}
 
 
 def attend_sources(kind: str, kv: str):
     """Source files of the kernels one attention call launches."""
     if kind == "decode":
         return ("decode.hip", "common.h")
-    return ("prefill.hip", "common.h") + (("widen.hip",) if kv != "native" else ())
+    return ("prefill.hip", "common.h")
 
 
 def summarize_pmc(args, fetch_dir, write_dir, copy_mib) -> int:
@@ -231,8 +231,8 @@ def summarize_pmc(args, fetch_dir, write_dir, copy_mib) -> int:
         scale = copy_bytes / (copy_val * 1024.0) if copy_val else 1.0
         ours = sorted((i, k, v) for (i, k), v in vals.items() if any(n in k for n in KERNELS[kind]))
         # group consecutive dispatches of one call: the split/prefill kernel
-        # starts a call, the widening kernel over 8-bit pools
-        first = "widen_kernel" if (kind == "prefill" and args.kv != "native") else KERNELS[kind][0]
+        # starts a call
+        first = KERNELS[kind][0]
         calls, cur = [], None
         for i, k, v in ours:
             if first in k:

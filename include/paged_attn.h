@@ -288,14 +288,6 @@ int paged_attn_decode_quant(const pkv_geometry_t* geom, float* out, float* lse, 
                             int32_t max_context_len, int32_t window, int32_t num_sinks, float scale,
                             int32_t num_workers, void* workspace, size_t workspace_bytes, void* stream);
 
-/* paged_attn_prefill_quant_workspace_bytes - bytes of device workspace
- * paged_attn_prefill_quant needs for num_seqs sequences of context at most
- * max_context_len with this (8-bit) geometry: two staging pools of
- * num_seqs * ceil(max_context_len / B) blocks in 16-bit, their row scales and
- * a staging table. 0 if the geometry is invalid or not 8-bit. */
-size_t paged_attn_prefill_quant_workspace_bytes(const pkv_geometry_t* geom, int32_t num_seqs,
-                                                int32_t max_context_len);
-
 /* paged_attn_prefill_quant - paged_attn_prefill over 8-bit pools ("Build a
  * Memory-Compressed Attention Engine with KV Caching from Scratch",
  * "Extending It" item 2, with the prefill of "Building a Streaming
@@ -303,20 +295,18 @@ size_t paged_attn_prefill_quant_workspace_bytes(const pkv_geometry_t* geom, int3
  * attention with every key and value replaced by its decoded value
  * code * scale.
  *
- * Two kernels on `stream`: the physical blocks the chunks read (below L,
- * and with a window from the first row's window on, plus sink blocks) are
- * widened into the workspace, codes unchanged as q_dtype values (exact),
- * once per block for all the sequences that map it at the same logical
- * index (a shared prefix); then the prefill kernel reads them through a
- * staging table. A key's score is the dot product with its codes times its
- * K scale (float32);
- * a weight is multiplied by its key's V scale times 2^4 (PKV_I8) or 2^6
- * (PKV_FP8) and rounded to fp16 for the matrix cores, and the output is
- * divided by the same power of two; the normaliser (and lse) sums those
- * rounded products divided by their V scales (float32), i.e. the weights the
- * matrix cores actually apply, so the output is their exact weighted
- * average. A row whose largest |value| exceeds 2031 (PKV_I8) or 1791
- * (PKV_FP8) is attended with its V scale capped there.
+ * One kernel on `stream`, no workspace: each tile of key positions is
+ * gathered as codes through the block table and widened in the kernel's
+ * on-chip memory (codes unchanged as q_dtype values for K and fp16 values
+ * for V; exact). Key t's score is its dot product with the codes times its
+ * K scale (float32). The softmax weight of key t times its V scale, taken
+ * relative to a running reference that keeps it at most 256 (log2 of the V
+ * scale joins the score before the maximum), is rounded to fp16 and
+ * multiplied with the V codes on the matrix cores; the normaliser (and lse)
+ * sums those rounded products divided by their V scales (float32), i.e. the
+ * weights the matrix cores actually apply, so the output is their exact
+ * weighted average. There is no limit on the scales' magnitudes. A zero V
+ * row (scale 0) keeps its weight in the normaliser.
  *
  *   geom->kv_dtype    PKV_I8 or PKV_FP8; head_dim, block_size and
  *                     num_heads / num_kv_heads as paged_attn_prefill
@@ -324,18 +314,13 @@ size_t paged_attn_prefill_quant_workspace_bytes(const pkv_geometry_t* geom, int3
  *                     PKV_BF16
  *   k_pool, v_pool    codes [NB, B, Hkv, D]
  *   k_scale, v_scale  float32 [NB, Hkv, B]
- *   workspace         device, 16-byte aligned, at least
- *                     paged_attn_prefill_quant_workspace_bytes(geom, num_seqs,
- *                     max_context_len) bytes (else PKV_EWORKSPACE); owned by
- *                     the caller and overwritten; calls that share it on
- *                     different streams race
  *   all other arguments as paged_attn_prefill. */
 int paged_attn_prefill_quant(const pkv_geometry_t* geom, float* out, float* lse, const void* q,
                              int32_t q_dtype, const int32_t* q_start, const void* k_pool, const void* v_pool,
                              const float* k_scale, const float* v_scale, const int32_t* block_tables,
                              int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
                              int32_t max_q_len, int32_t max_context_len, int32_t window, int32_t num_sinks,
-                             float scale, void* workspace, size_t workspace_bytes, void* stream);
+                             float scale, void* stream);
 
 /* paged_kv_copy_blocks - copy whole blocks: pair i copies block src[i] to
  * block dst[i] in both pools (every slot and kv head; with 8-bit pools the
@@ -374,25 +359,16 @@ int paged_attn_mixed(const pkv_geometry_t* geom, float* out, float* lse, const v
                      int32_t max_context_len, int32_t window, int32_t num_sinks, float scale,
                      int32_t num_workers, void* workspace, size_t workspace_bytes, void* stream);
 
-/* paged_attn_mixed_quant_workspace_bytes - workspace of paged_attn_mixed_quant:
- * the decode workspace (paged_attn_decode_workspace_bytes with the same
- * arguments), rounded up to 256 bytes, plus the prefill staging
- * (paged_attn_prefill_quant_workspace_bytes). 0 if either is 0. */
-size_t paged_attn_mixed_quant_workspace_bytes(const pkv_geometry_t* geom, int32_t num_seqs,
-                                              int32_t max_context_len, int32_t window, int32_t num_sinks,
-                                              int32_t num_workers);
-
 /* paged_attn_mixed_quant - paged_attn_mixed over 8-bit pools (the 8-bit
  * pages of paged_attn_decode_quant with the continuous batching of
  * paged_attn_mixed): sequences with one query row are computed as
  * paged_attn_decode_quant computes them, the others as
- * paged_attn_prefill_quant (only their blocks are widened), all enqueued on
- * `stream`.
+ * paged_attn_prefill_quant, all enqueued on `stream`.
  *
  *   geom->kv_dtype, q / q_dtype, k_pool, v_pool, k_scale, v_scale: as
  *                     paged_attn_prefill_quant (q has q_start[num_seqs] rows)
- *   workspace         device, 16-byte aligned, at least
- *                     paged_attn_mixed_quant_workspace_bytes(geom, num_seqs,
+ *   workspace         the decode workspace: device, 16-byte aligned, at
+ *                     least paged_attn_decode_workspace_bytes(geom, num_seqs,
  *                     max_context_len, window, num_sinks, num_workers) bytes
  *                     (else PKV_EWORKSPACE, before anything is enqueued)
  *   all other arguments as paged_attn_mixed. */

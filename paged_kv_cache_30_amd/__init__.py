@@ -5,8 +5,9 @@ Entry points (same names as the C functions in ``include/paged_attn.h``):
 ``paged_kv_write``, ``paged_attn_decode``, ``paged_attn_prefill``,
 ``paged_attn_decode_workspace_bytes``, ``paged_attn_decode_workers``, and for
 8-bit (INT8 / FP8 E4M3) pools ``paged_kv_write_quant`` and
-``paged_attn_decode_quant``, ``paged_attn_prefill_quant`` (with
-``paged_attn_prefill_quant_workspace_bytes``) and ``paged_attn_mixed_quant``;
+``paged_attn_decode_quant``, ``paged_attn_prefill_quant`` and
+``paged_attn_mixed_quant``; ``paged_attn_decode_noalloc`` (decode with the
+library's fixed scratch instead of a workspace);
 ``paged_kv_copy_blocks`` (copy-on-write) and
 ``paged_attn_mixed`` (prefill chunks and decode rows in one call);
 ``paged_kv_compress`` and ``paged_attn_decode_compressed`` (the compressed-slot
@@ -27,8 +28,7 @@ from ._lib import (  # noqa: F401
     PKV_ESCRATCH, paged_kv_write, paged_attn_decode, paged_attn_decode_noalloc, paged_attn_prefill,
     paged_attn_decode_workspace_bytes, paged_attn_decode_workers, decode_workspace,
     paged_kv_write_quant, paged_attn_decode_quant, bind_kv_write_quant, bind_decode_quant,
-    paged_attn_prefill_quant, paged_attn_prefill_quant_workspace_bytes, prefill_quant_workspace,
-    bind_prefill_quant, paged_attn_mixed_quant, paged_attn_mixed_quant_workspace_bytes, bind_mixed_quant,
+    paged_attn_prefill_quant, bind_prefill_quant, paged_attn_mixed_quant, bind_mixed_quant,
     paged_kv_copy_blocks, paged_attn_mixed, bind_mixed,
     paged_kv_compress, paged_attn_decode_compressed, bind_decode_compressed, bind_kv_compress,
 )

@@ -38,8 +38,8 @@ _QUANT = (torch.int8, torch.float8_e4m3fn)
 # Every symbol declared in include/paged_attn.h.
 EXPORTS = ("paged_kv_write", "paged_attn_decode_workspace_bytes", "paged_attn_decode_workers",
            "paged_attn_decode", "paged_attn_prefill", "paged_kv_write_quant", "paged_attn_decode_quant",
-           "paged_attn_prefill_quant_workspace_bytes", "paged_attn_prefill_quant", "paged_kv_copy_blocks",
-           "paged_attn_mixed_quant_workspace_bytes", "paged_attn_mixed_quant", "paged_attn_mixed", "paged_kv_compress",
+           "paged_attn_prefill_quant", "paged_kv_copy_blocks",
+           "paged_attn_mixed_quant", "paged_attn_mixed", "paged_kv_compress",
            "paged_attn_decode_compressed", "paged_attn_decode_noalloc",
            "pkv_status_string", "pkv_last_hip_error", "pkv_version")
 
@@ -81,13 +81,9 @@ def _load() -> ctypes.CDLL:
     lib.paged_attn_decode_quant.argtypes = [G, P, P, P, I32, P, P, P, P, P, I32, P, I32, I32, I32, I32, F, I32, P,
                                             SZ, P]
     lib.paged_attn_decode_quant.restype = ctypes.c_int
-    lib.paged_attn_prefill_quant_workspace_bytes.argtypes = [G, I32, I32]
-    lib.paged_attn_prefill_quant_workspace_bytes.restype = SZ
     lib.paged_attn_prefill_quant.argtypes = [G, P, P, P, I32, P, P, P, P, P, P, I32, P, I32, I32, I32, I32, I32, F,
-                                             P, SZ, P]
+                                             P]
     lib.paged_attn_prefill_quant.restype = ctypes.c_int
-    lib.paged_attn_mixed_quant_workspace_bytes.argtypes = [G, I32, I32, I32, I32, I32]
-    lib.paged_attn_mixed_quant_workspace_bytes.restype = SZ
     lib.paged_attn_mixed_quant.argtypes = [G, P, P, P, I32, P, P, P, P, P, P, I32, P, I32, I32, I32, I32, I32, F,
                                            I32, P, SZ, P]
     lib.paged_attn_mixed_quant.restype = ctypes.c_int
@@ -470,23 +466,10 @@ def paged_attn_decode_quant(out, q, k_pool, v_pool, k_scale, v_scale, block_tabl
                       sinks=sinks, debug=debug)(stream)
 
 
-def paged_attn_prefill_quant_workspace_bytes(k_pool, num_heads, num_seqs, max_context_len) -> int:
-    """C ``paged_attn_prefill_quant_workspace_bytes`` for an 8-bit pool."""
-    return int(LIB.paged_attn_prefill_quant_workspace_bytes(ctypes.byref(geometry(k_pool, num_heads)),
-                                                            int(num_seqs), int(max_context_len)))
-
-
-def prefill_quant_workspace(k_pool, num_heads, num_seqs, max_context_len):
-    """A device workspace tensor of the size paged_attn_prefill_quant needs."""
-    n = paged_attn_prefill_quant_workspace_bytes(k_pool, num_heads, num_seqs, max_context_len)
-    return torch.empty(max(n, 16), dtype=torch.uint8, device=k_pool.device)
-
-
 def bind_prefill_quant(out, q, q_start, k_pool, v_pool, k_scale, v_scale, block_tables, context_lens, max_q_len,
-                       max_context_len, *, window=0, scale, workspace=None, lse=None, sinks=0, debug=None):
+                       max_context_len, *, window=0, scale, lse=None, sinks=0, debug=None):
     """Check and marshal the arguments of ``paged_attn_prefill_quant`` once;
-    returns a callable ``f(stream=None)``.  Without ``workspace`` one of the
-    size the call needs is allocated here, once."""
+    returns a callable ``f(stream=None)``."""
     _check_quant_pools(k_pool, v_pool, k_scale, v_scale)
     _dev(q, "q", ndim=3)
     if q.dtype not in (torch.float16, torch.bfloat16):
@@ -503,16 +486,11 @@ def bind_prefill_quant(out, q, q_start, k_pool, v_pool, k_scale, v_scale, block_
         _dev(lse, "lse", dtype=torch.float32, ndim=2)
         if lse.shape != (T, H):
             raise ValueError("lse must be [T, H]")
-    if workspace is None:
-        workspace = prefill_quant_workspace(k_pool, H, S, max_context_len)
-    _dev(workspace, "workspace")
-    ws_bytes = workspace.numel() * workspace.element_size()
     g = geometry(k_pool, H)
     args = (ctypes.byref(g), _ptr(out), _ptr(lse), _ptr(q), _DTYPES[q.dtype], _ptr(q_start), _ptr(k_pool),
             _ptr(v_pool), _ptr(k_scale), _ptr(v_scale), _ptr(block_tables), block_tables.shape[1],
-            _ptr(context_lens), S, int(max_q_len), int(max_context_len), int(window), int(sinks), float(scale),
-            _ptr(workspace), ws_bytes)
-    keep = (g, out, q, q_start, k_pool, v_pool, k_scale, v_scale, block_tables, context_lens, workspace, lse)
+            _ptr(context_lens), S, int(max_q_len), int(max_context_len), int(window), int(sinks), float(scale))
+    keep = (g, out, q, q_start, k_pool, v_pool, k_scale, v_scale, block_tables, context_lens, lse)
     dbg = _debug(debug)
 
     def call(stream=None):
@@ -527,13 +505,12 @@ def bind_prefill_quant(out, q, q_start, k_pool, v_pool, k_scale, v_scale, block_
 
 
 def paged_attn_prefill_quant(out, q, q_start, k_pool, v_pool, k_scale, v_scale, block_tables, context_lens,
-                             max_q_len, max_context_len, *, window=0, scale, workspace=None, lse=None,
-                             stream=None, sinks=0, debug=None) -> None:
+                             max_q_len, max_context_len, *, window=0, scale, lse=None, stream=None, sinks=0,
+                             debug=None) -> None:
     """C ``paged_attn_prefill_quant``: chunked prefill over 8-bit pools with
     row scales."""
     bind_prefill_quant(out, q, q_start, k_pool, v_pool, k_scale, v_scale, block_tables, context_lens, max_q_len,
-                       max_context_len, window=window, scale=scale, workspace=workspace, lse=lse, sinks=sinks,
-                       debug=debug)(stream)
+                       max_context_len, window=window, scale=scale, lse=lse, sinks=sinks, debug=debug)(stream)
 
 
 # ------------------------------------------------- block copies, mixed batches
@@ -703,14 +680,6 @@ def paged_attn_decode_compressed(out, q, k_pool, v_pool, block_tables, context_l
                            workspace=workspace, lse=lse, debug=debug)(stream)
 
 
-def paged_attn_mixed_quant_workspace_bytes(k_pool, num_heads, num_seqs, max_context_len, window=0, num_workers=0,
-                                           sinks=0) -> int:
-    """C ``paged_attn_mixed_quant_workspace_bytes`` for an 8-bit pool."""
-    return int(LIB.paged_attn_mixed_quant_workspace_bytes(ctypes.byref(geometry(k_pool, num_heads)), int(num_seqs),
-                                                          int(max_context_len), int(window), int(sinks),
-                                                          int(num_workers)))
-
-
 def bind_mixed_quant(out, q, q_start, k_pool, v_pool, k_scale, v_scale, block_tables, context_lens, max_q_len,
                      max_context_len, *, window=0, scale, num_workers=0, workspace=None, lse=None, sinks=0,
                      debug=None):
@@ -734,8 +703,7 @@ def bind_mixed_quant(out, q, q_start, k_pool, v_pool, k_scale, v_scale, block_ta
         if lse.shape != (T, H):
             raise ValueError("lse must be [T, H]")
     if workspace is None:
-        n = paged_attn_mixed_quant_workspace_bytes(k_pool, H, S, max_context_len, window, num_workers, sinks)
-        workspace = torch.empty(max(n, 16), dtype=torch.uint8, device=k_pool.device)
+        workspace = decode_workspace(k_pool, H, S, max_context_len, window, num_workers, sinks=sinks)
     _dev(workspace, "workspace")
     ws_bytes = workspace.numel() * workspace.element_size()
     g = geometry(k_pool, H)

@@ -342,49 +342,15 @@ int paged_attn_prefill(const pkv_geometry_t* geom, float* out, float* lse, const
 
 namespace {
 
-// Workspace of paged_attn_prefill_quant for S sequences of at most msb
-// blocks: staging K and V pools in q's 16-bit type, their row scales and the
-// staging table, each 256-byte aligned.
-struct QuantPrefillStage {
-  int msb;
-  size_t pool_bytes, scale_bytes, table_bytes;
-  size_t total() const { return 2 * pool_bytes + 2 * scale_bytes + table_bytes; }
-};
-
-QuantPrefillStage quant_prefill_stage(const pkv_geometry_t* g, int num_seqs, int max_context_len) {
-  QuantPrefillStage q;
-  q.msb = (max_context_len + g->block_size - 1) / g->block_size;
-  const size_t blocks = (size_t)num_seqs * q.msb;
-  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
-  q.pool_bytes = up(blocks * g->block_size * g->num_kv_heads * g->head_dim * 2);
-  q.scale_bytes = up(blocks * g->num_kv_heads * g->block_size * sizeof(float));
-  q.table_bytes = up(blocks * sizeof(int32_t));
-  return q;
-}
-
-}  // namespace
-
-extern "C" {
-
-size_t paged_attn_prefill_quant_workspace_bytes(const pkv_geometry_t* geom, int32_t num_seqs,
-                                                int32_t max_context_len) {
-  if (check_geometry(geom) || !is_quant(geom->kv_dtype) || num_seqs <= 0 || max_context_len < 0) return 0;
-  return quant_prefill_stage(geom, num_seqs, max_context_len).total();
-}
-
-}  // extern "C"
-
-namespace {
-
-// Widening plus the prefill kernel over 8-bit pools, for the sequences with
-// at least min_rows query rows (1: every chunk; 2: the chunks of a mixed
-// batch, whose single rows decode computes).
+// The prefill kernel over 8-bit pools, for the sequences with at least
+// min_rows query rows (1: every chunk; 2: the chunks of a mixed batch, whose
+// single rows decode computes).
 int prefill_quant_common(const pkv_geometry_t* geom, float* out, float* lse, const void* q, int32_t q_dtype,
                          const int32_t* q_start, const void* k_pool, const void* v_pool, const float* k_scale,
                          const float* v_scale, const int32_t* block_tables, int32_t max_blocks_per_seq,
                          const int32_t* context_lens, int32_t num_seqs, int32_t max_q_len,
-                         int32_t max_context_len, int32_t window, int32_t num_sinks, float scale,
-                         void* workspace, size_t workspace_bytes, void* stream, int min_rows) {
+                         int32_t max_context_len, int32_t window, int32_t num_sinks, float scale, void* stream,
+                         int min_rows) {
   int st = check_geometry(geom);
   if (st) return st;
   if (!is_quant(geom->kv_dtype) || (q_dtype != PKV_F16 && q_dtype != PKV_BF16)) return PKV_EUNSUPPORTED;
@@ -399,37 +365,13 @@ int prefill_quant_common(const pkv_geometry_t* geom, float* out, float* lse, con
     return PKV_EINVAL;
   const int G = geom->num_heads / geom->num_kv_heads;
   if (!pkv::prefill_supported(q_dtype, geom->head_dim, geom->block_size, G)) return PKV_EUNSUPPORTED;
-  if ((long long)geom->block_size * geom->num_kv_heads * geom->head_dim * 2 > INT32_MAX) return PKV_EUNSUPPORTED;
-  const QuantPrefillStage sp = quant_prefill_stage(geom, num_seqs, max_context_len);
-  if ((long long)num_seqs * sp.msb > INT32_MAX) return PKV_EUNSUPPORTED;
-  if (!workspace || workspace_bytes < sp.total() || ((uintptr_t)workspace & 15)) return PKV_EWORKSPACE;
-  char* ws = (char*)workspace;
-  void* k_stage = ws;
-  void* v_stage = ws + sp.pool_bytes;
-  float* ks_stage = (float*)(ws + 2 * sp.pool_bytes);
-  float* vs_stage = (float*)(ws + 2 * sp.pool_bytes + sp.scale_bytes);
-  int32_t* t_stage = (int32_t*)(ws + 2 * sp.pool_bytes + 2 * sp.scale_bytes);
-  pkv::WidenArgs w{k_pool, v_pool, k_scale, v_scale, block_tables, context_lens, k_stage, v_stage, ks_stage,
-                   vs_stage, t_stage, num_seqs, max_blocks_per_seq, sp.msb, geom->num_blocks, geom->block_size,
-                   geom->num_kv_heads, geom->head_dim, geom->kv_dtype, q_dtype, max_context_len};
-  // V scales staged times 2^4 (INT8) or 2^6 (FP8), about QMAX / 8: a weight
-  // times a staged scale is then below fp16's normal range only where its
-  // rounding error, back in output units, is below 2^-22 (8 ulps of the
-  // smallest subnormal); the output is divided by the same power of two.
-  w.v_mul = geom->kv_dtype == PKV_I8 ? 16.f : 64.f;
-  w.q_start = q_start;
-  w.min_rows = min_rows;
-  w.window = window;
-  w.sinks = num_sinks;
-  st = hip_status(pkv::launch_widen(w, (hipStream_t)stream));
-  if (st) return st;
-  pkv::PrefillArgs a{out, lse, q, q_start, k_stage, v_stage, t_stage, context_lens, num_seqs,
+  pkv::PrefillArgs a{out, lse, q, q_start, k_pool, v_pool, block_tables, context_lens, num_seqs,
                      geom->num_heads, geom->num_kv_heads, geom->head_dim, geom->block_size,
-                     sp.msb, num_seqs * sp.msb, window, q_dtype, max_q_len,
+                     max_blocks_per_seq, geom->num_blocks, window, q_dtype, max_q_len,
                      max_context_len, scale, num_sinks};
-  a.k_scale = ks_stage;
-  a.v_scale = vs_stage;
-  a.o_mul = 1.f / w.v_mul;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.code_dtype = geom->kv_dtype;
   a.skip_single = min_rows > 1;
   return hip_status(pkv::launch_prefill(a, (hipStream_t)stream));
 }
@@ -443,10 +385,10 @@ int paged_attn_prefill_quant(const pkv_geometry_t* geom, float* out, float* lse,
                              const float* v_scale, const int32_t* block_tables, int32_t max_blocks_per_seq,
                              const int32_t* context_lens, int32_t num_seqs, int32_t max_q_len,
                              int32_t max_context_len, int32_t window, int32_t num_sinks, float scale,
-                             void* workspace, size_t workspace_bytes, void* stream) {
+                             void* stream) {
   return prefill_quant_common(geom, out, lse, q, q_dtype, q_start, k_pool, v_pool, k_scale, v_scale, block_tables,
                               max_blocks_per_seq, context_lens, num_seqs, max_q_len, max_context_len, window,
-                              num_sinks, scale, workspace, workspace_bytes, stream, 1);
+                              num_sinks, scale, stream, 1);
 }
 
 int paged_kv_copy_blocks(const pkv_geometry_t* geom, void* k_pool, void* v_pool, float* k_scale, float* v_scale,
@@ -502,16 +444,6 @@ int paged_attn_mixed(const pkv_geometry_t* geom, float* out, float* lse, const v
   return hip_status(pkv::launch_prefill(pa, (hipStream_t)stream));
 }
 
-size_t paged_attn_mixed_quant_workspace_bytes(const pkv_geometry_t* geom, int32_t num_seqs,
-                                              int32_t max_context_len, int32_t window, int32_t num_sinks,
-                                              int32_t num_workers) {
-  const size_t d = paged_attn_decode_workspace_bytes(geom, num_seqs, max_context_len, window, num_sinks,
-                                                     num_workers);
-  const size_t p = paged_attn_prefill_quant_workspace_bytes(geom, num_seqs, max_context_len);
-  if (!d || !p) return 0;
-  return (d + 255) / 256 * 256 + p;
-}
-
 int paged_attn_mixed_quant(const pkv_geometry_t* geom, float* out, float* lse, const void* q, int32_t q_dtype,
                            const int32_t* q_start, const void* k_pool, const void* v_pool, const float* k_scale,
                            const float* v_scale, const int32_t* block_tables, int32_t max_blocks_per_seq,
@@ -540,8 +472,7 @@ int paged_attn_mixed_quant(const pkv_geometry_t* geom, float* out, float* lse, c
   DecodeSplit sp;
   st = decode_split(&view, num_seqs, max_context_len, window, num_sinks, num_workers, &sp);
   if (st) return st;
-  const size_t dec_bytes = (sp.total() + 255) / 256 * 256;
-  if (!workspace || workspace_bytes < dec_bytes || ((uintptr_t)workspace & 15)) return PKV_EWORKSPACE;
+  if (!workspace || workspace_bytes < sp.total() || ((uintptr_t)workspace & 15)) return PKV_EWORKSPACE;
   char* ws = (char*)workspace;
   pkv::DecodeArgs da{out, lse, q, k_pool, v_pool, block_tables, context_lens, k_scale, v_scale, q_dtype,
                      (int32_t*)ws, (float*)(ws + sp.cum_bytes), (float*)(ws + sp.cum_bytes + sp.ml_bytes),
@@ -549,15 +480,11 @@ int paged_attn_mixed_quant(const pkv_geometry_t* geom, float* out, float* lse, c
                      max_blocks_per_seq, view.num_blocks, window, view.kv_dtype, max_context_len,
                      sp.workers, scale, num_sinks, q_start};
   da.kv_shift = kv_shift;
-  if (max_q_len >= 2) {  // the chunks' staging must fit too: check before enqueueing anything
-    if (workspace_bytes - dec_bytes < quant_prefill_stage(geom, num_seqs, max_context_len).total())
-      return PKV_EWORKSPACE;
-  }
   st = hip_status(pkv::launch_decode(da, (hipStream_t)stream));
   if (st || max_q_len < 2) return st;
   return prefill_quant_common(geom, out, lse, q, q_dtype, q_start, k_pool, v_pool, k_scale, v_scale, block_tables,
                               max_blocks_per_seq, context_lens, num_seqs, max_q_len, max_context_len, window,
-                              num_sinks, scale, ws + dec_bytes, workspace_bytes - dec_bytes, stream, 2);
+                              num_sinks, scale, stream, 2);
 }
 
 int paged_kv_compress(const pkv_geometry_t* geom, void* k_pool, void* v_pool, const int32_t* src_blocks,

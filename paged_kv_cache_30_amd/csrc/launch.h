@@ -104,44 +104,15 @@ struct PrefillArgs {
   float scale;
   int32_t sinks;      // with a window: positions below this are attended too
   int32_t skip_single;  // mixed batches: sequences with one row are left to decode
-  // Row scales [nb, Hkv, B] when the pools hold widened 8-bit codes (null
+  // Row scales [nb, Hkv, B] when the pools hold 8-bit codes (null
   // otherwise): a key's score is multiplied by its K scale, a weight by its
   // key's V scale.
   const float* k_scale;
   const float* v_scale;
-  float o_mul = 1.f;  // factor on the output rows (undoes a power of two folded into the V scales)
+  int32_t code_dtype = 0;  // 8-bit pools: PKV_I8 (3) or PKV_FP8 (4) codes; dtype is then q's type
   int32_t grid_q = 0, grid_y = 0;  // set by the launcher: query tiles and kv-head groups per sequence
 };
 
-// Widening of the 8-bit blocks a batch attends into 16-bit staging pools
-// (exact: every INT8 code and E4M3 value is a bf16 and an fp16 value), with
-// their row scales: staged block s * msb + j holds logical block j of
-// sequence s, and stage_tables [S, msb] maps each entry to the copy of its
-// physical block (-1 where nothing is staged; a block that several
-// sequences map at the same logical index is copied once). K scales are copied; V scales are multiplied by v_mul (a power of two) and
-// capped at 65504 / 256, so that a weight (at most 256) times a V scale is a
-// finite fp16 value.
-struct WidenArgs {
-  const void* k_codes;
-  const void* v_codes;
-  const float* k_scale;
-  const float* v_scale;
-  const int32_t* tables;
-  const int32_t* lens;
-  void* k_out;
-  void* v_out;
-  float* ks_out;
-  float* vs_out;
-  int32_t* stage_tables;
-  int32_t S, mb, msb, nb, B, Hkv, D, code_dtype, out_dtype, max_context_len;
-  float v_mul;
-  // What the prefill will read: sequences with at least min_rows query rows
-  // (q_start [S + 1]), and with a window only blocks that hold a position
-  // its first row attends or a sink position.
-  const int32_t* q_start;
-  int32_t min_rows, window, sinks;
-};
-hipError_t launch_widen(const WidenArgs& a, hipStream_t st);
 
 hipError_t launch_kv_write(const WriteArgs& a, hipStream_t st);
 bool kv_write_quant_supported(int kv_dtype, int in_dtype, int D);

@@ -43,8 +43,9 @@
 //    operands.
 //
 // Two kernels: prefill_kernel (16-bit pools; software-pipelined, described
-// at its definition) and prefill_kernel_staged (8-bit pools widened into
-// 16-bit staging blocks with row scales; one tile per step).
+// at its definition) and prefill_kernel_q8 (8-bit pools: codes gathered and
+// widened in LDS, row scales folded into scores and weights; one tile per
+// step).
 #include <type_traits>
 
 #include "common.h"
@@ -183,12 +184,58 @@ template <> __device__ __forceinline__ void v_to_f16<BF16T>(uint16_t* unit) {
   *reinterpret_cast<u32x4*>(unit) = u32x4{w[0], w[1], w[2], w[3]};
 }
 
-// QS: the pools hold widened 8-bit codes whose row scales multiply each
-// key's score (K scale) and weight (V scale).
-template <class T, int D, int B, int G, bool QS, int NW>
-__global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_kernel_staged(PrefillArgs a, float scale_log2) {
+// Sixteen 8-bit codes of one 16-byte unit as fp32 values (exact): INT8 as
+// the signed byte, FP8 E4M3 as the code's value.
+template <class C> __device__ __forceinline__ void codes16_to_f32(const u32x4& w, float* f);
+template <> __device__ __forceinline__ void codes16_to_f32<I8T>(const u32x4& w, float* f) {
+  const uint32_t x[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) f[4 * i + b] = (float)(int8_t)((x[i] >> (8 * b)) & 0xffu);
+}
+template <> __device__ __forceinline__ void codes16_to_f32<FP8T>(const u32x4& w, float* f) {
+  const uint32_t x[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) codes4_to_f32<FP8T>(x[i], f + 4 * i);  // BIAS 0: the code's value
+}
+
+// Eight values that the 16-bit type holds exactly, as one 16-byte unit.
+template <class O> __device__ __forceinline__ u32x4 pack8(const float* f);
+template <> __device__ __forceinline__ u32x4 pack8<BF16T>(const float* f) {
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) w[i] = (__float_as_uint(f[2 * i]) >> 16) | (__float_as_uint(f[2 * i + 1]) & 0xffff0000u);
+  return u32x4{w[0], w[1], w[2], w[3]};
+}
+template <> __device__ __forceinline__ u32x4 pack8<F16T>(const float* f) {
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    w[i] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f[2 * i]) |
+           ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f[2 * i + 1]) << 16);
+  return u32x4{w[0], w[1], w[2], w[3]};
+}
+
+// Prefill over 8-bit pools (INT8 or OCP FP8 E4M3 codes, CT, with one fp32
+// scale per row), one key tile per step, two LDS buffers. A tile's codes are
+// gathered into LDS by direct loads, then each thread widens the 16 codes
+// it loaded into the 16-bit tiles: K into q's type T, V into fp16 (exact:
+// every INT8 code and E4M3 value is both a bf16 and an fp16 value). Key t's
+// score is its dot product with the codes times its K scale; its weight
+// times its V scale is what the fp16 matrix cores multiply with the V
+// codes. log2 of the V scale is added to the score before the tile maximum
+// (e_t = scale * score_t * log2(e) + log2(vs_t)), so exp2(e_t - m) is weight
+// times V scale relative to a reference m that bounds it by 2^8, whatever
+// the scales' magnitudes; the normaliser sums those products as rounded to
+// fp16 times 1 / vs_t, the weights the matrix cores actually apply. A zero
+// V row (scale 0, all codes 0) takes scale 1 so that its weight stays in
+// the normaliser.
+template <class T, class CT, int D, int B, int G, int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_kernel_q8(PrefillArgs a, float scale_log2) {
+  constexpr bool QS = true;
   using M = Mma<T>;      // S = K.Q^T in the input type
-  using MP = Mma<F16T>;  // O += V^T.P^T in fp16 (V converted in LDS when bf16)
+  using MP = Mma<F16T>;  // O += V^T.P^T in fp16 (V codes widened to fp16)
   using V8 = typename M::V8;
   using P8 = typename MP::V8;
   constexpr int KC = D / 16;            // MFMA k-chunks over the head dim
@@ -196,8 +243,12 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_kernel_staged(Prefill
   constexpr int HPW = G < NW ? G : NW;  // query heads per workgroup
   constexpr int PSUB = NW / HPW;        // 32-row query sub-tiles per workgroup
   constexpr int QT = 32 * PSUB;         // query rows per workgroup
-  constexpr int U = D / 8;              // 16-byte units per key row
-  constexpr int NLD = kKT * U / (64 * NW);  // direct loads per thread per tile (each of K and V)
+  constexpr int U = D / 8;              // 16-byte units of a widened key row
+  constexpr int UQ = D / 16;            // 16-byte units of a key row of codes
+  constexpr int NIQ = kKT * UQ / 64;    // wavefront load instructions per tile (each of K and V)
+  constexpr int NLDQ = (NIQ + NW - 1) / NW;  // per wavefront (the last may be idle)
+  constexpr int RPIQ = 64 / UQ;         // key rows per load instruction
+  static_assert(B % RPIQ == 0, "a wavefront instruction must not straddle blocks");
 
   // Two buffers of each of K and V, as separate arrays: the compiler then
   // knows that reads of one buffer do not depend on direct loads in flight
@@ -206,10 +257,14 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_kernel_staged(Prefill
   __shared__ __attribute__((aligned(16))) uint16_t k_lds1[kKT * D];
   __shared__ __attribute__((aligned(16))) uint16_t v_lds0[kKT * D];
   __shared__ __attribute__((aligned(16))) uint16_t v_lds1[kKT * D];
+  // Codes as loaded (unswizzled: load unit P at byte 16 P). One buffer:
+  // each thread widens exactly the units it loaded, within the step.
+  __shared__ __attribute__((aligned(16))) uint8_t kc_lds[kKT * D];
+  __shared__ __attribute__((aligned(16))) uint8_t vc_lds[kKT * D];
   __shared__ unsigned long long kvalid[2];  // bit t: key t0 + t of the tile is mapped
-  // QS: the K and V scales of the tile's keys (zero for keys outside the
-  // range, which are masked), [slot][K or V][key].
-  __shared__ __attribute__((aligned(16))) float scl[QS ? 2 : 1][QS ? 3 : 1][kKT];
+  // Per key of each buffer's tile: K scale * scale * log2(e), log2 of the V
+  // scale and its inverse (0, 0, 1 for keys outside the range, masked).
+  __shared__ __attribute__((aligned(16))) float scl[2][3][kKT];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -274,70 +329,75 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_kernel_staged(Prefill
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) o[dt] = f32x16{};
   float m_run = -INFINITY;  // running max of the scaled scores (base 2)
-  float l_run = 0.f;        // normaliser: sum of the fp16-rounded weights (with QS, weight x V scale / V scale)
+  float l_run = 0.f;        // normaliser: sum of the fp16-rounded weight x V scale products / V scale
 
   const int wave_pmin = base + row0;
   const int wave_pmax = base + min(row0 + 31, C - 1);
   const bool wave_has_rows = row0 < C;
-  const uint32_t row_stride = (uint32_t)a.Hkv * D * 2;
+  const uint32_t row_stride = (uint32_t)a.Hkv * D;  // codes: one byte per element
   const uint32_t block_stride = (uint32_t)B * row_stride;
-  const char* kpool = (const char*)a.k_pool + (size_t)g * D * 2;
-  const char* vpool = (const char*)a.v_pool + (size_t)g * D * 2;
+  const char* kpool = (const char*)a.k_pool + (size_t)g * D;
+  const char* vpool = (const char*)a.v_pool + (size_t)g * D;
   const int32_t* trow = a.tables + (size_t)s * a.mb;
   const char* zero = (const char*)g_zero16;
 
-  // Tile gather. Load j of thread (wave, lane) fills unit P = 64 (4 j + wave)
-  // + lane of the tile: row P / U, stored unit P % U, holding the logical
-  // unit that the swizzle puts there. The 64 / U rows of one wavefront
-  // instruction start at a multiple of 64 / U, so they lie in one block: the
-  // table entry of instruction j is uniform over the wavefront and is read
-  // with a scalar load. Entries are read one tile ahead (`fetch_table`).
-  constexpr int RPI = 64 / U;  // rows per wavefront instruction
-  static_assert(B % RPI == 0, "a wavefront instruction must not straddle blocks");
-  int pb_ins[NLD];  // table entry of instruction j of this wavefront, next tile
-  int pb_key = -1;  // wavefront 0: table entry of key t0 + lane, next tile
-  // The entries are loaded as lane values (through an index offset the
-  // compiler cannot see is zero): a uniform load would be moved to a scalar
-  // register right away, which waits for it, and vector memory operations
-  // complete in order, so that wait would also wait for every direct load
-  // issued before it. As lane values they are first used one step later,
-  // after the end-of-tile wait has completed them anyway.
+  // Tile gather. Load j of thread (wave, lane), instruction x = NW j + wave
+  // (if below NIQ), fills code unit P = 64 x + lane of the tile: row P / UQ,
+  // 16 codes from element 16 (P % UQ). The RPIQ rows of one instruction lie
+  // in one block: its table entry is uniform over the wavefront. Entries are
+  // read one tile ahead (`fetch_table`), as lane values (through an index
+  // offset the compiler cannot see is zero): a uniform load would be moved
+  // to a scalar register right away, waiting for it and, since vector memory
+  // operations complete in order, for every direct load issued before it.
+  int pb_ins[NLDQ];  // table entry of instruction j of this wavefront, next tile
+  int pb_key = -1;   // wavefront 0: table entry of key t0 + lane, next tile
   int lane_zero;
   asm volatile("v_mov_b32 %0, 0" : "=v"(lane_zero));
   auto fetch_table = [&](int t0) {
 #pragma unroll
-    for (int j = 0; j < NLD; ++j)  // in range of the table row even past the context
-      pb_ins[j] = trow[min((t0 + (NW * j + wave) * RPI) / B, a.mb - 1) + lane_zero];
+    for (int j = 0; j < NLDQ; ++j)  // in range of the table row even past the context
+      pb_ins[j] = trow[min((t0 + min(NW * j + wave, NIQ - 1) * RPIQ) / B, a.mb - 1) + lane_zero];
     if (wave == 0) pb_key = trow[min((t0 + lane) / B, a.mb - 1)];
   };
-  // Per-lane byte offsets inside a block of load j (tiles start at multiples
-  // of kKT, a multiple of B, so row r of a tile is row r % B of its block).
-  auto unit_off = [&](int j, bool v) -> uint32_t {
-    const int r = (NW * j + wave) * RPI + lane / U, cs = lane % U;
-    return (uint32_t)((r % B) * row_stride) + 16 * (cs ^ (v ? Swz<D>::v(r) : Swz<D>::k(r)));
-  };
-  auto gather = [&](int t0, uint16_t* kd, uint16_t* vd) {
+  auto gather = [&](int t0, uint8_t* kd, uint8_t* vd) {
     // Whole tile inside the attended range: only the block entries decide.
     const bool whole = t0 >= kv_lo && t0 + kKT <= kv_hi;
 #pragma unroll
-    for (int j = 0; j < NLD; ++j) {
+    for (int j = 0; j < NLDQ; ++j) {
+      const int x = NW * j + wave;
+      if (x >= NIQ) break;
       const int pb = pb_ins[j];
       const bool blk_ok = pb >= 0 && pb < a.nb;
       const size_t boff = (size_t)(uint32_t)(blk_ok ? pb : 0) * block_stride;
+      const int r = x * RPIQ + lane / UQ;
+      const uint32_t off = (uint32_t)((r % B) * row_stride) + 16 * (lane % UQ);
       bool ok = blk_ok;
-      if (!whole) ok = ok && in_range(t0 + (NW * j + wave) * RPI + lane / U);
-      dma16(ok ? kpool + boff + unit_off(j, false) : zero, kd + (NW * j + wave) * 512);
-      dma16(ok ? vpool + boff + unit_off(j, true) : zero, vd + (NW * j + wave) * 512);
+      if (!whole) ok = ok && in_range(t0 + r);
+      dma16(ok ? kpool + boff + off : zero, (uint16_t*)(kd + 1024 * x));
+      dma16(ok ? vpool + boff + off : zero, (uint16_t*)(vd + 1024 * x));
     }
   };
-  // Convert the V units this thread's direct loads wrote (after dma_wait).
-  auto convert_v = [&](uint16_t* vd) {
+  // Widen the code units this thread loaded (after dma_wait): 16 codes of
+  // row r from element 16 c become the 16-bit logical units 2c and 2c + 1
+  // of row r, stored where the swizzle puts them; K in T, V in fp16.
+  auto widen = [&](const uint8_t* kcs, const uint8_t* vcs, uint16_t* kd, uint16_t* vd) {
 #pragma unroll
-    for (int j = 0; j < NLD; ++j) v_to_f16<T>(vd + (NW * j + wave) * 512 + 8 * lane);
+    for (int j = 0; j < NLDQ; ++j) {
+      const int x = NW * j + wave;
+      if (x >= NIQ) break;
+      const int P = 64 * x + lane, r = P / UQ, c = P % UQ;
+      float f[16];
+      codes16_to_f32<CT>(*reinterpret_cast<const u32x4*>(kcs + 16 * P), f);
+      *reinterpret_cast<u32x4*>(kd + r * D + 8 * ((2 * c) ^ Swz<D>::k(r))) = pack8<T>(f);
+      *reinterpret_cast<u32x4*>(kd + r * D + 8 * ((2 * c + 1) ^ Swz<D>::k(r))) = pack8<T>(f + 8);
+      codes16_to_f32<CT>(*reinterpret_cast<const u32x4*>(vcs + 16 * P), f);
+      *reinterpret_cast<u32x4*>(vd + r * D + 8 * ((2 * c) ^ Swz<D>::v(r))) = pack8<F16T>(f);
+      *reinterpret_cast<u32x4*>(vd + r * D + 8 * ((2 * c + 1) ^ Swz<D>::v(r))) = pack8<F16T>(f + 8);
+    }
   };
-  // Key validity bitmask of a tile (64 lanes = 64 keys), by wavefront 0;
-  // with QS also the keys' scales, into registers (stored to LDS by
-  // store_scales once the tile's loads are waited for).
+  // Key validity bitmask of a tile (64 lanes = 64 keys), by wavefront 0,
+  // with the keys' scales into registers (stored to LDS by store_scales
+  // once the tile's loads are waited for).
   float sk_reg = 0.f, sv_reg = 0.f;
   auto put_valid = [&](int t0, int slot) {
     if (wave == 0) {
@@ -353,12 +413,11 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_kernel_staged(Prefill
     }
   };
   auto store_scales = [&](int slot) {
-    if constexpr (QS) {
-      if (wave == 0) {
-        scl[slot][0][lane] = sk_reg;
-        scl[slot][1][lane] = sv_reg;
-        scl[slot][QS ? 2 : 0][lane] = sv_reg > 0.f ? 1.f / sv_reg : 0.f;
-      }
+    if (wave == 0) {
+      const bool pos = sv_reg > 0.f;  // a zero V row takes scale 1
+      scl[slot][0][lane] = sk_reg * scale_log2;
+      scl[slot][1][lane] = pos ? __log2f(sv_reg) : 0.f;
+      scl[slot][2][lane] = pos ? 1.f / sv_reg : 1.f;
     }
   };
 
@@ -382,12 +441,12 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_kernel_staged(Prefill
   // One tile: gather the next tile into the other buffers, compute this one
   // from (Ks, Vs, kvalid[slot]), wait for the gather, barrier. Returns
   // whether a next tile exists.
-  auto step = [&](int i, const uint16_t* Ks, const uint16_t* Vs, uint16_t* Kn, uint16_t* Vn,
-                  int slot) -> bool {
+  auto step = [&](int i, const uint16_t* Ks, const uint16_t* Vs, uint16_t* Kn, uint16_t* Vn, uint8_t* Kcn,
+                  uint8_t* Vcn, int slot) -> bool {
     const int t0 = tile_t0(i);
     const bool has_next = i + 1 < ntiles;
     if (has_next) {
-      gather(tile_t0(i + 1), Kn, Vn);
+      gather(tile_t0(i + 1), Kcn, Vcn);
       put_valid(tile_t0(i + 1), slot ^ 1);
       if (i + 2 < ntiles) fetch_table(tile_t0(i + 2));
     }
@@ -421,16 +480,17 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_kernel_staged(Prefill
         sacc[0] = M::mma(__builtin_bit_cast(V8, ka[cur][0]), qf[kc], sacc[0]);
         sacc[1] = M::mma(__builtin_bit_cast(V8, ka[cur][1]), qf[kc], sacc[1]);
       }
-      if constexpr (QS) {  // key t's score times its K scale (keys 8*(v/4) + 4*hf + v%4 of each half)
+      {  // e = dot * K scale * scale * log2(e) + log2(V scale) for keys 8*(v/4) + 4*hf + v%4 of each half
 #pragma unroll
         for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
           for (int q4 = 0; q4 < 4; ++q4) {
-            const float4 k4 = *reinterpret_cast<const float4*>(&scl[QS ? slot : 0][0][kh * 32 + 8 * q4 + 4 * hf]);
-            sacc[kh][4 * q4] *= k4.x;
-            sacc[kh][4 * q4 + 1] *= k4.y;
-            sacc[kh][4 * q4 + 2] *= k4.z;
-            sacc[kh][4 * q4 + 3] *= k4.w;
+            const float4 k4 = *reinterpret_cast<const float4*>(&scl[slot][0][kh * 32 + 8 * q4 + 4 * hf]);
+            const float4 l4 = *reinterpret_cast<const float4*>(&scl[slot][1][kh * 32 + 8 * q4 + 4 * hf]);
+            sacc[kh][4 * q4] = __builtin_fmaf(sacc[kh][4 * q4], k4.x, l4.x);
+            sacc[kh][4 * q4 + 1] = __builtin_fmaf(sacc[kh][4 * q4 + 1], k4.y, l4.y);
+            sacc[kh][4 * q4 + 2] = __builtin_fmaf(sacc[kh][4 * q4 + 2], k4.z, l4.z);
+            sacc[kh][4 * q4 + 3] = __builtin_fmaf(sacc[kh][4 * q4 + 3], k4.w, l4.w);
           }
       }
       // Mask (selection, branch-free), running maximum of the raw scores.
@@ -463,7 +523,6 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_kernel_staged(Prefill
                                                          __builtin_bit_cast(uint32_t, mt), false, false);
         mt = fmaxf(__builtin_bit_cast(float, (uint32_t)sw[0]), __builtin_bit_cast(float, (uint32_t)sw[1]));
       }
-      mt *= scale_log2;
       // The reference maximum m_run moves only when some row's tile maximum
       // exceeds it by more than kSlackLog2, so weights are at most
       // 2^kSlackLog2 and the output rescale (exact either way) is rare.
@@ -493,38 +552,26 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_kernel_staged(Prefill
           e47[dt] = lds_read_tr<(16 * c + 8) * D * 2>(vbase + tr_addr[dt]);
         }
         uint32_t hi[4];
-        float vs[8], vi[8];  // QS: V scales of this lane's 8 keys of the chunk, and their inverses
-        if constexpr (QS) {
-          const float4 va = *reinterpret_cast<const float4*>(&scl[QS ? slot : 0][1][16 * c + 4 * hf]);
-          const float4 vb = *reinterpret_cast<const float4*>(&scl[QS ? slot : 0][1][16 * c + 8 + 4 * hf]);
-          const float4 ia = *reinterpret_cast<const float4*>(&scl[QS ? slot : 0][QS ? 2 : 0][16 * c + 4 * hf]);
-          const float4 ib = *reinterpret_cast<const float4*>(&scl[QS ? slot : 0][QS ? 2 : 0][16 * c + 8 + 4 * hf]);
-          vs[0] = va.x; vs[1] = va.y; vs[2] = va.z; vs[3] = va.w;
-          vs[4] = vb.x; vs[5] = vb.y; vs[6] = vb.z; vs[7] = vb.w;
+        float vi[8];  // inverse V scales of this lane's 8 keys of the chunk
+        {
+          const float4 ia = *reinterpret_cast<const float4*>(&scl[slot][2][16 * c + 4 * hf]);
+          const float4 ib = *reinterpret_cast<const float4*>(&scl[slot][2][16 * c + 8 + 4 * hf]);
           vi[0] = ia.x; vi[1] = ia.y; vi[2] = ia.z; vi[3] = ia.w;
           vi[4] = ib.x; vi[5] = ib.y; vi[6] = ib.z; vi[7] = ib.w;
         }
 #pragma unroll
         for (int e2 = 0; e2 < 4; ++e2) {
-          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kh][8 * sub + 2 * e2], scale_log2, -ms));
-          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kh][8 * sub + 2 * e2 + 1], scale_log2, -ms));
-          if constexpr (QS) {
-            // V is multiplied by weight x V scale, rounded to fp16; the
-            // normaliser sums those rounded products divided by their
-            // scales, so that it holds exactly the weights the matrix cores
-            // multiply (a lone key's row then comes out exact).
-            const uint32_t hv = MP::pack(p0 * vs[2 * e2], p1 * vs[2 * e2 + 1]);
-            hi[e2] = hv;
-            const f16x2 w = as_h2(hv);
-            l_run = __builtin_fmaf((float)w[0], vi[2 * e2], l_run);
-            l_run = __builtin_fmaf((float)w[1], vi[2 * e2 + 1], l_run);
-          } else {
-            // The normaliser sums the weights as rounded for the matrix
-            // cores, so the output is their exact weighted average.
-            const uint32_t h = MP::pack(p0, p1);
-            hi[e2] = h;
-            l_run = __builtin_amdgcn_fdot2(as_h2(h), f16x2{(_Float16)1.f, (_Float16)1.f}, l_run, false);
-          }
+          // weight x V scale relative to the reference, rounded to fp16 for
+          // the matrix cores; the normaliser sums those rounded products
+          // divided by their scales, exactly the weights the matrix cores
+          // apply (a lone key's row then comes out exact)
+          const float p0 = __builtin_amdgcn_exp2f(sacc[kh][8 * sub + 2 * e2] - ms);
+          const float p1 = __builtin_amdgcn_exp2f(sacc[kh][8 * sub + 2 * e2 + 1] - ms);
+          const uint32_t hv = MP::pack(p0, p1);
+          hi[e2] = hv;
+          const f16x2 w = as_h2(hv);
+          l_run = __builtin_fmaf((float)w[0], vi[2 * e2], l_run);
+          l_run = __builtin_fmaf((float)w[1], vi[2 * e2 + 1], l_run);
         }
         const P8 bhi = __builtin_bit_cast(P8, u32x4{hi[0], hi[1], hi[2], hi[3]});
         lds_wait();
@@ -546,7 +593,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_kernel_staged(Prefill
     }
     dma_wait();
     if (has_next) {
-      convert_v(Vn);  // the next tile's V units this thread loaded
+      widen(Kcn, Vcn, Kn, Vn);  // the next tile's code units this thread loaded
       store_scales(slot ^ 1);
     }
     __syncthreads();
@@ -555,21 +602,21 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_kernel_staged(Prefill
 
   fetch_table(tile_t0(0));
   dma_wait();  // table entries in registers
-  gather(tile_t0(0), k_lds0, v_lds0);
+  gather(tile_t0(0), kc_lds, vc_lds);
   put_valid(tile_t0(0), 0);
   if (ntiles > 1) fetch_table(tile_t0(1));
   dma_wait();
-  convert_v(v_lds0);
+  widen(kc_lds, vc_lds, k_lds0, v_lds0);
   store_scales(0);
   __syncthreads();
   for (int i = 0;; i += 2) {
-    if (!step(i, k_lds0, v_lds0, k_lds1, v_lds1, 0)) break;
-    if (!step(i + 1, k_lds1, v_lds1, k_lds0, v_lds0, 1)) break;
+    if (!step(i, k_lds0, v_lds0, k_lds1, v_lds1, kc_lds, vc_lds, 0)) break;
+    if (!step(i + 1, k_lds1, v_lds1, k_lds0, v_lds0, kc_lds, vc_lds, 1)) break;
   }
 
   if (!row_ok) return;
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-  const float inv = l_tot > 0.f ? (QS ? a.o_mul : 1.f) / l_tot : 0.f;
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   float* op = a.out + ((size_t)(r0 + my_row) * a.H + hq) * D;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) {
@@ -1106,16 +1153,22 @@ template <class T, int D, int B, int G>
 static hipError_t launch_typed(const PrefillArgs& a, hipStream_t st) {
   PrefillArgs b = a;
   if (a.k_scale) {
-    // Widened 8-bit codes with row scales.
-    constexpr int NW = G >= 4 ? 8 : 4;
+    // 8-bit pools: codes widened in the kernel, row scales.
+    constexpr int NW = 8;
     constexpr int HPW = G < NW ? G : NW;
     constexpr int QT = 32 * (NW / HPW);
     b.grid_q = (a.max_q_len + QT - 1) / QT;
     b.grid_y = a.Hkv * (G / HPW);
     const long long n = (long long)b.grid_q * b.grid_y * a.S;
     if (n > INT32_MAX) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((prefill_kernel_staged<T, D, B, G, true, NW>), dim3((unsigned)n), dim3(64 * NW), 0, st, b,
-                       a.scale * kLog2e);
+    if (a.code_dtype == 3)
+      hipLaunchKernelGGL((prefill_kernel_q8<T, I8T, D, B, G, NW>), dim3((unsigned)n), dim3(64 * NW), 0, st, b,
+                         a.scale * kLog2e);
+    else if (a.code_dtype == 4)
+      hipLaunchKernelGGL((prefill_kernel_q8<T, FP8T, D, B, G, NW>), dim3((unsigned)n), dim3(64 * NW), 0, st, b,
+                         a.scale * kLog2e);
+    else
+      return hipErrorInvalidValue;
     return hipGetLastError();
   }
   constexpr int NW = 8;

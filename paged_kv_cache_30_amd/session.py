@@ -103,9 +103,8 @@ class DeviceWorkload:
         if w.kind == "decode":
             self.workspace = _lib.decode_workspace(self.k_pool, w.num_heads, w.num_seqs, w.max_context_len,
                                                    w.window, num_workers, sinks=w.sinks)
-        elif self.kv_format != "native":
-            self.workspace = _lib.prefill_quant_workspace(self.k_pool, w.num_heads, w.num_seqs,
-                                                          w.max_context_len)
+        else:
+            self.workspace = None
 
     def _write(self, k, v, seq, pos):
         if self.kv_format == "native":
@@ -157,7 +156,7 @@ class DeviceWorkload:
                 self._bound_attend = _lib.bind_prefill_quant(
                     self.out, self.q, self.q_start, self.k_pool, self.v_pool, self.k_scale, self.v_scale,
                     self.tables, self.lens, w.max_q_len, w.max_context_len, window=w.window, scale=w.scale,
-                    workspace=self.workspace, lse=self.lse, sinks=w.sinks)
+                    lse=self.lse, sinks=w.sinks)
             else:
                 self._bound_attend = _lib.bind_prefill(
                     self.out, self.q, self.q_start, self.k_pool, self.v_pool, self.tables, self.lens,

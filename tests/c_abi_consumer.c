@@ -33,15 +33,20 @@ int main(void) {
                           NULL) == PKV_EINVAL);
   CHECK(paged_attn_prefill(&g, NULL, NULL, NULL, NULL, NULL, NULL, NULL, 8, NULL, 4, 4, 100, 0, 0, 0.1f,
                            NULL) == PKV_EINVAL);
-  /* 8-bit pools: their own entry points and size queries */
+  /* 8-bit pools: their own entry points (prefill needs no workspace) */
   g.kv_dtype = PKV_I8;
-  CHECK(paged_attn_prefill_quant_workspace_bytes(&g, 4, 1000) > 0);
-  CHECK(paged_attn_mixed_quant_workspace_bytes(&g, 4, 1000, 0, 0, 0) > 0);
+  CHECK(paged_attn_decode_workspace_bytes(&g, 4, 1000, 0, 0, 0) > 0);
   CHECK(paged_attn_decode(&g, NULL, NULL, NULL, NULL, NULL, NULL, 8, NULL, 4, 100, 0, 0, 0.1f, 0, NULL, 0,
                           NULL) == PKV_EUNSUPPORTED);
+  CHECK(paged_attn_prefill_quant(&g, NULL, NULL, NULL, PKV_BF16, NULL, NULL, NULL, NULL, NULL, NULL, 8, NULL, 4, 4,
+                                 100, 0, 0, 0.1f, NULL) == PKV_EINVAL);
   /* an unsupported head size */
   g.head_dim = 96;
-  CHECK(paged_attn_prefill_quant_workspace_bytes(&g, 4, 1000) == 0);
+  CHECK(paged_attn_decode_workspace_bytes(&g, 4, 1000, 0, 0, 0) == 0);
+  /* the no-alloc decode refuses 8-bit pools before anything else */
+  g.head_dim = 128;
+  CHECK(paged_attn_decode_noalloc(&g, NULL, NULL, NULL, NULL, NULL, NULL, 8, NULL, 4, 100, 0, 0, 0.1f, 0, NULL) ==
+        PKV_EUNSUPPORTED);
   if (failures) return 1;
   printf("c abi consumer ok\n");
   return 0;

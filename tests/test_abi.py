@@ -159,55 +159,39 @@ def test_quant_argument_errors_before_any_launch():
         -(-3 * 4 // 256) * 256 + -(-(4 + 16) * 8 * 2 * 4 // 256) * 256 + (4 + 16) * 8 * 128 * 4)
 
 
-def test_prefill_quant_workspace_and_errors():
-    """8-bit prefill: the workspace holds two 16-bit staging pools, their
-    scales and a staging table (each 256-byte aligned); argument errors
-    return before anything is enqueued."""
+def test_prefill_quant_errors():
+    """8-bit prefill needs no workspace (its codes are widened in the
+    kernel); argument errors return before anything is enqueued. The mixed
+    call over 8-bit pools takes the decode workspace only."""
     P = ctypes.c_void_p
-    up = lambda x: -(-x // 256) * 256
     gi8 = geo(dt=pkv.PKV_I8)
     gfp8 = geo(nb=100, B=32, H=8, Hkv=2, D=64, dt=pkv.PKV_FP8)
-    for g, S, L in ((gi8, 8, 2560), (gi8, 1, 1), (gfp8, 3, 1000)):
-        blocks = S * -(-L // g.block_size)
-        want = (2 * up(blocks * g.block_size * g.num_kv_heads * g.head_dim * 2) +
-                2 * up(blocks * g.num_kv_heads * g.block_size * 4) + up(blocks * 4))
-        assert pkv.LIB.paged_attn_prefill_quant_workspace_bytes(ctypes.byref(g), S, L) == want
-    assert pkv.LIB.paged_attn_prefill_quant_workspace_bytes(ctypes.byref(geo()), 8, 2560) == 0  # 16-bit pool
-    assert pkv.LIB.paged_attn_prefill_quant_workspace_bytes(ctypes.byref(gi8), 0, 100) == 0
-    need = pkv.LIB.paged_attn_prefill_quant_workspace_bytes(ctypes.byref(gi8), 2, 100)
 
-    def pq(g, q_dtype=pkv.PKV_BF16, ks=P(1), ws=P(4096), wsb=need, S=2, max_q=4, mcl=100, mb=8, H=None):
+    def pq(g, q_dtype=pkv.PKV_BF16, ks=P(1), S=2, max_q=4, mcl=100, mb=8, H=None):
         if H is not None:
             g = geo(H=H, Hkv=g.num_kv_heads, dt=g.kv_dtype)
         return pkv.LIB.paged_attn_prefill_quant(ctypes.byref(g), P(1), None, P(1), q_dtype, P(1), P(1), P(1), ks,
-                                                P(1), P(1), mb, P(1), S, max_q, mcl, 0, 0, 0.1, ws, wsb, None)
+                                                P(1), P(1), mb, P(1), S, max_q, mcl, 0, 0, 0.1, None)
     assert pq(geo()) == pkv.PKV_EUNSUPPORTED                       # not an 8-bit pool
     assert pq(gi8, q_dtype=pkv.PKV_F32) == pkv.PKV_EUNSUPPORTED    # query type
     assert pq(gi8, ks=None) == pkv.PKV_EINVAL                      # missing scales
     assert pq(gi8, H=24) == pkv.PKV_EUNSUPPORTED                   # 3 query heads per kv head
-    assert pq(gi8, ws=None) == pkv.PKV_EWORKSPACE
-    assert pq(gi8, wsb=need - 1) == pkv.PKV_EWORKSPACE
-    assert pq(gi8, ws=P(4104)) == pkv.PKV_EWORKSPACE               # not 16-byte aligned
     assert pq(gi8, mcl=129) == pkv.PKV_EINVAL                      # beyond the table's 8 blocks
     assert pq(gi8, max_q=101) == pkv.PKV_EINVAL                    # chunk longer than any context
+    assert pq(gfp8, mcl=257) == pkv.PKV_EINVAL
     assert pq(gi8, S=0) == pkv.PKV_OK
     assert pq(gi8, max_q=0) == pkv.PKV_OK
-    # mixed batches over 8-bit pools: decode workspace (256-aligned) + staging
-    for g, S, L in ((gi8, 8, 2560), (gfp8, 3, 1000), (geo(H=64, Hkv=8, dt=pkv.PKV_I8), 4, 300)):
-        d = pkv.LIB.paged_attn_decode_workspace_bytes(ctypes.byref(g), S, L, 0, 0, 0)
-        p = pkv.LIB.paged_attn_prefill_quant_workspace_bytes(ctypes.byref(g), S, L)
-        assert pkv.LIB.paged_attn_mixed_quant_workspace_bytes(ctypes.byref(g), S, L, 0, 0, 0) == up(d) + p
-    assert pkv.LIB.paged_attn_mixed_quant_workspace_bytes(ctypes.byref(geo()), 8, 2560, 0, 0, 0) == 0
-    mneed = pkv.LIB.paged_attn_mixed_quant_workspace_bytes(ctypes.byref(gi8), 2, 100, 0, 0, 0)
+    dneed = pkv.LIB.paged_attn_decode_workspace_bytes(ctypes.byref(gi8), 2, 100, 0, 0, 0)
 
-    def mq(g, q_dtype=pkv.PKV_BF16, ks=P(1), ws=P(4096), wsb=mneed, S=2, max_q=4, mcl=100):
+    def mq(g, q_dtype=pkv.PKV_BF16, ks=P(1), ws=P(4096), wsb=dneed, S=2, max_q=4, mcl=100):
         return pkv.LIB.paged_attn_mixed_quant(ctypes.byref(g), P(1), None, P(1), q_dtype, P(1), P(1), P(1), ks,
                                               P(1), P(1), 8, P(1), S, max_q, mcl, 0, 0, 0.1, 0, ws, wsb, None)
     assert mq(geo()) == pkv.PKV_EUNSUPPORTED                       # not an 8-bit pool
     assert mq(gi8, q_dtype=pkv.PKV_F32) == pkv.PKV_EUNSUPPORTED
     assert mq(gi8, ks=None) == pkv.PKV_EINVAL
     assert mq(gi8, ws=None) == pkv.PKV_EWORKSPACE
-    assert mq(gi8, wsb=mneed - 1) == pkv.PKV_EWORKSPACE            # staging part short: refused before any launch
+    assert mq(gi8, wsb=dneed - 1) == pkv.PKV_EWORKSPACE
+    assert mq(gi8, ws=P(4104)) == pkv.PKV_EWORKSPACE               # not 16-byte aligned
     assert mq(gi8, mcl=129) == pkv.PKV_EINVAL
     assert mq(gi8, S=0) == pkv.PKV_OK
 

@@ -519,7 +519,7 @@ def test_debug_mode_checks_device_content(lib):
 def test_graph_replay_matches_eager(lib, kind):
     """The step's calls captured in a HIP graph: every replay, with eager work
     and synchronisations between replays, gives the eager result bit for bit
-    (16-bit pages, and 8-bit pages with their write, widening and prefill)."""
+    (16-bit pages, and 8-bit pages with their write and prefill)."""
     pkv, session = lib
     note(f"graph replay {kind}")
     kind, _, fmt = kind.partition("-")
