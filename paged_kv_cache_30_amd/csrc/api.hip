@@ -68,21 +68,6 @@ struct DecodeSplit {
   size_t total() const { return cum_bytes + ml_bytes + o_bytes; }
 };
 
-// The geometry the decode kernels run: 8-bit pools with 8 query heads per
-// kv head run as two groups of 4 query heads over each pool kv head (the
-// 8-bit kernels' registers hold 4 heads' work), so the kernels see twice the
-// kv heads and read pool kv head g >> 1 for their kv head g (*kv_shift = 1).
-// Every other geometry runs as it is (*kv_shift = 0).
-pkv_geometry_t decode_view(const pkv_geometry_t* g, int* kv_shift) {
-  pkv_geometry_t v = *g;
-  *kv_shift = 0;
-  if (is_quant(g->kv_dtype) && g->num_kv_heads > 0 && g->num_heads == 8 * g->num_kv_heads) {
-    v.num_kv_heads = 2 * g->num_kv_heads;
-    *kv_shift = 1;
-  }
-  return v;
-}
-
 int decode_split(const pkv_geometry_t* g, int num_seqs, int max_context_len, int window, int sinks,
                  int num_workers, DecodeSplit* out) {
   if (num_workers < 0) return PKV_EINVAL;
@@ -126,10 +111,8 @@ int paged_kv_write(const pkv_geometry_t* geom, void* k_pool, void* v_pool, const
 int32_t paged_attn_decode_workers(const pkv_geometry_t* geom, int32_t num_seqs, int32_t max_context_len,
                                   int32_t window, int32_t num_sinks) {
   if (check_geometry(geom) || num_seqs < 0 || max_context_len < 0 || window < 0 || num_sinks < 0) return 0;
-  int shift;
-  const pkv_geometry_t view = decode_view(geom, &shift);
   DecodeSplit sp;
-  if (decode_split(&view, num_seqs, max_context_len, window, window > 0 ? num_sinks : 0, 0, &sp)) return 0;
+  if (decode_split(geom, num_seqs, max_context_len, window, window > 0 ? num_sinks : 0, 0, &sp)) return 0;
   return sp.workers;
 }
 
@@ -137,10 +120,8 @@ size_t paged_attn_decode_workspace_bytes(const pkv_geometry_t* geom, int32_t num
                                          int32_t max_context_len, int32_t window, int32_t num_sinks,
                                          int32_t num_workers) {
   if (check_geometry(geom) || num_seqs <= 0 || max_context_len < 0 || window < 0 || num_sinks < 0) return 0;
-  int shift;
-  const pkv_geometry_t view = decode_view(geom, &shift);
   DecodeSplit sp;
-  if (decode_split(&view, num_seqs, max_context_len, window, window > 0 ? num_sinks : 0, num_workers, &sp))
+  if (decode_split(geom, num_seqs, max_context_len, window, window > 0 ? num_sinks : 0, num_workers, &sp))
     return 0;
   return sp.total();
 }
@@ -171,8 +152,7 @@ int decode_common(const pkv_geometry_t* geom, float* out, float* lse, const void
   if (num_seqs == 0) return PKV_OK;
   if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens) return PKV_EINVAL;
   if (is_quant(geom->kv_dtype) && (!k_scale || !v_scale)) return PKV_EINVAL;
-  int kv_shift;
-  const pkv_geometry_t view = decode_view(geom, &kv_shift);
+  const pkv_geometry_t& view = *geom;
   const int G = view.num_heads / view.num_kv_heads;
   if (!pkv::decode_supported(view.kv_dtype, q_dtype, view.head_dim, view.block_size, G))
     return PKV_EUNSUPPORTED;
@@ -187,7 +167,6 @@ int decode_common(const pkv_geometry_t* geom, float* out, float* lse, const void
                     max_blocks_per_seq, view.num_blocks, window, view.kv_dtype, max_context_len,
                     sp.workers, scale, num_sinks, nullptr, slots.full_start, slots.slot_tables,
                     slots.num_slots, slots.max_slot_blocks};
-  a.kv_shift = kv_shift;
   return hip_status(pkv::launch_decode(a, (hipStream_t)stream));
 }
 
@@ -463,8 +442,7 @@ int paged_attn_mixed_quant(const pkv_geometry_t* geom, float* out, float* lse, c
   if (!out || !q || !q_start || !k_pool || !v_pool || !k_scale || !v_scale || !block_tables || !context_lens)
     return PKV_EINVAL;
   const int G = geom->num_heads / geom->num_kv_heads;
-  int kv_shift;
-  const pkv_geometry_t view = decode_view(geom, &kv_shift);
+  const pkv_geometry_t& view = *geom;
   if (!pkv::prefill_supported(q_dtype, geom->head_dim, geom->block_size, G) ||
       !pkv::decode_supported(view.kv_dtype, q_dtype, view.head_dim, view.block_size,
                              view.num_heads / view.num_kv_heads))
@@ -479,7 +457,6 @@ int paged_attn_mixed_quant(const pkv_geometry_t* geom, float* out, float* lse, c
                      num_seqs, view.num_heads, view.num_kv_heads, view.head_dim, view.block_size,
                      max_blocks_per_seq, view.num_blocks, window, view.kv_dtype, max_context_len,
                      sp.workers, scale, num_sinks, q_start};
-  da.kv_shift = kv_shift;
   st = hip_status(pkv::launch_decode(da, (hipStream_t)stream));
   if (st || max_q_len < 2) return st;
   return prefill_quant_common(geom, out, lse, q, q_dtype, q_start, k_pool, v_pool, k_scale, v_scale, block_tables,

@@ -152,6 +152,11 @@ template <int N> __device__ __forceinline__ float group_max(float x) {
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
+// An int32 array in the constant address space: uniform loads from it become
+// scalar loads, which are counted apart from vector memory operations, so
+// waiting for one never waits for the vector loads issued before it.
+typedef const __attribute__((address_space(4))) int32_t* ctab_t;
+
 __device__ __forceinline__ u32x4 load16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 
 // 16-byte load of data read once (K/V pages in decode).

@@ -33,6 +33,8 @@
 //  Positions outside [lo, L) (the partial first block of a window, the
 //  partial last block) are removed by selection, never by multiplying with
 //  zero, so whatever unused slots hold cannot leak in.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -86,11 +88,7 @@ struct DecodeShape {
   // Pieces of a K/V row per lane: with 4 or more query heads per kv head the
   // per-position softmax work, done redundantly by every lane of a row, is
   // halved by giving each lane two pieces (fewer lanes per row).
-  // (Not with scores on the matrix cores, see MQK: the exchange that hands
-  // each lane its row's scores makes the softmax cheap, and one piece per
-  // lane halves the output registers.)
-  static constexpr bool MQK8 = !T::QUANT && EB == 2 && G >= 8 && D == 128;
-  static constexpr int PIECES = (G >= 4 && D * EB / 16 >= 16 && !MQK8) ? 2 : 1;
+  static constexpr int PIECES = (G >= 4 && D * EB / 16 >= 16) ? 2 : 1;
   static constexpr int LPR = D * EB / 16 / PIECES;     // lanes per K/V row
   static constexpr int RPL = 64 / LPR;                 // rows per step
   static constexpr int STEPS = B / RPL;                // steps per block
@@ -103,16 +101,6 @@ struct DecodeShape {
   static constexpr int CHUNK = RPL * CSTEPS;           // slots per chunk
   static constexpr int CPB = B / CHUNK;                // chunks per block
   static_assert(LPR >= 4 && LPR <= 32 && B % CHUNK == 0, "shape");
-  // Scores on the matrix cores: 16-bit pools with 8 query heads per kv
-  // head, in chunks of 16 positions. The chunk's K registers (CSTEPS *
-  // PIECES = D / 32 per lane) then hold exactly the D / 32 B operands of a
-  // 16x16x32 MFMA chain. With 4 heads the dot products on the vector ALU
-  // are cheaper than the chain's latency and the exchange (measured).
-  static constexpr bool MQK = MQK8 && CHUNK == 16;
-  // Workgroups per CU the register budget is set for: two for the matrix-
-  // core instances (two wavefronts per SIMD, at the cost of a few spilled
-  // registers), else whatever the compiler needs.
-  static constexpr int MIN_WG = MQK ? 2 : 1;
 };
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -236,8 +224,7 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(DecodeArgs a)
 // T: storage type of the pools; Q: type of q (T itself, or fp16/bf16 for the
 // 8-bit pools, whose rows also carry a scale each).
 template <class T, class Q, int D, int B, int G>
-__global__ __launch_bounds__(kThreads, (DecodeShape<T, D, B, G>::MIN_WG)) void decode_split_kernel(DecodeArgs a,
-                                                                                                float scale_log2) {
+__global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, float scale_log2) {
   using Sh = DecodeShape<T, D, B, G>;
   constexpr int E = Sh::E, LPR = Sh::LPR, RPL = Sh::RPL, CSTEPS = Sh::CSTEPS, CHUNK = Sh::CHUNK,
                 CPB = Sh::CPB, EB = Sh::EB, PC = Sh::PIECES;
@@ -247,8 +234,6 @@ __global__ __launch_bounds__(kThreads, (DecodeShape<T, D, B, G>::MIN_WG)) void d
   constexpr int QW = E * QB / 16;    // 16-byte words of q per piece
   constexpr float BIAS = T::BIAS;
   static_assert(QU || (QB == EB && QW == 1), "q has the pools' type unless the pools are 8-bit");
-  constexpr bool MQK = Sh::MQK;
-  constexpr int KS = D / 32;  // MFMA k-steps over the head dim (matrix-core scores)
 
   const int lane = threadIdx.x & 63;
   // Prefix of attended blocks, in one of three places: batches of fewer than
@@ -315,8 +300,7 @@ __global__ __launch_bounds__(kThreads, (DecodeShape<T, D, B, G>::MIN_WG)) void d
     s = s_lo;
   }
 
-  const int Hkv_pool = Hkv >> a.kv_shift;  // kv heads the pools hold
-  const size_t row_stride = (size_t)Hkv_pool * D * EB;  // bytes between slots
+  const size_t row_stride = (size_t)Hkv * D * EB;  // bytes between slots
   const size_t blk_stride = row_stride * B;
   float m[G], l[G], o[G][PC * E];
 
@@ -339,27 +323,13 @@ __global__ __launch_bounds__(kThreads, (DecodeShape<T, D, B, G>::MIN_WG)) void d
 
     const char* qb = (const char*)a.q + ((size_t)(q_row(a, s) * H + g * G) * D + c * E) * QB;
     u32x4 qv[G][PC][QW];
-    // Matrix-core scores: A operand = q of the group (row l % 16 = head,
-    // zero beyond G), dims 8 (l / 16) + 32 ks.
-    u32x4 qm[KS];
-    if constexpr (MQK) {
-      const int hh = lane & 15;  // rows past the group read head G - 1 and are zeroed
-      const char* qa =
-          (const char*)a.q + ((size_t)(q_row(a, s) * H + g * G + min(hh, G - 1)) * D + 8 * (lane >> 4)) * QB;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const u32x4 v = load16(qa + (size_t)ks * 32 * QB);
-        qm[ks] = hh < G ? v : u32x4{0, 0, 0, 0};
-      }
-    } else {
+    for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int h = 0; h < G; ++h)
+      for (int pc = 0; pc < PC; ++pc)
 #pragma unroll
-        for (int pc = 0; pc < PC; ++pc)
-#pragma unroll
-          for (int qw = 0; qw < QW; ++qw)
-            qv[h][pc][qw] = load16(qb + (size_t)h * D * QB + (size_t)pc * LPR * E * QB + qw * 16);
-    }
+        for (int qw = 0; qw < QW; ++qw)
+          qv[h][pc][qw] = load16(qb + (size_t)h * D * QB + (size_t)pc * LPR * E * QB + qw * 16);
     // INT8: the sum of this lane's q values, for the BIAS correction of its
     // partial dot products; lvb: the running sum of the V weights (same role).
     float qsum[G], lvb[G];
@@ -383,13 +353,8 @@ __global__ __launch_bounds__(kThreads, (DecodeShape<T, D, B, G>::MIN_WG)) void d
           }
       }
     }
-    const int gp = g >> a.kv_shift;  // pool kv head
-    const size_t lane_off = (size_t)gp * D * EB + (size_t)c * 16 + (size_t)r * row_stride;
-    // K lanes for matrix-core scores: position l % 16 of the chunk, dims
-    // 8 (l / 16) + 32 ks (16 bytes at 64 ks bytes further per k-step).
-    const char* kbase = (const char*)a.k_pool +
-                        (MQK ? (size_t)gp * D * EB + (size_t)(lane & 15) * row_stride + (size_t)(lane >> 4) * 16
-                             : lane_off);
+    const size_t lane_off = (size_t)g * D * EB + (size_t)c * 16 + (size_t)r * row_stride;
+    const char* kbase = (const char*)a.k_pool + lane_off;
     const char* vbase = (const char*)a.v_pool + lane_off;
 
     // Loads of chunk k of the segment; false when its table entry is out of
@@ -402,25 +367,18 @@ __global__ __launch_bounds__(kThreads, (DecodeShape<T, D, B, G>::MIN_WG)) void d
       if (pb < 0 || pb >= a.nb) return false;
       const size_t off = (size_t)pb * blk_stride + (size_t)sub * CHUNK * row_stride;
       if constexpr (QU) {  // this lane's row scales, [NB, Hkv, B]
-        const size_t sidx = ((size_t)pb * Hkv_pool + gp) * B + sub * CHUNK + r;
+        const size_t sidx = ((size_t)pb * Hkv + g) * B + sub * CHUNK + r;
 #pragma unroll
         for (int j = 0; j < CSTEPS; ++j) {
           ks[j] = a.k_scale[sidx + j * RPL];
           vs[j] = a.v_scale[sidx + j * RPL];
         }
       }
-      if constexpr (MQK) {  // k-step ks = j * PC + pc
 #pragma unroll
-        for (int j = 0; j < CSTEPS; ++j)
+      for (int j = 0; j < CSTEPS; ++j)
 #pragma unroll
-          for (int pc = 0; pc < PC; ++pc) kr[j][pc] = load_stream(kbase + off + (size_t)(j * PC + pc) * 32 * EB);
-      } else {
-#pragma unroll
-        for (int j = 0; j < CSTEPS; ++j)
-#pragma unroll
-          for (int pc = 0; pc < PC; ++pc)
-            kr[j][pc] = load_stream(kbase + off + (size_t)j * RPL * row_stride + pc * PSTRIDE);
-      }
+        for (int pc = 0; pc < PC; ++pc)
+          kr[j][pc] = load_stream(kbase + off + (size_t)j * RPL * row_stride + pc * PSTRIDE);
 #pragma unroll
       for (int j = 0; j < CSTEPS; ++j)
 #pragma unroll
@@ -439,26 +397,6 @@ __global__ __launch_bounds__(kThreads, (DecodeShape<T, D, B, G>::MIN_WG)) void d
       const bool pre = b_first + bi < at.sb;
       const bool full = pre ? t0 + CHUNK <= at.plim : (t0 >= lo || t0 + CHUNK <= a.sinks) && t0 + CHUNK <= L;
       float sc[CSTEPS][G];
-      if constexpr (MQK) {
-        // C[head][position] of the chunk: lane l holds heads 4 (l / 16) + i
-        // of position l % 16. Each lane then takes the scores of its row
-        // (position j * RPL + r) from lane position + 16 (h / 4).
-        f32x4_t cm = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) cm = mma16<T>(qm[ks], kr[ks / PC][ks % PC], cm);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) cm[i] *= scale_log2;
-        // (The element is copied to a scalar first: a bit cast of a vector
-        // element in place reads element 0 whatever the index.)
-        int cv[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) cv[i] = __float_as_int((float)cm[i]);
-#pragma unroll
-        for (int j = 0; j < CSTEPS; ++j)
-#pragma unroll
-          for (int h = 0; h < G; ++h)
-            sc[j][h] = __int_as_float(__builtin_amdgcn_ds_bpermute(4 * (j * RPL + r + 16 * (h >> 2)), cv[h & 3]));
-      } else {
 #pragma unroll
       for (int j = 0; j < CSTEPS; ++j) {
 #pragma unroll
@@ -475,7 +413,6 @@ __global__ __launch_bounds__(kThreads, (DecodeShape<T, D, B, G>::MIN_WG)) void d
             sc[j][h] = group_sum<LPR>(x) * scale_log2;
           }
         }
-      }
       }
       if (!full) {
 #pragma unroll
@@ -642,6 +579,427 @@ __global__ __launch_bounds__(kThreads, (DecodeShape<T, D, B, G>::MIN_WG)) void d
   }
 }
 
+// ---------------------------------------------------------------------------
+// Decode on the matrix cores, for groups of G >= 4 query heads per kv head.
+//
+// Same work split, partial format and merge as decode_split_kernel; inside a
+// segment every 16-position chunk of the kv head's pages is two small dense
+// products with the group's query heads as the 16 columns (zero beyond G):
+//   S^T (16 positions x 16 heads) = K_chunk . Q^T        D/32 x v_mfma_f32_16x16x32
+//   O^T (D x 16 heads)           += V_chunk^T . P^T      D/16 x 2 x v_mfma_f32_16x16x16
+// Lane l works for head h = l % 16 and lane group g4 = l / 16: it receives
+// the scores of positions 4 g4 + i (i = 0..3) of the chunk, supplies their
+// weights as the B operand of the second product, and accumulates outputs
+// of dims 16 dt + 4 g4 + i. The online softmax is thus per lane, apart from
+// the chunk maximum (two lane swaps). K rows go from HBM straight into the
+// A operand registers: lane l loads position l % 16, dims [g4 D/4, (g4+1) D/4),
+// and q is read in the same dim order (a contraction may take its terms in
+// any order as long as both operands agree). V rows are written to a
+// per-wavefront LDS tile and read back transposed (ds_read_b64_tr_b16: lane
+// l gets dim 16 dt + l % 16 of positions 4 g4 .. 4 g4 + 3, the A operand).
+// Each weight enters P.V as two 16-bit values hi + lo (two products), about
+// 16 significant bits, while the normaliser sums the fp32 weights.
+// 8-bit pools: codes widened in registers (exact) to q's type for K and to
+// bf16 for V; the K row scale multiplies the score and the V row scale the
+// weight. The reference maximum lags as in the prefill: it moves only when
+// some head's chunk maximum exceeds it by more than 2^8.
+
+// One v_mfma_f32_16x16x16 of the 16-bit type: lane l supplies A[l % 16][4 (l / 16) + e]
+// and B[4 (l / 16) + e][l % 16] (e = 0..3) and receives C[4 (l / 16) + i][l % 16].
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+template <class T> __device__ __forceinline__ f32x4_t mma16k16(const u32x2_t& a, const u32x2_t& b, f32x4_t c);
+template <> __device__ __forceinline__ f32x4_t mma16k16<BF16T>(const u32x2_t& a, const u32x2_t& b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, a), __builtin_bit_cast(s16x4_t, b), c,
+                                                   0, 0, 0);
+}
+template <> __device__ __forceinline__ f32x4_t mma16k16<F16T>(const u32x2_t& a, const u32x2_t& b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, a), __builtin_bit_cast(f16x4_t, b), c, 0,
+                                               0, 0);
+}
+// The two values of a packed 16-bit pair, as fp32.
+template <class P> __device__ __forceinline__ void unpack_pair(uint32_t h, float& a, float& b);
+template <> __device__ __forceinline__ void unpack_pair<BF16T>(uint32_t h, float& a, float& b) {
+  a = as_f(h << 16);
+  b = as_f(h & 0xffff0000u);
+}
+template <> __device__ __forceinline__ void unpack_pair<F16T>(uint32_t h, float& a, float& b) {
+  const f16x2 x = as_h2(h);
+  a = (float)x.x;
+  b = (float)x.y;
+}
+// a and b as hi + lo pairs of the 16-bit type (a - hi is exact in fp32).
+template <class P> __device__ __forceinline__ void split_pair(float a, float b, uint32_t& hi, uint32_t& lo) {
+  hi = pack_pair<P>(a, b);
+  float ah, bh;
+  unpack_pair<P>(hi, ah, bh);
+  lo = pack_pair<P>(a - ah, b - bh);
+}
+// Eight 8-bit codes (two words) as eight values of the 16-bit type P (exact).
+template <class T, class P> __device__ __forceinline__ u32x4 widen8(uint32_t w0, uint32_t w1) {
+  float f[8];
+  codes4_to_f32<T>(w0, f);
+  codes4_to_f32<T>(w1, f + 4);
+  u32x4 r;
+  r.x = pack_pair<P>(f[0] - T::BIAS, f[1] - T::BIAS);
+  r.y = pack_pair<P>(f[2] - T::BIAS, f[3] - T::BIAS);
+  r.z = pack_pair<P>(f[4] - T::BIAS, f[5] - T::BIAS);
+  r.w = pack_pair<P>(f[6] - T::BIAS, f[7] - T::BIAS);
+  return r;
+}
+// LDS access as inline asm (the compiler does not see the transposed read's
+// dependence on the stores; both stay in program order as volatile asm and
+// the LDS executes a wavefront's instructions in order).
+__device__ __forceinline__ void lds_store16(uint32_t addr, const u32x4& x) {
+  asm volatile("ds_write_b128 %0, %1" ::"v"(addr), "v"(x) : "memory");
+}
+__device__ __forceinline__ u32x2_t lds_read_tr16(uint32_t addr) {
+  u32x2_t r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(addr));
+  return r;
+}
+__device__ __forceinline__ void lds_wait_all() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void settle2(u32x2_t& x) { asm volatile("" : "+v"(x)); }
+// Maximum and sum over the four lanes l % 16 + 16 j (j = 0..3).
+__device__ __forceinline__ float max_over_groups(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float sum_over_groups(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+#ifndef PKV_MMA_KLAYOUT
+#define PKV_MMA_KLAYOUT 1
+#endif
+#ifndef PKV_MMA_KNT
+#define PKV_MMA_KNT 0
+#endif
+#ifndef PKV_MMA_VNT
+#define PKV_MMA_VNT 1
+#endif
+// Page loads of the matrix-core kernel. The K rows of a chunk are read by
+// several load instructions, each taking part of every cache line: as
+// ordinary loads (no streaming hint) the lines stay in the L1 cache for the
+// instructions after the first (the hint cost a quarter of the bandwidth).
+__device__ __forceinline__ u32x4 load_k(const void* p) {
+#if PKV_MMA_KNT
+  return load_stream(p);
+#else
+  return load16(p);
+#endif
+}
+__device__ __forceinline__ u32x4 load_v(const void* p) {
+#if PKV_MMA_VNT
+  return load_stream(p);
+#else
+  return load16(p);
+#endif
+}
+
+// Byte offset of logical 16-byte unit u of row r in a V tile of D 16-bit
+// values per row: units XOR-swizzled by row so that the transposed reads of
+// 16 rows x 32 bytes spread over all banks.
+template <int D> __device__ __forceinline__ uint32_t vtile_off(int r, int u) {
+  constexpr int RB = D * 2;
+  const int sw = D == 128 ? 2 * (r & 7) : 2 * ((r >> 1) & 3);
+  return (uint32_t)(r * RB + 16 * (u ^ sw));
+}
+
+template <class T, class Q, int D, int B, int G>
+__global__ __launch_bounds__(kThreads, 2) void decode_mma_kernel(DecodeArgs a, float scale_log2) {
+  constexpr bool QU = T::QUANT;
+  constexpr int EB = T::BYTES;
+  using P = typename std::conditional<QU, BF16T, T>::type;  // type of the P.V product
+  constexpr int CH = 16;                 // positions per chunk
+  constexpr int CPB = B / CH;            // chunks per block
+  constexpr int KS = D / 32;             // k-steps of the score product
+  constexpr int DT = D / 16;             // 16-dim tiles of the output
+  constexpr int DG = D / 4;              // dims per lane group (score product)
+  constexpr int NKL = DG * EB / 16;      // K loads per lane and chunk
+  constexpr int UV = D * EB / 16;        // 16-byte units of a V row in the pool
+  constexpr int RV = 64 / UV;            // V rows per wavefront load
+  constexpr int NVL = CH / RV;           // V loads per lane and chunk
+  static_assert(G >= 1 && G <= 16 && (D == 64 || D == 128) && B % CH == 0, "shape");
+
+  __shared__ int32_t cum_sh[kLdsSeqs + 1];
+  __shared__ __attribute__((aligned(16))) uint16_t vt_sh[kWaves][CH * D];
+
+  const int lane = threadIdx.x & 63;
+  const int hh = lane & 15;   // head column
+  const int g4 = lane >> 4;   // lane group
+  const int wv = uniform(threadIdx.x >> 6);
+  const uint32_t vt = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)&vt_sh[wv][0];
+
+  // Prefix of attended blocks: in a register (batches under 64 sequences),
+  // in LDS (up to kLdsSeqs), or in the workspace (plan launch).
+  const bool in_reg = a.S < 64;
+  const int32_t* cum_mem = a.ws_cum;
+  int cum_reg = 0, len_reg = 0;
+  if (in_reg) {
+    int v = 0;
+    if (lane < a.S) {
+      len_reg = decode_len(a, lane);
+      v = attended(a, lane, len_reg, B).nblk;
+    }
+    int x = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(x, off, 64);
+      if (lane >= off) x += y;
+    }
+    cum_reg = x - v;
+    if (blockIdx.x == 0 && threadIdx.x < 64 && lane <= a.S) a.ws_cum[lane] = cum_reg;
+  } else if (a.S <= kLdsSeqs) {
+    prefix_blocks<kThreads>(a, cum_sh);
+    cum_mem = cum_sh;
+    if (blockIdx.x == 0)
+      for (int i = threadIdx.x; i <= a.S; i += kThreads) a.ws_cum[i] = cum_sh[i];
+  }
+  auto cum = [&](int i) -> int { return in_reg ? __builtin_amdgcn_readlane(cum_reg, i) : cum_mem[i]; };
+  auto len_of = [&](int i) -> int { return in_reg ? __builtin_amdgcn_readlane(len_reg, i) : decode_len(a, i); };
+
+  const int w = blockIdx.x * kWaves + wv;
+  const int Hkv = a.Hkv, H = Hkv * G;
+  const long long total = (long long)Hkv * cum(a.S);
+  const long long nw = total < a.n_workers ? total : a.n_workers;
+  if (w >= nw) return;
+  const long long start = (long long)w * total / nw;
+  const long long end = (long long)(w + 1) * total / nw;
+  int s;
+  if (in_reg) {
+    const unsigned long long msk = __ballot(lane < a.S && (long long)Hkv * cum_reg <= start);
+    s = 63 - __builtin_clzll(msk);
+  } else {
+    int s_lo = 0, s_hi = a.S;
+    while (s_hi - s_lo > 1) {
+      const int step = (s_hi - s_lo + 63) / 64;
+      const int probe = s_lo + lane * step;
+      const bool le = probe < s_hi && (long long)Hkv * cum_mem[probe] <= start;
+      const unsigned long long msk = __ballot(le);
+      const int k = 63 - __builtin_clzll(msk);
+      s_lo = s_lo + k * step;
+      s_hi = min(s_hi, s_lo + step);
+    }
+    s = s_lo;
+  }
+
+  const size_t row_stride = (size_t)Hkv * D * EB;
+  const size_t blk_stride = row_stride * B;
+  // V load j of this lane: row RV j + lane / UV of the chunk, unit lane % UV.
+  const int v_row0 = lane / UV, v_unit = lane % UV;
+  // K operand of k-step ks: lane (hh, g4) holds dims kdim(ks) .. + 8 of
+  // position hh; K load j of the lane reads 16 bytes at byte kload_off(j) of
+  // the row. Each load instruction thus reads 64 consecutive bytes of each
+  // of 16 rows (16-bit: k-step j; 8-bit: k-steps 2j and 2j + 1).
+#if PKV_MMA_KLAYOUT
+  auto kload_off = [&](int j) -> uint32_t { return 64 * j + 16 * g4; };
+  auto kdim = [&](int ks) -> int { return EB == 2 ? 32 * ks + 8 * g4 : 64 * (ks >> 1) + 16 * g4 + 8 * (ks & 1); };
+#else
+  auto kload_off = [&](int j) -> uint32_t { return g4 * DG * EB + 16 * j; };
+  auto kdim = [&](int ks) -> int { return g4 * DG + 8 * ks; };
+#endif
+
+  for (long long pos = start; pos < end;) {
+    while ((long long)Hkv * cum(s + 1) <= pos) ++s;
+    s = uniform(s);
+    const int c0 = uniform(cum(s));
+    const int nblk = uniform(cum(s + 1)) - c0;
+    const long long rel = pos - (long long)Hkv * c0;
+    const int g = uniform((int)(rel / nblk));
+    const int b_first = uniform((int)(rel - (long long)g * nblk));
+    const long long seg_end = min(end, (long long)Hkv * c0 + (long long)(g + 1) * nblk);
+    const int n = uniform((int)(seg_end - pos));
+
+    Attended at = attended(a, s, len_of(s), B);
+    at.uniformize();
+    const int L = at.L, lo = at.lo;
+    // Table entry of attended block i of the list (i uniform): a scalar load,
+    // counted apart from the vector loads of the pages, so that waiting for
+    // an entry never waits for pages in flight.
+    const ctab_t ptab_c = (ctab_t)at.ptab;
+    const ctab_t trow_c = (ctab_t)(a.tables + (size_t)s * a.mb);
+    auto entry = [&](int i) -> int {
+      i = uniform(i);
+      return i < at.sb ? ptab_c[i] : trow_c[at.wb0 + (i - at.sb)];
+    };
+
+    // B operand of the score product: q of head g G + hh (zero beyond G),
+    // dims kdim(ks) + e, the dims the K operand of k-step ks holds.
+    u32x4 qm[KS];
+    {
+      const char* qa = (const char*)a.q + ((size_t)(q_row(a, s) * H + g * G + min(hh, G - 1)) * D) * Q::BYTES;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const u32x4 v = load16(qa + (size_t)kdim(ks) * Q::BYTES);
+        qm[ks] = hh < G ? v : u32x4{0, 0, 0, 0};
+      }
+    }
+    float m_ref = -INFINITY, l_run = 0.f;
+    f32x4_t o[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    const char* kbase = (const char*)a.k_pool + (size_t)g * D * EB + (size_t)hh * row_stride + kload_off(0);
+    const char* vbase =
+        (const char*)a.v_pool + (size_t)g * D * EB + (size_t)v_row0 * row_stride + (size_t)v_unit * 16;
+
+    // Loads of chunk min(k, last) of the segment, issued for k = 0, 1, 2, ...
+    // in order and without condition (past the end the last chunk is loaded
+    // again; a block out of range loads block 0 and the chunk is masked), so
+    // that every load is waited for only where its chunk is used. The next
+    // chunk's table entry is requested one chunk ahead.
+    const int nchunks = n * CPB;
+    int pb_next = entry(b_first);
+    auto issue = [&](int k, u32x4* kr, u32x4* vr, f32x4_t& ks4, f32x4_t& vs4) -> bool {
+      k = min(k, nchunks - 1);
+      const int bi = k / CPB;
+      const int sub = k - bi * CPB;
+      const int pb = pb_next;
+      const int bn = min(k + 1, nchunks - 1) / CPB;
+      pb_next = bn == bi ? pb : entry(b_first + bn);
+      const bool valid = pb >= 0 && pb < a.nb;
+      const size_t off = (size_t)(valid ? pb : 0) * blk_stride + (size_t)sub * CH * row_stride;
+#pragma unroll
+      for (int j = 0; j < NKL; ++j) kr[j] = load_k(kbase + off + (kload_off(j) - kload_off(0)));
+#pragma unroll
+      for (int j = 0; j < NVL; ++j) vr[j] = load_v(vbase + off + (size_t)j * RV * row_stride);
+      if constexpr (QU) {  // row scales of positions 4 g4 .. 4 g4 + 3, [NB, Hkv, B]
+        const size_t sidx = ((size_t)(valid ? pb : 0) * Hkv + g) * B + sub * CH + 4 * g4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          ks4[i] = a.k_scale[sidx + i];
+          vs4[i] = a.v_scale[sidx + i];
+        }
+      }
+      return valid;
+    };
+
+    auto process = [&](int k, bool valid, const u32x4* kr, const u32x4* vr, const f32x4_t& ks4,
+                       const f32x4_t& vs4) {
+      const int bi = k / CPB;
+      const int sub = k - bi * CPB;
+      const int t0 = at.block(b_first + bi) * B + sub * CH;
+      const bool pre = b_first + bi < at.sb;
+      const bool full =
+          valid && (pre ? t0 + CH <= at.plim : (t0 >= lo || t0 + CH <= a.sinks) && t0 + CH <= L);
+      auto attended_pos = [&](int t) {
+        return valid && (pre ? t < at.plim : (t >= lo || t < a.sinks) && t < L);
+      };
+      // V rows into the LDS tile as 16-bit values (rows of positions not
+      // attended as zeros: unused slots may hold anything).
+#pragma unroll
+      for (int j = 0; j < NVL; ++j) {
+        const int r = RV * j + v_row0;
+        const bool ok = full || attended_pos(t0 + r);
+        if constexpr (QU) {
+          u32x4 w0 = widen8<T, BF16T>(vr[j].x, vr[j].y), w1 = widen8<T, BF16T>(vr[j].z, vr[j].w);
+          if (!ok) w0 = w1 = u32x4{0, 0, 0, 0};
+          lds_store16(vt + vtile_off<D>(r, 2 * v_unit), w0);
+          lds_store16(vt + vtile_off<D>(r, 2 * v_unit + 1), w1);
+        } else {
+          lds_store16(vt + vtile_off<D>(r, v_unit), ok ? vr[j] : u32x4{0, 0, 0, 0});
+        }
+      }
+      // Scores of positions 4 g4 + i for head hh (base 2).
+      f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        u32x4 ka;
+        if constexpr (QU) {
+          const u32x4 c = kr[ks / 2];
+          ka = (ks & 1) ? widen8<T, Q>(c.z, c.w) : widen8<T, Q>(c.x, c.y);
+        } else {
+          ka = kr[ks];
+        }
+        sc = mma16<Q>(ka, qm[ks], sc);
+      }
+      float sv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float x = sc[i] * scale_log2;
+        if constexpr (QU) x *= ks4[i];
+        sv[i] = (full || attended_pos(t0 + 4 * g4 + i)) ? x : -INFINITY;
+      }
+      const float mx = max_over_groups(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])));
+      if (__any(mx > m_ref + 8.f)) {
+        const float mn = fmaxf(m_ref, mx);
+        const float alpha = __builtin_amdgcn_exp2f(m_ref - (mn == -INFINITY ? 0.f : mn));
+        l_run *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+        m_ref = mn;
+      }
+      const float ms = m_ref == -INFINITY ? 0.f : m_ref;
+      float p[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p[i] = __builtin_amdgcn_exp2f(sv[i] - ms);
+        l_run += p[i];
+        if constexpr (QU) p[i] = (full || sv[i] != -INFINITY) ? p[i] * vs4[i] : 0.f;
+      }
+      uint32_t h0, l0, h1, l1;
+      split_pair<P>(p[0], p[1], h0, l0);
+      split_pair<P>(p[2], p[3], h1, l1);
+      const u32x2_t whi = {h0, h1}, wlo = {l0, l1};
+      // V^T operands: row 4 g4 + hh / 4, dims 16 dt + 4 (hh % 4) .. + 4.
+      lds_wait_all();
+      u32x2_t va[DT];
+      const int tr_r = 4 * g4 + (hh >> 2);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        va[dt] = lds_read_tr16(vt + vtile_off<D>(tr_r, 2 * dt + ((hh & 3) >> 1)) + 8 * (hh & 1));
+      lds_wait_all();
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        settle2(va[dt]);
+        o[dt] = mma16k16<P>(va[dt], whi, o[dt]);
+        o[dt] = mma16k16<P>(va[dt], wlo, o[dt]);
+      }
+    };
+
+    // Two register sets: the next chunk's loads are in flight while the
+    // current chunk is processed.
+    u32x4 ka[NKL], va[NVL], kb[NKL], vb[NVL];
+    f32x4_t ksa, vsa, ksb, vsb;
+    bool oka = issue(0, ka, va, ksa, vsa);
+    for (int k = 0; k < nchunks; k += 2) {
+      const bool okb = issue(k + 1, kb, vb, ksb, vsb);
+      process(k, oka, ka, va, ksa, vsa);
+      oka = issue(k + 2, ka, va, ksa, vsa);
+      if (k + 1 < nchunks) process(k + 1, okb, kb, vb, ksb, vsb);
+    }
+
+    const float l_tot = sum_over_groups(l_run);
+    if (hh < G) {
+      const size_t orow = (size_t)q_row(a, s) * H + (size_t)g * G + hh;
+      if (b_first == 0 && n == nblk) {
+        // The whole segment: normalised output and log-sum-exp.
+        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+          *reinterpret_cast<float4*>(a.out + orow * D + 16 * dt + 4 * g4) =
+              make_float4(o[dt][0] * inv, o[dt][1] * inv, o[dt][2] * inv, o[dt][3] * inv);
+        if (a.lse && g4 == 0) a.lse[orow] = l_tot > 0.f ? (m_ref + __log2f(l_tot)) * kLn2 : -INFINITY;
+      } else {
+        const size_t slot = (size_t)w + (size_t)s * Hkv + g;
+        float* dst = a.ws_o + (slot * G + hh) * D + 4 * g4;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+          *reinterpret_cast<float4*>(dst + 16 * dt) = make_float4(o[dt][0], o[dt][1], o[dt][2], o[dt][3]);
+        if (g4 == 0) *reinterpret_cast<float2*>(a.ws_ml + (slot * G + hh) * 2) = make_float2(m_ref, l_tot);
+      }
+    }
+    pos = seg_end;
+  }
+}
+
 // Merge of the partials of one (sequence, kv head) by gridDim.z wavefronts,
 // each holding every gridDim.z-th group of 64 of the G x D outputs of its
 // query heads (one wavefront when there are many pairs, so that pairs with
@@ -749,8 +1107,25 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
   }
 }
 
+#ifndef PKV_MMA_MIN_G
+#define PKV_MMA_MIN_G 4
+#endif
+// Split kernel of an instance: the matrix-core one for 16-bit and 8-bit pools
+// with at least PKV_MMA_MIN_G query heads per kv head (8-bit pools with 8:
+// always), the vector-ALU one otherwise.
+template <class T, int G>
+constexpr bool use_mma() {
+  return T::BYTES <= 2 && (G >= PKV_MMA_MIN_G || (T::QUANT && G == 8));
+}
+
 template <class T, class Q, int D, int B, int G>
 struct DecodeKernels {
+  static constexpr auto split() {
+    if constexpr (use_mma<T, G>())
+      return decode_mma_kernel<T, Q, D, B, G>;
+    else
+      return decode_split_kernel<T, Q, D, B, G>;
+  }
   static hipError_t launch(const DecodeArgs& a, hipStream_t st) {
     hipError_t e;
     if (a.S > kLdsSeqs) {
@@ -759,8 +1134,7 @@ struct DecodeKernels {
       if (e != hipSuccess) return e;
     }
     const int grid = (a.n_workers + kWaves - 1) / kWaves;
-    hipLaunchKernelGGL((decode_split_kernel<T, Q, D, B, G>), dim3(grid), dim3(kThreads), 0, st, a,
-                       a.scale * kLog2e);
+    hipLaunchKernelGGL(split(), dim3(grid), dim3(kThreads), 0, st, a, a.scale * kLog2e);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     // Many (sequence, kv head) pairs: one wavefront each; few: one per 64
@@ -778,7 +1152,7 @@ struct DecodeKernels {
     static int cached = 0;
     if (!cached) {
       int n = 0;
-      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_split_kernel<T, Q, D, B, G>, kThreads, 0) !=
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, split(), kThreads, 0) !=
               hipSuccess ||
           n <= 0) {
         (void)hipGetLastError();
@@ -812,7 +1186,8 @@ static int instance_of(int dtype, int q_dtype) {
 }
 
 // Runtime (instance, head dim, block size, group size) -> template instance.
-// 8-bit pools are built for groups of up to 4 query heads.
+// 8-bit pools with 8 query heads per kv head run on the matrix-core kernel
+// only.
 template <template <class, class, int, int, int> class Op, class R, class... Args>
 static R dispatch(int inst, int D, int B, int G, R bad, const Args&... args) {
 #define PKV_G(T_, Q_, D_, B_)                               \
@@ -821,8 +1196,7 @@ static R dispatch(int inst, int D, int B, int G, R bad, const Args&... args) {
     case 2: return Op<T_, Q_, D_, B_, 2>::run(args...);     \
     case 4: return Op<T_, Q_, D_, B_, 4>::run(args...);     \
     case 8:                                                 \
-      if constexpr (!T_::QUANT) return Op<T_, Q_, D_, B_, 8>::run(args...); \
-      return bad;                                           \
+      return Op<T_, Q_, D_, B_, 8>::run(args...);           \
   }                                                         \
   return bad;
 #define PKV_B(T_, Q_, D_)                \
@@ -856,13 +1230,14 @@ bool decode_supported(int dtype, int q_dtype, int D, int B, int G) {
   const int inst = instance_of(dtype, q_dtype);
   if (inst < 0 || (D != 64 && D != 128) || (B != 16 && B != 32)) return false;
   if (G != 1 && G != 2 && G != 4 && G != 8) return false;
-  return dtype <= 2 || G <= 4;
+  return true;
 }
 
 // Automatic worker count: whole workgroups per compute unit (an uneven
 // spread leaves some units with more work); two per unit keep 128 KB of
 // loads in flight per unit (16 KB per wavefront), which covers HBM latency,
-// within what the unit holds at once.
+// within what the unit holds at once. 8-bit pages carry half the bytes per
+// chunk: three workgroups per unit measured best for them.
 int decode_auto_workers(int dtype, int q_dtype, int D, int B, int G) {
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
@@ -871,7 +1246,7 @@ int decode_auto_workers(int dtype, int q_dtype, int D, int B, int G) {
     cus = 256;
   }
   const int resident = dispatch<OccupancyOp, int>(instance_of(dtype, q_dtype), D, B, G, 2);
-  int per_cu = 2;
+  int per_cu = (dtype == 3 || dtype == 4) && G >= PKV_MMA_MIN_G ? 3 : 2;
   if (per_cu > resident) per_cu = resident;
   return cus * per_cu * kWaves;
 }

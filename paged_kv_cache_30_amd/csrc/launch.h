@@ -85,10 +85,6 @@ struct DecodeArgs {
   const int32_t* slot_tables;
   const int32_t* num_slots;
   int32_t msb;
-  // Kv head g of the kernel's view reads pool kv head g >> kv_shift (the
-  // pools hold Hkv >> kv_shift heads): 8-bit pools with 8 query heads per kv
-  // head run as two groups of 4 over each pool kv head.
-  int32_t kv_shift = 0;
 };
 
 struct PrefillArgs {

@@ -642,10 +642,6 @@ __device__ __forceinline__ void vm_wait() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// A table row in the constant address space: uniform loads from it become
-// scalar loads, which are counted apart from vector memory operations, so
-// waiting for a table entry never waits for a tile's direct loads.
-typedef const __attribute__((address_space(4))) int32_t* ctab_t;
 
 // Bits [0, n) of a 64-bit mask, n clamped to [0, 64].
 __device__ __forceinline__ unsigned long long low_bits(int n) {

@@ -146,18 +146,14 @@ def test_quant_argument_errors_before_any_launch():
     assert wq(gi8, ks=None) == pkv.PKV_EINVAL
     assert wq(gfp8, n=0) == pkv.PKV_OK
     assert wq(gfp8, n=-1) == pkv.PKV_EINVAL
-    # the workspace size of an 8-bit pool is that of any pool
-    assert (pkv.LIB.paged_attn_decode_workspace_bytes(ctypes.byref(gi8), 2, 100, 0, 0, 4) ==
-            pkv.LIB.paged_attn_decode_workspace_bytes(ctypes.byref(g16), 2, 100, 0, 0, 4))
-    # ... except with 8 query heads per kv head: two groups of 4 over each
-    # kv head, so partial slots for 16 kv heads of 4 query heads each
-    g8q = geo(H=64, Hkv=8, dt=pkv.PKV_I8)
-    slots = 4 + 2 * 16
-    want8 = -(-3 * 4 // 256) * 256 + -(-slots * 4 * 2 * 4 // 256) * 256 + slots * 4 * 128 * 4
-    assert pkv.LIB.paged_attn_decode_workspace_bytes(ctypes.byref(g8q), 2, 100, 0, 0, 4) == want8
+    # the workspace size of an 8-bit pool is that of any pool, for every
+    # group size (8 query heads per kv head included)
+    for H in (32, 64):
+        assert (pkv.LIB.paged_attn_decode_workspace_bytes(ctypes.byref(geo(H=H, Hkv=8, dt=pkv.PKV_I8)), 2, 100, 0, 0,
+                                                          4) ==
+                pkv.LIB.paged_attn_decode_workspace_bytes(ctypes.byref(geo(H=H, Hkv=8)), 2, 100, 0, 0, 4))
     assert pkv.LIB.paged_attn_decode_workspace_bytes(ctypes.byref(geo(H=64, Hkv=8)), 2, 100, 0, 0, 4) == (
         -(-3 * 4 // 256) * 256 + -(-(4 + 16) * 8 * 2 * 4 // 256) * 256 + (4 + 16) * 8 * 128 * 4)
-
 
 def test_prefill_quant_errors():
     """8-bit prefill needs no workspace (its codes are widened in the
