@@ -591,12 +591,14 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, fl
 // the scores of positions 4 g4 + i (i = 0..3) of the chunk, supplies their
 // weights as the B operand of the second product, and accumulates outputs
 // of dims 16 dt + 4 g4 + i. The online softmax is thus per lane, apart from
-// the chunk maximum (two lane swaps). K rows go from HBM straight into the
-// A operand registers: lane l loads position l % 16, dims [g4 D/4, (g4+1) D/4),
-// and q is read in the same dim order (a contraction may take its terms in
-// any order as long as both operands agree). V rows are written to a
-// per-wavefront LDS tile and read back transposed (ds_read_b64_tr_b16: lane
-// l gets dim 16 dt + l % 16 of positions 4 g4 .. 4 g4 + 3, the A operand).
+// the chunk maximum (two lane swaps).
+// K and V rows are loaded whole (16 lanes per 256-byte row, every cache
+// line by one instruction, with the streaming hint: a decode step reads its
+// pages once) and written to two per-wavefront LDS tiles. The K operand is
+// read back as 16-byte units (lane l: position l % 16, dims 32 ks + 8 g4;
+// q is read in the same dim order: a contraction may take its terms in any
+// order as long as both operands agree), the V operand with the transposing
+// read (lane l gets dim 16 dt + l % 16 of positions 4 g4 .. 4 g4 + 3).
 // Each weight enters P.V as two 16-bit values hi + lo (two products), about
 // 16 significant bits, while the normaliser sums the fp32 weights.
 // 8-bit pools: codes widened in registers (exact) to q's type for K and to
@@ -637,6 +639,8 @@ template <class P> __device__ __forceinline__ void split_pair(float a, float b, 
   lo = pack_pair<P>(a - ah, b - bh);
 }
 // Eight 8-bit codes (two words) as eight values of the 16-bit type P (exact).
+// (INT8 through code + 128 and one subtraction: converting the signed bytes
+// directly costs fewer instructions but more registers, and spilled.)
 template <class T, class P> __device__ __forceinline__ u32x4 widen8(uint32_t w0, uint32_t w1) {
   float f[8];
   codes4_to_f32<T>(w0, f);
@@ -648,19 +652,16 @@ template <class T, class P> __device__ __forceinline__ u32x4 widen8(uint32_t w0,
   r.w = pack_pair<P>(f[6] - T::BIAS, f[7] - T::BIAS);
   return r;
 }
-// LDS access as inline asm (the compiler does not see the transposed read's
-// dependence on the stores; both stay in program order as volatile asm and
-// the LDS executes a wavefront's instructions in order).
-__device__ __forceinline__ void lds_store16(uint32_t addr, const u32x4& x) {
-  asm volatile("ds_write_b128 %0, %1" ::"v"(addr), "v"(x) : "memory");
+// Transposing 8-byte LDS read (ds_read_b64_tr_b16) at byte offset off of
+// an LDS tile: within each 16 lanes, lane j reads 4 consecutive 16-bit
+// values of row j / 4 and lane i receives value i of those 4 rows. The
+// builtin, so that the compiler orders it after the tile's stores and waits
+// for it itself.
+typedef __attribute__((address_space(3))) char lds_char;
+__device__ __forceinline__ u32x2_t lds_read_tr16(lds_char* tile, uint32_t off) {
+  typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
+  return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + off)));
 }
-__device__ __forceinline__ u32x2_t lds_read_tr16(uint32_t addr) {
-  u32x2_t r;
-  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(addr));
-  return r;
-}
-__device__ __forceinline__ void lds_wait_all() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
-__device__ __forceinline__ void settle2(u32x2_t& x) { asm volatile("" : "+v"(x)); }
 // Maximum and sum over the four lanes l % 16 + 16 j (j = 0..3).
 __device__ __forceinline__ float max_over_groups(float x) {
   auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -675,34 +676,6 @@ __device__ __forceinline__ float sum_over_groups(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-#ifndef PKV_MMA_KLAYOUT
-#define PKV_MMA_KLAYOUT 1
-#endif
-#ifndef PKV_MMA_KNT
-#define PKV_MMA_KNT 0
-#endif
-#ifndef PKV_MMA_VNT
-#define PKV_MMA_VNT 1
-#endif
-// Page loads of the matrix-core kernel. The K rows of a chunk are read by
-// several load instructions, each taking part of every cache line: as
-// ordinary loads (no streaming hint) the lines stay in the L1 cache for the
-// instructions after the first (the hint cost a quarter of the bandwidth).
-__device__ __forceinline__ u32x4 load_k(const void* p) {
-#if PKV_MMA_KNT
-  return load_stream(p);
-#else
-  return load16(p);
-#endif
-}
-__device__ __forceinline__ u32x4 load_v(const void* p) {
-#if PKV_MMA_VNT
-  return load_stream(p);
-#else
-  return load16(p);
-#endif
-}
-
 // Byte offset of logical 16-byte unit u of row r in a V tile of D 16-bit
 // values per row: units XOR-swizzled by row so that the transposed reads of
 // 16 rows x 32 bytes spread over all banks.
@@ -712,8 +685,22 @@ template <int D> __device__ __forceinline__ uint32_t vtile_off(int r, int u) {
   return (uint32_t)(r * RB + 16 * (u ^ sw));
 }
 
+// Source of the loads issued past the end of a segment (never used): one
+// 16-byte line, so that those loads cost no page traffic.
+__device__ __attribute__((aligned(16))) uint32_t g_pad16[4];
+
+// Byte offset of logical 16-byte unit u of row r in a K tile: the A operand
+// reads (16 rows x 4 consecutive units) spread over all banks.
+template <int D> __device__ __forceinline__ uint32_t ktile_off(int r, int u) {
+  const int sw = D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
+  return (uint32_t)(r * D * 2 + 16 * (u ^ sw));
+}
+
+// Register budget: two wavefronts per SIMD for 16-bit pages, three for
+// 8-bit pages (half the bytes per chunk; more workgroups per unit keep
+// enough loads in flight).
 template <class T, class Q, int D, int B, int G>
-__global__ __launch_bounds__(kThreads, 2) void decode_mma_kernel(DecodeArgs a, float scale_log2) {
+__global__ __launch_bounds__(kThreads, T::QUANT ? 3 : 2) void decode_mma_kernel(DecodeArgs a, float scale_log2) {
   constexpr bool QU = T::QUANT;
   constexpr int EB = T::BYTES;
   using P = typename std::conditional<QU, BF16T, T>::type;  // type of the P.V product
@@ -721,21 +708,25 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mma_kernel(DecodeArgs a, f
   constexpr int CPB = B / CH;            // chunks per block
   constexpr int KS = D / 32;             // k-steps of the score product
   constexpr int DT = D / 16;             // 16-dim tiles of the output
-  constexpr int DG = D / 4;              // dims per lane group (score product)
-  constexpr int NKL = DG * EB / 16;      // K loads per lane and chunk
   constexpr int UV = D * EB / 16;        // 16-byte units of a V row in the pool
   constexpr int RV = 64 / UV;            // V rows per wavefront load
   constexpr int NVL = CH / RV;           // V loads per lane and chunk
+  constexpr int NKL = NVL;               // K loads per lane and chunk (laid out as V's)
   static_assert(G >= 1 && G <= 16 && (D == 64 || D == 128) && B % CH == 0, "shape");
 
   __shared__ int32_t cum_sh[kLdsSeqs + 1];
   __shared__ __attribute__((aligned(16))) uint16_t vt_sh[kWaves][CH * D];
+  __shared__ __attribute__((aligned(16))) uint16_t kt_sh[kWaves][CH * D];
 
   const int lane = threadIdx.x & 63;
   const int hh = lane & 15;   // head column
   const int g4 = lane >> 4;   // lane group
   const int wv = uniform(threadIdx.x >> 6);
-  const uint32_t vt = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)&vt_sh[wv][0];
+  lds_char* const vt = (lds_char*)&vt_sh[wv][0];
+  auto vt_store = [&](uint32_t off, const u32x4& x) { *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(vt + off) = x; };
+  lds_char* const kt = (lds_char*)&kt_sh[wv][0];
+  auto kt_store = [&](uint32_t off, const u32x4& x) { *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(kt + off) = x; };
+  auto kt_load = [&](uint32_t off) -> u32x4 { return *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(kt + off); };
 
   // Prefix of attended blocks: in a register (batches under 64 sequences),
   // in LDS (up to kLdsSeqs), or in the workspace (plan launch).
@@ -795,16 +786,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mma_kernel(DecodeArgs a, f
   // V load j of this lane: row RV j + lane / UV of the chunk, unit lane % UV.
   const int v_row0 = lane / UV, v_unit = lane % UV;
   // K operand of k-step ks: lane (hh, g4) holds dims kdim(ks) .. + 8 of
-  // position hh; K load j of the lane reads 16 bytes at byte kload_off(j) of
-  // the row. Each load instruction thus reads 64 consecutive bytes of each
-  // of 16 rows (16-bit: k-step j; 8-bit: k-steps 2j and 2j + 1).
-#if PKV_MMA_KLAYOUT
-  auto kload_off = [&](int j) -> uint32_t { return 64 * j + 16 * g4; };
-  auto kdim = [&](int ks) -> int { return EB == 2 ? 32 * ks + 8 * g4 : 64 * (ks >> 1) + 16 * g4 + 8 * (ks & 1); };
-#else
-  auto kload_off = [&](int j) -> uint32_t { return g4 * DG * EB + 16 * j; };
-  auto kdim = [&](int ks) -> int { return g4 * DG + 8 * ks; };
-#endif
+  // position hh (read from the K tile; q is read in the same dim order).
+  auto kdim = [&](int ks) -> int { return 32 * ks + 8 * g4; };
 
   for (long long pos = start; pos < end;) {
     while ((long long)Hkv * cum(s + 1) <= pos) ++s;
@@ -846,18 +829,21 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mma_kernel(DecodeArgs a, f
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    const char* kbase = (const char*)a.k_pool + (size_t)g * D * EB + (size_t)hh * row_stride + kload_off(0);
+    const char* kbase =
+        (const char*)a.k_pool + (size_t)g * D * EB + (size_t)v_row0 * row_stride + (size_t)v_unit * 16;
     const char* vbase =
         (const char*)a.v_pool + (size_t)g * D * EB + (size_t)v_row0 * row_stride + (size_t)v_unit * 16;
 
-    // Loads of chunk min(k, last) of the segment, issued for k = 0, 1, 2, ...
-    // in order and without condition (past the end the last chunk is loaded
-    // again; a block out of range loads block 0 and the chunk is masked), so
+    // Loads of chunk k of the segment, issued for k = 0, 1, 2, ... in order
+    // and without condition (past the end every lane loads the same 16-byte
+    // pad; a block out of range loads block 0 and the chunk is masked), so
     // that every load is waited for only where its chunk is used. The next
     // chunk's table entry is requested one chunk ahead.
     const int nchunks = n * CPB;
     int pb_next = entry(b_first);
     auto issue = [&](int k, u32x4* kr, u32x4* vr, f32x4_t& ks4, f32x4_t& vs4) -> bool {
+      const bool past = k >= nchunks;
+      const char* pad = (const char*)g_pad16;
       k = min(k, nchunks - 1);
       const int bi = k / CPB;
       const int sub = k - bi * CPB;
@@ -867,15 +853,17 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mma_kernel(DecodeArgs a, f
       const bool valid = pb >= 0 && pb < a.nb;
       const size_t off = (size_t)(valid ? pb : 0) * blk_stride + (size_t)sub * CH * row_stride;
 #pragma unroll
-      for (int j = 0; j < NKL; ++j) kr[j] = load_k(kbase + off + (kload_off(j) - kload_off(0)));
+      for (int j = 0; j < NKL; ++j) kr[j] = load_stream(past ? pad : kbase + off + (size_t)j * RV * row_stride);
 #pragma unroll
-      for (int j = 0; j < NVL; ++j) vr[j] = load_v(vbase + off + (size_t)j * RV * row_stride);
+      for (int j = 0; j < NVL; ++j) vr[j] = load_stream(past ? pad : vbase + off + (size_t)j * RV * row_stride);
       if constexpr (QU) {  // row scales of positions 4 g4 .. 4 g4 + 3, [NB, Hkv, B]
         const size_t sidx = ((size_t)(valid ? pb : 0) * Hkv + g) * B + sub * CH + 4 * g4;
+        const float* ksrc = past ? (const float*)g_pad16 : a.k_scale + sidx;
+        const float* vsrc = past ? (const float*)g_pad16 : a.v_scale + sidx;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          ks4[i] = a.k_scale[sidx + i];
-          vs4[i] = a.v_scale[sidx + i];
+          ks4[i] = ksrc[i];
+          vs4[i] = vsrc[i];
         }
       }
       return valid;
@@ -901,23 +889,28 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mma_kernel(DecodeArgs a, f
         if constexpr (QU) {
           u32x4 w0 = widen8<T, BF16T>(vr[j].x, vr[j].y), w1 = widen8<T, BF16T>(vr[j].z, vr[j].w);
           if (!ok) w0 = w1 = u32x4{0, 0, 0, 0};
-          lds_store16(vt + vtile_off<D>(r, 2 * v_unit), w0);
-          lds_store16(vt + vtile_off<D>(r, 2 * v_unit + 1), w1);
+          vt_store(vtile_off<D>(r, 2 * v_unit), w0);
+          vt_store(vtile_off<D>(r, 2 * v_unit + 1), w1);
         } else {
-          lds_store16(vt + vtile_off<D>(r, v_unit), ok ? vr[j] : u32x4{0, 0, 0, 0});
+          vt_store(vtile_off<D>(r, v_unit), ok ? vr[j] : u32x4{0, 0, 0, 0});
+        }
+      }
+      // K rows into their tile, in q's type.
+#pragma unroll
+      for (int j = 0; j < NKL; ++j) {
+        const int r = RV * j + v_row0;
+        if constexpr (QU) {
+          kt_store(ktile_off<D>(r, 2 * v_unit), widen8<T, Q>(kr[j].x, kr[j].y));
+          kt_store(ktile_off<D>(r, 2 * v_unit + 1), widen8<T, Q>(kr[j].z, kr[j].w));
+        } else {
+          kt_store(ktile_off<D>(r, v_unit), kr[j]);
         }
       }
       // Scores of positions 4 g4 + i for head hh (base 2).
       f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        u32x4 ka;
-        if constexpr (QU) {
-          const u32x4 c = kr[ks / 2];
-          ka = (ks & 1) ? widen8<T, Q>(c.z, c.w) : widen8<T, Q>(c.x, c.y);
-        } else {
-          ka = kr[ks];
-        }
+        const u32x4 ka = kt_load(ktile_off<D>(hh, 4 * ks + g4));
         sc = mma16<Q>(ka, qm[ks], sc);
       }
       float sv[4];
@@ -949,16 +942,13 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mma_kernel(DecodeArgs a, f
       split_pair<P>(p[2], p[3], h1, l1);
       const u32x2_t whi = {h0, h1}, wlo = {l0, l1};
       // V^T operands: row 4 g4 + hh / 4, dims 16 dt + 4 (hh % 4) .. + 4.
-      lds_wait_all();
       u32x2_t va[DT];
       const int tr_r = 4 * g4 + (hh >> 2);
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
-        va[dt] = lds_read_tr16(vt + vtile_off<D>(tr_r, 2 * dt + ((hh & 3) >> 1)) + 8 * (hh & 1));
-      lds_wait_all();
+        va[dt] = lds_read_tr16(vt, vtile_off<D>(tr_r, 2 * dt + ((hh & 3) >> 1)) + 8 * (hh & 1));
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        settle2(va[dt]);
         o[dt] = mma16k16<P>(va[dt], whi, o[dt]);
         o[dt] = mma16k16<P>(va[dt], wlo, o[dt]);
       }
@@ -1237,7 +1227,7 @@ bool decode_supported(int dtype, int q_dtype, int D, int B, int G) {
 // spread leaves some units with more work); two per unit keep 128 KB of
 // loads in flight per unit (16 KB per wavefront), which covers HBM latency,
 // within what the unit holds at once. 8-bit pages carry half the bytes per
-// chunk: three workgroups per unit measured best for them.
+// chunk: three workgroups per unit (where they fit) measured best for them.
 int decode_auto_workers(int dtype, int q_dtype, int D, int B, int G) {
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
@@ -1246,7 +1236,7 @@ int decode_auto_workers(int dtype, int q_dtype, int D, int B, int G) {
     cus = 256;
   }
   const int resident = dispatch<OccupancyOp, int>(instance_of(dtype, q_dtype), D, B, G, 2);
-  int per_cu = (dtype == 3 || dtype == 4) && G >= PKV_MMA_MIN_G ? 3 : 2;
+  int per_cu = dtype == 3 || dtype == 4 ? 3 : 2;
   if (per_cu > resident) per_cu = resident;
   return cus * per_cu * kWaves;
 }
