@@ -182,8 +182,10 @@ def cpu_baseline(w, target_s: float):
                       f"{elapsed:.2f} s, BLAS threads {threads} of {cores} visible cores"}
 
 
-KERNELS = {"decode": ("decode_split_kernel", "decode_merge_kernel", "decode_plan_kernel"),
+KERNELS = {"decode": ("decode_split_kernel", "decode_mma_kernel", "decode_merge_kernel", "decode_plan_kernel"),
            "prefill": ("prefill_kernel",)}
+# The kernel that starts an attention call (its split kernel, either kind).
+CALL_START = {"decode": ("decode_split_kernel", "decode_mma_kernel"), "prefill": ("prefill_kernel",)}
 
 
 def attend_sources(kind: str, kv: str):
@@ -232,10 +234,9 @@ def summarize_pmc(args, fetch_dir, write_dir, copy_mib) -> int:
         ours = sorted((i, k, v) for (i, k), v in vals.items() if any(n in k for n in KERNELS[kind]))
         # group consecutive dispatches of one call: the split/prefill kernel
         # starts a call
-        first = KERNELS[kind][0]
         calls, cur = [], None
         for i, k, v in ours:
-            if first in k:
+            if any(f in k for f in CALL_START[kind]):
                 cur = [v]
                 calls.append(cur)
             elif cur is not None:

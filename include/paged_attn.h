@@ -168,7 +168,11 @@ int32_t paged_attn_decode_workers(const pkv_geometry_t* geom, int32_t num_seqs,
  *                 calls in flight at once need different workspaces
  * Table entries of attended blocks that are -1 or >= NB are skipped: their
  * positions contribute nothing. The partially covered first block of a
- * window (and the blocks holding sink positions) must stay mapped. */
+ * window (and the blocks holding sink positions) must stay mapped.
+ * Scores and outputs accumulate in float32. With 4 or more query heads per
+ * kv head (16-bit pools) the products run on the matrix cores and each
+ * softmax weight enters P.V as two 16-bit values (hi + lo, about 16
+ * significant bits), while the normaliser and lse use the fp32 weights. */
 int paged_attn_decode(const pkv_geometry_t* geom, float* out, float* lse, const void* q,
                       const void* k_pool, const void* v_pool,
                       const int32_t* block_tables, int32_t max_blocks_per_seq,
@@ -218,11 +222,15 @@ int paged_attn_decode_noalloc(const pkv_geometry_t* geom, float* out, float* lse
  * Requires C <= L for every sequence. Scores and outputs accumulate in
  * float32. The softmax weights multiply V on the fp16 matrix cores for both
  * input types: each weight is rounded to fp16 (11 significant bits), and a
- * bf16 V is converted to fp16 (exact for |v| in [2^-17, 65504]; smaller
- * magnitudes keep their bits down to 2^-24, larger ones saturate). The
- * output divides by the sum of the weights as rounded, and lse uses the
- * same sum: within 2^-11 relative of the exact sum, plus 2^-25 per
- * subnormal weight against a sum of at least 1, so lse is within 6e-4. */
+ * bf16 V is converted to fp16, exact for |v| in [2^-17, 65280] (65280 is
+ * the largest bf16 value fp16 holds; smaller magnitudes keep their bits down
+ * to 2^-24). bf16 V rows with a larger magnitude are outside this call's
+ * range (they saturate at 65504); the binding's debug mode rejects them.
+ * The output divides by the sum of the weights as rounded, and lse uses the
+ * same sum, so that out and lse describe the same weights (partial results
+ * merged through lse stay exact): that sum is within 2^-11 relative of the
+ * exact one, plus 2^-25 per subnormal weight against a sum of at least 1,
+ * so lse is within 6e-4 of the exact log-sum-exp. */
 int paged_attn_prefill(const pkv_geometry_t* geom, float* out, float* lse, const void* q,
                        const int32_t* q_start, const void* k_pool, const void* v_pool,
                        const int32_t* block_tables, int32_t max_blocks_per_seq,
@@ -272,10 +280,8 @@ int paged_kv_write_quant(const pkv_geometry_t* geom, void* k_pool, void* v_pool,
  * factor out of each dot product).
  *
  *   geom->kv_dtype    PKV_I8 or PKV_FP8; num_heads / num_kv_heads in {1, 2, 4, 8}
- *                     (with 8, each kv head is read by two groups of 4 query
- *                     heads: twice its bytes, and the workspace of
- *                     paged_attn_decode_workspace_bytes for this geometry is
- *                     sized for that)
+ *                     (each page is read once for all query heads of its
+ *                     kv head, as with 16-bit pools)
  *   q                 q_dtype [num_seqs, H, D], q_dtype PKV_F16 or PKV_BF16
  *   k_pool, v_pool    codes [NB, B, Hkv, D]
  *   k_scale, v_scale  float32 [NB, Hkv, B]

@@ -29,7 +29,7 @@
 //    16-byte units its own direct loads wrote. The conversion is exact for
 //    |v| in [2^-17, 65280] (bf16 has 8 significant bits, and 65280 is its
 //    largest value fp16 holds); smaller values are truncated by less than
-//    2^-24 and larger ones saturate at 65504.
+//    2^-24, and larger ones, outside the call's range, saturate.
 //  * The weights are taken relative to a reference maximum that moves only
 //    when some row's maximum grows by more than a factor 2^8 (weights then
 //    stay <= 256, well inside fp32 and the 16-bit formats); the output is
@@ -168,21 +168,6 @@ __device__ __forceinline__ void lds_write16(uint32_t addr, const u32x4& x) {
 __device__ __forceinline__ void settle(u32x4& x) { asm volatile("" : "+v"(x)); }
 
 template <int N> struct IntC { static constexpr int value = N; };
-
-// In-place bf16 -> fp16 conversion of one 16-byte unit of a V tile (exact
-// for |v| in [2^-17, 65504], see above); fp16 tiles are left alone.
-template <class T> __device__ __forceinline__ void v_to_f16(uint16_t* unit);
-template <> __device__ __forceinline__ void v_to_f16<F16T>(uint16_t*) {}
-template <> __device__ __forceinline__ void v_to_f16<BF16T>(uint16_t* unit) {
-  u32x4 x = *reinterpret_cast<const u32x4*>(unit);
-  uint32_t w[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float lo = __builtin_bit_cast(float, w[i] << 16), hi = __builtin_bit_cast(float, w[i] & 0xffff0000u);
-    w[i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
-  }
-  *reinterpret_cast<u32x4*>(unit) = u32x4{w[0], w[1], w[2], w[3]};
-}
 
 // Sixteen 8-bit codes of one 16-byte unit as fp32 values (exact): INT8 as
 // the signed byte, FP8 E4M3 as the code's value.

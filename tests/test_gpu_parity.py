@@ -145,11 +145,12 @@ DECODE_CASES = [
     ("f32", 4, 2, 64, 16, [10, 70], 16, 3),
     ("bf16", 32, 8, 128, 16, [0, 0, 2000, 0, 4100, 1], 0, 0),
     ("f16", 64, 8, 128, 16, [300, 20000, 7], 0, 0),
-    # 8 query heads per kv head: scores on the matrix cores (16-bit, D = 128)
+    # 4 or more query heads per kv head run on the matrix cores
     ("bf16", 64, 8, 128, 32, [1, 15, 16, 17, 33, 1000, 5000], 0, 0),
     ("bf16", 64, 8, 128, 32, [1, 15, 16, 17, 33, 1000, 5000], 0, 9),
     ("f16", 32, 4, 128, 16, [20, 700, 2100], 300, 0),
     ("bf16", 16, 2, 64, 32, [40, 600, 1500], 0, 0),
+    ("f16", 16, 4, 64, 32, [3, 50, 900, 31], 64, 5),
 ]
 
 

@@ -136,7 +136,7 @@ DECODE_CASES = [
     ("fp8", "f16", 16, 4, 128, 32, [40, 600, 1500], 100, 1),
     ("i8", "f16", 4, 2, 64, 32, [3, 90, 129], 1, 0),
     ("fp8", "bf16", 32, 8, 128, 32, [0, 0, 2000, 0, 4100, 1], 0, 0),
-    # 8 query heads per kv head: two groups of 4 over each kv head
+    # 8 query heads per kv head (each page read once for the whole group)
     ("i8", "bf16", 64, 8, 128, 32, [1, 33, 700, 3000], 0, 0),
     ("fp8", "f16", 16, 2, 64, 16, [5, 200, 1500], 100, 0),
     ("fp8", "bf16", 8, 1, 128, 16, [17, 2048], 0, 5),
@@ -221,8 +221,8 @@ def test_quant_decode_worker_independence(lib):
 
 
 def test_quant_group_of_eight_worker_independence(lib):
-    """8 query heads per kv head run as two groups of 4: the result does not
-    depend on how the work is split."""
+    """8 query heads per kv head (one matrix-core group per kv head): the
+    result does not depend on how the work is split."""
     pkv, session = lib
     note("quant G=8 worker independence")
     w = wl.make_decode(lens=[20, 999, 64], num_heads=16, num_kv_heads=2, head_dim=128, block_size=16,
