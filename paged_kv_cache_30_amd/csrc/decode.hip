@@ -638,18 +638,18 @@ template <class P> __device__ __forceinline__ void split_pair(float a, float b, 
   unpack_pair<P>(hi, ah, bh);
   lo = pack_pair<P>(a - ah, b - bh);
 }
-// Eight 8-bit codes (two words) as eight values of the 16-bit type P (exact).
-// (INT8 through code + 128 and one subtraction: converting the signed bytes
-// directly costs fewer instructions but more registers, and spilled.)
+// Eight 8-bit codes (two words) as eight values code + T::BIAS of the 16-bit
+// type P (exact: INT8 as code + 128 in [0, 255], FP8 as its value). The
+// caller takes BIAS times the other operand's sum off each product once.
 template <class T, class P> __device__ __forceinline__ u32x4 widen8(uint32_t w0, uint32_t w1) {
   float f[8];
   codes4_to_f32<T>(w0, f);
   codes4_to_f32<T>(w1, f + 4);
   u32x4 r;
-  r.x = pack_pair<P>(f[0] - T::BIAS, f[1] - T::BIAS);
-  r.y = pack_pair<P>(f[2] - T::BIAS, f[3] - T::BIAS);
-  r.z = pack_pair<P>(f[4] - T::BIAS, f[5] - T::BIAS);
-  r.w = pack_pair<P>(f[6] - T::BIAS, f[7] - T::BIAS);
+  r.x = pack_pair<P>(f[0], f[1]);
+  r.y = pack_pair<P>(f[2], f[3]);
+  r.z = pack_pair<P>(f[4], f[5]);
+  r.w = pack_pair<P>(f[6], f[7]);
   return r;
 }
 // Transposing 8-byte LDS read (ds_read_b64_tr_b16) at byte offset off of
@@ -702,6 +702,7 @@ template <int D> __device__ __forceinline__ uint32_t ktile_off(int r, int u) {
 template <class T, class Q, int D, int B, int G>
 __global__ __launch_bounds__(kThreads, T::QUANT ? 3 : 2) void decode_mma_kernel(DecodeArgs a, float scale_log2) {
   constexpr bool QU = T::QUANT;
+  constexpr bool BIASED = T::BIAS != 0.f;  // INT8: codes widened as code + 128
   constexpr int EB = T::BYTES;
   using P = typename std::conditional<QU, BF16T, T>::type;  // type of the P.V product
   constexpr int CH = 16;                 // positions per chunk
@@ -824,6 +825,21 @@ __global__ __launch_bounds__(kThreads, T::QUANT ? 3 : 2) void decode_mma_kernel(
         qm[ks] = hh < G ? v : u32x4{0, 0, 0, 0};
       }
     }
+    // INT8 codes enter both products as code + 128: the score of head hh
+    // takes 128 * sum(q) off (qbias), the output 128 * sum of the weights as
+    // applied (wsum, a running sum like l_run).
+    float qbias = 0.f, wsum = 0.f;
+    if constexpr (BIASED) {
+      float t = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        float f[8];
+        chunk_to_f32<Q>(qm[ks], f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) t += f[e];
+      }
+      qbias = -T::BIAS * sum_over_groups(t);
+    }
     float m_ref = -INFINITY, l_run = 0.f;
     f32x4_t o[DT];
 #pragma unroll
@@ -916,7 +932,7 @@ __global__ __launch_bounds__(kThreads, T::QUANT ? 3 : 2) void decode_mma_kernel(
       float sv[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        float x = sc[i] * scale_log2;
+        float x = (BIASED ? sc[i] + qbias : sc[i]) * scale_log2;
         if constexpr (QU) x *= ks4[i];
         sv[i] = (full || attended_pos(t0 + 4 * g4 + i)) ? x : -INFINITY;
       }
@@ -925,6 +941,7 @@ __global__ __launch_bounds__(kThreads, T::QUANT ? 3 : 2) void decode_mma_kernel(
         const float mn = fmaxf(m_ref, mx);
         const float alpha = __builtin_amdgcn_exp2f(m_ref - (mn == -INFINITY ? 0.f : mn));
         l_run *= alpha;
+        if constexpr (BIASED) wsum *= alpha;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
         m_ref = mn;
@@ -941,6 +958,14 @@ __global__ __launch_bounds__(kThreads, T::QUANT ? 3 : 2) void decode_mma_kernel(
       split_pair<P>(p[0], p[1], h0, l0);
       split_pair<P>(p[2], p[3], h1, l1);
       const u32x2_t whi = {h0, h1}, wlo = {l0, l1};
+      if constexpr (BIASED) {  // the weights exactly as the products apply them
+        float a0, a1, b0, b1, c0, c1, d0, d1;
+        unpack_pair<P>(h0, a0, a1);
+        unpack_pair<P>(l0, b0, b1);
+        unpack_pair<P>(h1, c0, c1);
+        unpack_pair<P>(l1, d0, d1);
+        wsum += ((a0 + b0) + (a1 + b1)) + ((c0 + d0) + (c1 + d1));
+      }
       // V^T operands: row 4 g4 + hh / 4, dims 16 dt + 4 (hh % 4) .. + 4.
       u32x2_t va[DT];
       const int tr_r = 4 * g4 + (hh >> 2);
@@ -967,6 +992,11 @@ __global__ __launch_bounds__(kThreads, T::QUANT ? 3 : 2) void decode_mma_kernel(
     }
 
     const float l_tot = sum_over_groups(l_run);
+    if constexpr (BIASED) {
+      const float vbias = -T::BIAS * sum_over_groups(wsum);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) o[dt] += vbias;
+    }
     if (hh < G) {
       const size_t orow = (size_t)q_row(a, s) * H + (size_t)g * G + hh;
       if (b_first == 0 && n == nblk) {
