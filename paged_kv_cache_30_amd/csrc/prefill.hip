@@ -763,16 +763,35 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(PrefillArgs a, float sc
   // all of them for the key mask, and this wavefront's own (pb_j[j] for its
   // load j) loaded apart, so no register array is indexed at run time.
   int ent[TB], pb_j[NLD];
+  uint32_t bj_off[NLD];  // byte offset of this wavefront's entry for load j inside a tile's entries
+#pragma unroll
+  for (int j = 0; j < NLD; ++j) bj_off[j] = 4u * (uint32_t)bj[j];
   auto fetch = [&](int t0) {
     const int b0 = t0 / B;
+    if (b0 + TB <= a.mb) {
+      // The usual case: the tile's TB entries in one scalar load, and each
+      // of this wavefront's entries at its fixed offset from them.
+      typedef int32_t EntV __attribute__((ext_vector_type(TB), aligned(4)));
+      const __attribute__((address_space(4))) char* te = (const __attribute__((address_space(4))) char*)(trow + b0);
+      const EntV e = *(const __attribute__((address_space(4))) EntV*)te;
 #pragma unroll
-    for (int k = 0; k < TB; ++k) ent[k] = trow[min(b0 + k, a.mb - 1)];
+      for (int k = 0; k < TB; ++k) ent[k] = e[k];
 #pragma unroll
-    for (int j = 0; j < NLD; ++j) pb_j[j] = trow[min(b0 + bj[j], a.mb - 1)];
+      for (int j = 0; j < NLD; ++j) pb_j[j] = *(ctab_t)(te + bj_off[j]);
+    } else {
+#pragma unroll
+      for (int k = 0; k < TB; ++k) ent[k] = trow[min(b0 + k, a.mb - 1)];
+#pragma unroll
+      for (int j = 0; j < NLD; ++j) pb_j[j] = trow[min(b0 + bj[j], a.mb - 1)];
+    }
   };
   // Bit k of a tile's key mask: key t0 + k is in the workgroup's range and
   // its block is mapped.
   auto key_mask = [&](int t0) -> unsigned long long {
+    bool mapped = true;
+#pragma unroll
+    for (int k = 0; k < TB; ++k) mapped = mapped && (uint32_t)ent[k] < (uint32_t)a.nb;
+    if (mapped && t0 >= kv_lo && t0 + kKT <= kv_hi) return ~0ull;  // the usual case
     unsigned long long blk = 0;
 #pragma unroll
     for (int k = 0; k < TB; ++k)
@@ -787,11 +806,14 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(PrefillArgs a, float sc
     uint16_t* kd = k_lds + st * TILE;
     uint16_t* vd = v_lds + st * TILE;
     if (vmask == ~0ull) {
+      // Block bases in scalar registers, lane offsets in 32 bits.
 #pragma unroll
       for (int j = 0; j < NLD; ++j) {
         const size_t boff = (size_t)(uint32_t)pb_j[j] * block_stride;
-        dma16(kpool + boff + koff[j], kd + (NW * j + wave) * 512);
-        dma16(vpool + boff + voff[j], vd + (NW * j + wave) * 512);
+        const char* kb = kpool + boff;
+        const char* vb = vpool + boff;
+        dma16(kb + koff[j], kd + (NW * j + wave) * 512);
+        dma16(vb + voff[j], vd + (NW * j + wave) * 512);
       }
     } else {
 #pragma unroll
@@ -950,7 +972,8 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(PrefillArgs a, float sc
     else if (j == 9)
       m8[4] = fmaxf(fmaxf(m8[4], m8[5]), fmaxf(m8[6], m8[7]));
   };
-  auto phase_y = [&](const f32x16* sn, bool with_next, int vst, int gi, int gst) {
+  auto phase_y = [&](const f32x16* sn, auto wn, int vst, int gi, int gst) {
+    constexpr bool with_next = decltype(wn)::value;
     const uint32_t vb = lds_offset(v_lds + vst * TILE);
     u32x2 e03[2][DT], e47[2][DT];
     auto rd = [&](auto cc, int slot) {
@@ -976,7 +999,7 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(PrefillArgs a, float sc
         const P8 av = __builtin_bit_cast(P8, u32x4{e03[slot][dt].x, e03[slot][dt].y, e47[slot][dt].x,
                                                      e47[slot][dt].y});
         o[dt] = MP::mma(av, bw, o[dt]);
-        if (with_next) {
+        if constexpr (with_next) {
 #pragma unroll
           for (int k = 0; k < PPM; ++k) max_part(sn, (4 * c + dt) * PPM + k);
         }
@@ -1078,19 +1101,22 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(PrefillArgs a, float sc
   // X; tile i+3's loads are issued in phase Y (into the stage tile i-1
   // held); at the end every thread waits for its loads of tile i+2 (issued
   // one iteration earlier), and one barrier publishes both.
-  auto iteration = [&](int i, int st, const f32x16* sc, f32x16* sn) {
+  // has_next: compile-time (i + 1 < ntiles), so that the steady iterations
+  // carry no test of it.
+  auto iteration = [&](int i, int st, const f32x16* sc, f32x16* sn, auto hn) {
+    constexpr bool has_next = decltype(hn)::value;
     const int st1 = (st + 1) & (NST - 1);
     const int st3 = (st + 3) & (NST - 1);
-    const bool has_next = i + 1 < ntiles;
     vm2 = 0;
-    if (has_next)
+    if constexpr (has_next) {
       phase_x(sc, sn, st1, true, st1);
-    else
+      mask(sn, tile_t0(i + 1), vm1);
+    } else {
       weights_only(sc);
-    if (has_next) mask(sn, tile_t0(i + 1), vm1);
+    }
     // phase_y sets vm2 to the key mask of tile i+3 when it gathers it
-    phase_y(sn, has_next, st, i + 3, st3);
-    if (has_next) update_max();
+    phase_y(sn, hn, st, i + 3, st3);
+    if constexpr (has_next) update_max();
     if (i + 3 < ntiles)
       vm_wait<2 * NLD>();
     else
@@ -1102,12 +1128,17 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(PrefillArgs a, float sc
     vm3 = vm2;  // tile i+3
     return st1;
   };
-  int st = 0;
-  for (int i = 0;;) {
-    st = iteration(i, st, sA, sB);
-    if (++i == ntiles) break;
-    st = iteration(i, st, sB, sA);
-    if (++i == ntiles) break;
+  // Iteration i takes the scores of tile i from sA (i even) or sB (i odd).
+  int st = 0, i = 0;
+  for (; i + 2 < ntiles; i += 2) {
+    st = iteration(i, st, sA, sB, IntC<1>{});
+    st = iteration(i + 1, st, sB, sA, IntC<1>{});
+  }
+  if (i + 1 < ntiles) {
+    st = iteration(i, st, sA, sB, IntC<1>{});
+    iteration(i + 1, st, sB, sA, IntC<0>{});
+  } else {
+    iteration(i, st, sA, sB, IntC<0>{});
   }
 
   if (!row_ok) return;
