@@ -159,16 +159,10 @@ typedef const __attribute__((address_space(4))) int32_t* ctab_t;
 
 __device__ __forceinline__ u32x4 load16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 
-// 16-byte load of data read once (K/V pages in decode).
-#ifndef PKV_STREAM_NT
-#define PKV_STREAM_NT 1
-#endif
+// 16-byte load of data read once (K/V pages in decode), with the streaming
+// hint.
 __device__ __forceinline__ u32x4 load_stream(const void* p) {
-#if PKV_STREAM_NT
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-#else
-  return *reinterpret_cast<const u32x4*>(p);
-#endif
 }
 
 }  // namespace pkv

@@ -38,10 +38,6 @@
 #include "common.h"
 #include "launch.h"
 
-#ifndef PKV_DECODE_CHUNK_LOADS
-#define PKV_DECODE_CHUNK_LOADS(G) 4
-#endif
-
 namespace pkv {
 
 constexpr int kWaves = 4;
@@ -85,7 +81,8 @@ template <class T, int D, int B, int G>
 struct DecodeShape {
   static constexpr int EB = T::BYTES;
   static constexpr int E = 16 / EB;                    // elements per 16-byte piece
-  // Pieces of a K/V row per lane: with 4 or more query heads per kv head the
+  // Pieces of a K/V row per lane: with 4 or more query heads per kv head
+  // (fp32 pools; 16-bit and 8-bit ones take the matrix-core kernel there) the
   // per-position softmax work, done redundantly by every lane of a row, is
   // halved by giving each lane two pieces (fewer lanes per row).
   static constexpr int PIECES = (G >= 4 && D * EB / 16 >= 16) ? 2 : 1;
@@ -94,9 +91,7 @@ struct DecodeShape {
   static constexpr int STEPS = B / RPL;                // steps per block
   // Loads per chunk (of K and of V); two chunks are in registers at a time
   // (16 KB in flight per wavefront).
-  // 8-bit rows with 4 query heads keep two steps per chunk: their per-lane
-  // state (16 outputs per head) leaves room for fewer loads in flight.
-  static constexpr int CWANT = (T::QUANT && G >= 4) ? 2 : PKV_DECODE_CHUNK_LOADS(G) / PIECES;
+  static constexpr int CWANT = 4 / PIECES;
   static constexpr int CSTEPS = STEPS < CWANT ? STEPS : CWANT;
   static constexpr int CHUNK = RPL * CSTEPS;           // slots per chunk
   static constexpr int CPB = B / CHUNK;                // chunks per block
@@ -1127,15 +1122,11 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
   }
 }
 
-#ifndef PKV_MMA_MIN_G
-#define PKV_MMA_MIN_G 4
-#endif
 // Split kernel of an instance: the matrix-core one for 16-bit and 8-bit pools
-// with at least PKV_MMA_MIN_G query heads per kv head (8-bit pools with 8:
-// always), the vector-ALU one otherwise.
+// with 4 or more query heads per kv head, the vector-ALU one otherwise.
 template <class T, int G>
 constexpr bool use_mma() {
-  return T::BYTES <= 2 && (G >= PKV_MMA_MIN_G || (T::QUANT && G == 8));
+  return T::BYTES <= 2 && G >= 4;
 }
 
 template <class T, class Q, int D, int B, int G>
