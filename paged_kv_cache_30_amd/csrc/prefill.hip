@@ -637,18 +637,20 @@ __device__ __forceinline__ unsigned long long low_bits(int n) {
 //
 // A workgroup of 8 wavefronts covers the query heads of one kv head (up to
 // 8) and as many 32-row sub-tiles as the rest allows; each wavefront owns 32
-// query rows of one head. Key tiles of 64 positions rotate through three LDS
+// query rows of one head. Key tiles of 64 positions rotate through four LDS
 // stages. Iteration i of a wavefront overlaps two tiles:
 //   phase X: the 16 MFMAs of tile i+1's scores S^T = K.Q^T, interleaved with
-//            tile i's weights (exp2, fp16 rounding, row sum) on the vector ALU;
+//            tile i's weights (exp2, fp16 rounding, row sum) on the vector ALU
+//            and with the conversion of this thread's V units of tile i+1
+//            (bf16 -> fp16);
 //   phase Y: the 16 MFMAs of tile i's O^T += V^T.P^T, interleaved with tile
-//            i+1's mask and row maximum;
+//            i+1's mask and row maximum, and the direct loads of tile i+3
+//            into the stage tile i-1 held;
 // then the reference-maximum update of tile i+1 (rare output rescale).
 // K fragments are read from LDS two k-chunks ahead of their MFMAs, V
-// fragments one 16-key chunk ahead. Each iteration starts the direct loads
-// of tile i+2 into the stage tile i-1 held and ends with each thread waiting
-// for its own loads, converting its V units (bf16 -> fp16) and one barrier.
-// The table entries come from scalar loads one tile further ahead.
+// fragments one 16-key chunk ahead. Each iteration ends with each thread
+// waiting for its own loads of tile i+2 and one barrier. The table entries
+// come from scalar loads one tile further ahead.
 template <class T, int D, int B, int G>
 __global__ __launch_bounds__(512, 1) void prefill_kernel(PrefillArgs a, float scale_log2) {
   using M = Mma<T>;      // S = K.Q^T in the input type
