@@ -5,7 +5,8 @@
 // every sequence s and query head h, softmax(scale * q.K^T) V over positions
 // [lo, L) of the sequence, fetched through its block table.
 //
-// How, on gfx950 (two launches on the caller's stream):
+// How, on gfx950 (two launches on the caller's stream, three above 4096
+// sequences):
 //  1. plan: every wavefront (batches under 64 sequences, in a register) or
 //     every workgroup (up to 4096, in LDS) prefix-sums the attended block
 //     count of every sequence (cum[s]; a separate one-workgroup launch writes
@@ -22,10 +23,15 @@
 //     head's group with each page (a page is read from HBM once per group),
 //     keeps a running maximum and sum (online softmax in base 2), merges the
 //     states of its row groups with lane shuffles and writes one partial
-//     (max, sum, unnormalised output) per head.
+//     (max, sum, unnormalised output) per head, or, when it holds the whole
+//     segment, the normalised output and log-sum-exp.
 //  3. merge: per (sequence, query head) the partials of the wavefronts whose
 //     ranges cover it are combined exactly:
 //       M = max_i m_i,  out = sum_i 2^(m_i-M) o_i / sum_i 2^(m_i-M) l_i.
+//  With 1-2 query heads per kv head, and for fp32 pools, step 2 runs on the
+//  vector ALU (decode_split_kernel); with 4-8 heads on 16-bit and 8-bit
+//  pools it runs on the matrix cores (decode_mma_kernel, below), with the
+//  same split, partials and merge. In the vector-ALU kernel:
 //  Lane layout: a K or V row (D elements of one position and kv head) is
 //  D*bytes/16 lanes x 16 bytes; one wavefront load covers 64/(lanes per row)
 //  consecutive slots of a block. Scores are a dot product on each lane's
