@@ -19,17 +19,19 @@ __global__ __launch_bounds__(256) void kv_write_kernel(WriteArgs a, int chunks_p
     const int rem = (int)(i - (long long)n * 2 * chunks_per_row);
     const int which = rem >= chunks_per_row;  // 0 = K, 1 = V
     const int ch = rem - which * chunks_per_row;
+    // The piece itself is loaded first, alongside the sequence and position
+    // (it depends on neither), so the table lookup is the only dependent
+    // load before the store.
+    const long long row_bytes = (long long)chunks_per_row * 16;
+    const long long src = (long long)n * row_bytes + (long long)ch * 16;
+    const u32x4 piece = load16((const char*)(which ? a.v_new : a.k_new) + src);
     const int s = a.seq_idx[n];
     const int p = a.pos[n];
     if (s < 0 || s >= a.num_seqs || p < 0 || p >= a.mb * a.B) continue;
     const int pb = a.tables[(long long)s * a.mb + p / a.B];
     if (pb < 0 || pb >= a.nb) continue;
-    const long long row_bytes = (long long)chunks_per_row * 16;
     const long long dst = ((long long)pb * a.B + p % a.B) * row_bytes + (long long)ch * 16;
-    const long long src = (long long)n * row_bytes + (long long)ch * 16;
-    const char* from = (const char*)(which ? a.v_new : a.k_new) + src;
-    char* to = (char*)(which ? a.v_pool : a.k_pool) + dst;
-    *reinterpret_cast<u32x4*>(to) = load16(from);
+    *reinterpret_cast<u32x4*>((char*)(which ? a.v_pool : a.k_pool) + dst) = piece;
   }
 }
 
@@ -94,6 +96,11 @@ __global__ __launch_bounds__(256) void kv_write_quant_kernel(WriteQuantArgs a, l
     const int rem = (int)(row - (long long)n * 2 * a.Hkv);
     const int which = rem >= a.Hkv;  // 0 = K, 1 = V
     const int g = rem - which * a.Hkv;
+    // The row's values are loaded first, alongside the sequence and
+    // position (they depend on neither).
+    float x[8];
+    load8_f32<In>((const char*)(which ? a.v_new : a.k_new) + (((long long)n * a.Hkv + g) * D + c * 8) * In::BYTES,
+                  x);
     const int s = a.seq_idx[n];
     const int p = a.pos[n];
     bool ok = s >= 0 && s < a.num_seqs && p >= 0 && p < a.mb * a.B;
@@ -101,12 +108,7 @@ __global__ __launch_bounds__(256) void kv_write_quant_kernel(WriteQuantArgs a, l
     ok = ok && pb >= 0 && pb < a.nb;
     // Every lane of the row takes part in the group maximum (the row's lanes
     // share `ok`); only valid rows store.
-    float x[8];
-    if (ok) {
-      const char* src = (const char*)(which ? a.v_new : a.k_new) +
-                        (((long long)n * a.Hkv + g) * D + c * 8) * In::BYTES;
-      load8_f32<In>(src, x);
-    } else {
+    if (!ok) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) x[e] = 0.f;
     }
