@@ -302,6 +302,10 @@ PREFILL_CASES = [
     ("bf16", 16, 2, 64, 16, 48, [64, 17], 0, True),
     ("bf16", 8, 2, 128, 16, 160, [90, 31], 50, True),
     ("f16", 16, 2, 128, 32, 96, [200, 5], 0, False),
+    # two query heads per kv head; head dim 64 with 32-slot blocks (one table
+    # entry per wavefront load); 1 to 4 key tiles per workgroup with a window
+    ("f16", 8, 4, 64, 32, 64, [33, 64], 0, True),
+    ("bf16", 6, 3, 64, 16, 0, [10, 130, 190], 100, False),
 ]
 
 
