@@ -1058,7 +1058,7 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
   if (w_lo == w_hi) return;  // written by the split kernel
   const int np = w_hi - w_lo + 1;
   const size_t base0 = ((size_t)s * Hkv + g) * G + (size_t)w_lo * G;  // slot of worker w_lo, head 0
-  constexpr int NP = PER == 1 ? 16 : 4;  // partials the all-at-once path takes
+  constexpr int NP = PER == 1 ? 32 : 4;  // partials the all-at-once path takes
   if (np <= NP) {
     // Every load of the lane's outputs issued before any is used.
     float2 ml[PER][NP];
@@ -1093,19 +1093,13 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
     }
     return;
   }
-  constexpr int U = 8;  // partials whose loads are issued together
+  // More partials: batches of U whose loads are issued together, merged in
+  // one pass (the running maximum rescales what is summed so far).
+  constexpr int U = 16;
   for (int k = 0; k < PER; ++k) {
     const int i = elem(k), hh = i / D, d = i - hh * D;
     const size_t base = base0 + hh;
     float M = -INFINITY, sl = 0.f, so = 0.f;
-    for (int w0 = 0; w0 < np; w0 += U) {
-      float mv[U];
-#pragma unroll
-      for (int j = 0; j < U; ++j) mv[j] = w0 + j < np ? a.ws_ml[(base + (size_t)(w0 + j) * G) * 2] : -INFINITY;
-#pragma unroll
-      for (int j = 0; j < U; ++j) M = fmaxf(M, mv[j]);
-    }
-    const float Ms = M == -INFINITY ? 0.f : M;
     for (int w0 = 0; w0 < np; w0 += U) {
       float2 ml[U];
       float ov[U];
@@ -1116,12 +1110,20 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
         ml[j] = ok ? *reinterpret_cast<const float2*>(a.ws_ml + slot * 2) : make_float2(-INFINITY, 0.f);
         ov[j] = ok ? a.ws_o[slot * D + d] : 0.f;
       }
+      float Mn = M;
+#pragma unroll
+      for (int j = 0; j < U; ++j) Mn = fmaxf(Mn, ml[j].x);
+      const float Ms = Mn == -INFINITY ? 0.f : Mn;
+      const float r = __builtin_amdgcn_exp2f(M - Ms);
+      sl *= r;
+      so *= r;
 #pragma unroll
       for (int j = 0; j < U; ++j) {
         const float f = __builtin_amdgcn_exp2f(ml[j].x - Ms);
         sl = __builtin_fmaf(f, ml[j].y, sl);
         so = __builtin_fmaf(f, ov[j], so);
       }
+      M = Mn;
     }
     a.out[(row0 + hh) * D + d] = sl > 0.f ? so / sl : 0.f;
     if (a.lse && d == 0) a.lse[row0 + hh] = sl > 0.f ? (M + __log2f(sl)) * kLn2 : -INFINITY;
