@@ -895,7 +895,8 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(PrefillArgs a, float sc
     const int c = j >> 2, e2 = j & 3, kh = c >> 1, sub = c & 1;
     const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kh][8 * sub + 2 * e2], scale_log2, -ms));
     const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kh][8 * sub + 2 * e2 + 1], scale_log2, -ms));
-    const uint32_t h = MP::pack(p0, p1);
+    uint32_t h = MP::pack(p0, p1);
+    asm volatile("" : "+v"(h));  // computed here, between the matrix instructions
     pk[c][e2] = h;
     l_run = __builtin_amdgcn_fdot2(as_h2(h), f16x2{(_Float16)1.f, (_Float16)1.f}, l_run, false);
   };
